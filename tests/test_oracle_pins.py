@@ -1,0 +1,259 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every check here compares the oracle with something other than itself:
+hand-worked values of the pages' formulas (tests/golden/), closed forms,
+invariants, exact arithmetic, library routines for the special cases that
+reduce to them, and brute force on tiny inputs.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from conftest import read_golden
+
+
+def bf16_bits(values):
+    return torch.tensor(values, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+# --------------------------------------------------------------------------- packing
+
+def test_pack_closed_forms(orc):
+    rows = read_golden("pack_closed_forms.txt")
+    assert len(rows) >= 8
+    for r in rows:
+        w = np.array([[int(t) for t in r["lhs"]]], dtype=np.int8)
+        want = np.array([[int(t, 16) for t in r["rhs"]]], dtype=np.uint8)
+        got = orc.pack(w)
+        assert got.tolist() == want.tolist(), (r, got)
+
+
+def test_pack_roundtrip_exhaustive_81(orc):
+    tuples = np.array(list(itertools.product([-1, 0, 1], repeat=4)), dtype=np.int8)   # 81 x 4
+    P = orc.pack(tuples)
+    assert P.shape == (81, 1)
+    assert len(set(P[:, 0].tolist())) == 81           # injective on valid tuples
+    assert np.array_equal(orc.unpack(P, 4), tuples)   # exact round trip
+    # every code field of a packed byte is 1, 2 or 3 (code 0 never produced)
+    for b in P[:, 0].tolist():
+        assert all(((b >> (2 * i)) & 3) != 0 for i in range(4))
+
+
+def test_pack_roundtrip_random_and_size(orc):
+    W = synth.ternary_weights(37, 96, seed=11)
+    P = orc.pack(W)
+    assert P.shape == (37, 24)
+    assert P.nbytes * 8 == W.size * 2            # 2 bits per weight: 8x smaller than bf16
+    assert np.array_equal(orc.unpack(P, 96), W)
+
+
+def test_decode_of_unused_code_is_minus_two(orc):
+    # reading: decode is w = code - 2 for every code, so 0b00 gives -2
+    P = np.array([[0x00, 0xE4]], dtype=np.uint8)   # 0xE4 = codes 0,1,2,3 from low bits
+    assert orc.unpack(P, 8).tolist() == [[-2, -2, -2, -2, -2, -1, 0, 1]]
+
+
+def test_pack_rejects_bad_input(orc):
+    with pytest.raises(orc.OracleError):
+        orc.pack(np.zeros((2, 6), dtype=np.int8))          # K % 4 != 0
+    with pytest.raises(orc.OracleError):
+        orc.pack(np.array([[0, 2, 0, 0]], dtype=np.int8))  # value outside {-1,0,1}
+    with pytest.raises(orc.OracleError):
+        orc.pack(np.array([[-2, 0, 0, 0]], dtype=np.int8))
+
+
+# --------------------------------------------------------------------------- bf16
+
+def test_bf16_rounding_matches_torch(orc):
+    g = synth.rng(5)
+    vals = np.concatenate([
+        g.standard_normal(2000).astype(np.float32) * np.float32(1000.0),
+        np.array([257.0, 259.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, -257.0, 0.0, -0.0, 1e-30, 3.0e38],
+                 dtype=np.float32),
+    ])
+    want = bf16_bits(vals)
+    got = np.array([orc.bf16_from_f32(v) for v in vals], dtype=np.uint16)
+    assert np.array_equal(got, want)
+    for h in [0x3F80, 0xC284, 0x33A9, 0x7F7F, 0x0001]:
+        assert np.float32(orc.f32_from_bf16(h)) == synth.bf16_bits_to_f32(np.array([h]))[0]
+
+
+# --------------------------------------------------------------------------- quantisation
+
+def test_quantize_golden_vectors(orc):
+    rows = read_golden("quantize_vectors.txt")
+    assert len(rows) >= 5
+    for r in rows:
+        x = bf16_bits([float(t) for t in r["x"]])
+        # the fixture values are exactly representable in bf16
+        assert np.array_equal(synth.bf16_bits_to_f32(x), np.array([float(t) for t in r["x"]], dtype=np.float32))
+        q, sa = orc.quantize(x[None, :])
+        assert q[0].tolist() == [int(t) for t in r["q"]], r
+        assert int(sa[0]) == int(r["scale_bf16"][0], 16), (r, hex(sa[0]))
+
+
+def _rows_for_quant_checks():
+    a = synth.activations_bf16(48, 2560, seed=21)
+    b = synth.activations_bf16(16, 4096, seed=22, outlier_frac=0.01)
+    tiny = bf16_bits(np.array([[1e-7, -3e-8, 0.0, 2e-6]], dtype=np.float32))   # absmax below eps
+    return [a, b, tiny]
+
+
+def test_quantize_absmax_maps_to_127_and_range(orc):
+    for x in _rows_for_quant_checks()[:2]:
+        q, _ = orc.quantize(x)
+        xf = synth.bf16_bits_to_f32(x)
+        am = np.argmax(np.abs(xf), axis=1)
+        assert np.all(np.abs(q[np.arange(len(q)), am]) == 127)
+        assert np.all(np.sign(q[np.arange(len(q)), am]) == np.sign(xf[np.arange(len(q)), am]))
+        assert q.min() >= -127 and q.max() <= 127
+
+
+def test_quantize_double_division_identity(orc):
+    # fp32(x / s) == fp32((double)x / (double)s): double rounding is harmless for a
+    # quotient of two binary32 numbers (53 >= 2*24 + 2), so this is an independent
+    # route to the same IEEE quotient.  s itself: fp32(absmax / 127) computed the
+    # same way, eps = fp32(1e-5).
+    for x in _rows_for_quant_checks():
+        q, sa = orc.quantize(x)
+        xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+        a = np.max(np.abs(xf), axis=1)
+        a = np.maximum(a, np.float64(np.float32(1e-5)))
+        s = (a / 127.0).astype(np.float32).astype(np.float64)
+        y = (xf / s[:, None]).astype(np.float32)
+        want = np.clip(np.rint(y), -127, 127).astype(np.int8)   # numpy rint: half to even
+        assert np.array_equal(q, want)
+        assert np.array_equal(sa, bf16_bits(s.astype(np.float32)))
+
+
+def test_quantize_symmetry_and_power_of_two_scaling(orc):
+    x = synth.activations_bf16(8, 512, seed=23)
+    q, sa = orc.quantize(x)
+    qn, san = orc.quantize(x ^ np.uint16(0x8000))            # negate every element
+    assert np.array_equal(qn, -q) and np.array_equal(san, sa)
+    x4 = bf16_bits(synth.bf16_bits_to_f32(x) * np.float32(4.0))   # exact
+    q4, sa4 = orc.quantize(x4)
+    assert np.array_equal(q4, q)
+    assert np.array_equal(synth.bf16_bits_to_f32(sa4), synth.bf16_bits_to_f32(sa) * np.float32(4.0))
+
+
+def test_quantize_rows_independent(orc):
+    x = synth.activations_bf16(6, 256, seed=24)
+    q, sa = orc.quantize(x)
+    for m in range(6):
+        qm, sam = orc.quantize(x[m:m + 1])
+        assert np.array_equal(qm[0], q[m]) and sam[0] == sa[m]
+
+
+# --------------------------------------------------------------------------- contraction
+
+def test_gemm_hand_examples(orc):
+    rows = read_golden("gemm_hand.txt")
+    assert len(rows) >= 6
+    for r in rows:
+        q = np.array([[int(t) for t in r["q"]]], dtype=np.int8)
+        w = np.array([[int(t) for t in r["w"]]], dtype=np.int8)
+        acc = orc.gemm_i32(q, orc.pack(w))
+        assert int(acc[0, 0]) == int(r["acc"][0]), r
+
+
+def test_gemm_brute_force_tiny(orc):
+    # int64 dense product of the unpacked ternary matrix, for every small shape
+    seed = 100
+    for M in range(1, 6):
+        for N in range(1, 10):
+            for K in range(4, 68, 4):
+                seed += 1
+                W = synth.ternary_weights(N, K, seed)
+                q = synth.random_int8((M, K), seed + 7)
+                want = q.astype(np.int64) @ W.astype(np.int64).T
+                got = orc.gemm_i32(q, orc.pack(W))
+                assert np.array_equal(got, want), (M, N, K)
+
+
+def test_gemm_exhaustive_rows_k4_k8(orc):
+    for K, seed in ((4, 7), (8, 8)):
+        W = np.array(list(itertools.product([-1, 0, 1], repeat=K)), dtype=np.int8)   # 3^K rows
+        q = synth.random_int8((3, K), seed)
+        want = q.astype(np.int64) @ W.astype(np.int64).T
+        assert np.array_equal(orc.gemm_i32(q, orc.pack(W)), want)
+
+
+def test_gemm_closed_forms(orc):
+    q = synth.random_int8((5, 256), 31)
+    rowsum = q.astype(np.int64).sum(axis=1)
+    for val, expect in ((1, rowsum), (-1, -rowsum), (0, 0 * rowsum)):
+        W = np.full((7, 256), val, dtype=np.int8)
+        acc = orc.gemm_i32(q, orc.pack(W))
+        assert np.array_equal(acc, np.repeat(expect[:, None], 7, axis=1))
+
+
+def test_gemm_invariants(orc):
+    W = synth.ternary_weights(19, 320, seed=41)
+    q = synth.random_int8((4, 320), 42)
+    acc = orc.gemm_i32(q, orc.pack(W))
+    perm = synth.rng(43).permutation(320)
+    assert np.array_equal(orc.gemm_i32(q[:, perm], orc.pack(W[:, perm])), acc)   # permute K consistently
+    assert np.array_equal(orc.gemm_i32(q, orc.pack(-W)), -acc)
+    assert np.array_equal(orc.gemm_i32(-q, orc.pack(W)), -acc)
+    assert np.abs(acc).max() <= 127 * 320
+    # transposing the roles: row m of acc only depends on q[m], column n only on W[n]
+    assert np.array_equal(orc.gemm_i32(q[2:3], orc.pack(W[5:9])), acc[2:3, 5:9])
+
+
+# --------------------------------------------------------------------------- epilogue
+
+def test_epilogue_golden(orc):
+    rows = read_golden("epilogue_cases.txt")
+    assert len(rows) >= 8
+    for r in rows:
+        got = orc.epilogue_one(int(r["acc"][0]), int(r["sa"][0], 16), int(r["sw"][0], 16))
+        assert got == int(r["out"][0], 16), (r, hex(got))
+
+
+def test_epilogue_exact_product_identity(orc):
+    # (double)acc * (double)sa * (double)sw is exact in double (24 + 8 + 8 bits), so its
+    # rounding to fp32 is the single fp32 rounding of the exact product, which the
+    # epilogue must reproduce before its bf16 rounding.
+    g = synth.rng(51)
+    acc = g.integers(-(1 << 23), 1 << 23, size=4000).astype(np.int32)
+    acc[:50] = g.integers(-300, 300, size=50)
+    sa = bf16_bits(g.uniform(1e-3, 0.1, size=4000).astype(np.float32))
+    sw = bf16_bits(g.uniform(1e-3, 0.05, size=4000).astype(np.float32))
+    exact = acc.astype(np.float64) * synth.bf16_bits_to_f32(sa).astype(np.float64) \
+        * synth.bf16_bits_to_f32(sw).astype(np.float64)
+    want = bf16_bits(exact.astype(np.float32))
+    got = orc.epilogue(acc[None, :], sa[:1], sw)[0]   # one row: sa broadcast
+    got_rows = np.array([orc.epilogue_one(int(a), int(s1), int(s2)) for a, s1, s2 in zip(acc, sa, sw)],
+                        dtype=np.uint16)
+    assert np.array_equal(got_rows, want)
+    exact0 = acc.astype(np.float64) * np.float64(synth.bf16_bits_to_f32(sa[:1])[0]) \
+        * synth.bf16_bits_to_f32(sw).astype(np.float64)
+    assert np.array_equal(got, bf16_bits(exact0.astype(np.float32)))
+
+
+# --------------------------------------------------------------------------- whole layer
+
+def test_linear_is_composition_and_k8_example(orc):
+    x = bf16_bits([127, 2.5, -2.5, 1.5, -0.5, 0.5, -127, 64])[None, :]
+    W = np.array([[1] * 8, [-1] * 8, [0] * 8, [1, -1, 0, 1, -1, 0, -1, 1]], dtype=np.int8)
+    sw = np.full((4,), 0x3F80, dtype=np.uint16)
+    r = orc.linear(x, orc.pack(W), sw)
+    assert r["acc"].tolist() == [[66, -66, 0, 318]]
+    assert r["out"].tolist() == [[0x4284, 0xC284, 0x0000, 0x439F]]
+    # on a random problem: linear == epilogue(gemm(quantize))
+    x = synth.activations_bf16(5, 384, seed=61)
+    W = synth.ternary_weights(33, 384, seed=62)
+    P = orc.pack(W)
+    sw = synth.row_scales_bf16(33, seed=63)
+    r = orc.linear(x, P, sw)
+    q, sa = orc.quantize(x)
+    acc = orc.gemm_i32(q, P)
+    assert np.array_equal(r["q"], q) and np.array_equal(r["scale_act"], sa) and np.array_equal(r["acc"], acc)
+    assert np.array_equal(r["out"], orc.epilogue(acc, sa, sw))
+    for m, n in ((0, 0), (4, 32), (2, 17)):
+        o, a = orc.linear_one(q[m], sa[m], P, sw, n)
+        assert o == r["out"][m, n] and a == r["acc"][m, n]
