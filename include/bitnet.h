@@ -1,0 +1,169 @@
+/*
+ * bitnet.h -- C ABI of the MI355X (gfx950) W1.58A8 linear layer.
+ *
+ * The layer is BitNet b1.58's ternary-weight x INT8-activation matmul as
+ * described in "phanerozoic/bitnet-cpu v1, torch-ext/bitnet_cpu/__init__.py"
+ * (module docstring and the functions pack_weights, quantize_activation,
+ * bitnet_gemm, bitnet_gemv_fused and bitnet_linear) and in
+ * "kernels-community/README discussion #1 (bitnet-tc kernel request)"
+ * (request post: 2-bit packing, per-token INT8 activations, a batched matrix
+ * unit path and a fused decode path; numbers post: int32 accumulation).
+ *
+ * Conventions for every call:
+ *   - All matrices are row-major and dense (leading stride = row length).
+ *   - bf16 values travel as their uint16_t bit patterns.
+ *   - Shapes: x / x_int8 are [M][K]; packed weights are [N][K/4]; outputs are
+ *     [M][N]; scale_act is [M]; scale_wt is [N].
+ *   - Buffers are owned by the caller.  The library never allocates, frees or
+ *     synchronises device memory, and keeps no state besides a cached
+ *     per-device architecture check.
+ *   - Except bitnet_pack_weights (host memory), every pointer is device memory
+ *     and every call is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and returns without waiting.  Faults during execution surface at
+ *     the caller's next synchronisation, as for any stream-ordered work.
+ *   - M == 0 or N == 0 is a successful no-op.  Otherwise K must satisfy
+ *     0 < K <= BITNET_MAX_K and K % 4 == 0 (BITNET_ERR_SHAPE if not).  The
+ *     bound keeps |acc| <= 127 * K below 2^24 so the epilogue's int -> fp32
+ *     conversion is exact.
+ *   - Any shape in range is correct.  The fast kernels additionally want
+ *     K % 64 == 0 and 16-byte aligned base pointers; other shapes take
+ *     slower, plain kernels with the same results.
+ *   - Calls on distinct output buffers are independent and may overlap on
+ *     different streams.
+ */
+#ifndef BITNET_H
+#define BITNET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITNET_MAX_K 131072
+/* bitnet_gemv_fused takes M in [0, BITNET_FUSED_MAX_M]; bitnet_linear sends
+ * M <= BITNET_FUSED_MAX_M to the fused path and larger M to quantise + GEMM. */
+#define BITNET_FUSED_MAX_M 15
+
+typedef enum bitnet_status {
+    BITNET_OK = 0,
+    BITNET_ERR_NULL = 1,      /* a required pointer is NULL                        */
+    BITNET_ERR_SHAPE = 2,     /* negative size, K <= 0, K % 4 != 0, K > MAX_K,
+                                 or M > BITNET_FUSED_MAX_M for the fused call       */
+    BITNET_ERR_VALUE = 3,     /* a weight outside {-1, 0, +1} given to the packer   */
+    BITNET_ERR_WORKSPACE = 4, /* workspace smaller than bitnet_linear_workspace_bytes */
+    BITNET_ERR_DEVICE = 5,    /* current device is not gfx950, or no device         */
+    BITNET_ERR_LAUNCH = 6     /* the HIP runtime rejected a kernel launch           */
+} bitnet_status;
+
+/* A hipStream_t, kept opaque so that this header needs no HIP headers. */
+typedef void* bitnet_stream_t;
+
+/*
+ * Pack ternary weights, 2 bits each, 4 per byte (pack_weights of bitnet-cpu):
+ * code = w + 2 (-1 -> 1, 0 -> 2, +1 -> 3) and
+ *   w_packed[n][j] = code(w[n][4j]) | code(w[n][4j+1]) << 2
+ *                  | code(w[n][4j+2]) << 4 | code(w[n][4j+3]) << 6.
+ * HOST memory: w is int8 [N][K], w_packed is uint8 [N][K/4] (written).
+ * Errors: NULL pointers (if N*K > 0), N < 0, K < 0, K % 4 != 0 -> SHAPE;
+ * a value outside {-1,0,1} -> VALUE (w_packed contents are then unspecified).
+ * Runs on the calling thread; no device is touched.
+ */
+bitnet_status bitnet_pack_weights(uint8_t* w_packed, const int8_t* w, int64_t N, int64_t K);
+
+/*
+ * Per-token absmax INT8 quantisation (quantize_activation of bitnet-cpu), in
+ * fp32 on the widened bf16 input, for each row m:
+ *   a = max(max_k |x[m][k]|, 1e-5f);   s = a / 127.0f  (IEEE fp32 division)
+ *   x_int8[m][k] = clamp(round_half_even(x[m][k] / s), -127, 127)
+ *   scale_act[m] = bf16_round_nearest_even(s)
+ * x: bf16 [M][K] (read); x_int8: int8 [M][K] (written); scale_act: bf16 [M]
+ * (written).  Device pointers, enqueued on stream.
+ */
+bitnet_status bitnet_quantize_act(int8_t* x_int8, uint16_t* scale_act, const uint16_t* x, int64_t M, int64_t K,
+                                  bitnet_stream_t stream);
+
+/*
+ * Ternary x int8 matmul with the scale epilogue (bitnet_gemm of bitnet-cpu):
+ *   acc[m][n] = sum_k w[n][k] * x_int8[m][k]            (exact, int32)
+ *   out[m][n] = bf16_rne( fp32( (float)acc * fp32( (float)scale_act[m] * (float)scale_wt[n] ) ) )
+ * where w[n][k] = code - 2 decoded from w_packed.  out: bf16 [M][N] (written);
+ * x_int8: int8 [M][K]; w_packed: uint8 [N][K/4]; scale_act: bf16 [M];
+ * scale_wt: bf16 [N].  Device pointers, enqueued on stream.  Any M >= 0.
+ */
+bitnet_status bitnet_gemm(uint16_t* out, const int8_t* x_int8, const uint8_t* w_packed, const uint16_t* scale_act,
+                          const uint16_t* scale_wt, int64_t M, int64_t N, int64_t K, bitnet_stream_t stream);
+
+/*
+ * Fused quantise + ternary GEMV for the decode case (bitnet_gemv_fused of
+ * bitnet-cpu; the fused decode path of the bitnet-tc request).  Computes, for
+ * 0 <= M <= BITNET_FUSED_MAX_M, exactly the composition
+ *   bitnet_quantize_act(x) followed by bitnet_gemm,
+ * bit for bit, without writing the int8 activations anywhere.
+ * out: bf16 [M][N] (written); x: bf16 [M][K]; w_packed: uint8 [N][K/4];
+ * scale_wt: bf16 [N].  Device pointers, enqueued on stream.
+ * Errors: M > BITNET_FUSED_MAX_M -> SHAPE.
+ */
+bitnet_status bitnet_gemv_fused(uint16_t* out, const uint16_t* x, const uint8_t* w_packed, const uint16_t* scale_wt,
+                                int64_t M, int64_t N, int64_t K, bitnet_stream_t stream);
+
+/*
+ * Device workspace (bytes) that bitnet_linear needs for an [M][K] input:
+ * 0 when M <= BITNET_FUSED_MAX_M, else room for x_int8 [M][K] and
+ * scale_act [M] (each rounded up to 256 bytes).  Returns 0 for invalid sizes.
+ */
+size_t bitnet_linear_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * One-shot BitLinear forward (bitnet_linear of bitnet-cpu): dispatches on M.
+ * M <= BITNET_FUSED_MAX_M -> bitnet_gemv_fused; otherwise bitnet_quantize_act
+ * into the workspace, then bitnet_gemm.  The result is bit-identical on both
+ * paths.  out: bf16 [M][N]; x: bf16 [M][K]; w_packed: uint8 [N][K/4];
+ * scale_wt: bf16 [N]; workspace: device memory of workspace_bytes bytes, 256-byte
+ * aligned, used as scratch (may be NULL when bitnet_linear_workspace_bytes is 0).
+ * Errors: workspace_bytes too small -> WORKSPACE.
+ */
+bitnet_status bitnet_linear(uint16_t* out, const uint16_t* x, const uint8_t* w_packed, const uint16_t* scale_wt,
+                            int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                            bitnet_stream_t stream);
+
+/*
+ * Debug: the raw int32 accumulators of the batched path,
+ *   acc[m][n] = sum_k w[n][k] * x_int8[m][k],
+ * computed by the same matrix-core kernel as bitnet_gemm (its int32 output
+ * variant).  acc: int32 [M][N] (written).  Device pointers, enqueued on stream.
+ */
+bitnet_status bitnet_gemm_i32(int32_t* acc, const int8_t* x_int8, const uint8_t* w_packed, int64_t M, int64_t N,
+                              int64_t K, bitnet_stream_t stream);
+
+/*
+ * Debug: the fused decode path's intermediate results, computed by the same
+ * fused kernel as bitnet_gemv_fused (its int32 output variant):
+ * acc: int32 [M][N], the exact sum_k w[n][k] * q[m][k] of the in-kernel
+ * quantised rows q; scale_act: bf16 [M], the in-kernel scales.
+ * 0 <= M <= BITNET_FUSED_MAX_M.  Device pointers, enqueued on stream.
+ */
+bitnet_status bitnet_gemv_fused_i32(int32_t* acc, uint16_t* scale_act, const uint16_t* x, const uint8_t* w_packed,
+                                    int64_t M, int64_t N, int64_t K, bitnet_stream_t stream);
+
+/*
+ * Debug: the scale epilogue on its own,
+ *   out[m][n] = bf16_rne( fp32( (float)acc[m][n] * fp32( (float)scale_act[m] * (float)scale_wt[n] ) ) ).
+ * out: bf16 [M][N] (written); acc: int32 [M][N]; scale_act: bf16 [M];
+ * scale_wt: bf16 [N].  Device pointers, enqueued on stream.  No K involved.
+ */
+bitnet_status bitnet_scale_epilogue(uint16_t* out, const int32_t* acc, const uint16_t* scale_act,
+                                    const uint16_t* scale_wt, int64_t M, int64_t N, bitnet_stream_t stream);
+
+/* A static, human-readable name for a status code. */
+const char* bitnet_status_string(bitnet_status status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int bitnet_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITNET_H */

@@ -1,0 +1,237 @@
+"""Python binding of the gfx950 W1.58A8 linear-layer library (include/bitnet.h).
+
+Argument marshalling only: every function checks dtypes/shapes/devices of the
+torch tensors it is given, allocates outputs with torch (device memory is the
+only thing torch is used for, plus the current HIP stream), and calls the C ABI
+in libbitnet_hip.so through ctypes.  All arithmetic runs in the HIP kernels.
+
+The names follow the API of "phanerozoic/bitnet-cpu v1,
+torch-ext/bitnet_cpu/__init__.py": pack_weights, quantize_activation,
+bitnet_gemm, bitnet_gemv_fused, bitnet_linear; plus the int32 debug entry
+points bitnet_gemm_i32 / bitnet_gemv_fused_i32 and bitnet_scale_epilogue.
+
+There is no fallback: if the library is not built, or the device is not an
+MI355X (gfx950), calls raise.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "BitnetError", "load_library", "library_path", "pack_weights", "quantize_activation", "bitnet_gemm",
+    "bitnet_gemv_fused", "bitnet_linear", "bitnet_gemm_i32", "bitnet_gemv_fused_i32", "bitnet_scale_epilogue",
+    "linear_workspace_bytes", "FUSED_MAX_M", "MAX_K", "STATUS",
+]
+
+FUSED_MAX_M = 15
+MAX_K = 131072
+
+STATUS = {
+    0: "BITNET_OK", 1: "BITNET_ERR_NULL", 2: "BITNET_ERR_SHAPE", 3: "BITNET_ERR_VALUE",
+    4: "BITNET_ERR_WORKSPACE", 5: "BITNET_ERR_DEVICE", 6: "BITNET_ERR_LAUNCH",
+}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libbitnet_hip.so")
+_LIB = None
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+_st = ctypes.c_int
+
+
+class BitnetError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({_status_string(status)})")
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libbitnet_hip.so; raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with ternary_int8_gemm_amd/build.py (or __graft_entry__.build())")
+    lib = ctypes.CDLL(_LIB_PATH)
+    sig = {
+        "bitnet_pack_weights": [_p, _p, _i64, _i64],
+        "bitnet_quantize_act": [_p, _p, _p, _i64, _i64, _p],
+        "bitnet_gemm": [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p],
+        "bitnet_gemv_fused": [_p, _p, _p, _p, _i64, _i64, _i64, _p],
+        "bitnet_linear": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _sz, _p],
+        "bitnet_gemm_i32": [_p, _p, _p, _i64, _i64, _i64, _p],
+        "bitnet_gemv_fused_i32": [_p, _p, _p, _p, _i64, _i64, _i64, _p],
+        "bitnet_scale_epilogue": [_p, _p, _p, _p, _i64, _i64, _p],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = _st
+    lib.bitnet_linear_workspace_bytes.argtypes = [_i64, _i64]
+    lib.bitnet_linear_workspace_bytes.restype = _sz
+    lib.bitnet_status_string.argtypes = [_st]
+    lib.bitnet_status_string.restype = ctypes.c_char_p
+    lib.bitnet_version.argtypes = []
+    lib.bitnet_version.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def _status_string(status):
+    try:
+        return load_library().bitnet_status_string(int(status)).decode()
+    except Exception:  # noqa: BLE001 - only used to format an error
+        return "?"
+
+
+def _check(status, what):
+    if status != 0:
+        raise BitnetError(status, what)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, dtype, name, device=True):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device and t.device.type != "cuda":
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ----------------------------------------------------------------------------- host packing
+
+def pack_weights(W):
+    """int8 W[N, K] in {-1, 0, +1} (host tensor) -> uint8 [N, K/4] (host)."""
+    _need(W, torch.int8, "W", device=False)
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D")
+    N, K = W.shape
+    out = torch.empty((N, K // 4), dtype=torch.uint8)
+    _check(load_library().bitnet_pack_weights(_ptr(out), _ptr(W), N, K), "bitnet_pack_weights")
+    return out
+
+
+# ----------------------------------------------------------------------------- device calls
+
+def quantize_activation(x, out=None, scale=None):
+    """bf16 x[..., K] -> (int8 [M, K], bf16 scale [M]), M = prod of leading dims."""
+    _need(x, torch.bfloat16, "x")
+    K = x.shape[-1]
+    M = x.numel() // K if K else 0
+    x2 = x.reshape(M, K)
+    q = out if out is not None else torch.empty((M, K), dtype=torch.int8, device=x.device)
+    s = scale if scale is not None else torch.empty((M,), dtype=torch.bfloat16, device=x.device)
+    _check(load_library().bitnet_quantize_act(_ptr(q), _ptr(s), _ptr(x2), M, K, _stream(x)), "bitnet_quantize_act")
+    return q, s
+
+
+def bitnet_gemm(x_int8, w_packed, scale_act, scale_wt, out=None):
+    """int8 x[M, K] x packed w[N, K/4] -> bf16 [M, N] with the scale epilogue."""
+    _need(x_int8, torch.int8, "x_int8")
+    _need(w_packed, torch.uint8, "w_packed")
+    _need(scale_act, torch.bfloat16, "scale_act")
+    _need(scale_wt, torch.bfloat16, "scale_wt")
+    M, K = x_int8.shape
+    N = w_packed.shape[0]
+    if w_packed.shape[1] * 4 != K or scale_act.numel() != M or scale_wt.numel() != N:
+        raise ValueError("bitnet_gemm: inconsistent shapes")
+    o = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x_int8.device)
+    _check(load_library().bitnet_gemm(_ptr(o), _ptr(x_int8), _ptr(w_packed), _ptr(scale_act), _ptr(scale_wt),
+                                      M, N, K, _stream(x_int8)), "bitnet_gemm")
+    return o
+
+
+def bitnet_gemv_fused(x, w_packed, scale_wt, out=None):
+    """Fused quantise + GEMV for M <= 15: bf16 x[M, K] -> bf16 [M, N]."""
+    _need(x, torch.bfloat16, "x")
+    _need(w_packed, torch.uint8, "w_packed")
+    _need(scale_wt, torch.bfloat16, "scale_wt")
+    M, K = x.shape
+    N = w_packed.shape[0]
+    if w_packed.shape[1] * 4 != K or scale_wt.numel() != N:
+        raise ValueError("bitnet_gemv_fused: inconsistent shapes")
+    o = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(load_library().bitnet_gemv_fused(_ptr(o), _ptr(x), _ptr(w_packed), _ptr(scale_wt), M, N, K, _stream(x)),
+           "bitnet_gemv_fused")
+    return o
+
+
+def linear_workspace_bytes(M, K):
+    return int(load_library().bitnet_linear_workspace_bytes(M, K))
+
+
+def bitnet_linear(x, w_packed, scale_wt, out=None, workspace=None):
+    """One-shot BitLinear forward: bf16 x[..., K] -> bf16 [..., N]; dispatches on M."""
+    _need(x, torch.bfloat16, "x")
+    _need(w_packed, torch.uint8, "w_packed")
+    _need(scale_wt, torch.bfloat16, "scale_wt")
+    K = x.shape[-1]
+    M = x.numel() // K if K else 0
+    N = w_packed.shape[0]
+    if w_packed.shape[1] * 4 != K or scale_wt.numel() != N:
+        raise ValueError("bitnet_linear: inconsistent shapes")
+    ws_bytes = linear_workspace_bytes(M, K)
+    ws = workspace
+    if ws is None and ws_bytes > 0:
+        ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=x.device)
+    o = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(load_library().bitnet_linear(_ptr(o), _ptr(x), _ptr(w_packed), _ptr(scale_wt), M, N, K, _ptr(ws),
+                                        ws.numel() if ws is not None else 0, _stream(x)), "bitnet_linear")
+    return o.view(*x.shape[:-1], N)
+
+
+def bitnet_gemm_i32(x_int8, w_packed, out=None):
+    """Debug: int32 accumulators of the batched path."""
+    _need(x_int8, torch.int8, "x_int8")
+    _need(w_packed, torch.uint8, "w_packed")
+    M, K = x_int8.shape
+    N = w_packed.shape[0]
+    if w_packed.shape[1] * 4 != K:
+        raise ValueError("bitnet_gemm_i32: inconsistent shapes")
+    o = out if out is not None else torch.empty((M, N), dtype=torch.int32, device=x_int8.device)
+    _check(load_library().bitnet_gemm_i32(_ptr(o), _ptr(x_int8), _ptr(w_packed), M, N, K, _stream(x_int8)),
+           "bitnet_gemm_i32")
+    return o
+
+
+def bitnet_gemv_fused_i32(x, w_packed):
+    """Debug: (int32 accumulators [M, N], bf16 scales [M]) of the fused path."""
+    _need(x, torch.bfloat16, "x")
+    _need(w_packed, torch.uint8, "w_packed")
+    M, K = x.shape
+    N = w_packed.shape[0]
+    if w_packed.shape[1] * 4 != K:
+        raise ValueError("bitnet_gemv_fused_i32: inconsistent shapes")
+    acc = torch.empty((M, N), dtype=torch.int32, device=x.device)
+    sa = torch.empty((M,), dtype=torch.bfloat16, device=x.device)
+    _check(load_library().bitnet_gemv_fused_i32(_ptr(acc), _ptr(sa), _ptr(x), _ptr(w_packed), M, N, K, _stream(x)),
+           "bitnet_gemv_fused_i32")
+    return acc, sa
+
+
+def bitnet_scale_epilogue(acc, scale_act, scale_wt, out=None):
+    """Debug: the scale epilogue on given int32 accumulators -> bf16."""
+    _need(acc, torch.int32, "acc")
+    _need(scale_act, torch.bfloat16, "scale_act")
+    _need(scale_wt, torch.bfloat16, "scale_wt")
+    M, N = acc.shape
+    o = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=acc.device)
+    _check(load_library().bitnet_scale_epilogue(_ptr(o), _ptr(acc), _ptr(scale_act), _ptr(scale_wt), M, N,
+                                                _stream(acc)), "bitnet_scale_epilogue")
+    return o

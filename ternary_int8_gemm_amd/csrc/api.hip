@@ -1,0 +1,173 @@
+// api.hip -- the exported C ABI (include/bitnet.h): argument checks, the
+// gfx950 device check, dispatch by M, and kernel launches.  No entry point
+// allocates, frees or synchronises; device work is enqueued on the caller's
+// stream.
+#include <atomic>
+#include <cstring>
+
+#include "../../include/bitnet.h"
+#include "launch.h"
+
+#define BITNET_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using bitnet::launch_epilogue;
+using bitnet::launch_gemm;
+using bitnet::launch_gemv_fused;
+using bitnet::launch_quantize;
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+bitnet_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return BITNET_ERR_DEVICE;
+    if (dev >= kMaxDevices) return BITNET_ERR_DEVICE;
+    int state = g_arch_ok[dev].load(std::memory_order_acquire);
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BITNET_ERR_DEVICE;
+        state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_arch_ok[dev].store(state, std::memory_order_release);
+    }
+    return state == 1 ? BITNET_OK : BITNET_ERR_DEVICE;
+}
+
+bitnet_status check_k(int64_t K) {
+    if (K <= 0 || K % 4 != 0 || K > BITNET_MAX_K) return BITNET_ERR_SHAPE;
+    return BITNET_OK;
+}
+
+bitnet_status launched(hipError_t e) { return e == hipSuccess ? BITNET_OK : BITNET_ERR_LAUNCH; }
+
+// Sizes that fit the kernels' 32-bit index arithmetic.
+bool sizes_ok(int64_t M, int64_t N) { return M >= 0 && N >= 0 && M <= (int64_t)1 << 30 && N <= (int64_t)1 << 30; }
+
+size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace
+
+BITNET_API int bitnet_version(void) { return 100; }
+
+BITNET_API const char* bitnet_status_string(bitnet_status status) {
+    switch (status) {
+        case BITNET_OK: return "ok";
+        case BITNET_ERR_NULL: return "null pointer argument";
+        case BITNET_ERR_SHAPE: return "invalid shape";
+        case BITNET_ERR_VALUE: return "weight value outside {-1, 0, +1}";
+        case BITNET_ERR_WORKSPACE: return "workspace too small";
+        case BITNET_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
+        case BITNET_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+BITNET_API bitnet_status bitnet_pack_weights(uint8_t* w_packed, const int8_t* w, int64_t N, int64_t K) {
+    if (N < 0 || K < 0 || K % 4 != 0) return BITNET_ERR_SHAPE;
+    if (N == 0 || K == 0) return BITNET_OK;
+    if (w_packed == nullptr || w == nullptr) return BITNET_ERR_NULL;
+    const int64_t nbytes = N * (K / 4);
+    // Four weights per byte; the code of weight e of the byte (w + 2) sits in
+    // bits 2e..2e+1.  A lookup on (w + 1) in {0, 1, 2} is both the range check
+    // and the encoding.
+    for (int64_t i = 0; i < nbytes; ++i) {
+        const int8_t* q = w + 4 * i;
+        uint32_t byte = 0;
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t u = (uint32_t)((int32_t)q[e] + 1);
+            if (u > 2u) return BITNET_ERR_VALUE;
+            byte |= (u + 1u) << (2 * e);
+        }
+        w_packed[i] = (uint8_t)byte;
+    }
+    return BITNET_OK;
+}
+
+BITNET_API bitnet_status bitnet_quantize_act(int8_t* x_int8, uint16_t* scale_act, const uint16_t* x, int64_t M,
+                                             int64_t K, bitnet_stream_t stream) {
+    if (!sizes_ok(M, 0)) return BITNET_ERR_SHAPE;
+    if (bitnet_status st = check_k(K)) return st;
+    if (M == 0) return BITNET_OK;
+    if (!x_int8 || !scale_act || !x) return BITNET_ERR_NULL;
+    if (bitnet_status st = check_device()) return st;
+    return launched(launch_quantize(x_int8, scale_act, x, M, K, (hipStream_t)stream));
+}
+
+BITNET_API bitnet_status bitnet_gemm(uint16_t* out, const int8_t* x_int8, const uint8_t* w_packed,
+                                     const uint16_t* scale_act, const uint16_t* scale_wt, int64_t M, int64_t N,
+                                     int64_t K, bitnet_stream_t stream) {
+    if (!sizes_ok(M, N)) return BITNET_ERR_SHAPE;
+    if (bitnet_status st = check_k(K)) return st;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!out || !x_int8 || !w_packed || !scale_act || !scale_wt) return BITNET_ERR_NULL;
+    if (bitnet_status st = check_device()) return st;
+    return launched(launch_gemm(out, nullptr, x_int8, w_packed, scale_act, scale_wt, M, N, K, (hipStream_t)stream));
+}
+
+BITNET_API bitnet_status bitnet_gemm_i32(int32_t* acc, const int8_t* x_int8, const uint8_t* w_packed, int64_t M,
+                                         int64_t N, int64_t K, bitnet_stream_t stream) {
+    if (!sizes_ok(M, N)) return BITNET_ERR_SHAPE;
+    if (bitnet_status st = check_k(K)) return st;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!acc || !x_int8 || !w_packed) return BITNET_ERR_NULL;
+    if (bitnet_status st = check_device()) return st;
+    return launched(launch_gemm(nullptr, acc, x_int8, w_packed, nullptr, nullptr, M, N, K, (hipStream_t)stream));
+}
+
+BITNET_API bitnet_status bitnet_gemv_fused(uint16_t* out, const uint16_t* x, const uint8_t* w_packed,
+                                           const uint16_t* scale_wt, int64_t M, int64_t N, int64_t K,
+                                           bitnet_stream_t stream) {
+    if (!sizes_ok(M, N) || M > BITNET_FUSED_MAX_M) return BITNET_ERR_SHAPE;
+    if (bitnet_status st = check_k(K)) return st;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!out || !x || !w_packed || !scale_wt) return BITNET_ERR_NULL;
+    if (bitnet_status st = check_device()) return st;
+    return launched(launch_gemv_fused(out, nullptr, nullptr, x, w_packed, scale_wt, M, N, K, (hipStream_t)stream));
+}
+
+BITNET_API bitnet_status bitnet_gemv_fused_i32(int32_t* acc, uint16_t* scale_act, const uint16_t* x,
+                                               const uint8_t* w_packed, int64_t M, int64_t N, int64_t K,
+                                               bitnet_stream_t stream) {
+    if (!sizes_ok(M, N) || M > BITNET_FUSED_MAX_M) return BITNET_ERR_SHAPE;
+    if (bitnet_status st = check_k(K)) return st;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!acc || !scale_act || !x || !w_packed) return BITNET_ERR_NULL;
+    if (bitnet_status st = check_device()) return st;
+    return launched(launch_gemv_fused(nullptr, acc, scale_act, x, w_packed, nullptr, M, N, K, (hipStream_t)stream));
+}
+
+BITNET_API size_t bitnet_linear_workspace_bytes(int64_t M, int64_t K) {
+    if (M < 0 || K <= 0 || K % 4 != 0 || K > BITNET_MAX_K || !sizes_ok(M, 0)) return 0;
+    if (M <= BITNET_FUSED_MAX_M) return 0;
+    return round256((size_t)M * (size_t)K) + round256((size_t)M * 2);
+}
+
+BITNET_API bitnet_status bitnet_linear(uint16_t* out, const uint16_t* x, const uint8_t* w_packed,
+                                       const uint16_t* scale_wt, int64_t M, int64_t N, int64_t K, void* workspace,
+                                       size_t workspace_bytes, bitnet_stream_t stream) {
+    if (!sizes_ok(M, N)) return BITNET_ERR_SHAPE;
+    if (bitnet_status st = check_k(K)) return st;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (M <= BITNET_FUSED_MAX_M) return bitnet_gemv_fused(out, x, w_packed, scale_wt, M, N, K, stream);
+    if (!out || !x || !w_packed || !scale_wt) return BITNET_ERR_NULL;
+    const size_t need = bitnet_linear_workspace_bytes(M, K);
+    if (workspace == nullptr || workspace_bytes < need) return BITNET_ERR_WORKSPACE;
+    if (bitnet_status st = check_device()) return st;
+    int8_t* x_int8 = static_cast<int8_t*>(workspace);
+    uint16_t* scale_act = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + round256((size_t)M * K));
+    hipStream_t s = (hipStream_t)stream;
+    if (hipError_t e = launch_quantize(x_int8, scale_act, x, M, K, s)) return launched(e);
+    return launched(launch_gemm(out, nullptr, x_int8, w_packed, scale_act, scale_wt, M, N, K, s));
+}
+
+BITNET_API bitnet_status bitnet_scale_epilogue(uint16_t* out, const int32_t* acc, const uint16_t* scale_act,
+                                               const uint16_t* scale_wt, int64_t M, int64_t N,
+                                               bitnet_stream_t stream) {
+    if (!sizes_ok(M, N)) return BITNET_ERR_SHAPE;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!out || !acc || !scale_act || !scale_wt) return BITNET_ERR_NULL;
+    if (bitnet_status st = check_device()) return st;
+    return launched(launch_epilogue(out, acc, scale_act, scale_wt, M, N, (hipStream_t)stream));
+}

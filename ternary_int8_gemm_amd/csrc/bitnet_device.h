@@ -1,0 +1,148 @@
+// bitnet_device.h -- device-side building blocks shared by the gfx950 kernels.
+//
+// Everything here is written for CDNA4 (gfx950, wave64): DPP lane exchanges,
+// v_dot4 integer dot products, v_cvt_pk_bf16_f32 rounding, and the exact
+// per-token quantisation of "phanerozoic/bitnet-cpu v1,
+// torch-ext/bitnet_cpu/__init__.py" (function quantize_activation).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bitnet {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (nontemporal hint: data used once, keep it out of the caches' way).
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ----------------------------------------------------------------- bf16
+
+// bf16 bit pattern (low 16 bits of h) -> fp32, exact.
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __builtin_bit_cast(float, h << 16); }
+
+// fp32 -> bf16 bit pattern, round to nearest even (v_cvt_pk_bf16_f32 under the
+// default round-to-nearest-even mode).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
+
+// ----------------------------------------------------------------- DPP
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+constexpr int DPP_QUAD_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane i <-> 7-i within each 8 lanes
+constexpr int DPP_ROW_MIRROR = 0x140;       // lane i <-> 15-i within each 16 lanes
+
+// Sum over each aligned group of 8 lanes; every lane of the group gets the total.
+__device__ __forceinline__ int group8_sum(int v) {
+    v += dpp_mov<DPP_QUAD_XOR1>(v);
+    v += dpp_mov<DPP_QUAD_XOR2>(v);
+    v += dpp_mov<DPP_ROW_HALF_MIRROR>(v);
+    return v;
+}
+
+// Maximum over each aligned group of 16 lanes (unsigned); every lane gets it.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)dpp_mov<DPP_QUAD_XOR1>((int)v));
+    v = max(v, (uint32_t)dpp_mov<DPP_QUAD_XOR2>((int)v));
+    v = max(v, (uint32_t)dpp_mov<DPP_ROW_HALF_MIRROR>((int)v));
+    v = max(v, (uint32_t)dpp_mov<DPP_ROW_MIRROR>((int)v));
+    return v;
+}
+
+// Maximum over the whole wave; the result is wave-uniform.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = row16_max_u32(v);
+    uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(a, b), max(c, d));
+}
+
+// Sum over the whole wave; the result is wave-uniform.
+__device__ __forceinline__ int wave_sum_i32(int v) {
+    v += dpp_mov<DPP_QUAD_XOR1>(v);
+    v += dpp_mov<DPP_QUAD_XOR2>(v);
+    v += dpp_mov<DPP_ROW_HALF_MIRROR>(v);
+    v += dpp_mov<DPP_ROW_MIRROR>(v);
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+           __builtin_amdgcn_readlane(v, 48);
+}
+
+// ----------------------------------------------------------------- quantisation
+
+// |x| of a bf16 value as an unsigned integer: for non-NaN inputs the order of
+// these integers is the order of the magnitudes, so the row absmax can be taken
+// on the raw bits.  Two bf16 values per 32-bit word.
+__device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t w) { return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu); }
+
+struct QuantScale {
+    float s;  // fp32(absmax / 127): the divisor
+    float r;  // fp32(1 / s): used only for a pre-rounding estimate
+};
+
+// From the row absmax (as bf16 magnitude bits): clamp below at fp32(1e-5), then
+// the IEEE fp32 quotient by 127 (the compiler's division is correctly rounded).
+__device__ __forceinline__ QuantScale quant_scale(uint32_t absmax_bits) {
+    float a = bf16_to_f32(absmax_bits);
+    a = a < 1e-5f ? 1e-5f : a;
+    QuantScale q;
+    q.s = a / 127.0f;
+    q.r = 1.0f / q.s;
+    return q;
+}
+
+// q = clamp(round_half_even(fp32(x / s)), -127, 127), exactly.
+//
+// y = x * r is within 2^-23 + 2^-48 (relative) of x / s and |x / s| <= 127 * (1 + 2^-23),
+// so |y - fp32(x / s)| < 2.5e-5.  Rounding to an integer only depends on which
+// side of a half-integer the value falls, so unless y lies within 2^-12 of a
+// half-integer, round(y) == round(fp32(x / s)); in that rare case the correctly
+// rounded quotient is computed and used instead.
+__device__ __forceinline__ int quantize_one(float x, const QuantScale& q) {
+    float y = x * q.r;
+    float d = y - __builtin_floorf(y);
+    if (__builtin_expect(__builtin_fabsf(d - 0.5f) < 0x1p-12f, 0)) y = x / q.s;
+    float t = __builtin_rintf(y);
+    t = __builtin_fminf(__builtin_fmaxf(t, -127.0f), 127.0f);
+    return (int)t;
+}
+
+// Quantise two bf16 values held in one 32-bit word; returns them in the low
+// two bytes (low element first).
+__device__ __forceinline__ uint32_t quantize_bf16x2(uint32_t w, const QuantScale& q) {
+    int a = quantize_one(bf16_to_f32(w & 0xFFFFu), q);
+    int b = quantize_one(bf16_to_f32(w >> 16), q);
+    return ((uint32_t)a & 0xFFu) | (((uint32_t)b & 0xFFu) << 8);
+}
+
+// ----------------------------------------------------------------- epilogue
+
+// out = bf16_rne( fp32( (float)acc * fp32(sa * sw) ) ).  sa * sw is exact (two
+// bf16 significands fit in fp32), (float)acc is exact for |acc| < 2^24, so the
+// result has a single fp32 rounding followed by the bf16 rounding.  There is
+// no addition, so no contraction can change it.
+__device__ __forceinline__ uint16_t epilogue_bf16(int acc, float sa, float sw) {
+    const float scale = sa * sw;
+    const float y = (float)acc * scale;
+    return f32_to_bf16(y);
+}
+
+// ----------------------------------------------------------------- 2-bit codes
+
+// For a 32-bit word of packed weights (16 codes; byte r holds the elements
+// 4r..4r+3, element e of the byte in bits 2e..2e+1), the byte-lane masks that
+// isolate element e of every byte: (p >> 2e) & 0x03030303 gives, in byte r,
+// the code of element 4r + e.
+constexpr uint32_t CODE_MASK = 0x03030303u;
+
+}  // namespace bitnet

@@ -1,0 +1,371 @@
+// gemv.hip -- fused quantise + ternary GEMV for the decode case (K-GEMV).
+//
+// Computes bitnet_gemv_fused of "phanerozoic/bitnet-cpu v1,
+// torch-ext/bitnet_cpu/__init__.py" (the fused decode path named in the
+// request post of "kernels-community/README discussion #1 (bitnet-tc kernel
+// request)") for M <= 15 activation rows:
+//   q = quantize_activation(x)            (in-kernel, bit-identical to K-QUANT)
+//   acc[m][n] = sum_k (code[n][k] - 2) * q[m][k]     (exact int32)
+//   out[m][n] = epilogue(acc, bf16(s_m), scale_wt[n])
+//
+// The decode GEMV is bound by streaming the packed weights from HBM (2 bits per
+// weight, read once), so the design keeps every other cost off that stream:
+//
+//  * Weights.  Each wave owns 8*RB output rows.  Eight consecutive lanes share
+//    a row; in one step the eight lanes read 8 x 16 B = 128 B contiguous of that
+//    row (512 weights), so a wave instruction fetches 8 full 128-byte lines.
+//    The loads for the next step are issued before the current one is
+//    computed, and the very first loads are issued before the quantisation
+//    prologue, so HBM latency overlaps the prologue.
+//  * Unpack without a lookup.  For a 32-bit word p of codes, p & 0x03030303,
+//    p & 0x0C0C0C0C, p & 0x30303030 and (p >> 6) & 0x03030303 hold, in byte r,
+//    the code of element 4r+e times 1, 4, 16 and 1 (e = 0..3).  Each is fed to
+//    v_dot4_i32_i8 against the activations pre-permuted into the same byte
+//    order, with separate accumulators for the x4 and x16 lanes; the exact
+//    total sum(code * q) then loses 2 * sum_k q[m][k] to give sum((code-2) * q).
+//    That is 5 logic ops + 4 dot4 per 16 weights.
+//  * Activations.  Every workgroup quantises x itself (x is at most 15 rows and
+//    stays in L2) into LDS as int8, each 16-element group stored as the 4x4
+//    byte transpose the unpack needs, with the 16-byte slots of each 64-byte
+//    segment XOR-swizzled so that the eight sub-lanes of a step hit distinct
+//    LDS banks.  Long rows are processed in K-chunks that fit the LDS budget.
+//  * Reduction.  A row's eight partial sums are combined with three DPP adds
+//    (quad_perm xor 1, quad_perm xor 2, row_half_mirror).
+//
+// Shapes the fast kernel takes: K % 64 == 0 and 16-byte aligned x and w (every
+// BitNet/LLaMA projection).  Anything else goes to gemv_fused_plain, a direct
+// one-wave-per-row kernel with the same arithmetic.
+#include "bitnet_device.h"
+#include "launch.h"
+
+namespace bitnet {
+
+namespace {
+
+constexpr int GV_STEP = 512;            // weights per row per wave step (8 lanes x 64)
+constexpr int GV_LDS_BUDGET = 32768;    // bytes of quantised activations held per chunk
+
+__device__ __forceinline__ int lds_word_offset(int word) {
+    // word = 16-element group within a chunk; seg = 64-element segment
+    const int seg = word >> 2;
+    const int j = word & 3;
+    return (seg << 6) + ((j ^ ((seg >> 1) & 3)) << 4);
+}
+
+// 4x4 byte transpose: n_r holds elements 4r..4r+3; result t_e holds element e of
+// every n_r (t_e byte r = element 4r + e).
+__device__ __forceinline__ uint4 transpose4x4(uint32_t n0, uint32_t n1, uint32_t n2, uint32_t n3) {
+    const uint32_t u01lo = __builtin_amdgcn_perm(n1, n0, 0x05010400u);  // n0.b0 n1.b0 n0.b1 n1.b1
+    const uint32_t u01hi = __builtin_amdgcn_perm(n1, n0, 0x07030602u);  // n0.b2 n1.b2 n0.b3 n1.b3
+    const uint32_t u23lo = __builtin_amdgcn_perm(n3, n2, 0x05010400u);
+    const uint32_t u23hi = __builtin_amdgcn_perm(n3, n2, 0x07030602u);
+    uint4 t;
+    t.x = __builtin_amdgcn_perm(u23lo, u01lo, 0x05040100u);
+    t.y = __builtin_amdgcn_perm(u23lo, u01lo, 0x07060302u);
+    t.z = __builtin_amdgcn_perm(u23hi, u01hi, 0x05040100u);
+    t.w = __builtin_amdgcn_perm(u23hi, u01hi, 0x07060302u);
+    return t;
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int j) {
+    return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
+}
+
+template <int MT, int RB, int WAVES, bool OUT_I32>
+__global__ __launch_bounds__(WAVES * 64) void gemv_fused_kernel(uint16_t* __restrict__ out,
+                                                                int32_t* __restrict__ acc_out,
+                                                                uint16_t* __restrict__ sa_out,
+                                                                const uint16_t* __restrict__ x,
+                                                                const uint8_t* __restrict__ w,
+                                                                const uint16_t* __restrict__ sw, int M, int N, int K,
+                                                                int KC) {
+    extern __shared__ __align__(16) uint8_t lds_x[];  // [MT][KC] quantised, transposed, swizzled
+    __shared__ uint32_t red_u[WAVES][MT];
+    __shared__ int red_i[WAVES][MT];
+    __shared__ float s_scale[MT];
+    __shared__ float s_recip[MT];
+    __shared__ int s_sumq[MT];
+
+    constexpr int NT = WAVES * 64;
+    constexpr int ROWS = WAVES * 8 * RB;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 3;   // row of the 8-row group
+    const int sl = lane & 7;   // 64-weight piece within a 512-weight step
+    const int n_first = blockIdx.x * ROWS + wave * 8 * RB + g;
+    const int64_t KB = K >> 2;
+
+    const uint8_t* wrow[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int n = min(n_first + rb * 8, N - 1);  // rows past N load a valid row; their results are dropped
+        wrow[rb] = w + (int64_t)n * KB;
+    }
+
+    const int nchunks = (K + KC - 1) / KC;
+    auto steps_in_chunk = [&](int c) {
+        const int len = min(KC, K - c * KC);
+        return (len + GV_STEP - 1) / GV_STEP;
+    };
+    auto load_step = [&](int c, int t, uint4 (&dst)[RB]) {
+        const int kp = c * KC + t * GV_STEP + sl * 64;  // first weight of this lane's piece
+        if (kp < K) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                dst[rb] = load_stream16(wrow[rb] + (kp >> 2));
+        } else {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) dst[rb] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+
+    // First weight loads go out before the prologue.
+    uint4 wcur[RB];
+    load_step(0, 0, wcur);
+
+    // ---- prologue: row absmax of every activation row (all threads)
+    {
+        uint32_t am[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) am[m] = 0u;
+        const int n8 = K >> 3;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            if (m < M) {
+                const uint4* xv = reinterpret_cast<const uint4*>(x + (int64_t)m * K);
+                for (int i = tid; i < n8; i += NT) {
+                    const uint4 v = xv[i];
+                    am[m] = max(am[m], max(max(absmax_bf16x2(v.x), absmax_bf16x2(v.y)),
+                                           max(absmax_bf16x2(v.z), absmax_bf16x2(v.w))));
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint32_t a = wave_max_u32(am[m]);
+            if (lane == 0) red_u[wave][m] = a;
+        }
+        __syncthreads();
+        if (tid < MT) {
+            uint32_t a = 0u;
+#pragma unroll
+            for (int wv = 0; wv < WAVES; ++wv) a = max(a, red_u[wv][tid]);
+            const QuantScale qs = quant_scale(a);
+            s_scale[tid] = qs.s;
+            s_recip[tid] = qs.r;
+            if (sa_out != nullptr && blockIdx.x == 0 && tid < M) sa_out[tid] = f32_to_bf16(qs.s);
+        }
+        __syncthreads();
+    }
+    QuantScale qsc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        qsc[m].s = s_scale[m];
+        qsc[m].r = s_recip[m];
+    }
+
+    int a0[RB][MT], a1[RB][MT], a2[RB][MT];
+    int sq[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        sq[m] = 0;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) a0[rb][m] = a1[rb][m] = a2[rb][m] = 0;
+    }
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int k0 = c * KC;
+        const int steps = steps_in_chunk(c);
+        const int len = min(KC, K - k0);
+        const int words = steps * (GV_STEP / 16);
+
+        // ---- quantise this chunk of every row into LDS
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            for (int wd = tid; wd < words; wd += NT) {
+                uint4 t = make_uint4(0u, 0u, 0u, 0u);
+                if (m < M && wd * 16 < len) {
+                    const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)m * K + k0 + wd * 16);
+                    const uint4 lo = src[0];
+                    const uint4 hi = src[1];
+                    const uint32_t n0 = quantize_bf16x2(lo.x, qsc[m]) | (quantize_bf16x2(lo.y, qsc[m]) << 16);
+                    const uint32_t n1 = quantize_bf16x2(lo.z, qsc[m]) | (quantize_bf16x2(lo.w, qsc[m]) << 16);
+                    const uint32_t n2 = quantize_bf16x2(hi.x, qsc[m]) | (quantize_bf16x2(hi.y, qsc[m]) << 16);
+                    const uint32_t n3 = quantize_bf16x2(hi.z, qsc[m]) | (quantize_bf16x2(hi.w, qsc[m]) << 16);
+                    int s = __builtin_amdgcn_sdot4((int)n0, 0x01010101, 0, false);
+                    s = __builtin_amdgcn_sdot4((int)n1, 0x01010101, s, false);
+                    s = __builtin_amdgcn_sdot4((int)n2, 0x01010101, s, false);
+                    s = __builtin_amdgcn_sdot4((int)n3, 0x01010101, s, false);
+                    sq[m] += s;
+                    t = transpose4x4(n0, n1, n2, n3);
+                }
+                *reinterpret_cast<uint4*>(lds_x + m * KC + lds_word_offset(wd)) = t;
+            }
+        }
+        __syncthreads();
+
+        // ---- stream the packed weights of this chunk
+        for (int t = 0; t < steps; ++t) {
+            uint4 wnext[RB];
+            const bool more = (t + 1 < steps) || (c + 1 < nchunks);
+            if (more) {
+                if (t + 1 < steps)
+                    load_step(c, t + 1, wnext);
+                else
+                    load_step(c + 1, 0, wnext);
+            }
+            const int seg = t * 8 + sl;
+            const int swz = (seg >> 1) & 3;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t cd0[RB], cd1[RB], cd2[RB], cd3[RB];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const uint32_t p = word_of(wcur[rb], j);
+                    cd0[rb] = p & 0x03030303u;
+                    cd1[rb] = p & 0x0C0C0C0Cu;
+                    cd2[rb] = p & 0x30303030u;
+                    cd3[rb] = (p >> 6) & 0x03030303u;
+                }
+                const int off = (seg << 6) + ((j ^ swz) << 4);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const uint4 xq = *reinterpret_cast<const uint4*>(lds_x + m * KC + off);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        a0[rb][m] = __builtin_amdgcn_sdot4((int)cd0[rb], (int)xq.x, a0[rb][m], false);
+                        a1[rb][m] = __builtin_amdgcn_sdot4((int)cd1[rb], (int)xq.y, a1[rb][m], false);
+                        a2[rb][m] = __builtin_amdgcn_sdot4((int)cd2[rb], (int)xq.z, a2[rb][m], false);
+                        a0[rb][m] = __builtin_amdgcn_sdot4((int)cd3[rb], (int)xq.w, a0[rb][m], false);
+                    }
+                }
+            }
+            if (more) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) wcur[rb] = wnext[rb];
+            }
+        }
+        __syncthreads();  // LDS is rewritten by the next chunk
+    }
+
+    // ---- sum_k q[m][k] over the whole block
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int v = wave_sum_i32(sq[m]);
+        if (lane == 0) red_i[wave][m] = v;
+    }
+    __syncthreads();
+    if (tid < MT) {
+        int s = 0;
+#pragma unroll
+        for (int wv = 0; wv < WAVES; ++wv) s += red_i[wv][tid];
+        s_sumq[tid] = s;
+    }
+    __syncthreads();
+
+    // ---- reduce the 8 lanes of each row, correct the code offset, write
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int n = n_first + rb * 8;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            int tot = a0[rb][m] + (a1[rb][m] >> 2) + (a2[rb][m] >> 4);
+            tot = group8_sum(tot);
+            tot -= 2 * s_sumq[m];
+            const int idx = rb * MT + m;
+            if ((idx & 7) == sl && n < N && m < M) {
+                if (OUT_I32)
+                    acc_out[(int64_t)m * N + n] = tot;
+                else
+                    out[(int64_t)m * N + n] = epilogue_bf16(tot, bf16_to_f32(f32_to_bf16(qsc[m].s)), bf16_to_f32(sw[n]));
+            }
+        }
+    }
+}
+
+// Plain fused path: one wave per output row, any K % 4 == 0 and any alignment.
+template <bool OUT_I32>
+__global__ __launch_bounds__(64) void gemv_fused_plain(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
+                                                       uint16_t* __restrict__ sa_out, const uint16_t* __restrict__ x,
+                                                       const uint8_t* __restrict__ w,
+                                                       const uint16_t* __restrict__ sw, int M, int N, int K) {
+    const int n = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int64_t KB = K >> 2;
+    for (int m = 0; m < M; ++m) {
+        const uint16_t* xr = x + (int64_t)m * K;
+        uint32_t am = 0u;
+        for (int k = lane; k < K; k += 64) am = max(am, (uint32_t)xr[k] & 0x7FFFu);
+        am = wave_max_u32(am);
+        const QuantScale qs = quant_scale(am);
+        if (sa_out != nullptr && n == 0 && lane == 0) sa_out[m] = f32_to_bf16(qs.s);
+        int acc = 0;
+        for (int k = lane; k < K; k += 64) {
+            const int code = (w[(int64_t)n * KB + (k >> 2)] >> (2 * (k & 3))) & 3;
+            acc += (code - 2) * quantize_one(bf16_to_f32(xr[k]), qs);
+        }
+        acc = wave_sum_i32(acc);
+        if (lane == 0) {
+            if (OUT_I32)
+                acc_out[(int64_t)m * N + n] = acc;
+            else
+                out[(int64_t)m * N + n] = epilogue_bf16(acc, bf16_to_f32(f32_to_bf16(qs.s)), bf16_to_f32(sw[n]));
+        }
+    }
+}
+
+template <int MT, int RB, bool OUT_I32>
+hipError_t launch_fast(uint16_t* out, int32_t* acc, uint16_t* sa_out, const uint16_t* x, const uint8_t* w,
+                       const uint16_t* sw, int M, int N, int K, hipStream_t s) {
+    constexpr int WAVES = 4;
+    constexpr int ROWS = WAVES * 8 * RB;
+    int kc_max = (GV_LDS_BUDGET / MT) / GV_STEP * GV_STEP;
+    const int kpad = (K + GV_STEP - 1) / GV_STEP * GV_STEP;
+    const int KC = kpad < kc_max ? kpad : kc_max;
+    const size_t lds = (size_t)MT * KC;
+    const unsigned blocks = (unsigned)((N + ROWS - 1) / ROWS);
+    hipLaunchKernelGGL((gemv_fused_kernel<MT, RB, WAVES, OUT_I32>), dim3(blocks), dim3(WAVES * 64), lds, s, out, acc,
+                       sa_out, x, w, sw, M, N, K, KC);
+    return hipGetLastError();
+}
+
+// Row blocks per wave: as many as keep >= 512 workgroups, at most the cap for MT.
+template <int MT, bool OUT_I32>
+hipError_t dispatch_rb(uint16_t* out, int32_t* acc, uint16_t* sa_out, const uint16_t* x, const uint8_t* w,
+                       const uint16_t* sw, int M, int N, int K, hipStream_t s) {
+    constexpr int RB_CAP = MT <= 2 ? 4 : (MT <= 4 ? 2 : 1);
+    if (RB_CAP >= 4 && (int64_t)N >= 512 * 128)
+        return launch_fast<MT, (RB_CAP >= 4 ? 4 : 1), OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
+    if (RB_CAP >= 2 && (int64_t)N >= 512 * 64)
+        return launch_fast<MT, (RB_CAP >= 2 ? 2 : 1), OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
+    return launch_fast<MT, 1, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
+}
+
+template <bool OUT_I32>
+hipError_t dispatch(uint16_t* out, int32_t* acc, uint16_t* sa_out, const uint16_t* x, const uint8_t* w,
+                    const uint16_t* sw, int M, int N, int K, hipStream_t s) {
+    const bool fast = (K % 64 == 0) && aligned16(x) && aligned16(w);
+    if (!fast) {
+        hipLaunchKernelGGL((gemv_fused_plain<OUT_I32>), dim3((unsigned)N), dim3(64), 0, s, out, acc, sa_out, x, w, sw,
+                           M, N, K);
+        return hipGetLastError();
+    }
+    if (M == 1) return dispatch_rb<1, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
+    if (M == 2) return dispatch_rb<2, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
+    if (M <= 4) return dispatch_rb<4, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
+    if (M <= 8) return dispatch_rb<8, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
+    return dispatch_rb<16, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_fused(uint16_t* out, int32_t* acc, uint16_t* scale_act_out, const uint16_t* x,
+                             const uint8_t* w, const uint16_t* scale_wt, int64_t M, int64_t N, int64_t K,
+                             hipStream_t s) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    if (acc != nullptr) return dispatch<true>(nullptr, acc, scale_act_out, x, w, scale_wt, (int)M, (int)N, (int)K, s);
+    return dispatch<false>(out, nullptr, scale_act_out, x, w, scale_wt, (int)M, (int)N, (int)K, s);
+}
+
+}  // namespace bitnet

@@ -1,0 +1,30 @@
+// launch.h -- internal kernel launchers of the C ABI (not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bitnet {
+
+// Per-token absmax INT8 quantisation of x [M][K] (bf16) into q [M][K] and the
+// bf16 scales [M].
+hipError_t launch_quantize(int8_t* q, uint16_t* scale, const uint16_t* x, int64_t M, int64_t K, hipStream_t s);
+
+// Batched ternary x int8 product.  Exactly one of out (bf16 [M][N], scaled
+// with scale_act / scale_wt) and acc (int32 [M][N], unscaled) is non-null.
+hipError_t launch_gemm(uint16_t* out, int32_t* acc, const int8_t* x, const uint8_t* w, const uint16_t* scale_act,
+                       const uint16_t* scale_wt, int64_t M, int64_t N, int64_t K, hipStream_t s);
+
+// Fused quantise + GEMV for M <= 15.  Exactly one of out (bf16 [M][N]) and acc
+// (int32 [M][N]) is non-null; scale_act_out (bf16 [M]) may be null.
+hipError_t launch_gemv_fused(uint16_t* out, int32_t* acc, uint16_t* scale_act_out, const uint16_t* x,
+                             const uint8_t* w, const uint16_t* scale_wt, int64_t M, int64_t N, int64_t K,
+                             hipStream_t s);
+
+// out[m][n] = epilogue(acc[m][n], scale_act[m], scale_wt[n]).
+hipError_t launch_epilogue(uint16_t* out, const int32_t* acc, const uint16_t* scale_act, const uint16_t* scale_wt,
+                           int64_t M, int64_t N, hipStream_t s);
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace bitnet

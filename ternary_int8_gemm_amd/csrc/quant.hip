@@ -1,0 +1,87 @@
+// quant.hip -- per-token absmax INT8 quantisation (K-QUANT).
+//
+// Implements quantize_activation of "phanerozoic/bitnet-cpu v1,
+// torch-ext/bitnet_cpu/__init__.py" in fp32 on the widened bf16 input:
+// absmax per row clamped below at 1e-5, s = absmax / 127 (IEEE fp32 division),
+// q = clamp(round_half_even(x / s), -127, 127), scale stored as bf16(s).
+//
+// Layout on gfx950: one wave64 per row, four rows per 256-thread workgroup.
+// Pass 1 streams the row with 16-byte loads and reduces the absmax on the raw
+// bf16 magnitude bits (an integer max; DPP inside each 16-lane row, readlane
+// across rows).  Pass 2 re-reads the row (it is still in L2) and writes 16
+// int8 per lane with one 16-byte store.  The whole kernel is HBM-bound at
+// 3 bytes per element.
+#include "bitnet_device.h"
+#include "launch.h"
+
+namespace bitnet {
+
+namespace {
+
+constexpr int QUANT_ROWS_PER_BLOCK = 4;
+
+__device__ __forceinline__ uint32_t pack4(uint32_t lo2, uint32_t hi2) { return lo2 | (hi2 << 16); }
+
+// Vector path: K % 16 == 0, x and q 16-byte aligned.
+__global__ __launch_bounds__(256) void quantize_rows_vec(int8_t* __restrict__ q, uint16_t* __restrict__ scale,
+                                                         const uint16_t* __restrict__ x, int64_t M, int64_t K) {
+    const int lane = threadIdx.x & 63;
+    const int64_t m = (int64_t)blockIdx.x * QUANT_ROWS_PER_BLOCK + (threadIdx.x >> 6);
+    if (m >= M) return;  // wave-uniform
+    const uint4* xv = reinterpret_cast<const uint4*>(x + m * K);
+    const int64_t n16 = K / 16;  // groups of 16 elements = 2 x 16 bytes of bf16
+
+    uint32_t amax = 0;
+    for (int64_t i = lane; i < n16; i += 64) {
+        const uint4 a = xv[2 * i];
+        const uint4 b = xv[2 * i + 1];
+        amax = max(amax, max(max(absmax_bf16x2(a.x), absmax_bf16x2(a.y)), max(absmax_bf16x2(a.z), absmax_bf16x2(a.w))));
+        amax = max(amax, max(max(absmax_bf16x2(b.x), absmax_bf16x2(b.y)), max(absmax_bf16x2(b.z), absmax_bf16x2(b.w))));
+    }
+    amax = wave_max_u32(amax);
+    const QuantScale qs = quant_scale(amax);
+    if (lane == 0) scale[m] = f32_to_bf16(qs.s);
+
+    uint4* qv = reinterpret_cast<uint4*>(q + m * K);
+    for (int64_t i = lane; i < n16; i += 64) {
+        const uint4 a = xv[2 * i];
+        const uint4 b = xv[2 * i + 1];
+        uint4 o;
+        o.x = pack4(quantize_bf16x2(a.x, qs), quantize_bf16x2(a.y, qs));
+        o.y = pack4(quantize_bf16x2(a.z, qs), quantize_bf16x2(a.w, qs));
+        o.z = pack4(quantize_bf16x2(b.x, qs), quantize_bf16x2(b.y, qs));
+        o.w = pack4(quantize_bf16x2(b.z, qs), quantize_bf16x2(b.w, qs));
+        qv[i] = o;
+    }
+}
+
+// Plain path for any K and alignment: one element per lane per iteration.
+__global__ __launch_bounds__(256) void quantize_rows_plain(int8_t* __restrict__ q, uint16_t* __restrict__ scale,
+                                                           const uint16_t* __restrict__ x, int64_t M, int64_t K) {
+    const int lane = threadIdx.x & 63;
+    const int64_t m = (int64_t)blockIdx.x * QUANT_ROWS_PER_BLOCK + (threadIdx.x >> 6);
+    if (m >= M) return;
+    const uint16_t* xr = x + m * K;
+    uint32_t amax = 0;
+    for (int64_t k = lane; k < K; k += 64) amax = max(amax, (uint32_t)xr[k] & 0x7FFFu);
+    amax = wave_max_u32(amax);
+    const QuantScale qs = quant_scale(amax);
+    if (lane == 0) scale[m] = f32_to_bf16(qs.s);
+    int8_t* qr = q + m * K;
+    for (int64_t k = lane; k < K; k += 64) qr[k] = (int8_t)quantize_one(bf16_to_f32(xr[k]), qs);
+}
+
+}  // namespace
+
+hipError_t launch_quantize(int8_t* q, uint16_t* scale, const uint16_t* x, int64_t M, int64_t K, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    const int64_t blocks = (M + QUANT_ROWS_PER_BLOCK - 1) / QUANT_ROWS_PER_BLOCK;
+    if (K % 16 == 0 && aligned16(x) && aligned16(q)) {
+        hipLaunchKernelGGL(quantize_rows_vec, dim3((unsigned)blocks), dim3(256), 0, s, q, scale, x, M, K);
+    } else {
+        hipLaunchKernelGGL(quantize_rows_plain, dim3((unsigned)blocks), dim3(256), 0, s, q, scale, x, M, K);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace bitnet

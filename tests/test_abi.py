@@ -1,0 +1,111 @@
+"""CPU-side checks of the C ABI: the library loads, exports what include/bitnet.h
+declares, packs on the host bit-exactly like the oracle, and rejects bad
+arguments before touching any device.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import ternary_int8_gemm_amd as tg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitnet.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitnet_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ["bitnet_pack_weights", "bitnet_quantize_act", "bitnet_gemm", "bitnet_gemv_fused",
+                     "bitnet_linear", "bitnet_gemm_i32", "bitnet_gemv_fused_i32", "bitnet_scale_epilogue",
+                     "bitnet_linear_workspace_bytes", "bitnet_status_string", "bitnet_version"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tg.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_library_exports_nothing_else():
+    # the .so's dynamic symbol table: only the C ABI is visible
+    out = os.popen(f"nm -D --defined-only {tg.library_path()}").read()
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert exported == set(declared_functions()), exported ^ set(declared_functions())
+
+
+def test_library_links_no_oracle():
+    deps = os.popen(f"ldd {tg.library_path()} 2>/dev/null").read()
+    assert "oracle" not in deps
+    syms = os.popen(f"nm -D {tg.library_path()}").read()
+    assert "oracle_" not in syms
+
+
+def test_host_pack_matches_oracle():
+    for (N, K, seed) in ((1, 4, 1), (7, 12, 2), (33, 256, 3), (128, 2560, 4)):
+        W = synth.ternary_weights(N, K, seed)
+        got = tg.pack_weights(torch.from_numpy(W)).numpy()
+        assert np.array_equal(got, oracle.pack(W))
+
+
+def test_host_pack_errors():
+    lib = tg.load_library()
+    w = np.zeros((2, 8), dtype=np.int8)
+    p = np.zeros((2, 2), dtype=np.uint8)
+    vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    assert lib.bitnet_pack_weights(vp(p), vp(w), 2, 6) == 2          # K % 4
+    assert lib.bitnet_pack_weights(vp(p), vp(w), -1, 8) == 2         # N < 0
+    assert lib.bitnet_pack_weights(None, vp(w), 2, 8) == 1           # NULL
+    assert lib.bitnet_pack_weights(vp(p), vp(w), 0, 8) == 0          # empty is fine
+    w[1, 3] = 2
+    assert lib.bitnet_pack_weights(vp(p), vp(w), 2, 8) == 3          # value outside {-1,0,1}
+    w[1, 3] = -2
+    assert lib.bitnet_pack_weights(vp(p), vp(w), 2, 8) == 3
+    with pytest.raises(tg.BitnetError):
+        tg.pack_weights(torch.full((1, 4), 5, dtype=torch.int8))
+
+
+def test_shape_errors_precede_device_use():
+    # These all fail argument validation and return before any HIP call.
+    lib = tg.load_library()
+    d = ctypes.c_void_p(16)  # never dereferenced
+    assert lib.bitnet_gemm(d, d, d, d, d, 4, 8, 6, None) == 2                 # K % 4
+    assert lib.bitnet_gemm(d, d, d, d, d, 4, 8, 0, None) == 2                 # K == 0
+    assert lib.bitnet_gemm(d, d, d, d, d, 4, 8, 131072 + 4, None) == 2       # K > MAX_K
+    assert lib.bitnet_gemm(d, d, d, d, d, -1, 8, 64, None) == 2               # M < 0
+    assert lib.bitnet_gemm(d, d, d, d, d, 0, 8, 64, None) == 0                # M == 0: no-op
+    assert lib.bitnet_gemm(d, d, d, d, d, 4, 0, 64, None) == 0                # N == 0: no-op
+    assert lib.bitnet_gemm(None, d, d, d, d, 4, 8, 64, None) == 1             # NULL out
+    assert lib.bitnet_gemv_fused(d, d, d, d, 16, 8, 64, None) == 2            # M > 15
+    assert lib.bitnet_gemv_fused_i32(d, d, d, d, 16, 8, 64, None) == 2
+    assert lib.bitnet_quantize_act(d, d, d, 4, 10, None) == 2
+    assert lib.bitnet_quantize_act(None, d, d, 4, 64, None) == 1
+    assert lib.bitnet_gemm_i32(d, d, d, 4, 8, 63, None) == 2
+    assert lib.bitnet_linear(d, d, d, d, 32, 8, 64, None, 0, None) == 4       # workspace missing
+    assert lib.bitnet_linear(d, d, d, d, 32, 8, 64, d, 100, None) == 4        # workspace too small
+    assert lib.bitnet_scale_epilogue(None, d, d, d, 2, 2, None) == 1
+
+
+def test_workspace_size():
+    assert tg.linear_workspace_bytes(1, 2560) == 0
+    assert tg.linear_workspace_bytes(15, 2560) == 0
+    assert tg.linear_workspace_bytes(16, 4096) == 16 * 4096 + 256
+    assert tg.linear_workspace_bytes(17, 100) == 1792 + 256
+    assert tg.linear_workspace_bytes(17, 6) == 0   # invalid K
+
+
+def test_status_strings():
+    lib = tg.load_library()
+    for code in range(7):
+        assert lib.bitnet_status_string(code).decode() not in ("", "unknown status")
+    assert lib.bitnet_version() >= 100

@@ -1,0 +1,286 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, element by element.
+
+Bar: int8 activations, bf16 scales and int32 accumulators bit-exact; bf16
+outputs within 1 bf16 ulp (ordered-integer distance, +0 == -0), and in fact
+expected bit-exact because both sides fix the same fp32 operation order.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import ternary_int8_gemm_amd as tg
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def host_bf16(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def ulp_distance(a, b):
+    a = a.astype(np.int32)
+    b = b.astype(np.int32)
+    oa = np.where(a & 0x8000, -(a & 0x7FFF), a & 0x7FFF)
+    ob = np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    return np.abs(oa - ob)
+
+
+def assert_bf16_parity(got, want, what):
+    d = ulp_distance(got, want)
+    assert d.max(initial=0) <= 1, f"{what}: max ulp {d.max()} at {np.unravel_index(np.argmax(d), d.shape)}"
+    assert np.array_equal(got, want), f"{what}: {int((got != want).sum())} outputs differ by 1 ulp"
+
+
+def misaligned(t):
+    """A contiguous copy of t whose data pointer is 2 bytes past a 16-byte boundary."""
+    flat = t.reshape(-1)
+    esz = flat.element_size()
+    pad = max(1, 2 // esz)
+    buf = torch.empty(flat.numel() + 16, dtype=t.dtype, device=t.device)
+    view = buf[pad:pad + flat.numel()]
+    view.copy_(flat)
+    assert view.data_ptr() % 16 != 0
+    return view.view(t.shape)
+
+
+def problem(M, N, K, seed, outliers=0.0, row_scales=False):
+    x = synth.activations_bf16(M, K, seed, outlier_frac=outliers)
+    W = synth.ternary_weights(N, K, seed + 1)
+    P = oracle.pack(W)
+    sw = synth.row_scales_bf16(N, seed + 2) if row_scales else synth.weight_scale_bf16(N, K, seed + 2)
+    return x, W, P, sw
+
+
+# ----------------------------------------------------------------------------- quantisation
+
+QUANT_SHAPES = [(4, 256), (1, 4), (3, 12), (7, 100), (16, 2560), (33, 4096), (5, 6912), (2, 131072), (130, 64)]
+
+
+@pytest.mark.parametrize("M,K", QUANT_SHAPES)
+def test_quantize_parity(M, K):
+    x = synth.activations_bf16(M, K, seed=1000 + M + K, outlier_frac=0.01 if K >= 100 else 0.0)
+    if M > 2:
+        x[1, :] = 0                          # all-zero row: eps floor
+        x[2, : K // 2] = 0x3000              # a run of tiny values (2^-31)
+    q_ref, s_ref = oracle.quantize(x)
+    q, s = tg.quantize_activation(dev_bf16(x))
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(host_bf16(s), s_ref)
+
+
+def test_quantize_golden_vectors_on_gpu():
+    from conftest import read_golden
+    for r in read_golden("quantize_vectors.txt"):
+        vals = [float(t) for t in r["x"]]
+        K = (len(vals) + 3) // 4 * 4                 # pad with zeros: changes neither absmax nor q
+        xb = torch.tensor(vals + [0.0] * (K - len(vals)), dtype=torch.float32).to(torch.bfloat16)
+        q, s = tg.quantize_activation(xb.view(1, K).to(DEV))
+        assert q.cpu().numpy()[0, :len(vals)].tolist() == [int(t) for t in r["q"]]
+        assert int(host_bf16(s)[0]) == int(r["scale_bf16"][0], 16)
+
+
+def test_quantize_misaligned_plain_path():
+    x = synth.activations_bf16(6, 96, seed=7)
+    q_ref, s_ref = oracle.quantize(x)
+    xd = misaligned(dev_bf16(x))
+    q = misaligned(torch.zeros((6, 96), dtype=torch.int8, device=DEV))
+    s = torch.empty((6,), dtype=torch.bfloat16, device=DEV)
+    tg.quantize_activation(xd, out=q, scale=s)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(host_bf16(s), s_ref)
+
+
+# ----------------------------------------------------------------------------- int32 GEMM
+
+GEMM_SHAPES = [
+    (1, 1, 64), (4, 128, 256), (17, 33, 64), (128, 128, 128), (129, 130, 192), (300, 257, 320),
+    (16, 4096, 4096), (64, 512, 2560), (255, 129, 6912), (8, 64, 68), (5, 7, 100), (3, 3, 4),
+]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_i32_parity(M, N, K):
+    q = synth.random_int8((M, K), seed=2000 + M + N + K)
+    W = synth.ternary_weights(N, K, seed=2100 + M + N + K)
+    P = oracle.pack(W)
+    acc_ref = oracle.gemm_i32(q, P)
+    acc = tg.bitnet_gemm_i32(dev(q), dev(P))
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+
+
+def test_gemm_i32_random_bytes_include_code_zero():
+    M, N, K = 70, 96, 512
+    q = synth.random_int8((M, K), seed=31)
+    P = synth.random_bytes(N * K // 4, seed=32).reshape(N, K // 4)   # code 0 decodes to -2
+    assert np.array_equal(tg.bitnet_gemm_i32(dev(q), dev(P)).cpu().numpy(), oracle.gemm_i32(q, P))
+
+
+def test_gemm_i32_extremes():
+    M, N, K = 32, 64, 4096
+    q = np.full((M, K), 127, dtype=np.int8)
+    q[1::2] = -127
+    W = np.ones((N, K), dtype=np.int8)
+    W[::3] = -1
+    P = oracle.pack(W)
+    assert np.array_equal(tg.bitnet_gemm_i32(dev(q), dev(P)).cpu().numpy(), oracle.gemm_i32(q, P))
+
+
+def test_gemm_i32_misaligned_plain_path():
+    M, N, K = 9, 20, 128
+    q = synth.random_int8((M, K), seed=41)
+    W = synth.ternary_weights(N, K, seed=42)
+    P = oracle.pack(W)
+    acc = tg.bitnet_gemm_i32(misaligned(dev(q)), dev(P))
+    assert np.array_equal(acc.cpu().numpy(), oracle.gemm_i32(q, P))
+
+
+# ----------------------------------------------------------------------------- bf16 GEMM
+
+@pytest.mark.parametrize("M,N,K", [(4, 128, 256), (16, 4096, 4096), (200, 300, 1024), (33, 65, 68)])
+def test_gemm_bf16_parity(M, N, K):
+    x, W, P, _ = problem(M, N, K, seed=3000 + M)
+    sw = synth.row_scales_bf16(N, seed=3100 + M)
+    q, sa = oracle.quantize(x)
+    out_ref = oracle.epilogue(oracle.gemm_i32(q, P), sa, sw)
+    out = tg.bitnet_gemm(dev(q), dev(P), dev_bf16(sa), dev_bf16(sw))
+    assert_bf16_parity(host_bf16(out), out_ref, f"gemm {M}x{N}x{K}")
+
+
+# ----------------------------------------------------------------------------- fused GEMV
+
+GEMV_SHAPES = [
+    (1, 1, 64), (1, 7, 256), (4, 128, 256), (2, 1000, 512), (3, 129, 576), (5, 64, 2560), (8, 3840, 2560),
+    (9, 100, 6912), (15, 256, 4096), (1, 2560, 6912), (16 - 1, 33, 40960), (1, 300, 68), (7, 50, 100),
+]
+
+
+@pytest.mark.parametrize("M,N,K", GEMV_SHAPES)
+def test_gemv_fused_parity(M, N, K):
+    x, W, P, sw = problem(M, N, K, seed=4000 + M * 7 + N + K, row_scales=True)
+    ref = oracle.linear(x, P, sw)
+    xd, Pd = dev_bf16(x), dev(P)
+    out = tg.bitnet_gemv_fused(xd, Pd, dev_bf16(sw))
+    acc, sa = tg.bitnet_gemv_fused_i32(xd, Pd)
+    assert np.array_equal(host_bf16(sa), ref["scale_act"])
+    assert np.array_equal(acc.cpu().numpy(), ref["acc"])
+    assert_bf16_parity(host_bf16(out), ref["out"], f"gemv {M}x{N}x{K}")
+
+
+def test_gemv_fused_misaligned_plain_path():
+    M, N, K = 3, 40, 256
+    x, W, P, sw = problem(M, N, K, seed=51)
+    ref = oracle.linear(x, P, sw)
+    out = tg.bitnet_gemv_fused(misaligned(dev_bf16(x)), dev(P), dev_bf16(sw))
+    assert_bf16_parity(host_bf16(out), ref["out"], "gemv misaligned")
+
+
+# ----------------------------------------------------------------------------- dispatch
+
+@pytest.mark.parametrize("M", [1, 2, 15, 16, 17, 64])
+def test_linear_dispatch_neutral(M):
+    N, K = 192, 1024
+    x, W, P, sw = problem(M, N, K, seed=5000 + M, outliers=0.01, row_scales=True)
+    ref = oracle.linear(x, P, sw)
+    out = tg.bitnet_linear(dev_bf16(x), dev(P), dev_bf16(sw))
+    assert_bf16_parity(host_bf16(out), ref["out"], f"linear M={M}")
+    if M <= tg.FUSED_MAX_M:   # the split path gives the same bits too
+        q, sa = tg.quantize_activation(dev_bf16(x))
+        out2 = tg.bitnet_gemm(q, dev(P), sa, dev_bf16(sw))
+        assert np.array_equal(host_bf16(out2), host_bf16(out))
+
+
+def test_linear_leading_dims():
+    x, W, P, sw = problem(6, 64, 256, seed=61)
+    ref = oracle.linear(x, P, sw)
+    out = tg.bitnet_linear(dev_bf16(x).view(2, 3, 256), dev(P), dev_bf16(sw))
+    assert out.shape == (2, 3, 64)
+    assert np.array_equal(host_bf16(out).reshape(6, 64), ref["out"])
+
+
+# ----------------------------------------------------------------------------- epilogue
+
+@pytest.mark.parametrize("M,N", [(3, 8), (5, 7), (64, 1000)])
+def test_scale_epilogue_parity(M, N):
+    g = synth.rng(70 + N)
+    acc = g.integers(-(1 << 23), 1 << 23, size=(M, N)).astype(np.int32)
+    sa = synth.row_scales_bf16(M, seed=71, lo=1e-3, hi=0.1)
+    sw = synth.row_scales_bf16(N, seed=72)
+    ref = oracle.epilogue(acc, sa, sw)
+    out = tg.bitnet_scale_epilogue(dev(acc), dev_bf16(sa), dev_bf16(sw))
+    assert_bf16_parity(host_bf16(out), ref, "epilogue")
+
+
+def test_scale_epilogue_golden_ties():
+    from conftest import read_golden
+    rows = read_golden("epilogue_cases.txt")
+    acc = np.array([[int(r["acc"][0]) for r in rows]], dtype=np.int32)
+    for i, r in enumerate(rows):
+        sa = np.array([int(r["sa"][0], 16)], dtype=np.uint16)
+        sw = np.array([int(r["sw"][0], 16)], dtype=np.uint16)
+        out = tg.bitnet_scale_epilogue(dev(acc[:, i:i + 1]), dev_bf16(sa), dev_bf16(sw))
+        assert int(host_bf16(out)[0, 0]) == int(r["out"][0], 16), r
+
+
+# ----------------------------------------------------------------------------- degenerate cases
+
+def test_zero_sizes_are_noops():
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    P = torch.zeros((8, 16), dtype=torch.uint8, device=DEV)
+    sw = torch.ones((8,), dtype=torch.bfloat16, device=DEV)
+    assert tg.bitnet_linear(x, P, sw).shape == (0, 8)
+    out = tg.bitnet_linear(torch.zeros((4, 64), dtype=torch.bfloat16, device=DEV),
+                           torch.zeros((0, 16), dtype=torch.uint8, device=DEV),
+                           torch.ones((0,), dtype=torch.bfloat16, device=DEV))
+    assert out.shape == (4, 0)
+
+
+def test_zero_activation_row_and_constant_weights():
+    M, N, K = 4, 48, 512
+    x = synth.activations_bf16(M, K, seed=81)
+    x[0] = 0
+    W = np.ones((N, K), dtype=np.int8)
+    W[N // 2:] = -1
+    W[N - 1] = 0
+    P = oracle.pack(W)
+    sw = np.full((N,), 0x3F80, dtype=np.uint16)
+    ref = oracle.linear(x, P, sw)
+    for fn in (lambda: tg.bitnet_gemv_fused(dev_bf16(x), dev(P), dev_bf16(sw)),):
+        out = host_bf16(fn())
+        assert_bf16_parity(out, ref["out"], "constant W")
+        assert np.all(out[0] == 0)                       # zero row -> +0.0 everywhere
+    q, sa = tg.quantize_activation(dev_bf16(x))
+    assert int(host_bf16(sa)[0]) == 0x33A9
+
+
+def test_max_k():
+    K = tg.MAX_K
+    for M in (1, 16):
+        x, W, P, sw = problem(M, 24, K, seed=90 + M)
+        ref = oracle.linear(x, P, sw)
+        out = tg.bitnet_linear(dev_bf16(x), dev(P), dev_bf16(sw))
+        assert_bf16_parity(host_bf16(out), ref["out"], f"max K M={M}")
+
+
+def test_device_errors_raise():
+    x = torch.zeros((16, 64), dtype=torch.bfloat16, device=DEV)
+    P = torch.zeros((8, 16), dtype=torch.uint8, device=DEV)
+    sw = torch.ones((8,), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(tg.BitnetError):
+        tg.bitnet_gemv_fused(x, P, sw)                   # M = 16 > 15
+    with pytest.raises(tg.BitnetError):
+        tg.bitnet_linear(x, P, sw, workspace=torch.empty((8,), dtype=torch.uint8, device=DEV))
