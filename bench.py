@@ -1,0 +1,331 @@
+"""Benchmark of the W1.58A8 linear layer on one MI355X.
+
+Headline (`value`): HBM GB/s of the M=1 decode path at the BitNet-2B-4T
+projection shapes -- one step = the five projections (qkv 3840x2560,
+o_proj 2560x2560, gate_up 13824x2560, down 2560x6912, lm_head 128256x2560) of one
+token through bitnet_linear (fused quantise + GEMV), bytes counted as the
+algorithmic bytes the method must move (packed weights + weight scales +
+activations in + outputs).  Inputs are resident in HBM; the weights rotate
+over a pool of >= 1 GiB of distinct copies so the 256 MB last-level cache
+cannot hold them.  Steps run as replays of a captured HIP graph.
+
+Beside it: INT8 TOPS of the matrix-core GEMM at M=2048 on the LLaMA-7B shapes
+(pre-quantised activations, the GEMM kernel alone, plus the quantise+GEMM
+bitnet_linear time), the roofline of the dominant kernel (the lm_head GEMV
+launch), and the CPU oracle timed on the host as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+import ternary_int8_gemm_amd as tg  # noqa: E402
+
+METRIC = "W1.58A8 GEMV HBM GB/s (M=1) + GEMM INT8 TOPS (M=2048), % of roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published (5.0 POPS)
+POOL_BYTES = 1 << 30           # rotating weight pool, >= 4x the 256 MB last-level cache
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_lm_head_m1_traffic.json")
+KERNEL_SOURCES = ["ternary_int8_gemm_amd/csrc/gemv.hip", "ternary_int8_gemm_amd/csrc/bitnet_device.h"]
+
+
+def gemv_bytes(M, N, K):
+    """Algorithmic bytes of the fused path: packed W + bf16 scale_wt + bf16 x in + bf16 out."""
+    return N * K // 4 + 2 * N + 2 * M * K + 2 * M * N
+
+
+def gemm_bytes(M, N, K):
+    """Algorithmic bytes of the GEMM: packed W + scale_wt + int8 x + scale_act + bf16 out."""
+    return N * K // 4 + 2 * N + M * K + 2 * M + 2 * M * N
+
+
+def dev_bf16(bits, device):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def time_graph(graph, replays, stream):
+    """Replay `graph` on `stream` and time the replays with events on that stream."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(replays):
+            graph.replay()   # launches on the current stream, i.e. `stream`
+        end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e-3  # seconds
+
+
+def capture(fn, stream):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        fn()  # warm once outside capture (first-touch of the library, lazy init)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+# ----------------------------------------------------------------------------- decode GEMV
+
+def build_decode(device, log):
+    """Weights, pools and outputs for the five M=1 projections."""
+    shapes = synth.BITNET_2B_DECODE
+    host = {}
+    per_set = 0
+    for i, (name, N, K) in enumerate(shapes):
+        W = synth.ternary_weights(N, K, synth.seed_for(1, 16 * i + synth.T_WEIGHT))
+        P = tg.pack_weights(torch.from_numpy(W)).numpy()
+        sw = synth.weight_scale_bf16(N, K, synth.seed_for(1, 16 * i + synth.T_SCALE))
+        x = synth.activations_bf16(1, K, synth.seed_for(1, 16 * i + synth.T_ACT))
+        host[name] = (W, P, sw, x)
+        per_set += P.nbytes
+        del W
+    copies = max(2, -(-POOL_BYTES // per_set))
+    log(f"decode: weight set {per_set / 1e6:.1f} MB, {copies} rotating copies ({copies * per_set / 1e9:.2f} GB)")
+    dev_sets = []
+    for r in range(copies):
+        d = {}
+        for name, N, K in shapes:
+            W, P, sw, x = host[name]
+            Pd = torch.from_numpy(P).to(device) if r == 0 else dev_sets[0][name][0].clone()
+            d[name] = (Pd, dev_bf16(sw, device), dev_bf16(x, device),
+                       torch.empty((1, N), dtype=torch.bfloat16, device=device))
+        dev_sets.append(d)
+    return shapes, host, dev_sets
+
+
+def run_decode(shapes, dev_sets, steps, warmup, stream, log):
+    copies = len(dev_sets)
+
+    def one_rotation():
+        for d in dev_sets:
+            for name, N, K in shapes:
+                Pd, swd, xd, od = d[name]
+                tg.bitnet_linear(xd, Pd, swd, out=od)
+
+    g = capture(one_rotation, stream)
+    reps = max(1, -(-steps // copies))
+    wreps = max(1, -(-warmup // copies))
+    time_graph(g, wreps, stream)
+    secs = time_graph(g, reps, stream)
+    n_steps = reps * copies
+    step_bytes = sum(gemv_bytes(1, N, K) for _, N, K in shapes)
+    result = {"steps": n_steps, "warmup": wreps * copies, "seconds": secs, "ms_per_step": secs / n_steps * 1e3,
+              "gbs": step_bytes * n_steps / secs / 1e9, "step_bytes": step_bytes}
+
+    # Per-projection launch durations: a graph of back-to-back launches of one
+    # shape over the rotating copies, timed with events around its replays.
+    per_shape = {}
+    for name, N, K in shapes:
+        def launches(name=name):
+            for d in dev_sets:
+                Pd, swd, xd, od = d[name]
+                tg.bitnet_linear(xd, Pd, swd, out=od)
+        gs = capture(launches, stream)
+        time_graph(gs, 2, stream)
+        r = 30
+        t = time_graph(gs, r, stream) / (r * copies)
+        per_shape[name] = {"N": N, "K": K, "us": t * 1e6, "gbs": gemv_bytes(1, N, K) / t / 1e9,
+                           "bytes": gemv_bytes(1, N, K)}
+        log(f"  {name:8s} N={N:6d} K={K:5d}: {t * 1e6:8.2f} us  {per_shape[name]['gbs']:8.1f} GB/s")
+    result["per_shape"] = per_shape
+    return result
+
+
+# ----------------------------------------------------------------------------- prefill GEMM
+
+def run_gemm(device, stream, M, log, rotate=4):
+    out = {}
+    for i, (name, N, K) in enumerate(synth.LLAMA7B_SHAPES):
+        W = synth.ternary_weights(N, K, synth.seed_for(3, 16 * i + synth.T_WEIGHT))
+        P = tg.pack_weights(torch.from_numpy(W))
+        del W
+        sw = dev_bf16(synth.weight_scale_bf16(N, K, synth.seed_for(3, 16 * i + synth.T_SCALE)), device)
+        x = dev_bf16(synth.activations_bf16(M, K, synth.seed_for(3, 16 * i + synth.T_ACT), outlier_frac=0.01), device)
+        Ps = [P.to(device)] + [None] * (rotate - 1)
+        for r in range(1, rotate):
+            Ps[r] = Ps[0].clone()
+        q, sa = tg.quantize_activation(x)
+        o = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+        ws = torch.empty((tg.linear_workspace_bytes(M, K),), dtype=torch.uint8, device=device)
+
+        def gemm_only():
+            for Pd in Ps:
+                tg.bitnet_gemm(q, Pd, sa, sw, out=o)
+
+        def linear_full():
+            for Pd in Ps:
+                tg.bitnet_linear(x, Pd, sw, out=o, workspace=ws)
+
+        def quant_only():
+            for _ in Ps:
+                tg.quantize_activation(x, out=q, scale=sa)
+
+        res = {"N": N, "K": K}
+        for tag, fn in (("gemm", gemm_only), ("linear", linear_full), ("quant", quant_only)):
+            g = capture(fn, stream)
+            time_graph(g, 2, stream)
+            reps = 10
+            t = time_graph(g, reps, stream) / (reps * rotate)
+            res[tag + "_us"] = t * 1e6
+        ops = 2.0 * M * N * K
+        res["tops"] = ops / (res["gemm_us"] * 1e-6) / 1e12
+        res["linear_tops"] = ops / (res["linear_us"] * 1e-6) / 1e12
+        res["frac_int8_peak"] = res["tops"] / INT8_PEAK_TOPS
+        out[name] = res
+        log(f"  M={M} {name:8s} N={N:6d} K={K:5d}: gemm {res['gemm_us']:8.1f} us {res['tops']:7.1f} TOPS "
+            f"({100 * res['frac_int8_peak']:.1f}% of peak); quant {res['quant_us']:.1f} us; "
+            f"linear {res['linear_us']:.1f} us")
+        del Ps, q, sa, o, ws, x
+        torch.cuda.empty_cache()
+    return out
+
+
+# ----------------------------------------------------------------------------- CPU oracle
+
+def run_cpu_baseline(host, shapes, budget_s, log):
+    import oracle  # the oracle is only ever used here, for the CPU baseline leg
+    packed = {name: oracle.pack(host[name][0]) for name, _, _ in shapes}
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for name, N, K in shapes:
+            _, _, sw, x = host[name]
+            oracle.linear(x, packed[name], sw)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 1000:
+            break
+    step_bytes = sum(gemv_bytes(1, N, K) for _, N, K in shapes)
+    gbs = step_bytes * n / el / 1e9
+    log(f"cpu oracle: {n} steps in {el:.1f} s -> {gbs:.3f} GB/s on {oracle.num_threads()} threads")
+    return {"value": gbs, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} full M=1 decode steps (all five BitNet-2B-4T projections), {el:.1f} s",
+            "ms_per_step": el / n * 1e3}
+
+
+def load_traffic(lm_head_launch_bytes):
+    """HBM traffic of the dominant kernel from the committed rocprofv3 counter runs,
+    or None if absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=220)
+    ap.add_argument("--warmup", type=int, default=22)
+    ap.add_argument("--gemm-m", type=int, default=2048)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    def log(msg):
+        if not args.quiet:
+            print(msg, file=sys.stderr, flush=True)
+
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    tg.load_library()
+    stream = torch.cuda.Stream(device)
+
+    shapes, host, dev_sets = build_decode(device, log)
+    log("decode GEMV M=1 (BitNet-2B-4T shapes):")
+    dec = run_decode(shapes, dev_sets, args.steps, args.warmup, stream, log)
+    log(f"decode step: {dec['ms_per_step'] * 1e3:.2f} us/step, {dec['gbs']:.1f} GB/s "
+        f"({100 * dec['gbs'] / HBM_PEAK_GBS:.1f}% of HBM peak)")
+    del dev_sets
+    torch.cuda.empty_cache()
+
+    gemm = None
+    if not args.no_gemm:
+        log(f"prefill GEMM M={args.gemm_m} (LLaMA-7B shapes):")
+        gemm = run_gemm(device, stream, args.gemm_m, log)
+
+    lm = dec["per_shape"]["lm_head"]
+    traffic = load_traffic(lm["bytes"])
+    roofline = {"bound": "hbm", "achieved": round(lm["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(lm["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "gemv_fused_kernel (lm_head 128256x2560, M=1)",
+                "bytes_per_launch": lm["bytes"], "avg_launch_us": round(lm["us"], 3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = run_cpu_baseline(host, shapes, args.cpu_budget, log)
+
+    line = {
+        "metric": METRIC,
+        "value": round(dec["gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": dec["steps"],
+        "warmup": dec["warmup"],
+        "ms_per_step": round(dec["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "BitNet-2B-4T decode projections at M=1 through bitnet_linear (fused quantise + GEMV): "
+                        "qkv 3840x2560, o_proj 2560x2560, gate_up 13824x2560, down 2560x6912, lm_head 128256x2560",
+            "M": 1, "step_bytes": dec["step_bytes"],
+            "per_shape_gbs": {k: round(v["gbs"], 1) for k, v in dec["per_shape"].items()},
+            "per_shape_us": {k: round(v["us"], 3) for k, v in dec["per_shape"].items()},
+            "frac_hbm_peak": round(dec["gbs"] / HBM_PEAK_GBS, 4),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if gemm is not None:
+        tot_ops = sum(2.0 * args.gemm_m * v["N"] * v["K"] for v in gemm.values())
+        tot_t = sum(v["gemm_us"] for v in gemm.values()) * 1e-6
+        line["gemm"] = {
+            "metric": f"GEMM INT8 TOPS (M={args.gemm_m}), LLaMA-7B shapes, pre-quantised activations",
+            "value": round(tot_ops / tot_t / 1e12, 1), "unit": "TOPS",
+            "frac_int8_peak": round(tot_ops / tot_t / 1e12 / INT8_PEAK_TOPS, 4),
+            "per_shape": {k: {"tops": round(v["tops"], 1), "gemm_us": round(v["gemm_us"], 2),
+                              "quant_us": round(v["quant_us"], 2), "linear_us": round(v["linear_us"], 2)}
+                          for k, v in gemm.items()},
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

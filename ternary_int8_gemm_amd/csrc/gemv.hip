@@ -71,8 +71,395 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int j) {
     return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
 }
 
+// ---------------------------------------------------------------- prologue helpers
+
+// Row scales of the MT activation rows (rows >= M count as all-zero), computed
+// by the whole workgroup: integer absmax over the bf16 magnitude bits, then
+// quant_scale.  Block 0 also writes the bf16 scales when sa_out is given.
+template <int MT, int WAVES>
+__device__ __forceinline__ void block_row_scales(const uint16_t* __restrict__ x, int M, int K, uint32_t (*red_u)[MT],
+                                                 float* s_scale, float* s_recip, uint16_t* __restrict__ sa_out,
+                                                 QuantScale (&qsc)[MT]) {
+    constexpr int NT = WAVES * 64;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    uint32_t am[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) am[m] = 0u;
+    const int n8 = K >> 3;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        if (m < M) {
+            const uint4* xv = reinterpret_cast<const uint4*>(x + (int64_t)m * K);
+            for (int i = tid; i < n8; i += NT) {
+                const uint4 v = xv[i];
+                am[m] = max(am[m], max(max(absmax_bf16x2(v.x), absmax_bf16x2(v.y)),
+                                       max(absmax_bf16x2(v.z), absmax_bf16x2(v.w))));
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const uint32_t a = wave_max_u32(am[m]);
+        if (lane == 0) red_u[wave][m] = a;
+    }
+    __syncthreads();
+    if (tid < MT) {
+        uint32_t a = 0u;
+#pragma unroll
+        for (int wv = 0; wv < WAVES; ++wv) a = max(a, red_u[wv][tid]);
+        const QuantScale qs = quant_scale(a);
+        s_scale[tid] = qs.s;
+        s_recip[tid] = qs.r;
+        if (sa_out != nullptr && blockIdx.x == 0 && tid < M) sa_out[tid] = f32_to_bf16(qs.s);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        qsc[m].s = s_scale[m];
+        qsc[m].r = s_recip[m];
+    }
+}
+
+// Quantise x[m][k0 .. k0 + len) of every row into LDS (row stride ldsz bytes),
+// 16 elements per thread-iteration, zero-filling words [len/16, words); adds
+// this thread's share of sum_k q[m][k] into sq.  len % 64 == 0.
+template <int MT, int WAVES>
+__device__ __forceinline__ void block_quantize_to_lds(uint8_t* lds_x, int ldsz, const uint16_t* __restrict__ x, int M,
+                                                      int K, int k0, int len, int words, const QuantScale (&qsc)[MT],
+                                                      int (&sq)[MT]) {
+    constexpr int NT = WAVES * 64;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        for (int wd = tid; wd < words; wd += NT) {
+            uint4 t = make_uint4(0u, 0u, 0u, 0u);
+            if (m < M && wd * 16 < len) {
+                const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)m * K + k0 + wd * 16);
+                const uint4 lo = src[0];
+                const uint4 hi = src[1];
+                const uint32_t n0 = quantize_bf16x2(lo.x, qsc[m]) | (quantize_bf16x2(lo.y, qsc[m]) << 16);
+                const uint32_t n1 = quantize_bf16x2(lo.z, qsc[m]) | (quantize_bf16x2(lo.w, qsc[m]) << 16);
+                const uint32_t n2 = quantize_bf16x2(hi.x, qsc[m]) | (quantize_bf16x2(hi.y, qsc[m]) << 16);
+                const uint32_t n3 = quantize_bf16x2(hi.z, qsc[m]) | (quantize_bf16x2(hi.w, qsc[m]) << 16);
+                int s = __builtin_amdgcn_sdot4((int)n0, 0x01010101, 0, false);
+                s = __builtin_amdgcn_sdot4((int)n1, 0x01010101, s, false);
+                s = __builtin_amdgcn_sdot4((int)n2, 0x01010101, s, false);
+                s = __builtin_amdgcn_sdot4((int)n3, 0x01010101, s, false);
+                sq[m] += s;
+                t = transpose4x4(n0, n1, n2, n3);
+            }
+            *reinterpret_cast<uint4*>(lds_x + m * ldsz + lds_word_offset(wd)) = t;
+        }
+    }
+}
+
+// Block-wide sum of each row's partial sum_k q; result in s_sumq.
+template <int MT, int WAVES>
+__device__ __forceinline__ void block_sum_q(const int (&sq)[MT], int (*red_i)[MT], int* s_sumq) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int v = wave_sum_i32(sq[m]);
+        if (lane == 0) red_i[wave][m] = v;
+    }
+    __syncthreads();
+    if (tid < MT) {
+        int s = 0;
+#pragma unroll
+        for (int wv = 0; wv < WAVES; ++wv) s += red_i[wv][tid];
+        s_sumq[tid] = s;
+    }
+    __syncthreads();
+}
+
+// Dot products of one 16-byte piece of packed weights (64 codes, 4 words)
+// with the matching 64 quantised activations of every row, read from LDS at
+// byte offset `base` of each row (the slot of word j is base + ((j ^ swz) << 4)).
+template <int MT>
+__device__ __forceinline__ void dot_piece(const uint4& wv, const uint8_t* lds_x, int ldsz, int base, int swz,
+                                          int (&a0)[MT], int (&a1)[MT], int (&a2)[MT]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t p = word_of(wv, j);
+        const uint32_t c0 = p & 0x03030303u;
+        const uint32_t c1 = p & 0x0C0C0C0Cu;
+        const uint32_t c2 = p & 0x30303030u;
+        const uint32_t c3 = (p >> 6) & 0x03030303u;
+        const int off = base + ((j ^ swz) << 4);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint4 xq = *reinterpret_cast<const uint4*>(lds_x + m * ldsz + off);
+            a0[m] = __builtin_amdgcn_sdot4((int)c0, (int)xq.x, a0[m], false);
+            a1[m] = __builtin_amdgcn_sdot4((int)c1, (int)xq.y, a1[m], false);
+            a2[m] = __builtin_amdgcn_sdot4((int)c2, (int)xq.z, a2[m], false);
+            a0[m] = __builtin_amdgcn_sdot4((int)c3, (int)xq.w, a0[m], false);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- streaming kernel
+//
+// Workgroup b owns the contiguous 8-row units [b*UPB, (b+1)*UPB); its four
+// waves take every fourth unit.  A wave's work is a flat sequence of items
+// (unit, 512-weight step); a ring of D 16-byte weight loads runs D items ahead
+// of the items being multiplied, across unit boundaries.
+//
+//  * Every ring load is unconditional, so the in-order load counter lets the
+//    compiler wait for exactly the oldest load and keep D-1 in flight.  Loads
+//    past the wave's work re-read its last unit and are never used.
+//  * A load address is a wave-uniform base (unit row pointer + 128 B per step,
+//    scalar registers) plus a per-lane offset (row within the unit, 16-byte
+//    piece) that only changes at unit boundaries, so the steady loop spends no
+//    vector instructions on addressing.  Rows past N re-read row N-1 and pieces
+//    past the row end (K % 512 != 0) re-read the row's last 16 bytes; their x
+//    is zero or their result is dropped.
+//  * Quantised x sits in LDS in 64-byte segments padded to 80 bytes: the eight
+//    lanes of a row then hit eight disjoint 4-bank groups, and a lane's four
+//    16-byte reads are one base address with immediate offsets.
+//
+// Prologue.  All global reads it needs (this thread's XW 16-element words of
+// x, and at most one weight scale) are issued before the ring, so waiting for
+// them never waits for weights.  x is read once and kept in registers: the
+// block absmax (one barrier), then every thread derives the scales itself,
+// quantises its words into LDS and publishes its share of sum_k q (second
+// barrier).  The weight scales of the workgroup's rows sit in LDS, so the
+// per-unit epilogue issues no vector loads.  Needs MT * Kpad <= GV_LDS_BUDGET
+// and UPB * 8 <= 256.
+constexpr int GV_SEG = 80;  // LDS bytes per 64-element segment of quantised x
+
+template <int MT>
+__device__ __forceinline__ void dot_piece_padded(const uint4& wv, const uint8_t* lds_row0, int row_stride,
+                                                 int (&a0)[MT], int (&a1)[MT], int (&a2)[MT]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t p = word_of(wv, j);
+        const uint32_t c0 = p & 0x03030303u;
+        const uint32_t c1 = p & 0x0C0C0C0Cu;
+        const uint32_t c2 = p & 0x30303030u;
+        const uint32_t c3 = (p >> 6) & 0x03030303u;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint4 xq = *reinterpret_cast<const uint4*>(lds_row0 + m * row_stride + j * 16);
+            a0[m] = __builtin_amdgcn_sdot4((int)c0, (int)xq.x, a0[m], false);
+            a1[m] = __builtin_amdgcn_sdot4((int)c1, (int)xq.y, a1[m], false);
+            a2[m] = __builtin_amdgcn_sdot4((int)c2, (int)xq.z, a2[m], false);
+            a0[m] = __builtin_amdgcn_sdot4((int)c3, (int)xq.w, a0[m], false);
+        }
+    }
+}
+
+template <int MT, int D, int XW, bool OUT_I32>
+__global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
+                                                          uint16_t* __restrict__ sa_out,
+                                                          const uint16_t* __restrict__ x,
+                                                          const uint8_t* __restrict__ w,
+                                                          const uint16_t* __restrict__ sw, int M, int N, int K,
+                                                          int steps, int units, int upb) {
+    constexpr int WAVES = 4;
+    constexpr int NT = WAVES * 64;
+    extern __shared__ __align__(16) uint8_t lds_x[];  // [MT][steps * 8 segments of GV_SEG bytes]
+    __shared__ uint32_t red_u[WAVES][MT];
+    __shared__ int red_i[WAVES][MT];
+    __shared__ uint16_t sw_lds[NT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps unit bookkeeping scalar
+    const int g = lane >> 3;
+    const int sl = lane & 7;
+    const int KB = K >> 2;
+    const int row_stride = steps * 8 * GV_SEG;
+    const int wpr = steps * (GV_STEP / 16);  // 16-element words per activation row in LDS
+
+    const int ub0 = blockIdx.x * upb;
+    const int ub1 = min(ub0 + upb, units);
+    const int my_units = (ub0 + wave < ub1) ? (ub1 - 1 - ub0 - wave) / WAVES + 1 : 0;
+    const int items = my_units * steps;
+
+    // ---- prologue reads, before any weight load
+    uint4 xr[XW][2];
+    int xm[XW], xw[XW];
+#pragma unroll
+    for (int i = 0; i < XW; ++i) {
+        const int idx = tid + NT * i;
+        xm[i] = idx / wpr;
+        xw[i] = idx - xm[i] * wpr;
+        if (xm[i] < M && xm[i] < MT && xw[i] * 16 < K) {
+            const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)xm[i] * K + xw[i] * 16);
+            xr[i][0] = src[0];
+            xr[i][1] = src[1];
+        } else {
+            xr[i][0] = xr[i][1] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    const int row0 = ub0 * 8;
+    const int nrows = min(ub1 * 8, N) - row0;
+    const uint16_t sw_mine = (tid < nrows && sw != nullptr) ? sw[row0 + tid] : (uint16_t)0;
+
+    // ---- the weight ring
+    const int last_step = steps - 1;
+    const bool ktail = (K % GV_STEP) != 0;  // wave-uniform
+    // this lane's 16-byte piece in a step, clamped into the row for the last step
+    const uint32_t piece = (uint32_t)(sl * 16);
+    const uint32_t piece_last = (uint32_t)min(sl * 16, KB - last_step * (GV_STEP / 4) - 16);
+    int lj = 0, lt = 0;         // load cursor: unit index (of this wave) and step
+    const uint8_t* unit_ptr;    // row 0 of the unit being loaded (wave-uniform)
+    uint32_t voff, voff_last;   // this lane's byte offset from unit_ptr (normal / last step)
+    auto set_unit = [&]() {
+        // past the wave's work (or for a wave without units) re-read a valid unit
+        const int u = min(ub0 + wave + WAVES * min(lj, max(my_units - 1, 0)), units - 1);
+        unit_ptr = w + (int64_t)u * 8 * KB;
+        const uint32_t lane_row = (uint32_t)((min(u * 8 + g, N - 1) - u * 8) * KB);
+        voff = lane_row + piece;
+        voff_last = lane_row + piece_last;
+    };
+    set_unit();
+    auto issue = [&](uint4& dst) {
+        const uint8_t* b = unit_ptr + lt * (GV_STEP / 4);
+        dst = load_stream16(b + ((ktail && lt == last_step) ? voff_last : voff));
+        if (++lt == steps) {
+            lt = 0;
+            ++lj;
+            set_unit();
+        }
+    };
+    uint4 buf[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) issue(buf[i]);
+
+    // ---- absmax of every activation row over the block
+    uint32_t am[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) am[m] = 0u;
+#pragma unroll
+    for (int i = 0; i < XW; ++i) {
+        uint32_t a = 0u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            a = max(a, max(max(absmax_bf16x2(xr[i][h].x), absmax_bf16x2(xr[i][h].y)),
+                           max(absmax_bf16x2(xr[i][h].z), absmax_bf16x2(xr[i][h].w))));
+#pragma unroll
+        for (int m = 0; m < MT; ++m) am[m] = (xm[i] == m) ? max(am[m], a) : am[m];
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const uint32_t a = wave_max_u32(am[m]);
+        if (lane == 0) red_u[wave][m] = a;
+    }
+    sw_lds[tid] = sw_mine;
+    __syncthreads();
+
+    // ---- scales (every thread), quantise own words into LDS, sum_k q
+    QuantScale qsc[MT];
+    float sa_f[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        uint32_t a = red_u[0][m];
+#pragma unroll
+        for (int wv = 1; wv < WAVES; ++wv) a = max(a, red_u[wv][m]);
+        qsc[m] = quant_scale(a);
+        sa_f[m] = bf16_to_f32(f32_to_bf16(qsc[m].s));
+    }
+    if (sa_out != nullptr && blockIdx.x == 0 && tid < M && tid < MT) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            if (m == tid) sa_out[m] = f32_to_bf16(qsc[m].s);
+    }
+    int sq[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) sq[m] = 0;
+#pragma unroll
+    for (int i = 0; i < XW; ++i) {
+        if (xm[i] < MT) {
+            QuantScale qs = qsc[0];
+#pragma unroll
+            for (int m = 1; m < MT; ++m)
+                if (xm[i] == m) qs = qsc[m];
+            const uint4 lo = xr[i][0];
+            const uint4 hi = xr[i][1];
+            const uint32_t n0 = quantize_bf16x2(lo.x, qs) | (quantize_bf16x2(lo.y, qs) << 16);
+            const uint32_t n1 = quantize_bf16x2(lo.z, qs) | (quantize_bf16x2(lo.w, qs) << 16);
+            const uint32_t n2 = quantize_bf16x2(hi.x, qs) | (quantize_bf16x2(hi.y, qs) << 16);
+            const uint32_t n3 = quantize_bf16x2(hi.z, qs) | (quantize_bf16x2(hi.w, qs) << 16);
+            int t = __builtin_amdgcn_sdot4((int)n0, 0x01010101, 0, false);
+            t = __builtin_amdgcn_sdot4((int)n1, 0x01010101, t, false);
+            t = __builtin_amdgcn_sdot4((int)n2, 0x01010101, t, false);
+            t = __builtin_amdgcn_sdot4((int)n3, 0x01010101, t, false);
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                if (xm[i] == m) sq[m] += t;
+            const int off = xm[i] * row_stride + (xw[i] >> 2) * GV_SEG + (xw[i] & 3) * 16;
+            *reinterpret_cast<uint4*>(lds_x + off) = transpose4x4(n0, n1, n2, n3);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int v = wave_sum_i32(sq[m]);
+        if (lane == 0) red_i[wave][m] = v;
+    }
+    __syncthreads();  // publishes the quantised x and the partial sums
+    int sumq2[MT];    // 2 * sum_k q[m][k]
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        int v = red_i[0][m];
+#pragma unroll
+        for (int wv = 1; wv < WAVES; ++wv) v += red_i[wv][m];
+        sumq2[m] = 2 * v;
+    }
+
+    // ---- stream
+    int a0[MT], a1[MT], a2[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) a0[m] = a1[m] = a2[m] = 0;
+
+    const uint8_t* lds_lane = lds_x + sl * GV_SEG;
+    int cj = 0, ct = 0;  // consume cursor
+    auto consume = [&](const uint4& piece) {
+        dot_piece_padded<MT>(piece, lds_lane + ct * (8 * GV_SEG), row_stride, a0, a1, a2);
+        if (++ct == steps) {  // unit complete: reduce its 8 lanes per row and write
+            const int ul = wave + WAVES * cj;  // unit index within the workgroup
+            const int n = (ub0 + ul) * 8 + g;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                int tot = a0[m] + (a1[m] >> 2) + (a2[m] >> 4);
+                tot = group8_sum(tot) - sumq2[m];
+                a0[m] = a1[m] = a2[m] = 0;
+                if ((m & 7) == sl && n < N && m < M) {
+                    if (OUT_I32)
+                        acc_out[(int64_t)m * N + n] = tot;
+                    else
+                        out[(int64_t)m * N + n] = epilogue_bf16(tot, sa_f[m], bf16_to_f32(sw_lds[ul * 8 + g]));
+                }
+            }
+            ct = 0;
+            ++cj;
+        }
+    };
+
+    int base = 0;
+    for (; base + D <= items; base += D) {  // steady state: every item issues the load D items ahead
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            consume(buf[i]);
+            issue(buf[i]);
+        }
+    }
+    const int rem = items - base;  // the last < D items are already in the ring
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        if (i < rem) consume(buf[i]);
+}
+
+// ---------------------------------------------------------------- chunked kernel
+//
+// For activations too large for LDS at once (MT * Kpad > GV_LDS_BUDGET): each
+// wave owns 8*RB rows and the K dimension is processed in LDS-sized chunks.
 template <int MT, int RB, int WAVES, bool OUT_I32>
-__global__ __launch_bounds__(WAVES * 64) void gemv_fused_kernel(uint16_t* __restrict__ out,
+__global__ __launch_bounds__(WAVES * 64) void gemv_chunked_kernel(uint16_t* __restrict__ out,
                                                                 int32_t* __restrict__ acc_out,
                                                                 uint16_t* __restrict__ sa_out,
                                                                 const uint16_t* __restrict__ x,
@@ -315,31 +702,76 @@ __global__ __launch_bounds__(64) void gemv_fused_plain(uint16_t* __restrict__ ou
     }
 }
 
-template <int MT, int RB, bool OUT_I32>
-hipError_t launch_fast(uint16_t* out, int32_t* acc, uint16_t* sa_out, const uint16_t* x, const uint8_t* w,
-                       const uint16_t* sw, int M, int N, int K, hipStream_t s) {
+// Workgroups of the streaming kernel: enough to fill the GPU several times
+// over, never more than there are 4-wave groups of units.
+constexpr int GV_STREAM_MAX_BLOCKS = 512;
+
+template <int MT, int D, bool OUT_I32>
+hipError_t launch_stream_xw(int xw, dim3 grid, size_t lds, hipStream_t s, uint16_t* out, int32_t* acc, uint16_t* sa_out,
+                            const uint16_t* x, const uint8_t* w, const uint16_t* sw, int M, int N, int K, int steps,
+                            int units, int upb) {
+    if (xw <= 1)
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 1, OUT_I32>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
+                           sw, M, N, K, steps, units, upb);
+    else if (xw <= 2)
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 2, OUT_I32>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
+                           sw, M, N, K, steps, units, upb);
+    else if (xw <= 4)
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 4, OUT_I32>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
+                           sw, M, N, K, steps, units, upb);
+    else
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 8, OUT_I32>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
+                           sw, M, N, K, steps, units, upb);
+    return hipGetLastError();
+}
+
+template <int MT, bool OUT_I32>
+hipError_t launch_stream(uint16_t* out, int32_t* acc, uint16_t* sa_out, const uint16_t* x, const uint8_t* w,
+                         const uint16_t* sw, int M, int N, int K, hipStream_t s) {
+    const int steps = (K + GV_STEP - 1) / GV_STEP;
+    const int units = (N + 7) / 8;
+    // At most 32 units (256 rows, one weight scale per thread) per workgroup;
+    // otherwise as few workgroups as keep the GPU full.
+    int blocks = (units + 3) / 4;
+    if (blocks > GV_STREAM_MAX_BLOCKS) blocks = GV_STREAM_MAX_BLOCKS;
+    if (blocks < (units + 31) / 32) blocks = (units + 31) / 32;
+    const int upb = (units + blocks - 1) / blocks;
+    blocks = (units + upb - 1) / upb;
+    const size_t lds = (size_t)MT * steps * 8 * GV_SEG;
+    const int xw = (MT * steps * (GV_STEP / 16) + 255) / 256;  // x words per thread (<= 8 by the budget)
+    // Ring depth: 16 loads per lane for long rows, 8 normally, 4 when the MT
+    // accumulators already take most of the register file.
+    constexpr int D_SHORT = MT >= 8 ? 4 : 8;
+    constexpr int D_LONG = MT == 1 ? 16 : D_SHORT;
+    if (steps >= 12)
+        return launch_stream_xw<MT, D_LONG, OUT_I32>(xw, dim3(blocks), lds, s, out, acc, sa_out, x, w, sw, M, N, K,
+                                                     steps, units, upb);
+    return launch_stream_xw<MT, D_SHORT, OUT_I32>(xw, dim3(blocks), lds, s, out, acc, sa_out, x, w, sw, M, N, K, steps,
+                                                  units, upb);
+}
+
+template <int MT, bool OUT_I32>
+hipError_t launch_chunked(uint16_t* out, int32_t* acc, uint16_t* sa_out, const uint16_t* x, const uint8_t* w,
+                          const uint16_t* sw, int M, int N, int K, hipStream_t s) {
     constexpr int WAVES = 4;
+    constexpr int RB = 1;
     constexpr int ROWS = WAVES * 8 * RB;
-    int kc_max = (GV_LDS_BUDGET / MT) / GV_STEP * GV_STEP;
+    const int kc_max = (GV_LDS_BUDGET / MT) / GV_STEP * GV_STEP;
     const int kpad = (K + GV_STEP - 1) / GV_STEP * GV_STEP;
     const int KC = kpad < kc_max ? kpad : kc_max;
     const size_t lds = (size_t)MT * KC;
     const unsigned blocks = (unsigned)((N + ROWS - 1) / ROWS);
-    hipLaunchKernelGGL((gemv_fused_kernel<MT, RB, WAVES, OUT_I32>), dim3(blocks), dim3(WAVES * 64), lds, s, out, acc,
-                       sa_out, x, w, sw, M, N, K, KC);
+    hipLaunchKernelGGL((gemv_chunked_kernel<MT, RB, WAVES, OUT_I32>), dim3(blocks), dim3(WAVES * 64), lds, s, out,
+                       acc, sa_out, x, w, sw, M, N, K, KC);
     return hipGetLastError();
 }
 
-// Row blocks per wave: as many as keep >= 512 workgroups, at most the cap for MT.
 template <int MT, bool OUT_I32>
-hipError_t dispatch_rb(uint16_t* out, int32_t* acc, uint16_t* sa_out, const uint16_t* x, const uint8_t* w,
+hipError_t dispatch_mt(uint16_t* out, int32_t* acc, uint16_t* sa_out, const uint16_t* x, const uint8_t* w,
                        const uint16_t* sw, int M, int N, int K, hipStream_t s) {
-    constexpr int RB_CAP = MT <= 2 ? 4 : (MT <= 4 ? 2 : 1);
-    if (RB_CAP >= 4 && (int64_t)N >= 512 * 128)
-        return launch_fast<MT, (RB_CAP >= 4 ? 4 : 1), OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
-    if (RB_CAP >= 2 && (int64_t)N >= 512 * 64)
-        return launch_fast<MT, (RB_CAP >= 2 ? 2 : 1), OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
-    return launch_fast<MT, 1, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
+    const int64_t kpad = (K + GV_STEP - 1) / GV_STEP * GV_STEP;
+    if (MT * kpad <= GV_LDS_BUDGET) return launch_stream<MT, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
+    return launch_chunked<MT, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
 }
 
 template <bool OUT_I32>
@@ -351,11 +783,11 @@ hipError_t dispatch(uint16_t* out, int32_t* acc, uint16_t* sa_out, const uint16_
                            M, N, K);
         return hipGetLastError();
     }
-    if (M == 1) return dispatch_rb<1, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
-    if (M == 2) return dispatch_rb<2, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
-    if (M <= 4) return dispatch_rb<4, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
-    if (M <= 8) return dispatch_rb<8, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
-    return dispatch_rb<16, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
+    if (M == 1) return dispatch_mt<1, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
+    if (M == 2) return dispatch_mt<2, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
+    if (M <= 4) return dispatch_mt<4, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
+    if (M <= 8) return dispatch_mt<8, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
+    return dispatch_mt<16, OUT_I32>(out, acc, sa_out, x, w, sw, M, N, K, s);
 }
 
 }  // namespace
