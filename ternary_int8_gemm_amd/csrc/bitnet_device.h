@@ -13,6 +13,7 @@ namespace bitnet {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 // 16-byte streaming load (nontemporal hint: data used once, keep it out of the caches' way).
 __device__ __forceinline__ uint4 load_stream16(const void* p) {

@@ -42,38 +42,41 @@ namespace bitnet {
 
 namespace {
 
-constexpr int GM_BM = 128;
-constexpr int GM_BN = 128;
-constexpr int GM_THREADS = 256;
+constexpr int GM_BM = 256;      // block tile rows
+constexpr int GM_BN = 128;      // block tile columns
+constexpr int GM_KS = 128;      // K per pipeline stage (4 MFMA k-steps of 32)
+constexpr int GM_KSTEPS = GM_KS / 32;
+constexpr int GM_WAVES = 8;     // 4 along M x 2 along N, each a 64 x 64 wave tile
+constexpr int GM_THREADS = GM_WAVES * 64;
+constexpr int GM_FRAG = 1024;   // bytes of one 32 x 32 int8 MFMA operand fragment
+constexpr int GM_A_STAGE = (GM_BM / 32) * GM_KSTEPS * GM_FRAG;  // 32 KB
+constexpr int GM_B_STAGE = (GM_BN / 32) * GM_KSTEPS * GM_FRAG;  // 16 KB
+// Depth of the global-load pipeline: the loads of stage k + GM_AHEAD are issued
+// while stage k is multiplied (register-staged); LDS is double-buffered.
+constexpr int GM_AHEAD = 3;
+constexpr size_t GM_LDS_BYTES = 2 * (size_t)(GM_A_STAGE + GM_B_STAGE);
 
-template <int KT>
-struct GemmCfg {
-    static constexpr int S = KT / 64;                 // MFMA k-steps per K-tile
-    static constexpr int ROWB = KT + 16;              // LDS bytes per A row (padded)
-    static constexpr int GROUPS = KT / 16;            // 16-byte A pieces per row per K-tile
-    static constexpr int PPT = GM_BM * GROUPS / GM_THREADS;  // A pieces per thread
-    static constexpr int LDS_A = GM_BM * ROWB;        // one buffer
-    static constexpr size_t LDS_BYTES = 2 * (size_t)LDS_A + GM_BM * sizeof(int);
-};
-
-// 4x4 byte transpose (see gemv.hip): t_e byte r = element 4r + e.
-__device__ __forceinline__ uint4 transpose16(const uint4& n) {
-    const uint32_t u01lo = __builtin_amdgcn_perm(n.y, n.x, 0x05010400u);
-    const uint32_t u01hi = __builtin_amdgcn_perm(n.y, n.x, 0x07030602u);
-    const uint32_t u23lo = __builtin_amdgcn_perm(n.w, n.z, 0x05010400u);
-    const uint32_t u23hi = __builtin_amdgcn_perm(n.w, n.z, 0x07030602u);
-    uint4 t;
-    t.x = __builtin_amdgcn_perm(u23lo, u01lo, 0x05040100u);
-    t.y = __builtin_amdgcn_perm(u23lo, u01lo, 0x07060302u);
-    t.z = __builtin_amdgcn_perm(u23hi, u01hi, 0x05040100u);
-    t.w = __builtin_amdgcn_perm(u23hi, u01hi, 0x07060302u);
-    return t;
+// Signed weights of one packed byte, in natural order: byte e of the result is
+// code(e) - 2 for the code in bits 2e..2e+1 of b (b < 256).  The byte is
+// spread with two shift-ors (b | b<<6 | b<<12 | b<<18 puts bits 2e..2e+1 of b
+// at bits 8e..8e+1), masked to 2 bits per byte, and the codes are mapped by a
+// byte permute through the table [0xFE, 0xFF, 0x00, 0x01] (code 0, never
+// produced by packing, decodes to -2 like the rest of the library).
+__device__ __forceinline__ uint32_t decode_byte(uint32_t b) {
+    uint32_t s = b | (b << 6);
+    s = s | (s << 12);
+    s &= CODE_MASK;
+    return __builtin_amdgcn_perm(0u, 0x0100FFFEu, s);
 }
 
-template <int S>
-struct BPack {
-    uint32_t d[S];
-};
+__device__ __forceinline__ v4u decode_word(uint32_t p) {
+    v4u v;
+    v.x = decode_byte(p & 0xFFu);
+    v.y = decode_byte((p >> 8) & 0xFFu);
+    v.z = decode_byte((p >> 16) & 0xFFu);
+    v.w = decode_byte(p >> 24);
+    return v;
+}
 
 __device__ __forceinline__ int xcd_remap(int bid, int total) {
     const int per = total / 8;
@@ -83,7 +86,20 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
     return xcd * per + min(xcd, rem) + idx;
 }
 
-template <int KT, bool OUT_I32>
+// 16-byte slot of fragment lane fl in a fragment of k-step ks: an XOR with an
+// even constant below 16, so that lane-contiguous fragment reads stay
+// conflict-free and the coalesced staging writes (two rows x eight 16-byte
+// chunks per 16 lanes, spread over eight (k-step, k-half) fragments) land in 16
+// distinct slots mod 16.
+__device__ __forceinline__ int frag_slot(int fl, int ks) { return fl ^ (2 * (fl >> 5) + 4 * ks); }
+
+// Registers of one stage in flight: four 16-byte A pieces and two packed B words.
+struct StageRegs {
+    v4u a0, a1, a2, a3;
+    uint32_t b0, b1;
+};
+
+template <bool OUT_I32>
 __global__ __launch_bounds__(GM_THREADS) void gemm_mfma_kernel(uint16_t* __restrict__ out,
                                                                int32_t* __restrict__ acc_out,
                                                                const int8_t* __restrict__ x,
@@ -91,12 +107,11 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_mfma_kernel(uint16_t* __restr
                                                                const uint16_t* __restrict__ sa,
                                                                const uint16_t* __restrict__ sw, int M, int N, int K,
                                                                int tiles_m, int tiles_n) {
-    using C = GemmCfg<KT>;
-    constexpr int S = C::S;
+    // LDS: [2 buffers][A: 8 row-tiles x 4 k-steps | B: 4 column-tiles x 4 k-steps]
+    // of 1 KB fragments (32 rows or columns x 32 k); fragment lane l (row or
+    // column l % 32, 16 bytes of k-half l / 32) sits in slot frag_slot(l, ks).
     extern __shared__ __align__(16) uint8_t lds[];
-    uint8_t* As0 = lds;
-    uint8_t* As1 = lds + C::LDS_A;
-    int* rowsum_lds = reinterpret_cast<int*>(lds + 2 * C::LDS_A);
+    constexpr int STAGE_BYTES = GM_A_STAGE + GM_B_STAGE;
 
     const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
     const int tm = tile / tiles_n;
@@ -106,165 +121,149 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_mfma_kernel(uint16_t* __restr
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
-    const int j16 = lane & 15;
-    const int g4 = lane >> 4;
-    const int64_t KB = K >> 2;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1;   // 64-row slab (row-tiles 2wm, 2wm+1)
+    const int wn = wave & 1;    // 64-column slab (column tiles 2wn, 2wn+1)
+    const int KB = K >> 2;
+    const int nk = K / GM_KS;
 
-    // A staging: piece p = tid + 256 i -> row p / GROUPS, 16-byte group p % GROUPS.
-    const int8_t* a_src[C::PPT];
-    bool a_row_ok[C::PPT];
+    // A staging: a load instruction covers 8 rows x 128 contiguous bytes (8
+    // lanes per row); wave w stages block rows 32w .. 32w+31 in four pieces.
+    const int8_t* a_src;
+    int a_off[4];  // LDS byte offsets within a stage
+    {
+        const int qa = lane & 7;
+        const int ks = qa >> 1, kh = qa & 1;
+        const int rb = wave * 32 + (lane >> 3);
+        a_src = x + (int64_t)min(m0 + rb, M - 1) * K + qa * 16;  // rows past M repeat row M-1
 #pragma unroll
-    for (int i = 0; i < C::PPT; ++i) {
-        const int p = tid + GM_THREADS * i;
-        const int row = p / C::GROUPS;
-        const int grp = p % C::GROUPS;
-        const int gm = m0 + row;
-        a_row_ok[i] = gm < M;
-        a_src[i] = x + (int64_t)(a_row_ok[i] ? gm : 0) * K + grp * 16;
+        for (int i = 0; i < 4; ++i) {
+            const int r = rb + 8 * i;
+            a_off[i] = ((r >> 5) * GM_KSTEPS + ks) * GM_FRAG + frag_slot((r & 31) + 32 * kh, ks) * 16;
+        }
     }
-    // B: this lane's column in each of the wave's four 16-column tiles.
-    const uint8_t* b_src[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-        const int gn = min(n0 + wn * 64 + ct * 16 + j16, N - 1);
-        b_src[ct] = w + (int64_t)gn * KB + g4 * 4 * S;
+    const int64_t a_row8 = (int64_t)8 * K;  // the next piece is 8 rows down
+    const bool a_clamp = m0 + GM_BM > M;     // rows past M: recompute each piece's row
+    // B staging: thread t loads the two packed words 2h, 2h+1 (h = t % 4) of
+    // block column t / 4 (32 weights) and writes them to their fragment slots.
+    const uint8_t* b_src;
+    int b_off0, b_off1;
+    {
+        const int h = tid & 3;
+        const int cb = tid >> 2;
+        b_src = w + (int64_t)min(n0 + cb, N - 1) * KB + h * 8;  // columns past N repeat column N-1
+        const int q0 = 2 * h, q1 = 2 * h + 1;
+        b_off0 = GM_A_STAGE + ((cb >> 5) * GM_KSTEPS + (q0 >> 1)) * GM_FRAG + frag_slot((cb & 31) + 32 * (q0 & 1), q0 >> 1) * 16;
+        b_off1 = GM_A_STAGE + ((cb >> 5) * GM_KSTEPS + (q1 >> 1)) * GM_FRAG + frag_slot((cb & 31) + 32 * (q1 & 1), q1 >> 1) * 16;
     }
+    int rd[GM_KSTEPS];  // this lane's fragment slot (bytes) per k-step
+#pragma unroll
+    for (int ks = 0; ks < GM_KSTEPS; ++ks) rd[ks] = frag_slot(lane, ks) * 16;
 
-    uint4 a_reg[C::PPT];
-    BPack<S> b_cur[4], b_nxt[4];
-    int rs[C::PPT];
-#pragma unroll
-    for (int i = 0; i < C::PPT; ++i) rs[i] = 0;
-
-    auto load_a = [&](int kt) {
-        const int kb = kt * KT;
-#pragma unroll
-        for (int i = 0; i < C::PPT; ++i) {
-            const int grp = (tid + GM_THREADS * i) % C::GROUPS;
-            if (a_row_ok[i] && kb + grp * 16 < K)
-                a_reg[i] = *reinterpret_cast<const uint4*>(a_src[i] + kb);
-            else
-                a_reg[i] = make_uint4(0u, 0u, 0u, 0u);
+    // Loads of stage s (clamped to the last stage, so every step issues the
+    // same loads and the waits the compiler derives are exact).
+    auto a_ptr = [&](int i, int kb) -> const int8_t* {
+        if (a_clamp) {
+            const int r = min(m0 + wave * 32 + (lane >> 3) + 8 * i, M - 1);
+            return x + (int64_t)r * K + (lane & 7) * 16 + kb;
         }
+        return a_src + i * a_row8 + kb;
     };
-    auto load_b = [&](int kt, BPack<S> (&dst)[4]) {
-        const int kb = kt * KT;
-        const bool ok = kb + g4 * 16 * S < K;  // K % 64 == 0: a lane's bytes are all in range or all out
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            if (ok) {
-                if constexpr (S == 4) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(b_src[ct] + (kb >> 2));
-                    dst[ct].d[0] = v.x; dst[ct].d[1] = v.y; dst[ct].d[2] = v.z; dst[ct].d[3] = v.w;
-                } else if constexpr (S == 2) {
-                    const uint2 v = *reinterpret_cast<const uint2*>(b_src[ct] + (kb >> 2));
-                    dst[ct].d[0] = v.x; dst[ct].d[1] = v.y;
-                } else {
-                    dst[ct].d[0] = *reinterpret_cast<const uint32_t*>(b_src[ct] + (kb >> 2));
-                }
-            } else {
-#pragma unroll
-                for (int s = 0; s < S; ++s) dst[ct].d[s] = 0u;
-            }
-        }
+    auto load_stage = [&](int s, StageRegs& r) {
+        const int kb = min(s, nk - 1) * GM_KS;
+        r.a0 = *reinterpret_cast<const v4u*>(a_ptr(0, kb));
+        r.a1 = *reinterpret_cast<const v4u*>(a_ptr(1, kb));
+        r.a2 = *reinterpret_cast<const v4u*>(a_ptr(2, kb));
+        r.a3 = *reinterpret_cast<const v4u*>(a_ptr(3, kb));
+        const uint2 b = *reinterpret_cast<const uint2*>(b_src + (kb >> 2));
+        r.b0 = b.x;
+        r.b1 = b.y;
     };
-    auto store_a = [&](uint8_t* As) {
-#pragma unroll
-        for (int i = 0; i < C::PPT; ++i) {
-            const int p = tid + GM_THREADS * i;
-            const int row = p / C::GROUPS;
-            const int grp = p % C::GROUPS;
-            int s = __builtin_amdgcn_sdot4((int)a_reg[i].x, 0x01010101, rs[i], false);
-            s = __builtin_amdgcn_sdot4((int)a_reg[i].y, 0x01010101, s, false);
-            s = __builtin_amdgcn_sdot4((int)a_reg[i].z, 0x01010101, s, false);
-            rs[i] = __builtin_amdgcn_sdot4((int)a_reg[i].w, 0x01010101, s, false);
-            *reinterpret_cast<uint4*>(As + row * C::ROWB + grp * 16) = transpose16(a_reg[i]);
-        }
+    auto store_stage = [&](int s, const StageRegs& r) {
+        uint8_t* S = lds + (s & 1) * STAGE_BYTES;
+        *reinterpret_cast<v4u*>(S + a_off[0]) = r.a0;
+        *reinterpret_cast<v4u*>(S + a_off[1]) = r.a1;
+        *reinterpret_cast<v4u*>(S + a_off[2]) = r.a2;
+        *reinterpret_cast<v4u*>(S + a_off[3]) = r.a3;
+        *reinterpret_cast<v4u*>(S + b_off0) = decode_word(r.b0);
+        *reinterpret_cast<v4u*>(S + b_off1) = decode_word(r.b1);
     };
 
-    v4i acc[4][4];
+    v16i acc[2][2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = v4i{0, 0, 0, 0};
+        for (int c = 0; c < 2; ++c) acc[mt][c] = v16i{};
 
-    auto compute = [&](const uint8_t* As, const BPack<S> (&b)[4]) {
+    auto compute_stage = [&](int s) {
+        const uint8_t* A = lds + (s & 1) * STAGE_BYTES + (wm * 2) * GM_KSTEPS * GM_FRAG;
+        const uint8_t* B = lds + (s & 1) * STAGE_BYTES + GM_A_STAGE + (wn * 2) * GM_KSTEPS * GM_FRAG;
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            v4i af[4], bf[4];
+        for (int ks = 0; ks < GM_KSTEPS; ++ks) {
+            v4i af[2], bf[2];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                af[mt] = *reinterpret_cast<const v4i*>(As + (wm * 64 + mt * 16 + j16) * C::ROWB + (g4 * S + s) * 16);
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                const uint32_t p = b[ct].d[s];
-                bf[ct] = v4i{(int)(p & CODE_MASK), (int)((p >> 2) & CODE_MASK), (int)((p >> 4) & CODE_MASK),
-                             (int)((p >> 6) & CODE_MASK)};
+            for (int t = 0; t < 2; ++t) {
+                af[t] = *reinterpret_cast<const v4i*>(A + (t * GM_KSTEPS + ks) * GM_FRAG + rd[ks]);
+                bf[t] = *reinterpret_cast<const v4i*>(B + (t * GM_KSTEPS + ks) * GM_FRAG + rd[ks]);
             }
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct)
-                    acc[mt][ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[mt], bf[ct], acc[mt][ct], 0, 0, 0);
+                for (int c = 0; c < 2; ++c)
+                    acc[mt][c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mt], bf[c], acc[mt][c], 0, 0, 0);
         }
     };
 
-    const int nk = (K + KT - 1) / KT;
-    load_a(0);
-    load_b(0, b_cur);
-    store_a(As0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        uint8_t* cur = (kt & 1) ? As1 : As0;
-        uint8_t* nxt = (kt & 1) ? As0 : As1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            load_a(kt + 1);
-            load_b(kt + 1, b_nxt);
-        }
-        compute(cur, b_cur);
-        if (more) store_a(nxt);
-        __syncthreads();
-        if (more) {
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) b_cur[ct] = b_nxt[ct];
-        }
-    }
+    // Stages k+1 .. k+3 sit in three register sets used in a fixed rotation, so
+    // every register is named statically (no array indexing, no copies).
+    static_assert(GM_AHEAD == 3, "the rotation below is written out for three sets");
+    StageRegs r0, r1, r2;
+    load_stage(0, r0);
+    load_stage(1, r1);
+    load_stage(2, r2);
+    store_stage(0, r0);
+    load_stage(3, r0);
 
-    // Row sums of the A tile: the GROUPS threads of a row are consecutive lanes.
-#pragma unroll
-    for (int i = 0; i < C::PPT; ++i) {
-        int v = rs[i];
-        v += dpp_mov<DPP_QUAD_XOR1>(v);
-        v += dpp_mov<DPP_QUAD_XOR2>(v);
-        v += dpp_mov<DPP_ROW_HALF_MIRROR>(v);
-        if constexpr (C::GROUPS == 16) v += dpp_mov<DPP_ROW_MIRROR>(v);
-        const int p = tid + GM_THREADS * i;
-        if ((p % C::GROUPS) == 0) rowsum_lds[p / C::GROUPS] = v;
+    // Every step issues its loads and LDS stores unconditionally (stage indices
+    // past the end are clamped and never multiplied), so the number of loads
+    // between any two points is the same on every path and the compiler's
+    // waits are exact.
+#define BITNET_GEMM_STEP(K_, R_)                                       \
+    __syncthreads(); /* stage K_ visible; the other buffer is free */ \
+    store_stage((K_) + 1, R_);                                         \
+    load_stage((K_) + 1 + GM_AHEAD, R_);                               \
+    if ((K_) < nk) compute_stage(K_); /* uniform */
+    for (int k = 0; k < nk; k += GM_AHEAD) {
+        BITNET_GEMM_STEP(k, r1)
+        BITNET_GEMM_STEP(k + 1, r2)
+        BITNET_GEMM_STEP(k + 2, r0)
     }
-    __syncthreads();
+#undef BITNET_GEMM_STEP
 
+    // ---- epilogue straight from the accumulators: register r of lane l of a
+    //      32 x 32 tile holds row 8(r/4) + 4(l/32) + r%4, column l%32
+    float swf[2];
+    int gcol[2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int c = 0; c < 2; ++c) {
+        gcol[c] = n0 + (wn * 2 + c) * 32 + (lane & 31);
+        swf[c] = (!OUT_I32 && gcol[c] < N) ? bf16_to_f32(sw[gcol[c]]) : 0.0f;
+    }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int lrow = wm * 64 + mt * 16 + g4 * 4 + r;
-            const int gm = m0 + lrow;
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int gm = m0 + (wm * 2 + mt) * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
             if (gm >= M) continue;
-            const int corr = 2 * rowsum_lds[lrow];
             const float fa = OUT_I32 ? 0.0f : bf16_to_f32(sa[gm]);
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                const int gn = n0 + wn * 64 + ct * 16 + j16;
-                if (gn >= N) continue;
-                const int v = acc[mt][ct][r] - corr;
+            for (int c = 0; c < 2; ++c) {
+                if (gcol[c] >= N) continue;
+                const int v = acc[mt][c][r];
                 if (OUT_I32)
-                    acc_out[(int64_t)gm * N + gn] = v;
+                    acc_out[(int64_t)gm * N + gcol[c]] = v;
                 else
-                    out[(int64_t)gm * N + gn] = epilogue_bf16(v, fa, bf16_to_f32(sw[gn]));
+                    out[(int64_t)gm * N + gcol[c]] = epilogue_bf16(v, fa, swf[c]);
             }
         }
     }
@@ -295,21 +294,22 @@ __global__ __launch_bounds__(64) void gemm_plain(uint16_t* __restrict__ out, int
     }
 }
 
-constexpr int GEMM_KT = 128;
-
 template <bool OUT_I32>
 hipError_t dispatch(uint16_t* out, int32_t* acc, const int8_t* x, const uint8_t* w, const uint16_t* sa,
                     const uint16_t* sw, int M, int N, int K, hipStream_t s) {
-    const bool fast = (K % 64 == 0) && aligned16(x) && aligned16(w);
+    const bool fast = (K % GM_KS == 0) && aligned16(x) && aligned16(w);
     if (!fast) {
         hipLaunchKernelGGL((gemm_plain<OUT_I32>), dim3((unsigned)N), dim3(64), 0, s, out, acc, x, w, sa, sw, M, N, K);
         return hipGetLastError();
     }
-    using C = GemmCfg<GEMM_KT>;
     const int tiles_m = (M + GM_BM - 1) / GM_BM;
     const int tiles_n = (N + GM_BN - 1) / GM_BN;
-    hipLaunchKernelGGL((gemm_mfma_kernel<GEMM_KT, OUT_I32>), dim3((unsigned)(tiles_m * tiles_n)), dim3(GM_THREADS),
-                       C::LDS_BYTES, s, out, acc, x, w, sa, sw, M, N, K, tiles_m, tiles_n);
+    // more than 64 KB of dynamic LDS: raise the kernel's limit (idempotent)
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mfma_kernel<OUT_I32>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)GM_LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemm_mfma_kernel<OUT_I32>), dim3((unsigned)(tiles_m * tiles_n)), dim3(GM_THREADS),
+                       GM_LDS_BYTES, s, out, acc, x, w, sa, sw, M, N, K, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
