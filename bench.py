@@ -15,8 +15,18 @@ bitnet_linear time), the roofline of the dominant kernel (the lm_head GEMV
 launch), and the CPU oracle timed on the host as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Profiling helpers (not part of the timed benchmark):
+  python bench.py --pmc-target            eager launches for rocprofv3 --pmc passes: a 256 MiB
+                                          device copy (counter calibration), then the lm_head GEMV
+  python bench.py --summarize-pmc F W     turn the FETCH_SIZE (F) and WRITE_SIZE (W) rocprofv3 csv
+                                          output folders into profiles/gemv_lm_head_m1_traffic.{json,md}
+  python bench.py --summarize-trace T     turn a rocprofv3 --kernel-trace --stats csv output folder
+                                          into a per-kernel, per-grid table on stdout
 """
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -37,6 +47,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published (5.0 POPS)
 POOL_BYTES = 1 << 30           # rotating weight pool, >= 4x the 256 MB last-level cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_lm_head_m1_traffic.json")
+CALIB_COPY_BYTES = 256 << 20   # plain device copy used to scale the rocprofv3 byte counters
 KERNEL_SOURCES = ["ternary_int8_gemm_amd/csrc/gemv.hip", "ternary_int8_gemm_amd/csrc/bitnet_device.h"]
 
 
@@ -239,6 +250,151 @@ def load_traffic(lm_head_launch_bytes):
     return t.get("bytes_per_launch")
 
 
+# ----------------------------------------------------------------------------- profiling helpers
+
+def lm_head_inputs(device, copies):
+    """The lm_head projection of the decode step (same seeds as the timed run), with `copies` weight copies."""
+    i, (name, N, K) = next((i, s) for i, s in enumerate(synth.BITNET_2B_DECODE) if s[0] == "lm_head")
+    W = synth.ternary_weights(N, K, synth.seed_for(1, 16 * i + synth.T_WEIGHT))
+    P = tg.pack_weights(torch.from_numpy(W)).to(device)
+    del W
+    Ps = [P] + [P.clone() for _ in range(copies - 1)]
+    sw = dev_bf16(synth.weight_scale_bf16(N, K, synth.seed_for(1, 16 * i + synth.T_SCALE)), device)
+    x = dev_bf16(synth.activations_bf16(1, K, synth.seed_for(1, 16 * i + synth.T_ACT)), device)
+    return N, K, Ps, sw, x
+
+
+def run_pmc_target(device, reps=3):
+    """Eager launches for hardware-counter passes (counter collection serialises
+    dispatches, so no graph): a plain device-to-device copy of CALIB_COPY_BYTES,
+    then the lm_head GEMV over four weight copies (328 MB, more than the 256 MB
+    last-level cache)."""
+    a = torch.full((CALIB_COPY_BYTES,), 7, dtype=torch.uint8, device=device)
+    b = torch.empty_like(a)
+    N, K, Ps, sw, x = lm_head_inputs(device, 4)
+    out = torch.empty((1, N), dtype=torch.bfloat16, device=device)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        for P in Ps:
+            tg.bitnet_linear(x, P, sw, out=out)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_target": "done", "copy_bytes": CALIB_COPY_BYTES, "gemv_launches": reps * len(Ps),
+                      "N": N, "K": K}), flush=True)
+
+
+def _csv_rows(folder, suffix):
+    rows = []
+    for path in sorted(glob.glob(os.path.join(folder, "**", "*" + suffix), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {folder}")
+    return rows
+
+
+def _col(row, *names):
+    low = {k.lower(): k for k in row}
+    for n in names:
+        if n.lower() in low:
+            return row[low[n.lower()]]
+    raise KeyError(f"none of {names} in {sorted(row)}")
+
+
+def _grid(row):
+    try:
+        return int(_col(row, "Grid_Size", "Grid_Size_X"))
+    except KeyError:
+        return -1
+
+
+def summarize_trace(folder):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of this script:
+    the --stats table as rocprofv3 wrote it, then the trace split by launch grid
+    (one template instance serves several projection shapes)."""
+    out = ["# rocprofv3 kernel trace of the benchmark", "",
+           "Command (from the repository root, after `cd /tmp && export TMPDIR=/tmp`):", "",
+           "    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_bench -o bench -- "
+           "python3 bench.py --steps 22 --warmup 5 --no-cpu-baseline",
+           f"    python bench.py --summarize-trace gpurun_out/trace_bench", "",
+           "## --stats (kernel_stats.csv)", "",
+           "| kernel | calls | total ms | avg us | min us | max us | % |", "|---|---:|---:|---:|---:|---:|---:|"]
+    for r in _csv_rows(folder, "kernel_stats.csv"):
+        out.append(f"| `{_col(r, 'Name')[:100]}` | {_col(r, 'Calls')} | {float(_col(r, 'TotalDurationNs')) / 1e6:.3f} | "
+                   f"{float(_col(r, 'AverageNs')) / 1e3:.3f} | {float(_col(r, 'MinNs')) / 1e3:.3f} | "
+                   f"{float(_col(r, 'MaxNs')) / 1e3:.3f} | {float(_col(r, 'Percentage')):.2f} |")
+    stats = {}
+    for r in _csv_rows(folder, "kernel_trace.csv"):
+        name = _col(r, "Kernel_Name")
+        dur = int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))
+        stats.setdefault((name, _grid(r)), []).append(dur)
+    out += ["", "## Per launch grid (kernel_trace.csv)", "",
+            "| kernel | grid (threads) | calls | avg us | min us | max us |", "|---|---|---:|---:|---:|---:|"]
+    for (name, grid), d in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| `{name[:100]}` | {grid} | {len(d)} | {sum(d) / len(d) / 1e3:.3f} | "
+                   f"{min(d) / 1e3:.3f} | {max(d) / 1e3:.3f} |")
+    print("\n".join(out))
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """HBM bytes per lm_head GEMV launch from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for the plain copy of
+    CALIB_COPY_BYTES."""
+    def per_dispatch(folder, counter):
+        rows = []
+        for r in _csv_rows(folder, "counter_collection.csv"):
+            if _col(r, "Counter_Name") == counter:
+                rows.append((_col(r, "Kernel_Name"), _grid(r), float(_col(r, "Counter_Value"))))
+        return rows
+
+    res = {}
+    for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = per_dispatch(folder, counter)
+        # The calibration copy is the largest device copy of the run (the weight
+        # clones are smaller copies with the same kernel and grid).
+        copies = [v for n, g, v in rows if "copyBuffer" in n]
+        gemv = [(g, v) for n, g, v in rows if "gemv_stream_kernel" in n]
+        if not copies or not gemv:
+            raise SystemExit(f"{counter}: copy or GEMV dispatches missing in {folder}")
+        big = [v for v in copies if v >= 0.9 * max(copies)]
+        copy_kib = sum(big) / len(big)
+        factor = CALIB_COPY_BYTES / (copy_kib * 1024.0)
+        grid = max(g for g, _ in gemv)
+        vals = [v for g, v in gemv if g == grid]
+        gemv_kib = sum(vals) / len(vals)
+        res[counter] = {"copy_kib": copy_kib, "copy_dispatches": len(big), "factor": factor, "gemv_kib": gemv_kib,
+                        "gemv_dispatches": len(vals), "grid": grid, "gemv_bytes": gemv_kib * 1024.0 * factor}
+    N, K = next((N, K) for n, N, K in synth.BITNET_2B_DECODE if n == "lm_head")
+    algo = gemv_bytes(1, N, K)
+    total = res["FETCH_SIZE"]["gemv_bytes"] + res["WRITE_SIZE"]["gemv_bytes"]
+    out = {"kernel": "gemv_stream_kernel (lm_head 128256x2560, M=1)", "kernel_source_sha256_16": kernel_source_hash(),
+           "bytes_per_launch": round(total), "algorithmic_bytes_per_launch": algo,
+           "traffic_over_algorithmic": round(total / algo, 4), "counters": res,
+           "commands": [
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --pmc-target",
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --pmc-target",
+               "python bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write"]}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    md = [f"# HBM traffic of the lm_head GEMV launch (M=1, N={N}, K={K})", "",
+          "Commands (each counter in its own pass, run from the repository root after `cd /tmp && export TMPDIR=/tmp`):", ""]
+    md += ["    " + c for c in out["commands"]]
+    md += ["", "| counter | copy of 256 MiB reads (KiB) | scale factor | GEMV launch (KiB) | GEMV bytes (scaled) |",
+           "|---|---:|---:|---:|---:|"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        r = res[c]
+        md.append(f"| {c} | {r['copy_kib']:.1f} | {r['factor']:.4f} | {r['gemv_kib']:.1f} | {r['gemv_bytes']:.0f} |")
+    md += ["", f"Traffic per launch: {total:.0f} B; algorithmic bytes per launch: {algo} B "
+           f"(packed weights N*K/4 + bf16 weight scales + bf16 x + bf16 out); ratio {total / algo:.4f}.",
+           f"Kernel source hash (gemv.hip + bitnet_device.h): {out['kernel_source_sha256_16']}."]
+    with open(TRAFFIC_FILE[:-5] + ".md", "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,7 +405,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--pmc-target", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -263,6 +429,9 @@ def main():
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
     tg.load_library()
+    if args.pmc_target:
+        run_pmc_target(device)
+        return
     stream = torch.cuda.Stream(device)
 
     shapes, host, dev_sets = build_decode(device, log)
@@ -282,7 +451,7 @@ def main():
     traffic = load_traffic(lm["bytes"])
     roofline = {"bound": "hbm", "achieved": round(lm["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(lm["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "gemv_fused_kernel (lm_head 128256x2560, M=1)",
+                "kernel": "gemv_stream_kernel (lm_head 128256x2560, M=1)",
                 "bytes_per_launch": lm["bytes"], "avg_launch_us": round(lm["us"], 3)}
 
     cpu = None

@@ -231,6 +231,12 @@ __device__ __forceinline__ void dot_piece(const uint4& wv, const uint8_t* lds_x,
 // and UPB * 8 <= 256.
 constexpr int GV_SEG = 80;  // LDS bytes per 64-element segment of quantised x
 
+// Target of the streaming kernel's loads past a wave's last unit: covers the
+// largest step offset (GV_LDS_BUDGET / GV_STEP steps of GV_STEP / 4 bytes) plus
+// one 16-byte piece per lane.
+constexpr int GV_PAD_BYTES = (GV_LDS_BUDGET / GV_STEP) * (GV_STEP / 4) + 64 * 16;
+__device__ __align__(256) uint8_t gv_pad[GV_PAD_BYTES];
+
 template <int MT>
 __device__ __forceinline__ void dot_piece_padded(const uint4& wv, const uint8_t* lds_row0, int row_stride,
                                                  int (&a0)[MT], int (&a1)[MT], int (&a2)[MT]) {
@@ -310,12 +316,16 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
     const uint8_t* unit_ptr;    // row 0 of the unit being loaded (wave-uniform)
     uint32_t voff, voff_last;   // this lane's byte offset from unit_ptr (normal / last step)
     auto set_unit = [&]() {
-        // past the wave's work (or for a wave without units) re-read a valid unit
+        // Past this wave's work the ring still issues (never consumed) loads:
+        // they read a small pad that stays cached, instead of weight lines the
+        // streaming loads have already evicted.  Selects, not branches, so the
+        // ring's loads stay in straight-line code.
+        const bool live = lj < my_units;  // wave-uniform
         const int u = min(ub0 + wave + WAVES * min(lj, max(my_units - 1, 0)), units - 1);
-        unit_ptr = w + (int64_t)u * 8 * KB;
         const uint32_t lane_row = (uint32_t)((min(u * 8 + g, N - 1) - u * 8) * KB);
-        voff = lane_row + piece;
-        voff_last = lane_row + piece_last;
+        unit_ptr = live ? w + (int64_t)u * 8 * KB : gv_pad;
+        voff = live ? lane_row + piece : (uint32_t)(lane * 16);
+        voff_last = live ? lane_row + piece_last : (uint32_t)(lane * 16);
     };
     set_unit();
     auto issue = [&](uint4& dst) {
