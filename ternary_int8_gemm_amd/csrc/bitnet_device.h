@@ -138,6 +138,16 @@ __device__ __forceinline__ uint16_t epilogue_bf16(int acc, float sa, float sw) {
     return f32_to_bf16(y);
 }
 
+// The same for two outputs, rounded to bf16 by one v_cvt_pk_bf16_f32; the
+// result holds the first in its low half.
+__device__ __forceinline__ uint32_t epilogue_bf16x2(int acc0, float sa0, int acc1, float sa1, float sw) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const float y0 = (float)acc0 * (sa0 * sw);
+    const float y1 = (float)acc1 * (sa1 * sw);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){y0, y1}, bf16x2));
+}
+
 // ----------------------------------------------------------------- 2-bit codes
 
 // For a 32-bit word of packed weights (16 codes; byte r holds the elements
@@ -145,5 +155,20 @@ __device__ __forceinline__ uint16_t epilogue_bf16(int acc, float sa, float sw) {
 // isolate element e of every byte: (p >> 2e) & 0x03030303 gives, in byte r,
 // the code of element 4r + e.
 constexpr uint32_t CODE_MASK = 0x03030303u;
+
+// 4x4 byte transpose: n_r holds elements 4r..4r+3; result t_e holds element e of
+// every n_r (t_e byte r = element 4r + e).
+__device__ __forceinline__ uint4 transpose4x4(uint32_t n0, uint32_t n1, uint32_t n2, uint32_t n3) {
+    const uint32_t u01lo = __builtin_amdgcn_perm(n1, n0, 0x05010400u);  // n0.b0 n1.b0 n0.b1 n1.b1
+    const uint32_t u01hi = __builtin_amdgcn_perm(n1, n0, 0x07030602u);  // n0.b2 n1.b2 n0.b3 n1.b3
+    const uint32_t u23lo = __builtin_amdgcn_perm(n3, n2, 0x05010400u);
+    const uint32_t u23hi = __builtin_amdgcn_perm(n3, n2, 0x07030602u);
+    uint4 t;
+    t.x = __builtin_amdgcn_perm(u23lo, u01lo, 0x05040100u);
+    t.y = __builtin_amdgcn_perm(u23lo, u01lo, 0x07060302u);
+    t.z = __builtin_amdgcn_perm(u23hi, u01hi, 0x05040100u);
+    t.w = __builtin_amdgcn_perm(u23hi, u01hi, 0x07060302u);
+    return t;
+}
 
 }  // namespace bitnet

@@ -6,35 +6,46 @@
 //   out[m][n] = epilogue(acc, scale_act[m], scale_wt[n])   (or acc itself)
 // The request post of "kernels-community/README discussion #1 (bitnet-tc kernel
 // request)" runs this on the matrix units for batched shapes; here that is
-// v_mfma_i32_16x16x64_i8 with int32 accumulators.
+// v_mfma_i32_32x32x32_i8 (32 x 32 output tile, 32 k per instruction, int32
+// accumulators).
 //
-// Data flow of one 128x128 output tile (4 waves, 2 x 2, each 64 x 64 = 4 x 4
-// MFMA tiles), per K-tile of KT elements:
+// Where the time goes on gfx950, and the layout that follows from it.  One CU
+// retires about 3840 int8 MACs per clock on the 32x32x32 MFMA, reads LDS at
+// about 184 B/clk with conflict-free ds_read_b128 and writes it at about
+// 74 B/clk with ds_write_b128.  Staging both operands as int8 bytes in LDS
+// costs more LDS time per MAC than the MFMAs take, so:
 //
-//  * A (activations, int8, row-major [M][K]) is read with 16-byte loads,
-//    4x4-byte transposed in registers and staged in LDS (double-buffered, rows
-//    padded by 16 bytes so that the fragment reads of 16 consecutive rows fall
-//    in distinct banks).  The same pass sums each row's bytes (v_dot4 with
-//    0x01010101), giving sum_k x[m][k] for free.
-//  * B (packed weights, [N][K/4]) never goes through LDS: each lane loads the
-//    4*S bytes of one column that its MFMA fragments need and expands them in
-//    registers, (p >> 2e) & 0x03030303 for e = 0..3, which are exactly the four
-//    fragment dwords in the transposed byte order of A.  The fragments carry
-//    the codes (1, 2, 3), not the weights.
-//  * MFMA: for each of the S = KT/64 steps, one 16-byte A fragment per 16-row
-//    tile from LDS, one 16-byte B fragment per 16-column tile from registers,
-//    16 MFMAs per wave.  Lane l of a fragment holds row (or column) l % 16 and
-//    the k-group l / 16; A and B use the same k order, which is all the
-//    contraction needs.
-//  * Epilogue: acc = sum(code * x) - 2 * sum_k x[m][k], then the fp32 scale
-//    step and bf16 rounding, straight from the accumulator registers.
+//  * B (packed weights) stays packed in LDS: 2 bits per weight, a quarter of
+//    the bytes to write and to read.  A lane's B operand for one MFMA is 16
+//    codes, i.e. one packed dword p of its column, expanded in registers as
+//    (p >> 2e) & 0x03030303 for e = 0..3: byte r of dword e is the code of
+//    element 4r + e.  That is 7 VALU per 16 weights, and the MFMA multiplies
+//    the codes (1, 2, 3) themselves; acc = sum(code * x) - 2 * sum_k x[m][k].
+//  * A (int8 activations) is staged through registers into LDS, each 16-byte
+//    group 4x4-byte transposed on the way so that it has the same element
+//    order as the expanded B dwords (dword e byte r = element 4r + e).  The same
+//    pass sums the row's bytes (v_dot4 with 0x01010101) for the -2 * sum_k x term.
+//  * Within a 128-element K stage, MFMA k-step s of lane half h covers elements
+//    64h + 16s .. 64h + 16s + 15: then a lane's four B dwords for the whole
+//    stage are 16 contiguous packed bytes (one ds_read_b128), and its A
+//    fragment for step s is the 16-byte group 4h + s of its row.
+//  * Block tile BM x BN with WAVES_M x WAVES_N waves, each owning a
+//    (BM/WAVES_M) x (BN/WAVES_N) tile of 32 x 32 MFMA tiles.  Larger wave tiles
+//    mean fewer LDS bytes per MAC; the register file bounds them.
+//  * LDS slots are XOR-swizzled so that the staging writes (8 rows x 8 groups
+//    per instruction for A; 32 columns x 2 halves for B) and the fragment reads
+//    (lane-contiguous) both keep every 16 lanes on distinct 16-byte bank groups.
+//  * Global loads are issued three stages ahead into three register sets and
+//    the LDS stages are double-buffered, one barrier per stage.  Every step
+//    issues the same loads (stage indices past the end are clamped and never
+//    multiplied), so the waits the compiler derives are exact.
 //
 // Tiles are assigned XCD-aware: the hardware deals workgroups round-robin to
 // the 8 XCDs, so the block index is remapped to give each XCD a contiguous run
 // of tiles that share A row-panels in its own L2.
 //
-// The fast kernel needs K % 64 == 0 and 16-byte aligned x and w; anything
-// else goes to gemm_plain (one wave per output row, same arithmetic).
+// The fast kernel needs K % 128 == 0 and 16-byte aligned x and w; anything
+// else goes to gemm_plain (one wave per output column, same arithmetic).
 #include "bitnet_device.h"
 #include "launch.h"
 
@@ -42,41 +53,27 @@ namespace bitnet {
 
 namespace {
 
-constexpr int GM_BM = 256;      // block tile rows
-constexpr int GM_BN = 128;      // block tile columns
-constexpr int GM_KS = 128;      // K per pipeline stage (4 MFMA k-steps of 32)
-constexpr int GM_KSTEPS = GM_KS / 32;
-constexpr int GM_WAVES = 8;     // 4 along M x 2 along N, each a 64 x 64 wave tile
-constexpr int GM_THREADS = GM_WAVES * 64;
-constexpr int GM_FRAG = 1024;   // bytes of one 32 x 32 int8 MFMA operand fragment
-constexpr int GM_A_STAGE = (GM_BM / 32) * GM_KSTEPS * GM_FRAG;  // 32 KB
-constexpr int GM_B_STAGE = (GM_BN / 32) * GM_KSTEPS * GM_FRAG;  // 16 KB
-// Depth of the global-load pipeline: the loads of stage k + GM_AHEAD are issued
-// while stage k is multiplied (register-staged); LDS is double-buffered.
-constexpr int GM_AHEAD = 3;
-constexpr size_t GM_LDS_BYTES = 2 * (size_t)(GM_A_STAGE + GM_B_STAGE);
+constexpr int GM_KS = 128;     // K elements per pipeline stage (4 MFMA k-steps of 32)
+constexpr int GM_FRAG = 1024;  // bytes of one 32 x 32 int8 A operand fragment (64 lanes x 16 B)
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format;
+// stride 0, so bounds are checked against the byte count in word 2).
+constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
 
-// Signed weights of one packed byte, in natural order: byte e of the result is
-// code(e) - 2 for the code in bits 2e..2e+1 of b (b < 256).  The byte is
-// spread with two shift-ors (b | b<<6 | b<<12 | b<<18 puts bits 2e..2e+1 of b
-// at bits 8e..8e+1), masked to 2 bits per byte, and the codes are mapped by a
-// byte permute through the table [0xFE, 0xFF, 0x00, 0x01] (code 0, never
-// produced by packing, decodes to -2 like the rest of the library).
-__device__ __forceinline__ uint32_t decode_byte(uint32_t b) {
-    uint32_t s = b | (b << 6);
-    s = s | (s << 12);
-    s &= CODE_MASK;
-    return __builtin_amdgcn_perm(0u, 0x0100FFFEu, s);
-}
-
-__device__ __forceinline__ v4u decode_word(uint32_t p) {
-    v4u v;
-    v.x = decode_byte(p & 0xFFu);
-    v.y = decode_byte((p >> 8) & 0xFFu);
-    v.z = decode_byte((p >> 16) & 0xFFu);
-    v.w = decode_byte(p >> 24);
-    return v;
-}
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+struct GemmShape {
+    static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+    static constexpr int MT = BM / WAVES_M / 32;  // MFMA row tiles per wave
+    static constexpr int NT = BN / WAVES_N / 32;  // MFMA column tiles per wave
+    static constexpr int A_STAGE = BM * GM_KS;     // int8, [row tile][k-step] fragments
+    static constexpr int B_STAGE = BN * GM_KS / 4; // packed, [column tile] of 32 x 32 B
+    static constexpr int STAGE = A_STAGE + B_STAGE;
+    static constexpr int A_CH = BM * (GM_KS / 16) / THREADS;  // 16-byte A groups per thread per stage
+    static constexpr int B_CH = BN * 2 / THREADS;             // 16-byte B halves per thread per stage
+    static constexpr size_t LDS = 2 * (size_t)STAGE + 8 * BM + 4 * BN;  // two stages, row sums, scales
+    static_assert(THREADS >= BM && THREADS >= BN, "one thread per block row / column fetches its scale");
+    static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "wave tiles are whole MFMA tiles");
+    static_assert(A_CH * THREADS == BM * 8 && B_CH * THREADS == BN * 2, "staging splits evenly");
+};
 
 __device__ __forceinline__ int xcd_remap(int bid, int total) {
     const int per = total / 8;
@@ -86,184 +83,260 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
     return xcd * per + min(xcd, rem) + idx;
 }
 
-// 16-byte slot of fragment lane fl in a fragment of k-step ks: an XOR with an
-// even constant below 16, so that lane-contiguous fragment reads stay
-// conflict-free and the coalesced staging writes (two rows x eight 16-byte
-// chunks per 16 lanes, spread over eight (k-step, k-half) fragments) land in 16
-// distinct slots mod 16.
-__device__ __forceinline__ int frag_slot(int fl, int ks) { return fl ^ (2 * (fl >> 5) + 4 * ks); }
+// Byte offset, within a 1 KB A fragment of k-step s, of the 16-byte slot of
+// fragment lane l (row l % 32, lane half h = l / 32).  Staging writes: 16
+// consecutive lanes are two rows x the eight groups 2h' + ... of a 128-byte row
+// chunk, which the XOR with 2 * (4h + s) spreads over 16 distinct slots mod 16;
+// fragment reads: 16 consecutive lanes share h, so an XOR keeps them distinct.
+__device__ __forceinline__ int a_slot(int l, int s) { return (l ^ (2 * (4 * (l >> 5) + s))) * 16; }
 
-// Registers of one stage in flight: four 16-byte A pieces and two packed B words.
+// Byte offset, within the 1 KB packed B tile of 32 columns, of half h of
+// column n (n < 32): 16 consecutive columns of one half fall on 16 distinct
+// slots mod 16, as do eight columns x both halves.
+__device__ __forceinline__ int b_slot(int n, int h) { return (2 * n + (h ^ ((n >> 3) & 1))) * 16; }
+
+template <int A_CH, int B_CH>
 struct StageRegs {
-    v4u a0, a1, a2, a3;
-    uint32_t b0, b1;
+    v4u a[A_CH];
+    v4u b[B_CH];
 };
 
-template <bool OUT_I32>
-__global__ __launch_bounds__(GM_THREADS) void gemm_mfma_kernel(uint16_t* __restrict__ out,
-                                                               int32_t* __restrict__ acc_out,
-                                                               const int8_t* __restrict__ x,
-                                                               const uint8_t* __restrict__ w,
-                                                               const uint16_t* __restrict__ sa,
-                                                               const uint16_t* __restrict__ sw, int M, int N, int K,
-                                                               int tiles_m, int tiles_n) {
-    // LDS: [2 buffers][A: 8 row-tiles x 4 k-steps | B: 4 column-tiles x 4 k-steps]
-    // of 1 KB fragments (32 rows or columns x 32 k); fragment lane l (row or
-    // column l % 32, 16 bytes of k-half l / 32) sits in slot frag_slot(l, ks).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int WAVES_PER_EU, bool OUT_I32>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
+void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out, const int8_t* __restrict__ x,
+                      const uint8_t* __restrict__ w, const uint16_t* __restrict__ sa,
+                      const uint16_t* __restrict__ sw, int M, int N, int K, int tiles_m, int tiles_n) {
+    using S = GemmShape<BM, BN, WAVES_M, WAVES_N>;
+    constexpr int MT = S::MT, NT = S::NT, A_CH = S::A_CH, B_CH = S::B_CH;
     extern __shared__ __align__(16) uint8_t lds[];
-    constexpr int STAGE_BYTES = GM_A_STAGE + GM_B_STAGE;
+    int* rowsum = reinterpret_cast<int*>(lds + 2 * S::STAGE);
+    float* rowscale = reinterpret_cast<float*>(lds + 2 * S::STAGE + 4 * BM);
+    float* colscale = reinterpret_cast<float*>(lds + 2 * S::STAGE + 8 * BM);
 
     const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
     const int tm = tile / tiles_n;
     const int tn = tile - tm * tiles_n;
-    const int m0 = tm * GM_BM;
-    const int n0 = tn * GM_BN;
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1;   // 64-row slab (row-tiles 2wm, 2wm+1)
-    const int wn = wave & 1;    // 64-column slab (column tiles 2wn, 2wn+1)
+    const int wm = wave / WAVES_N;
+    const int wn = wave - wm * WAVES_N;
     const int KB = K >> 2;
     const int nk = K / GM_KS;
 
-    // A staging: a load instruction covers 8 rows x 128 contiguous bytes (8
-    // lanes per row); wave w stages block rows 32w .. 32w+31 in four pieces.
-    const int8_t* a_src;
-    int a_off[4];  // LDS byte offsets within a stage
-    {
-        const int qa = lane & 7;
-        const int ks = qa >> 1, kh = qa & 1;
-        const int rb = wave * 32 + (lane >> 3);
-        a_src = x + (int64_t)min(m0 + rb, M - 1) * K + qa * 16;  // rows past M repeat row M-1
+    // Staging loads are buffer loads: one SGPR resource per operand, a 32-bit
+    // per-lane offset and the stage's K offset in an SGPR.  Rows past M and
+    // columns past N lie past the end of their buffer and read as zero, which
+    // contributes nothing (and they are never written out).
+    const __amdgpu_buffer_rsrc_t x_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(x), (short)0, M * K, BUFFER_RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t w_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w), (short)0, N * KB, BUFFER_RSRC_WORD3);
+
+    // A staging: group g = tid + THREADS * i covers row g / 8, 16-byte group
+    // c = g % 8 (= tid % 8) of the stage's 128 bytes, i.e. lane half h = c / 4
+    // and k-step s = c % 4.
+    const int ac = tid & 7;
+    int a_voff[A_CH], a_off[A_CH];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = rb + 8 * i;
-            a_off[i] = ((r >> 5) * GM_KSTEPS + ks) * GM_FRAG + frag_slot((r & 31) + 32 * kh, ks) * 16;
-        }
+    for (int i = 0; i < A_CH; ++i) {
+        const int r = (tid >> 3) + (S::THREADS / 8) * i;
+        a_voff[i] = (m0 + r) * K + ac * 16;
+        a_off[i] = ((r >> 5) * 4 + (ac & 3)) * GM_FRAG + a_slot((r & 31) + 32 * (ac >> 2), ac & 3);
     }
-    const int64_t a_row8 = (int64_t)8 * K;  // the next piece is 8 rows down
-    const bool a_clamp = m0 + GM_BM > M;     // rows past M: recompute each piece's row
-    // B staging: thread t loads the two packed words 2h, 2h+1 (h = t % 4) of
-    // block column t / 4 (32 weights) and writes them to their fragment slots.
-    const uint8_t* b_src;
-    int b_off0, b_off1;
-    {
-        const int h = tid & 3;
-        const int cb = tid >> 2;
-        b_src = w + (int64_t)min(n0 + cb, N - 1) * KB + h * 8;  // columns past N repeat column N-1
-        const int q0 = 2 * h, q1 = 2 * h + 1;
-        b_off0 = GM_A_STAGE + ((cb >> 5) * GM_KSTEPS + (q0 >> 1)) * GM_FRAG + frag_slot((cb & 31) + 32 * (q0 & 1), q0 >> 1) * 16;
-        b_off1 = GM_A_STAGE + ((cb >> 5) * GM_KSTEPS + (q1 >> 1)) * GM_FRAG + frag_slot((cb & 31) + 32 * (q1 & 1), q1 >> 1) * 16;
+    // B staging: half g % 2 (= tid % 2) of column g / 2.
+    const int bh = tid & 1;
+    int b_voff[B_CH], b_off[B_CH];
+#pragma unroll
+    for (int j = 0; j < B_CH; ++j) {
+        const int n = (tid >> 1) + (S::THREADS / 2) * j;
+        b_voff[j] = (n0 + n) * KB + bh * 16;
+        b_off[j] = S::A_STAGE + (n >> 5) * GM_FRAG + b_slot(n & 31, bh);
     }
-    int rd[GM_KSTEPS];  // this lane's fragment slot (bytes) per k-step
-#pragma unroll
-    for (int ks = 0; ks < GM_KSTEPS; ++ks) rd[ks] = frag_slot(lane, ks) * 16;
+    // Scales for the epilogue, fetched now so that their latency hides under
+    // the K loop, and parked in LDS until then.
+    const float sa_mine = (!OUT_I32 && tid < BM && m0 + tid < M) ? bf16_to_f32(sa[m0 + tid]) : 0.0f;
+    const float sw_mine = (!OUT_I32 && tid < BN && n0 + tid < N) ? bf16_to_f32(sw[n0 + tid]) : 0.0f;
 
-    // Loads of stage s (clamped to the last stage, so every step issues the
-    // same loads and the waits the compiler derives are exact).
-    auto a_ptr = [&](int i, int kb) -> const int8_t* {
-        if (a_clamp) {
-            const int r = min(m0 + wave * 32 + (lane >> 3) + 8 * i, M - 1);
-            return x + (int64_t)r * K + (lane & 7) * 16 + kb;
-        }
-        return a_src + i * a_row8 + kb;
+    int rs[A_CH];  // this thread's share of sum_k x over its A rows
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) rs[i] = 0;
+
+    auto load_stage = [&](int st, StageRegs<A_CH, B_CH>& R) {
+        const int kb = min(st, nk - 1) * GM_KS;  // wave-uniform
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i) R.a[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, a_voff[i], kb, 0);
+#pragma unroll
+        for (int j = 0; j < B_CH; ++j) R.b[j] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, b_voff[j], kb >> 2, 0);
     };
-    auto load_stage = [&](int s, StageRegs& r) {
-        const int kb = min(s, nk - 1) * GM_KS;
-        r.a0 = *reinterpret_cast<const v4u*>(a_ptr(0, kb));
-        r.a1 = *reinterpret_cast<const v4u*>(a_ptr(1, kb));
-        r.a2 = *reinterpret_cast<const v4u*>(a_ptr(2, kb));
-        r.a3 = *reinterpret_cast<const v4u*>(a_ptr(3, kb));
-        const uint2 b = *reinterpret_cast<const uint2*>(b_src + (kb >> 2));
-        r.b0 = b.x;
-        r.b1 = b.y;
-    };
-    auto store_stage = [&](int s, const StageRegs& r) {
-        uint8_t* S = lds + (s & 1) * STAGE_BYTES;
-        *reinterpret_cast<v4u*>(S + a_off[0]) = r.a0;
-        *reinterpret_cast<v4u*>(S + a_off[1]) = r.a1;
-        *reinterpret_cast<v4u*>(S + a_off[2]) = r.a2;
-        *reinterpret_cast<v4u*>(S + a_off[3]) = r.a3;
-        *reinterpret_cast<v4u*>(S + b_off0) = decode_word(r.b0);
-        *reinterpret_cast<v4u*>(S + b_off1) = decode_word(r.b1);
+    v16i acc[MT][NT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int u = 0; u < NT; ++u) acc[t][u] = v16i{};
+
+    int a_rd[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a_rd[s] = a_slot(lane, s);
+    const int b_rd = b_slot(lane & 31, lane >> 5);
+
+    // Staging of one 16-byte A group into LDS: transpose, store, and add its
+    // bytes to the row sum (clamped repeats of the last stage are not summed).
+    auto store_a = [&](uint8_t* base, int i, const v4u& v, int live) {
+        const uint4 t = transpose4x4(v.x, v.y, v.z, v.w);
+        *reinterpret_cast<v4u*>(base + a_off[i]) = v4u{t.x, t.y, t.z, t.w};
+        int sum = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, 0, false);
+        sum = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, sum, false);
+        sum = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, sum, false);
+        sum = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, sum, false);
+        rs[i] += live * sum;
     };
 
-    v16i acc[2][2];
+    // One pipeline step k, between two barriers: issue the global loads of
+    // stage k+3 into the set that held stage k, multiply stage k from LDS, and
+    // move stage k+1 from its register set into the other LDS buffer.  The
+    // program order is chosen for overlap, because the compiler keeps LDS
+    // reads and writes in program order (it cannot tell the two buffers
+    // apart): each k-step's fragment reads are issued before the MFMAs of the
+    // previous k-step, and the stores of stage k+1 are spread over the k-steps.
+    auto step = [&](int k, const StageRegs<A_CH, B_CH>& SS, StageRegs<A_CH, B_CH>& SL) {
+        __syncthreads();  // stage k visible; the other buffer is free
+        load_stage(k + 3, SL);
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads at the top: three steps of latency to hide
+        const uint8_t* cur = lds + (k & 1) * S::STAGE;
+        uint8_t* nxt = lds + ((k + 1) & 1) * S::STAGE;
+        const int live = (k + 1 < nk) ? 1 : 0;
+        const uint8_t* A = cur + (wm * MT) * 4 * GM_FRAG;
+        const uint8_t* B = cur + S::A_STAGE + (wn * NT) * GM_FRAG;
+        v4u pb[NT];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+        for (int u = 0; u < NT; ++u) pb[u] = *reinterpret_cast<const v4u*>(B + u * GM_FRAG + b_rd);
+        v4i af[2][MT];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) acc[mt][c] = v16i{};
-
-    auto compute_stage = [&](int s) {
-        const uint8_t* A = lds + (s & 1) * STAGE_BYTES + (wm * 2) * GM_KSTEPS * GM_FRAG;
-        const uint8_t* B = lds + (s & 1) * STAGE_BYTES + GM_A_STAGE + (wn * 2) * GM_KSTEPS * GM_FRAG;
+        for (int t = 0; t < MT; ++t) af[0][t] = *reinterpret_cast<const v4i*>(A + (t * 4) * GM_FRAG + a_rd[0]);
 #pragma unroll
-        for (int ks = 0; ks < GM_KSTEPS; ++ks) {
-            v4i af[2], bf[2];
+        for (int s = 0; s < 4; ++s) {
+            if (s < 3) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                af[t] = *reinterpret_cast<const v4i*>(A + (t * GM_KSTEPS + ks) * GM_FRAG + rd[ks]);
-                bf[t] = *reinterpret_cast<const v4i*>(B + (t * GM_KSTEPS + ks) * GM_FRAG + rd[ks]);
+                for (int t = 0; t < MT; ++t)
+                    af[(s + 1) & 1][t] = *reinterpret_cast<const v4i*>(A + (t * 4 + s + 1) * GM_FRAG + a_rd[s + 1]);
             }
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int i = 0; i < A_CH; ++i)
+                if (i % 4 == s) store_a(nxt, i, SS.a[i], live);
+            if (s == 1) {
 #pragma unroll
-                for (int c = 0; c < 2; ++c)
-                    acc[mt][c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mt], bf[c], acc[mt][c], 0, 0, 0);
+                for (int j = 0; j < B_CH; ++j) *reinterpret_cast<v4u*>(nxt + b_off[j]) = SS.b[j];
+            }
+#pragma unroll
+            for (int u = 0; u < NT; ++u) {
+                const uint32_t p = pb[u][s];
+                const v4i bf = {(int)(p & CODE_MASK), (int)((p >> 2) & CODE_MASK), (int)((p >> 4) & CODE_MASK),
+                                (int)((p >> 6) & CODE_MASK)};
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    acc[t][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s & 1][t], bf, acc[t][u], 0, 0, 0);
+            }
         }
     };
 
-    // Stages k+1 .. k+3 sit in three register sets used in a fixed rotation, so
-    // every register is named statically (no array indexing, no copies).
-    static_assert(GM_AHEAD == 3, "the rotation below is written out for three sets");
-    StageRegs r0, r1, r2;
-    load_stage(0, r0);
-    load_stage(1, r1);
-    load_stage(2, r2);
-    store_stage(0, r0);
-    load_stage(3, r0);
-
-    // Every step issues its loads and LDS stores unconditionally (stage indices
-    // past the end are clamped and never multiplied), so the number of loads
-    // between any two points is the same on every path and the compiler's
-    // waits are exact.
-#define BITNET_GEMM_STEP(K_, R_)                                       \
-    __syncthreads(); /* stage K_ visible; the other buffer is free */ \
-    store_stage((K_) + 1, R_);                                         \
-    load_stage((K_) + 1 + GM_AHEAD, R_);                               \
-    if ((K_) < nk) compute_stage(K_); /* uniform */
-    for (int k = 0; k < nk; k += GM_AHEAD) {
-        BITNET_GEMM_STEP(k, r1)
-        BITNET_GEMM_STEP(k + 1, r2)
-        BITNET_GEMM_STEP(k + 2, r0)
+    // Stage j lives in register set j % 3 from its load until its LDS store.
+    StageRegs<A_CH, B_CH> s0, s1, s2;
+    load_stage(0, s0);
+    load_stage(1, s1);
+    load_stage(2, s2);
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) store_a(lds, i, s0.a[i], 1);
+#pragma unroll
+    for (int j = 0; j < B_CH; ++j) *reinterpret_cast<v4u*>(lds + b_off[j]) = s0.b[j];
+    int k = 0;
+    for (; k + 3 <= nk; k += 3) {
+        step(k, s1, s0);
+        step(k + 1, s2, s1);
+        step(k + 2, s0, s2);
     }
-#undef BITNET_GEMM_STEP
+    if (k < nk) step(k, s1, s0);
+    if (k + 1 < nk) step(k + 1, s2, s1);
+
+    // ---- row sums (the 8 threads of a row are aligned lanes) and row scales to LDS
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+        const int v = group8_sum(rs[i]);
+        if (ac == 0) rowsum[(tid >> 3) + (S::THREADS / 8) * i] = v;
+    }
+    if (tid < BM) rowscale[tid] = sa_mine;
+    if (tid < BN) colscale[tid] = sw_mine;
+    __syncthreads();
 
     // ---- epilogue straight from the accumulators: register r of lane l of a
     //      32 x 32 tile holds row 8(r/4) + 4(l/32) + r%4, column l%32
-    float swf[2];
-    int gcol[2];
+    if (m0 + BM <= M && n0 + BN <= N) {
+        // Whole tile in range: branch-free buffer stores whose per-register row
+        // offset is a scalar, two rows per bf16 conversion.
+        constexpr int ES = OUT_I32 ? 4 : 2;
+        void* dst = OUT_I32 ? static_cast<void*>(acc_out) : static_cast<void*>(out);
+        const __amdgpu_buffer_rsrc_t o_rsrc =
+            __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, M * N * ES, BUFFER_RSRC_WORD3);
+        const int lrow0 = wm * MT * 32 + (lane >> 5) * 4;  // block row of (t = 0, r = 0)
+        const int lcol0 = wn * NT * 32 + (lane & 31);
+        const int voff = ((m0 + lrow0) * N + n0 + lcol0) * ES;
+        float swf[NT];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        gcol[c] = n0 + (wn * 2 + c) * 32 + (lane & 31);
-        swf[c] = (!OUT_I32 && gcol[c] < N) ? bf16_to_f32(sw[gcol[c]]) : 0.0f;
+        for (int u = 0; u < NT; ++u) swf[u] = colscale[lcol0 + u * 32];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const int dr = t * 32 + (r >> 2) * 8 + (r & 3);  // row offset, lane-independent
+                const int lr = lrow0 + dr;
+                const int c0 = 2 * rowsum[lr], c1 = 2 * rowsum[lr + 1];
+                const float a0 = rowscale[lr], a1 = rowscale[lr + 1];
+#pragma unroll
+                for (int u = 0; u < NT; ++u) {
+                    const int soff = (dr * N + u * 32) * ES;
+                    const int v0 = acc[t][u][r] - c0;
+                    const int v1 = acc[t][u][r + 1] - c1;
+                    if (OUT_I32) {
+                        __builtin_amdgcn_raw_buffer_store_b32(v0, o_rsrc, voff, soff, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(v1, o_rsrc, voff, soff + N * ES, 0);
+                    } else {
+                        const uint32_t pk = epilogue_bf16x2(v0, a0, v1, a1, swf[u]);
+                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, o_rsrc, voff, soff, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), o_rsrc, voff, soff + N * ES, 0);
+                    }
+                }
+            }
+        }
+        return;
+    }
+    float swf[NT];
+    int gcol[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+        const int lc = (wn * NT + u) * 32 + (lane & 31);
+        gcol[u] = n0 + lc;
+        swf[u] = colscale[lc];
     }
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int t = 0; t < MT; ++t) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int gm = m0 + (wm * 2 + mt) * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            const int lr = (wm * MT + t) * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            const int gm = m0 + lr;
             if (gm >= M) continue;
-            const float fa = OUT_I32 ? 0.0f : bf16_to_f32(sa[gm]);
+            const int corr = 2 * rowsum[lr];
+            const float fa = rowscale[lr];
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                if (gcol[c] >= N) continue;
-                const int v = acc[mt][c][r];
+            for (int u = 0; u < NT; ++u) {
+                if (gcol[u] >= N) continue;
+                const int v = acc[t][u][r] - corr;
                 if (OUT_I32)
-                    acc_out[(int64_t)gm * N + gcol[c]] = v;
+                    acc_out[(int64_t)gm * N + gcol[u]] = v;
                 else
-                    out[(int64_t)gm * N + gcol[c]] = epilogue_bf16(v, fa, swf[c]);
+                    out[(int64_t)gm * N + gcol[u]] = epilogue_bf16(v, fa, swf[u]);
             }
         }
     }
@@ -294,23 +367,62 @@ __global__ __launch_bounds__(64) void gemm_plain(uint16_t* __restrict__ out, int
     }
 }
 
+template <int BM, int BN, int WAVES_M, int WAVES_N, int WAVES_PER_EU, bool OUT_I32>
+hipError_t launch_mfma(uint16_t* out, int32_t* acc, const int8_t* x, const uint8_t* w, const uint16_t* sa,
+                       const uint16_t* sw, int M, int N, int K, hipStream_t s) {
+    using S = GemmShape<BM, BN, WAVES_M, WAVES_N>;
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN - 1) / BN;
+    auto kern = gemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, WAVES_PER_EU, OUT_I32>;
+    if (S::LDS > 65536) {  // beyond the default dynamic LDS limit: raise it (idempotent)
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::LDS);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n)), dim3(S::THREADS), S::LDS, s, out, acc, x, w, sa,
+                       sw, M, N, K, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+template <bool OUT_I32>
+hipError_t launch_tiles(uint16_t* out, int32_t* acc, const int8_t* x, const uint8_t* w, const uint16_t* sa,
+                        const uint16_t* sw, int M, int N, int K, hipStream_t s) {
+    // Tile choice.  128 x 512 blocks (eight 128 x 64 wave tiles) decode each B
+    // fragment for four MFMAs and stage each A byte for 512 columns, so they
+    // spend the least VALU per MFMA; they are used when there are enough of them
+    // to give every CU at least two.  Otherwise 128 x 256 blocks (eight 64 x 64
+    // wave tiles), which keep two waves per SIMD busy on N = 4096-sized shapes.
+    const int64_t wide_tiles = (int64_t)((M + 127) / 128) * ((N + 511) / 512);
+    if (wide_tiles >= 2 * 256)
+        return launch_mfma<128, 512, 1, 8, 2, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+    return launch_mfma<128, 256, 2, 4, 2, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+}
+
 template <bool OUT_I32>
 hipError_t dispatch(uint16_t* out, int32_t* acc, const int8_t* x, const uint8_t* w, const uint16_t* sa,
-                    const uint16_t* sw, int M, int N, int K, hipStream_t s) {
-    const bool fast = (K % GM_KS == 0) && aligned16(x) && aligned16(w);
+                    const uint16_t* sw, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    // The MFMA kernel addresses x, w and the output with 32-bit byte offsets
+    // (buffer loads and stores).  Rows are processed in chunks that keep every
+    // offset below 2^31, including those of the tile rows past the end of a
+    // chunk; weights whose padded size reaches 2^31 bytes take the plain path.
+    constexpr int64_t LIMIT = (int64_t)1 << 31;
+    const int64_t KB = K / 4;
+    const int64_t row_bytes = K > 4 * N ? K : 4 * N;
+    const int64_t chunk = ((LIMIT - 1) / row_bytes - 128) / 128 * 128;
+    const bool fast = (K % GM_KS == 0) && aligned16(x) && aligned16(w) && (N + 511) * KB < LIMIT && chunk >= 128;
     if (!fast) {
-        hipLaunchKernelGGL((gemm_plain<OUT_I32>), dim3((unsigned)N), dim3(64), 0, s, out, acc, x, w, sa, sw, M, N, K);
+        hipLaunchKernelGGL((gemm_plain<OUT_I32>), dim3((unsigned)N), dim3(64), 0, s, out, acc, x, w, sa, sw, (int)M,
+                           (int)N, (int)K);
         return hipGetLastError();
     }
-    const int tiles_m = (M + GM_BM - 1) / GM_BM;
-    const int tiles_n = (N + GM_BN - 1) / GM_BN;
-    // more than 64 KB of dynamic LDS: raise the kernel's limit (idempotent)
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mfma_kernel<OUT_I32>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)GM_LDS_BYTES);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_mfma_kernel<OUT_I32>), dim3((unsigned)(tiles_m * tiles_n)), dim3(GM_THREADS),
-                       GM_LDS_BYTES, s, out, acc, x, w, sa, sw, M, N, K, tiles_m, tiles_n);
-    return hipGetLastError();
+    for (int64_t r0 = 0; r0 < M; r0 += chunk) {
+        const int64_t rows = M - r0 < chunk ? M - r0 : chunk;
+        const hipError_t e = launch_tiles<OUT_I32>(OUT_I32 ? nullptr : out + r0 * N, OUT_I32 ? acc + r0 * N : nullptr,
+                                                   x + r0 * K, w, OUT_I32 ? nullptr : sa + r0, sw, (int)rows, (int)N,
+                                                   (int)K, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -318,8 +430,8 @@ hipError_t dispatch(uint16_t* out, int32_t* acc, const int8_t* x, const uint8_t*
 hipError_t launch_gemm(uint16_t* out, int32_t* acc, const int8_t* x, const uint8_t* w, const uint16_t* scale_act,
                        const uint16_t* scale_wt, int64_t M, int64_t N, int64_t K, hipStream_t s) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    if (acc != nullptr) return dispatch<true>(nullptr, acc, x, w, nullptr, nullptr, (int)M, (int)N, (int)K, s);
-    return dispatch<false>(out, nullptr, x, w, scale_act, scale_wt, (int)M, (int)N, (int)K, s);
+    if (acc != nullptr) return dispatch<true>(nullptr, acc, x, w, nullptr, nullptr, M, N, K, s);
+    return dispatch<false>(out, nullptr, x, w, scale_act, scale_wt, M, N, K, s);
 }
 
 }  // namespace bitnet

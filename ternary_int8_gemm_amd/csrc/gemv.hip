@@ -52,21 +52,6 @@ __device__ __forceinline__ int lds_word_offset(int word) {
     return (seg << 6) + ((j ^ ((seg >> 1) & 3)) << 4);
 }
 
-// 4x4 byte transpose: n_r holds elements 4r..4r+3; result t_e holds element e of
-// every n_r (t_e byte r = element 4r + e).
-__device__ __forceinline__ uint4 transpose4x4(uint32_t n0, uint32_t n1, uint32_t n2, uint32_t n3) {
-    const uint32_t u01lo = __builtin_amdgcn_perm(n1, n0, 0x05010400u);  // n0.b0 n1.b0 n0.b1 n1.b1
-    const uint32_t u01hi = __builtin_amdgcn_perm(n1, n0, 0x07030602u);  // n0.b2 n1.b2 n0.b3 n1.b3
-    const uint32_t u23lo = __builtin_amdgcn_perm(n3, n2, 0x05010400u);
-    const uint32_t u23hi = __builtin_amdgcn_perm(n3, n2, 0x07030602u);
-    uint4 t;
-    t.x = __builtin_amdgcn_perm(u23lo, u01lo, 0x05040100u);
-    t.y = __builtin_amdgcn_perm(u23lo, u01lo, 0x07060302u);
-    t.z = __builtin_amdgcn_perm(u23hi, u01hi, 0x05040100u);
-    t.w = __builtin_amdgcn_perm(u23hi, u01hi, 0x07060302u);
-    return t;
-}
-
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int j) {
     return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
 }
