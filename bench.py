@@ -214,6 +214,107 @@ def run_gemm(device, stream, M, log, rotate=4):
     return out
 
 
+# ----------------------------------------------------------------------------- small-batch GEMM
+
+SMALL_M = (8, 16, 32, 64, 128, 256)
+
+
+def roofline_frac(ops, nbytes, seconds):
+    """Fraction of min(INT8 peak, arithmetic intensity x HBM peak) achieved."""
+    bound_tops = min(INT8_PEAK_TOPS, ops / nbytes * HBM_PEAK_GBS / 1e3)
+    return ops / seconds / 1e12 / bound_tops
+
+
+def run_small_batch(device, stream, log):
+    """bitnet_gemm at M = 8..256 on the LLaMA-7B layer shapes (pre-quantised
+    activations), weights rotating over >= 1 GiB of copies."""
+    out = {}
+    for i, (name, N, K) in enumerate(synth.LLAMA7B_SHAPES[:3]):
+        W = synth.ternary_weights(N, K, synth.seed_for(2, 16 * i + synth.T_WEIGHT))
+        P = tg.pack_weights(torch.from_numpy(W)).to(device)
+        del W
+        copies = max(2, -(-POOL_BYTES // P.numel()))
+        Ps = [P] + [P.clone() for _ in range(copies - 1)]
+        sw = dev_bf16(synth.row_scales_bf16(N, synth.seed_for(2, 16 * i + synth.T_ROWSCALE)), device)
+        for M in SMALL_M:
+            x = dev_bf16(synth.activations_bf16(M, K, synth.seed_for(2, 16 * i + synth.T_ACT) + M), device)
+            q, sa = tg.quantize_activation(x)
+            o = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+
+            def run():
+                for Pd in Ps:
+                    tg.bitnet_gemm(q, Pd, sa, sw, out=o)
+
+            g = capture(run, stream)
+            time_graph(g, 1, stream)
+            t = time_graph(g, 3, stream) / (3 * copies)
+            ops, nbytes = 2.0 * M * N * K, gemm_bytes(M, N, K)
+            r = {"us": round(t * 1e6, 2), "gbs": round(nbytes / t / 1e9, 1), "tops": round(ops / t / 1e12, 1),
+                 "frac_roofline": round(roofline_frac(ops, nbytes, t), 4)}
+            out[f"{name}_M{M}"] = r
+            log(f"  {name:8s} M={M:4d}: {r['us']:8.2f} us {r['gbs']:8.1f} GB/s {r['tops']:8.1f} TOPS "
+                f"({100 * r['frac_roofline']:.1f}% of roofline)")
+        del Ps
+        torch.cuda.empty_cache()
+    return out
+
+
+# ----------------------------------------------------------------------------- full decode step
+
+def run_decode_full(device, stream, log, layers=30):
+    """One token through every BitLinear of a 30-layer BitNet-2B-4T (4 fused
+    projections per layer) plus the LM head: 121 calls on 121 distinct weight
+    buffers (603 MB).  The layers hold copies of one synthetic layer's packed
+    weights (distinct memory, same values).  M = 1 (fused GEMV) and M = 16
+    (quantise + GEMM), each step captured as one graph."""
+    shapes = synth.BITNET_2B_DECODE
+    layer_shapes = [s for s in shapes if s[0] != "lm_head"]
+    head = [s for s in shapes if s[0] == "lm_head"]
+    base = {}
+    for i, (name, N, K) in enumerate(shapes):
+        W = synth.ternary_weights(N, K, synth.seed_for(1, 16 * i + synth.T_WEIGHT))
+        base[name] = (tg.pack_weights(torch.from_numpy(W)).to(device),
+                      dev_bf16(synth.weight_scale_bf16(N, K, synth.seed_for(1, 16 * i + synth.T_SCALE)), device))
+        del W
+    calls = []
+    for _ in range(layers):
+        for name, N, K in layer_shapes:
+            calls.append((name, N, K, base[name][0].clone(), base[name][1]))
+    for name, N, K in head:
+        calls.append((name, N, K, base[name][0], base[name][1]))
+    total_w = sum(c[3].numel() for c in calls)
+    res = {"calls": len(calls), "weight_bytes": total_w}
+    for M in (1, 16):
+        xs, outs = [], []
+        for j, (name, N, K, _, _) in enumerate(calls):
+            xs.append(dev_bf16(synth.activations_bf16(M, K, synth.seed_for(5, j) + M), device))
+            outs.append(torch.empty((M, N), dtype=torch.bfloat16, device=device))
+        ws = torch.empty((max(tg.linear_workspace_bytes(M, c[2]) for c in calls) + 256,), dtype=torch.uint8,
+                         device=device)
+
+        def step():
+            for (name, N, K, Pd, swd), xd, od in zip(calls, xs, outs):
+                tg.bitnet_linear(xd, Pd, swd, out=od, workspace=ws)
+
+        g = capture(step, stream)
+        time_graph(g, 2, stream)
+        reps = 20
+        t = time_graph(g, reps, stream) / reps
+        if M == 1:
+            nbytes = sum(gemv_bytes(M, N, K) for _, N, K, _, _ in calls)
+        else:  # quantise (2MK in, MK + 2M out) + GEMM
+            nbytes = sum(gemm_bytes(M, N, K) + 3 * M * K + 2 * M for _, N, K, _, _ in calls)
+        res[f"M{M}"] = {"us_per_step": round(t * 1e6, 2), "tokens_per_s": round(M / t, 1),
+                        "gbs": round(nbytes / t / 1e9, 1), "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                        "step_bytes": nbytes}
+        log(f"  full decode step M={M:2d}: {t * 1e6:8.1f} us/step, {M / t:9.1f} tok/s, "
+            f"{nbytes / t / 1e9:7.1f} GB/s ({100 * nbytes / t / 1e9 / HBM_PEAK_GBS:.1f}% of HBM peak)")
+        del xs, outs, ws
+    del calls, base
+    torch.cuda.empty_cache()
+    return res
+
+
 # ----------------------------------------------------------------------------- CPU oracle
 
 def run_cpu_baseline(host, shapes, budget_s, log):
@@ -404,6 +505,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the small-batch GEMM and full decode-step lines")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--pmc-target", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -446,6 +548,13 @@ def main():
     if not args.no_gemm:
         log(f"prefill GEMM M={args.gemm_m} (LLaMA-7B shapes):")
         gemm = run_gemm(device, stream, args.gemm_m, log)
+
+    small = full = None
+    if not args.no_extra:
+        log("small-batch GEMM M=8..256 (LLaMA-7B layer shapes, pre-quantised):")
+        small = run_small_batch(device, stream, log)
+        log("full BitNet-2B-4T decode step (30 layers x 4 + lm_head = 121 calls):")
+        full = run_decode_full(device, stream, log)
 
     lm = dec["per_shape"]["lm_head"]
     traffic = load_traffic(lm["bytes"])
@@ -493,6 +602,9 @@ def main():
                               "quant_us": round(v["quant_us"], 2), "linear_us": round(v["linear_us"], 2)}
                           for k, v in gemm.items()},
         }
+    if small is not None:
+        line["small_batch_gemm"] = small
+        line["decode_full_step"] = full
     print(json.dumps(line), flush=True)
 
 

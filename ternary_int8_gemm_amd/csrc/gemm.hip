@@ -35,10 +35,12 @@
 //  * LDS slots are XOR-swizzled so that the staging writes (8 rows x 8 groups
 //    per instruction for A; 32 columns x 2 halves for B) and the fragment reads
 //    (lane-contiguous) both keep every 16 lanes on distinct 16-byte bank groups.
-//  * Global loads are issued three stages ahead into three register sets and
-//    the LDS stages are double-buffered, one barrier per stage.  Every step
-//    issues the same loads (stage indices past the end are clamped and never
-//    multiplied), so the waits the compiler derives are exact.
+//  * Global loads are issued four stages ahead into three register sets; LDS
+//    holds three stages, so a stage is stored two steps before it is multiplied
+//    and the first fragments of the next stage are read at the end of each step
+//    (one barrier per stage).  Every step issues the same loads (stage indices
+//    past the end are clamped and never multiplied), so the waits the compiler
+//    derives are exact.
 //
 // Tiles are assigned XCD-aware: the hardware deals workgroups round-robin to
 // the 8 XCDs, so the block index is remapped to give each XCD a contiguous run
@@ -69,7 +71,7 @@ struct GemmShape {
     static constexpr int STAGE = A_STAGE + B_STAGE;
     static constexpr int A_CH = BM * (GM_KS / 16) / THREADS;  // 16-byte A groups per thread per stage
     static constexpr int B_CH = BN * 2 / THREADS;             // 16-byte B halves per thread per stage
-    static constexpr size_t LDS = 2 * (size_t)STAGE + 8 * BM + 4 * BN;  // two stages, row sums, scales
+    static constexpr size_t LDS = 3 * (size_t)STAGE + 8 * BM + 4 * BN;  // three stages, row sums, scales
     static_assert(THREADS >= BM && THREADS >= BN, "one thread per block row / column fetches its scale");
     static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "wave tiles are whole MFMA tiles");
     static_assert(A_CH * THREADS == BM * 8 && B_CH * THREADS == BN * 2, "staging splits evenly");
@@ -109,9 +111,9 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
     using S = GemmShape<BM, BN, WAVES_M, WAVES_N>;
     constexpr int MT = S::MT, NT = S::NT, A_CH = S::A_CH, B_CH = S::B_CH;
     extern __shared__ __align__(16) uint8_t lds[];
-    int* rowsum = reinterpret_cast<int*>(lds + 2 * S::STAGE);
-    float* rowscale = reinterpret_cast<float*>(lds + 2 * S::STAGE + 4 * BM);
-    float* colscale = reinterpret_cast<float*>(lds + 2 * S::STAGE + 8 * BM);
+    int* rowsum = reinterpret_cast<int*>(lds + 3 * S::STAGE);
+    float* rowscale = reinterpret_cast<float*>(lds + 3 * S::STAGE + 4 * BM);
+    float* colscale = reinterpret_cast<float*>(lds + 3 * S::STAGE + 8 * BM);
 
     const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
     const int tm = tile / tiles_n;
@@ -195,28 +197,43 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
         rs[i] += live * sum;
     };
 
-    // One pipeline step k, between two barriers: issue the global loads of
-    // stage k+3 into the set that held stage k, multiply stage k from LDS, and
-    // move stage k+1 from its register set into the other LDS buffer.  The
-    // program order is chosen for overlap, because the compiler keeps LDS
-    // reads and writes in program order (it cannot tell the two buffers
-    // apart): each k-step's fragment reads are issued before the MFMAs of the
-    // previous k-step, and the stores of stage k+1 are spread over the k-steps.
-    auto step = [&](int k, const StageRegs<A_CH, B_CH>& SS, StageRegs<A_CH, B_CH>& SL) {
-        __syncthreads();  // stage k visible; the other buffer is free
-        load_stage(k + 3, SL);
-        __builtin_amdgcn_sched_barrier(0);  // keep the loads at the top: three steps of latency to hide
-        const uint8_t* cur = lds + (k & 1) * S::STAGE;
-        uint8_t* nxt = lds + ((k + 1) & 1) * S::STAGE;
-        const int live = (k + 1 < nk) ? 1 : 0;
-        const uint8_t* A = cur + (wm * MT) * 4 * GM_FRAG;
-        const uint8_t* B = cur + S::A_STAGE + (wn * NT) * GM_FRAG;
-        v4u pb[NT];
+    // Fragments a step needs first: the packed B dwords of the whole stage and
+    // the A fragments of its first k-step.  The previous step reads them.
+    auto read_first = [&](const uint8_t* base, v4u (&pb)[NT], v4i (&af)[MT]) {
+        const uint8_t* A = base + (wm * MT) * 4 * GM_FRAG;
+        const uint8_t* B = base + S::A_STAGE + (wn * NT) * GM_FRAG;
 #pragma unroll
         for (int u = 0; u < NT; ++u) pb[u] = *reinterpret_cast<const v4u*>(B + u * GM_FRAG + b_rd);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) af[t] = *reinterpret_cast<const v4i*>(A + (t * 4) * GM_FRAG + a_rd[0]);
+    };
+
+    // One pipeline step k, between two barriers, with LDS buffer bi = k % 3:
+    // issue the global loads of stage k+4 into the register set that held
+    // stage k+1, multiply stage k, move stage k+2 from its register set into
+    // buffer (k+2) % 3, and read the first fragments of stage k+1 (written
+    // during step k-1, visible since this step's barrier).  The program order
+    // is chosen for overlap, because the compiler keeps LDS reads and writes in
+    // program order (it cannot tell the buffers apart): each k-step's fragment
+    // reads are issued before the MFMAs of the previous k-step, and the stores
+    // of stage k+2 are spread over the k-steps.
+    v4u pb[NT];
+    v4i af0[MT];
+    auto step = [&](const int bi, int k, const StageRegs<A_CH, B_CH>& SS, StageRegs<A_CH, B_CH>& SL) {
+        __syncthreads();  // stage k+1 visible; buffer (k+2) % 3 no longer read
+        load_stage(k + 4, SL);
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads at the top
+        const uint8_t* cur = lds + bi * S::STAGE;
+        uint8_t* later = lds + ((bi + 2) % 3) * S::STAGE;
+        const uint8_t* next = lds + ((bi + 1) % 3) * S::STAGE;
+        const int live = (k + 2 < nk) ? 1 : 0;
+        const uint8_t* A = cur + (wm * MT) * 4 * GM_FRAG;
         v4i af[2][MT];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) af[0][t] = *reinterpret_cast<const v4i*>(A + (t * 4) * GM_FRAG + a_rd[0]);
+        for (int t = 0; t < MT; ++t) af[0][t] = af0[t];
+        v4u pbc[NT];
+#pragma unroll
+        for (int u = 0; u < NT; ++u) pbc[u] = pb[u];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             if (s < 3) {
@@ -226,14 +243,15 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
             }
 #pragma unroll
             for (int i = 0; i < A_CH; ++i)
-                if (i % 4 == s) store_a(nxt, i, SS.a[i], live);
+                if (i % 4 == s) store_a(later, i, SS.a[i], live);
             if (s == 1) {
 #pragma unroll
-                for (int j = 0; j < B_CH; ++j) *reinterpret_cast<v4u*>(nxt + b_off[j]) = SS.b[j];
+                for (int j = 0; j < B_CH; ++j) *reinterpret_cast<v4u*>(later + b_off[j]) = SS.b[j];
             }
+            if (s == 3) read_first(next, pb, af0);
 #pragma unroll
             for (int u = 0; u < NT; ++u) {
-                const uint32_t p = pb[u][s];
+                const uint32_t p = pbc[u][s];
                 const v4i bf = {(int)(p & CODE_MASK), (int)((p >> 2) & CODE_MASK), (int)((p >> 4) & CODE_MASK),
                                 (int)((p >> 6) & CODE_MASK)};
 #pragma unroll
@@ -243,7 +261,8 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
         }
     };
 
-    // Stage j lives in register set j % 3 from its load until its LDS store.
+    // Stage j lives in register set j % 3 from its load until its LDS store,
+    // and in LDS buffer j % 3 from its store until it is multiplied.
     StageRegs<A_CH, B_CH> s0, s1, s2;
     load_stage(0, s0);
     load_stage(1, s1);
@@ -252,14 +271,21 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
     for (int i = 0; i < A_CH; ++i) store_a(lds, i, s0.a[i], 1);
 #pragma unroll
     for (int j = 0; j < B_CH; ++j) *reinterpret_cast<v4u*>(lds + b_off[j]) = s0.b[j];
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) store_a(lds + S::STAGE, i, s1.a[i], nk > 1 ? 1 : 0);
+#pragma unroll
+    for (int j = 0; j < B_CH; ++j) *reinterpret_cast<v4u*>(lds + S::STAGE + b_off[j]) = s1.b[j];
+    load_stage(3, s0);
+    __syncthreads();
+    read_first(lds, pb, af0);
     int k = 0;
     for (; k + 3 <= nk; k += 3) {
-        step(k, s1, s0);
-        step(k + 1, s2, s1);
-        step(k + 2, s0, s2);
+        step(0, k, s2, s1);
+        step(1, k + 1, s0, s2);
+        step(2, k + 2, s1, s0);
     }
-    if (k < nk) step(k, s1, s0);
-    if (k + 1 < nk) step(k + 1, s2, s1);
+    if (k < nk) step(0, k, s2, s1);
+    if (k + 1 < nk) step(1, k + 1, s0, s2);
 
     // ---- row sums (the 8 threads of a row are aligned lanes) and row scales to LDS
 #pragma unroll

@@ -9,14 +9,21 @@
 //   out[m][n] = epilogue(acc, bf16(s_m), scale_wt[n])
 //
 // The decode GEMV is bound by streaming the packed weights from HBM (2 bits per
-// weight, read once), so the design keeps every other cost off that stream:
+// weight, read once), so the design keeps every other cost off that stream.
 //
-//  * Weights.  Each wave owns 8*RB output rows.  Eight consecutive lanes share
-//    a row; in one step the eight lanes read 8 x 16 B = 128 B contiguous of that
-//    row (512 weights), so a wave instruction fetches 8 full 128-byte lines.
-//    The loads for the next step are issued before the current one is
-//    computed, and the very first loads are issued before the quantisation
-//    prologue, so HBM latency overlaps the prologue.
+// gemv_stream_kernel (activations fit in LDS: M * K <= 32768):
+//  * Activations.  Every 256-thread workgroup quantises x itself (at most 15
+//    rows; they stay in L2) into LDS as int8, each 16-element group stored as
+//    the 4x4 byte transpose the unpack needs, in 64-element segments padded to
+//    80 bytes so that the eight sub-lanes of a step hit distinct LDS banks.
+//    The first weight loads are issued before this prologue.
+//  * Weights.  Work is split into units of 8 output rows; a workgroup owns up
+//    to 32 consecutive units and its 4 waves take them round-robin.  Eight
+//    consecutive lanes share a row and read 8 x 16 B = 128 contiguous bytes of
+//    it per step (512 weights), so one wave instruction fetches 8 whole
+//    128-byte lines.  Each wave keeps a ring of D loads in flight, every one of
+//    them issued unconditionally (loads past the wave's work read a small,
+//    always-cached pad), so the compiler's waits stay exact.
 //  * Unpack without a lookup.  For a 32-bit word p of codes, p & 0x03030303,
 //    p & 0x0C0C0C0C, p & 0x30303030 and (p >> 6) & 0x03030303 hold, in byte r,
 //    the code of element 4r+e times 1, 4, 16 and 1 (e = 0..3).  Each is fed to
@@ -24,15 +31,13 @@
 //    order, with separate accumulators for the x4 and x16 lanes; the exact
 //    total sum(code * q) then loses 2 * sum_k q[m][k] to give sum((code-2) * q).
 //    That is 5 logic ops + 4 dot4 per 16 weights.
-//  * Activations.  Every workgroup quantises x itself (x is at most 15 rows and
-//    stays in L2) into LDS as int8, each 16-element group stored as the 4x4
-//    byte transpose the unpack needs, with the 16-byte slots of each 64-byte
-//    segment XOR-swizzled so that the eight sub-lanes of a step hit distinct
-//    LDS banks.  Long rows are processed in K-chunks that fit the LDS budget.
 //  * Reduction.  A row's eight partial sums are combined with three DPP adds
-//    (quad_perm xor 1, quad_perm xor 2, row_half_mirror).
+//    (quad_perm xor 1, quad_perm xor 2, row_half_mirror); the epilogue is fused.
 //
-// Shapes the fast kernel takes: K % 64 == 0 and 16-byte aligned x and w (every
+// gemv_chunked_kernel (longer activations): each wave owns 8*RB rows and K is
+// processed in LDS-sized chunks, with the same unpack and reduction.
+//
+// Shapes the fast kernels take: K % 64 == 0 and 16-byte aligned x and w (every
 // BitNet/LLaMA projection).  Anything else goes to gemv_fused_plain, a direct
 // one-wave-per-row kernel with the same arithmetic.
 #include "bitnet_device.h"

@@ -6,11 +6,16 @@
 // q = clamp(round_half_even(x / s), -127, 127), scale stored as bf16(s).
 //
 // Layout on gfx950: one wave64 per row, four rows per 256-thread workgroup.
-// Pass 1 streams the row with 16-byte loads and reduces the absmax on the raw
-// bf16 magnitude bits (an integer max; DPP inside each 16-lane row, readlane
-// across rows).  Pass 2 re-reads the row (it is still in L2) and writes 16
-// int8 per lane with one 16-byte store.  The whole kernel is HBM-bound at
-// 3 bytes per element.
+// The kernel is HBM-bound at 3 bytes per element, so what matters is keeping
+// enough bytes in flight:
+//  * quantize_rows_reg<CH> (rows of up to 512 * CH elements, K % 8 == 0): each
+//    lane loads its CH 16-byte groups of the row up front (consecutive lanes,
+//    consecutive groups), reduces the absmax on the bf16 magnitude bits (an
+//    integer max; DPP inside each 16-lane row, readlane across rows), and
+//    quantises from registers: one read of x, 8-byte int8 stores.
+//  * quantize_rows_vec (longer rows, K % 16 == 0): two passes over the row, the
+//    second re-reading it from L2.
+//  * quantize_rows_plain: any K and alignment, one element per lane.
 #include "bitnet_device.h"
 #include "launch.h"
 
@@ -55,6 +60,44 @@ __global__ __launch_bounds__(256) void quantize_rows_vec(int8_t* __restrict__ q,
     }
 }
 
+// Register-resident path: lane l holds the 8-element groups g = c * 64 + l
+// (c < CH) of its row.  Needs K % 8 == 0, K <= 512 * CH, 16-byte aligned x rows
+// and 8-byte aligned q rows.
+template <int CH>
+__global__ __launch_bounds__(256) void quantize_rows_reg(int8_t* __restrict__ q, uint16_t* __restrict__ scale,
+                                                         const uint16_t* __restrict__ x, int64_t M, int64_t K) {
+    const int lane = threadIdx.x & 63;
+    const int64_t m = (int64_t)blockIdx.x * QUANT_ROWS_PER_BLOCK + (threadIdx.x >> 6);
+    if (m >= M) return;  // wave-uniform
+    const int groups = (int)(K >> 3);
+    const uint4* xv = reinterpret_cast<const uint4*>(x + m * K);
+    uint4 v[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int g = c * 64 + lane;
+        v[c] = g < groups ? xv[g] : make_uint4(0u, 0u, 0u, 0u);  // zeros do not change the absmax
+    }
+    uint32_t amax = 0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+        amax = max(amax, max(max(absmax_bf16x2(v[c].x), absmax_bf16x2(v[c].y)),
+                             max(absmax_bf16x2(v[c].z), absmax_bf16x2(v[c].w))));
+    amax = wave_max_u32(amax);
+    const QuantScale qs = quant_scale(amax);
+    if (lane == 0) scale[m] = f32_to_bf16(qs.s);
+    uint2* qv = reinterpret_cast<uint2*>(q + m * K);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int g = c * 64 + lane;
+        if (g < groups) {
+            uint2 o;
+            o.x = pack4(quantize_bf16x2(v[c].x, qs), quantize_bf16x2(v[c].y, qs));
+            o.y = pack4(quantize_bf16x2(v[c].z, qs), quantize_bf16x2(v[c].w, qs));
+            qv[g] = o;
+        }
+    }
+}
+
 // Plain path for any K and alignment: one element per lane per iteration.
 __global__ __launch_bounds__(256) void quantize_rows_plain(int8_t* __restrict__ q, uint16_t* __restrict__ scale,
                                                            const uint16_t* __restrict__ x, int64_t M, int64_t K) {
@@ -76,10 +119,27 @@ __global__ __launch_bounds__(256) void quantize_rows_plain(int8_t* __restrict__ 
 hipError_t launch_quantize(int8_t* q, uint16_t* scale, const uint16_t* x, int64_t M, int64_t K, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     const int64_t blocks = (M + QUANT_ROWS_PER_BLOCK - 1) / QUANT_ROWS_PER_BLOCK;
-    if (K % 16 == 0 && aligned16(x) && aligned16(q)) {
-        hipLaunchKernelGGL(quantize_rows_vec, dim3((unsigned)blocks), dim3(256), 0, s, q, scale, x, M, K);
+    const dim3 grid((unsigned)blocks), block(256);
+    if (K % 8 == 0 && aligned16(x) && reinterpret_cast<uintptr_t>(q) % 8 == 0 && K <= 512 * 32) {
+        const int64_t ch = (K / 8 + 63) / 64;  // 16-byte groups per lane
+        if (ch <= 2)
+            hipLaunchKernelGGL(quantize_rows_reg<2>, grid, block, 0, s, q, scale, x, M, K);
+        else if (ch <= 4)
+            hipLaunchKernelGGL(quantize_rows_reg<4>, grid, block, 0, s, q, scale, x, M, K);
+        else if (ch <= 8)
+            hipLaunchKernelGGL(quantize_rows_reg<8>, grid, block, 0, s, q, scale, x, M, K);
+        else if (ch <= 12)
+            hipLaunchKernelGGL(quantize_rows_reg<12>, grid, block, 0, s, q, scale, x, M, K);
+        else if (ch <= 16)
+            hipLaunchKernelGGL(quantize_rows_reg<16>, grid, block, 0, s, q, scale, x, M, K);
+        else if (ch <= 24)
+            hipLaunchKernelGGL(quantize_rows_reg<24>, grid, block, 0, s, q, scale, x, M, K);
+        else
+            hipLaunchKernelGGL(quantize_rows_reg<32>, grid, block, 0, s, q, scale, x, M, K);
+    } else if (K % 16 == 0 && aligned16(x) && aligned16(q)) {
+        hipLaunchKernelGGL(quantize_rows_vec, grid, block, 0, s, q, scale, x, M, K);
     } else {
-        hipLaunchKernelGGL(quantize_rows_plain, dim3((unsigned)blocks), dim3(256), 0, s, q, scale, x, M, K);
+        hipLaunchKernelGGL(quantize_rows_plain, grid, block, 0, s, q, scale, x, M, K);
     }
     return hipGetLastError();
 }
