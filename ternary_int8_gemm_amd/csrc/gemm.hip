@@ -368,6 +368,156 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
     }
 }
 
+// Skinny path: few rows (M up to a few hundred), where the block tiles above
+// would leave most CUs idle and each block would walk the whole K loop alone.
+// A block owns a BM x BN output tile (BM = 32 * MT, BN = 32 * NT) and its KW
+// waves split K: wave w takes the 128-element chunks w, w + KW, ...  Operands
+// go straight from global memory into MFMA registers (no LDS staging, no
+// barriers in the K loop): lane (r, h) loads, for each k-step s of a chunk,
+// the 16 activation bytes 64h + 16s .. 64h + 16s + 15 of row r and transposes
+// them, and the 16 packed bytes 16h .. 16h + 15 of the chunk of column r,
+// which hold its B operand dwords for the four k-steps (the k order of the
+// tiled kernel).  A ring of D chunks keeps loads in flight.  At the end the
+// waves add their partial accumulators (and partial row sums) into an int32
+// LDS tile with ds_add and the block writes the epilogue row by row.
+template <int MT, int NT, int KW, int D, bool OUT_I32>
+__global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(uint16_t* __restrict__ out,
+                                                              int32_t* __restrict__ acc_out,
+                                                              const int8_t* __restrict__ x,
+                                                              const uint8_t* __restrict__ w,
+                                                              const uint16_t* __restrict__ sa,
+                                                              const uint16_t* __restrict__ sw, int M, int N, int K,
+                                                              int tiles_n) {
+    constexpr int BM = 32 * MT, BN = 32 * NT;
+    constexpr int LDN = BN + 8;  // padded row: the two lane halves of an MFMA row group hit different banks
+    constexpr int THREADS = 64 * KW;
+    __shared__ int red[BM * LDN];
+    __shared__ int rsum[BM];
+    __shared__ float rscale[BM];
+    __shared__ float cscale[BN];
+
+    const int tm = blockIdx.x / tiles_n;
+    const int tn = blockIdx.x - tm * tiles_n;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int KB = K >> 2;
+    const int nc = K / GM_KS;
+    const int r = lane & 31, h = lane >> 5;
+
+    for (int i = tid; i < BM * LDN; i += THREADS) red[i] = 0;
+    for (int i = tid; i < BM; i += THREADS) {
+        rsum[i] = 0;
+        rscale[i] = (!OUT_I32 && m0 + i < M) ? bf16_to_f32(sa[m0 + i]) : 0.0f;
+    }
+    for (int i = tid; i < BN; i += THREADS) cscale[i] = (!OUT_I32 && n0 + i < N) ? bf16_to_f32(sw[n0 + i]) : 0.0f;
+
+    const __amdgpu_buffer_rsrc_t x_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(x), (short)0, M * K, BUFFER_RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t w_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w), (short)0, N * KB, BUFFER_RSRC_WORD3);
+    int a_voff[MT], b_voff[NT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) a_voff[t] = (m0 + 32 * t + r) * K + 64 * h;  // rows past M read zeros
+#pragma unroll
+    for (int u = 0; u < NT; ++u) b_voff[u] = (n0 + 32 * u + r) * KB + 16 * h;  // columns past N read zeros
+
+    struct Chunk {
+        v4u a[MT][4];
+        v4u b[NT];
+    };
+    auto load = [&](int j, Chunk& C) {
+        const int c = min(wave + KW * j, nc - 1);  // clamped repeats past the end are never multiplied
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                C.a[t][s] = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, a_voff[t], c * GM_KS + 16 * s, 0);
+#pragma unroll
+        for (int u = 0; u < NT; ++u) C.b[u] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, b_voff[u], c * (GM_KS / 4), 0);
+    };
+
+    v16i acc[MT][NT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int u = 0; u < NT; ++u) acc[t][u] = v16i{};
+    int rs[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) rs[t] = 0;
+
+    auto compute = [&](const Chunk& C) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            v4i af[MT];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const v4u v = C.a[t][s];
+                const uint4 tt = transpose4x4(v.x, v.y, v.z, v.w);
+                af[t] = v4i{(int)tt.x, (int)tt.y, (int)tt.z, (int)tt.w};
+                int sum = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, rs[t], false);
+                sum = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, sum, false);
+                sum = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, sum, false);
+                rs[t] = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, sum, false);
+            }
+#pragma unroll
+            for (int u = 0; u < NT; ++u) {
+                const uint32_t p = C.b[u][s];
+                const v4i bf = {(int)(p & CODE_MASK), (int)((p >> 2) & CODE_MASK), (int)((p >> 4) & CODE_MASK),
+                                (int)((p >> 6) & CODE_MASK)};
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    acc[t][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[t], bf, acc[t][u], 0, 0, 0);
+            }
+        }
+    };
+
+    // The ring: every iteration issues the load D chunks ahead unconditionally,
+    // so the compiler's waits stay exact; the last < D chunks are already in.
+    const int nj = (nc - 1 - wave) / KW + 1;  // chunks of this wave (the host guarantees nc >= KW)
+    Chunk ring[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) load(i, ring[i]);
+    int j = 0;
+    for (; j + D <= nj; j += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            compute(ring[i]);
+            load(j + D + i, ring[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        if (j + i < nj) compute(ring[i]);
+
+    // ---- split-K reduction in LDS, then the epilogue
+    __syncthreads();  // the tile is zeroed
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int row = 32 * t + 8 * (q >> 2) + 4 * h + (q & 3);
+                atomicAdd(&red[row * LDN + 32 * u + r], acc[t][u][q]);
+            }
+        atomicAdd(&rsum[32 * t + r], rs[t]);
+    }
+    __syncthreads();
+    for (int e = tid; e < BM * BN; e += THREADS) {
+        const int row = e / BN, col = e - row * BN;
+        const int gm = m0 + row, gn = n0 + col;
+        if (gm < M && gn < N) {
+            const int v = red[row * LDN + col] - 2 * rsum[row];
+            if (OUT_I32)
+                acc_out[(int64_t)gm * N + gn] = v;
+            else
+                out[(int64_t)gm * N + gn] = epilogue_bf16(v, rscale[row], cscale[col]);
+        }
+    }
+}
+
 // Plain path: one wave per output row n, any K % 4 == 0 and any alignment.
 template <bool OUT_I32>
 __global__ __launch_bounds__(64) void gemm_plain(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
@@ -410,6 +560,16 @@ hipError_t launch_mfma(uint16_t* out, int32_t* acc, const int8_t* x, const uint8
     return hipGetLastError();
 }
 
+template <int MT, int NT, int KW, int D, bool OUT_I32>
+hipError_t launch_skinny(uint16_t* out, int32_t* acc, const int8_t* x, const uint8_t* w, const uint16_t* sa,
+                         const uint16_t* sw, int M, int N, int K, hipStream_t s) {
+    const int tiles_m = (M + 32 * MT - 1) / (32 * MT);
+    const int tiles_n = (N + 32 * NT - 1) / (32 * NT);
+    hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, KW, D, OUT_I32>), dim3((unsigned)(tiles_m * tiles_n)),
+                       dim3(64 * KW), 0, s, out, acc, x, w, sa, sw, M, N, K, tiles_n);
+    return hipGetLastError();
+}
+
 template <bool OUT_I32>
 hipError_t launch_tiles(uint16_t* out, int32_t* acc, const int8_t* x, const uint8_t* w, const uint16_t* sa,
                         const uint16_t* sw, int M, int N, int K, hipStream_t s) {
@@ -418,6 +578,18 @@ hipError_t launch_tiles(uint16_t* out, int32_t* acc, const int8_t* x, const uint
     // spend the least VALU per MFMA; they are used when there are enough of them
     // to give every CU at least two.  Otherwise 128 x 256 blocks (eight 64 x 64
     // wave tiles), which keep two waves per SIMD busy on N = 4096-sized shapes.
+    // Too few 128 x 256 tiles to give every CU one: the split-K skinny kernel
+    // (each wave needs at least one 128-element chunk of K).  Configurations
+    // measured on the LLaMA-7B layer shapes: short rings and more resident
+    // waves beat deep per-wave prefetch here.
+    const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 255) / 256);
+    const int nc = K / GM_KS;
+    if (tiles < 256 && nc >= 4) {
+        if (M <= 16 && nc >= 8) return launch_skinny<1, 1, 8, 1, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+        if (M <= 64) return launch_skinny<1, 1, 4, 1, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+        if (M <= 128) return launch_skinny<1, 2, 4, 1, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+        return launch_skinny<2, 2, 4, 1, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+    }
     const int64_t wide_tiles = (int64_t)((M + 127) / 128) * ((N + 511) / 512);
     if (wide_tiles >= 2 * 256)
         return launch_mfma<128, 512, 1, 8, 2, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);

@@ -110,6 +110,8 @@ def test_quantize_misaligned_plain_path():
 GEMM_SHAPES = [
     (1, 1, 64), (4, 128, 256), (17, 33, 64), (128, 128, 128), (129, 130, 192), (300, 257, 320),
     (16, 4096, 4096), (64, 512, 2560), (255, 129, 6912), (8, 64, 68), (5, 7, 100), (3, 3, 4),
+    # split-K path for few rows: every configuration, ragged N, K of 4..9 chunks of 128
+    (9, 100, 1152), (20, 777, 1024), (100, 1000, 640), (130, 70, 512), (1, 33, 4096), (64, 31, 512),
 ]
 
 
