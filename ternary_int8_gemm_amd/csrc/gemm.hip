@@ -56,6 +56,7 @@ namespace bitnet {
 namespace {
 
 constexpr int GM_KS = 128;     // K elements per pipeline stage (4 MFMA k-steps of 32)
+constexpr int GROUP_M = 8;     // row panels swept per column tile (tile order)
 constexpr int GM_FRAG = 1024;  // bytes of one 32 x 32 int8 A operand fragment (64 lanes x 16 B)
 // Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format;
 // stride 0, so bounds are checked against the byte count in word 2).
@@ -115,9 +116,17 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
     float* rowscale = reinterpret_cast<float*>(lds + 3 * S::STAGE + 4 * BM);
     float* colscale = reinterpret_cast<float*>(lds + 3 * S::STAGE + 8 * BM);
 
+    // Block -> tile: consecutive logical tiles land on one XCD (xcd_remap) and
+    // sweep GROUP_M row panels per column tile, so an XCD's concurrent tiles
+    // share a few activation panels and a few weight panels in its L2.
     const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
-    const int tm = tile / tiles_n;
-    const int tn = tile - tm * tiles_n;
+    const int per_group = GROUP_M * tiles_n;
+    const int group = tile / per_group;
+    const int first_m = group * GROUP_M;
+    const int gsize = min(tiles_m - first_m, GROUP_M);
+    const int in_group = tile - group * per_group;
+    const int tm = first_m + in_group % gsize;
+    const int tn = in_group / gsize;
     const int m0 = tm * BM;
     const int n0 = tn * BN;
 

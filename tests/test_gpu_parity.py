@@ -67,7 +67,9 @@ def problem(M, N, K, seed, outliers=0.0, row_scales=False):
 
 # ----------------------------------------------------------------------------- quantisation
 
-QUANT_SHAPES = [(4, 256), (1, 4), (3, 12), (7, 100), (16, 2560), (33, 4096), (5, 6912), (2, 131072), (130, 64)]
+QUANT_SHAPES = [(4, 256), (1, 4), (3, 12), (7, 100), (16, 2560), (33, 4096), (5, 6912), (2, 131072), (130, 64),
+                # two rows per wave (M >= 2048), with an odd last wave
+                (2049, 4096), (2051, 6912), (2053, 520)]
 
 
 @pytest.mark.parametrize("M,K", QUANT_SHAPES)
