@@ -15,6 +15,9 @@ Parity status of each function (what pins it is listed in the tests):
   gemm_i32                        pinned (hand-worked K=4/K=8, brute force, closed forms)
   epilogue                        pinned (exact-product identity, tie cases)
   linear / linear_one             pinned through the three above and by composition
+  quantize_f32 / linear_f32       pinned (hand-worked f32 vector; equal to the bf16 path on
+                                  bf16-representable inputs; composition)
+  add_bias                        pinned (hand-worked round-to-even ties; zero bias; zero rows)
 """
 import ctypes
 import os
@@ -56,6 +59,12 @@ def load(path=None):
     lib.oracle_quantize_row.restype = None
     lib.oracle_quantize.argtypes = [_p, _i64, _i64, _p, _p]
     lib.oracle_quantize.restype = ctypes.c_int
+    lib.oracle_quantize_f32.argtypes = [_p, _i64, _i64, _p, _p]
+    lib.oracle_quantize_f32.restype = ctypes.c_int
+    lib.oracle_add_bias.argtypes = [_p, _p, _i64, _i64]
+    lib.oracle_add_bias.restype = None
+    lib.oracle_linear_f32.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p]
+    lib.oracle_linear_f32.restype = ctypes.c_int
     lib.oracle_dot_i64.argtypes = [_p, _p, _i64, _i64]
     lib.oracle_dot_i64.restype = ctypes.c_int64
     lib.oracle_gemm_i32.argtypes = [_p, _p, _i64, _i64, _i64, _p]
@@ -188,3 +197,41 @@ def linear_one(q_row, sa, P, sw, n, lib=None):
     K = q_row.shape[0]
     out = lib.oracle_linear_one(_ptr(q_row), int(sa), _ptr(P), _ptr(sw), K, int(n), ctypes.byref(acc))
     return int(out), int(acc.value)
+
+
+def quantize_f32(x, lib=None):
+    """float32 x[M,K] -> (int8 q[M,K], uint16 bf16 scale_act[M])."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    M, K = x.shape
+    q = np.zeros((M, K), dtype=np.int8)
+    sa = np.zeros((M,), dtype=np.uint16)
+    _check(lib.oracle_quantize_f32(_ptr(x), M, K, _ptr(q), _ptr(sa)), "quantize_f32")
+    return q, sa
+
+
+def add_bias(out_bits, bias_bits, lib=None):
+    """bf16 bits out[M,N] + bf16 bits bias[N] -> new bf16 bits array."""
+    lib = lib or load()
+    out = np.array(out_bits, dtype=np.uint16, copy=True, order="C")
+    bias = np.ascontiguousarray(bias_bits, dtype=np.uint16)
+    M, N = out.shape
+    lib.oracle_add_bias(_ptr(out), _ptr(bias), M, N)
+    return out
+
+
+def linear_f32(x, P, sw, lib=None):
+    """Whole layer on float32 activations.  Returns dict(out, q, scale_act, acc)."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    P = np.ascontiguousarray(P, dtype=np.uint8)
+    sw = np.ascontiguousarray(sw, dtype=np.uint16)
+    M, K = x.shape
+    N = P.shape[0]
+    out = np.zeros((M, N), dtype=np.uint16)
+    q = np.zeros((M, K), dtype=np.int8)
+    sa = np.zeros((M,), dtype=np.uint16)
+    acc = np.zeros((M, N), dtype=np.int32)
+    _check(lib.oracle_linear_f32(_ptr(x), _ptr(P), _ptr(sw), M, N, K, _ptr(out), _ptr(q), _ptr(sa), _ptr(acc)),
+           "linear_f32")
+    return {"out": out, "q": q, "scale_act": sa, "acc": acc}

@@ -16,6 +16,10 @@
 //                                        oracle_linear
 //   * "kernels-community/README discussion #1 (bitnet-tc kernel request)",
 //       numbers post: the product accumulates in int32.
+//       - f32 activations (accepted by quantize_activation, bitnet_gemv_fused
+//         and bitnet_linear)       -> oracle_quantize_row_f32, oracle_linear_f32
+//       - class BitLinear, the bias added to the layer's output
+//                                     -> oracle_add_bias
 //   * "CoolDip00/tiny-llm src/tinyllm/kernels/int8_gemv.py", docstring of
 //       int8_matmul: the integer/matmul result is scaled without an
 //       intermediate rounding to bf16.
@@ -139,23 +143,32 @@ void oracle_unpack(const uint8_t* P, int64_t N, int64_t K, int8_t* W) {
 //   q[k]  = clamp(round_half_even(xf[k] / s), -127, 127) as int8
 //   scale = bf16_rne(s)
 // ---------------------------------------------------------------------------
-void oracle_quantize_row(const uint16_t* x, int64_t K, int8_t* q, uint16_t* scale) {
+// One row of per-token absmax quantisation on fp32 values xf[0..K).
+static void quantize_values(const float* xf, int64_t K, int8_t* q, uint16_t* scale) {
     float a = 0.0f;
     for (int64_t k = 0; k < K; ++k) {
-        const float v = std::fabs(oracle_f32_from_bf16(x[k]));
+        const float v = std::fabs(xf[k]);
         if (v > a) a = v;
     }
     const float eps = 1e-5f;
     if (a < eps) a = eps;
     const float s = a / 127.0f;
     for (int64_t k = 0; k < K; ++k) {
-        const float y = oracle_f32_from_bf16(x[k]) / s;
+        const float y = xf[k] / s;
         float r = std::nearbyint(y);  // default rounding mode: to nearest, ties to even
         if (r > 127.0f) r = 127.0f;
         if (r < -127.0f) r = -127.0f;
         q[k] = (int8_t)r;
     }
     *scale = oracle_bf16_from_f32(s);
+}
+
+// bf16 activations: widened exactly to fp32, then quantised.
+void oracle_quantize_row(const uint16_t* x, int64_t K, int8_t* q, uint16_t* scale) {
+    float* xf = (float*)std::malloc((size_t)(K > 0 ? K : 1) * sizeof(float));
+    for (int64_t k = 0; k < K; ++k) xf[k] = oracle_f32_from_bf16(x[k]);
+    quantize_values(xf, K, q, scale);
+    std::free(xf);
 }
 
 int oracle_quantize(const uint16_t* x, int64_t M, int64_t K, int8_t* q, uint16_t* scale) {
@@ -214,6 +227,33 @@ void oracle_epilogue(const int32_t* acc, const uint16_t* sa, const uint16_t* sw,
 // R6): quantise each row, contract, scale.  Fills q/scale_act/acc when the
 // caller passes buffers for them (NULL to skip).
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// f32 activations.  bitnet-cpu's quantize_activation, bitnet_gemv_fused and
+// bitnet_linear accept x in bf16 or f32; for f32 the same per-token absmax
+// quantisation runs on the f32 values themselves (no rounding to bf16 first).
+// ---------------------------------------------------------------------------
+void oracle_quantize_row_f32(const float* x, int64_t K, int8_t* q, uint16_t* scale) {
+    quantize_values(x, K, q, scale);  // the f32 values themselves, no rounding to bf16
+}
+
+int oracle_quantize_f32(const float* x, int64_t M, int64_t K, int8_t* q, uint16_t* scale) {
+    if (M < 0 || K <= 0) return ORC_ERR_SHAPE;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) oracle_quantize_row_f32(x + m * K, K, q + m * K, scale + m);
+    return ORC_OK;
+}
+
+// Bias, as bitnet-cpu's BitLinear applies it: the layer's bf16 output y plus a
+// bf16 bias per output column, added in fp32 and rounded to bf16 once:
+//   out[m][n] = bf16_rne( fp32(y[m][n]) + fp32(bias[n]) ).
+void oracle_add_bias(uint16_t* out, const uint16_t* bias, int64_t M, int64_t N) {
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            const float y = oracle_f32_from_bf16(out[m * N + n]) + oracle_f32_from_bf16(bias[n]);
+            out[m * N + n] = oracle_bf16_from_f32(y);
+        }
+}
+
 int oracle_linear(const uint16_t* x, const uint8_t* P, const uint16_t* sw, int64_t M, int64_t N, int64_t K,
                   uint16_t* out, int8_t* q_out, uint16_t* sa_out, int32_t* acc_out) {
     if (M < 0 || N < 0 || K <= 0 || K % 4 != 0) return ORC_ERR_SHAPE;
@@ -231,6 +271,22 @@ int oracle_linear(const uint16_t* x, const uint8_t* P, const uint16_t* sw, int64
 
 // One output element of the layer from an already quantised row: used to
 // check sampled outputs of full-size problems one by one.
+// The whole layer on f32 activations: quantise (f32), contract, scale.
+int oracle_linear_f32(const float* x, const uint8_t* P, const uint16_t* sw, int64_t M, int64_t N, int64_t K,
+                      uint16_t* out, int8_t* q_out, uint16_t* sa_out, int32_t* acc_out) {
+    if (M < 0 || N < 0 || K <= 0 || K % 4 != 0) return ORC_ERR_SHAPE;
+    int8_t* q = q_out ? q_out : (int8_t*)std::malloc((size_t)(M * K > 0 ? M * K : 1));
+    uint16_t* sa = sa_out ? sa_out : (uint16_t*)std::malloc((size_t)(M > 0 ? M : 1) * sizeof(uint16_t));
+    int32_t* acc = acc_out ? acc_out : (int32_t*)std::malloc((size_t)(M * N > 0 ? M * N : 1) * sizeof(int32_t));
+    int rc = oracle_quantize_f32(x, M, K, q, sa);
+    if (rc == ORC_OK) rc = oracle_gemm_i32(q, P, M, N, K, acc);
+    if (rc == ORC_OK) oracle_epilogue(acc, sa, sw, M, N, out);
+    if (!q_out) std::free(q);
+    if (!sa_out) std::free(sa);
+    if (!acc_out) std::free(acc);
+    return rc;
+}
+
 uint16_t oracle_linear_one(const int8_t* q_row, uint16_t sa, const uint8_t* P, const uint16_t* sw, int64_t K,
                            int64_t n, int32_t* acc_out) {
     const int64_t s = oracle_dot_i64(q_row, P, K, n);

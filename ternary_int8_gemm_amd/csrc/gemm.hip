@@ -104,7 +104,7 @@ struct StageRegs {
     v4u b[B_CH];
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int WAVES_PER_EU, bool OUT_I32>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int WAVES_PER_EU, int NS, bool OUT_I32>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out, const int8_t* __restrict__ x,
                       const uint8_t* __restrict__ w, const uint16_t* __restrict__ sa,
@@ -218,7 +218,7 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
     };
 
     // One pipeline step k, between two barriers, with LDS buffer bi = k % 3:
-    // issue the global loads of stage k+4 into the register set that held
+    // issue the global loads of stage k+NS+1 into the register set that held
     // stage k+1, multiply stage k, move stage k+2 from its register set into
     // buffer (k+2) % 3, and read the first fragments of stage k+1 (written
     // during step k-1, visible since this step's barrier).  The program order
@@ -230,7 +230,7 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
     v4i af0[MT];
     auto step = [&](const int bi, int k, const StageRegs<A_CH, B_CH>& SS, StageRegs<A_CH, B_CH>& SL) {
         __syncthreads();  // stage k+1 visible; buffer (k+2) % 3 no longer read
-        load_stage(k + 4, SL);
+        load_stage(k + NS + 1, SL);
         __builtin_amdgcn_sched_barrier(0);  // keep the loads at the top
         const uint8_t* cur = lds + bi * S::STAGE;
         uint8_t* later = lds + ((bi + 2) % 3) * S::STAGE;
@@ -270,31 +270,32 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
         }
     };
 
-    // Stage j lives in register set j % 3 from its load until its LDS store,
-    // and in LDS buffer j % 3 from its store until it is multiplied.
-    StageRegs<A_CH, B_CH> s0, s1, s2;
-    load_stage(0, s0);
-    load_stage(1, s1);
-    load_stage(2, s2);
+    // Stage j lives in register set j % NS from its load (step j - NS - 1)
+    // until its LDS store (step j - 2), and in LDS buffer j % 3 from its store
+    // until it is multiplied.
+    constexpr int LEAD = NS + 1;
+    StageRegs<A_CH, B_CH> sets[NS];
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) store_a(lds, i, s0.a[i], 1);
+    for (int i = 0; i < NS; ++i) load_stage(i, sets[i]);
 #pragma unroll
-    for (int j = 0; j < B_CH; ++j) *reinterpret_cast<v4u*>(lds + b_off[j]) = s0.b[j];
+    for (int i = 0; i < A_CH; ++i) store_a(lds, i, sets[0].a[i], 1);
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) store_a(lds + S::STAGE, i, s1.a[i], nk > 1 ? 1 : 0);
+    for (int j = 0; j < B_CH; ++j) *reinterpret_cast<v4u*>(lds + b_off[j]) = sets[0].b[j];
 #pragma unroll
-    for (int j = 0; j < B_CH; ++j) *reinterpret_cast<v4u*>(lds + S::STAGE + b_off[j]) = s1.b[j];
-    load_stage(3, s0);
+    for (int i = 0; i < A_CH; ++i) store_a(lds + S::STAGE, i, sets[1].a[i], nk > 1 ? 1 : 0);
+#pragma unroll
+    for (int j = 0; j < B_CH; ++j) *reinterpret_cast<v4u*>(lds + S::STAGE + b_off[j]) = sets[1].b[j];
+    load_stage(NS, sets[0]);
     __syncthreads();
     read_first(lds, pb, af0);
     int k = 0;
-    for (; k + 3 <= nk; k += 3) {
-        step(0, k, s2, s1);
-        step(1, k + 1, s0, s2);
-        step(2, k + 2, s1, s0);
+    for (; k + NS <= nk; k += NS) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) step(i % 3, k + i, sets[(i + 2) % NS], sets[(i + LEAD) % NS]);
     }
-    if (k < nk) step(0, k, s2, s1);
-    if (k + 1 < nk) step(1, k + 1, s0, s2);
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+        if (k + i < nk) step(i % 3, k + i, sets[(i + 2) % NS], sets[(i + LEAD) % NS]);
 
     // ---- row sums (the 8 threads of a row are aligned lanes) and row scales to LDS
 #pragma unroll
@@ -552,13 +553,13 @@ __global__ __launch_bounds__(64) void gemm_plain(uint16_t* __restrict__ out, int
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int WAVES_PER_EU, bool OUT_I32>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int WAVES_PER_EU, int NS, bool OUT_I32>
 hipError_t launch_mfma(uint16_t* out, int32_t* acc, const int8_t* x, const uint8_t* w, const uint16_t* sa,
                        const uint16_t* sw, int M, int N, int K, hipStream_t s) {
     using S = GemmShape<BM, BN, WAVES_M, WAVES_N>;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
-    auto kern = gemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, WAVES_PER_EU, OUT_I32>;
+    auto kern = gemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, WAVES_PER_EU, NS, OUT_I32>;
     if (S::LDS > 65536) {  // beyond the default dynamic LDS limit: raise it (idempotent)
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::LDS);
@@ -601,8 +602,8 @@ hipError_t launch_tiles(uint16_t* out, int32_t* acc, const int8_t* x, const uint
     }
     const int64_t wide_tiles = (int64_t)((M + 127) / 128) * ((N + 511) / 512);
     if (wide_tiles >= 2 * 256)
-        return launch_mfma<128, 512, 1, 8, 2, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
-    return launch_mfma<128, 256, 2, 4, 2, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+        return launch_mfma<128, 512, 1, 8, 2, 3, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+    return launch_mfma<128, 256, 2, 4, 2, 3, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
 }
 
 template <bool OUT_I32>

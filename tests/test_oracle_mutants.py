@@ -103,7 +103,25 @@ def _pin_battery(lib):
         r = oracle.linear(x, P, np.full((5,), 0x3F80, dtype=np.uint16), lib=lib)
         return np.array_equal(r["acc"], r["q"].astype(np.int64) @ W.astype(np.int64).T)
 
+    def quant_f32_golden():
+        for r in read_golden("quantize_f32_vectors.txt"):
+            x = np.array([int(t, 16) for t in r["x"]], dtype=np.uint32).view(np.float32)[None, :]
+            q, sa = oracle.quantize_f32(x, lib=lib)
+            if q[0].tolist() != [int(t) for t in r["q"]] or int(sa[0]) != int(r["scale_bf16"][0], 16):
+                return False
+        return True
+
+    def bias_golden():
+        for r in read_golden("bias_cases.txt"):
+            y = np.array([[int(r["y"][0], 16), 0]], dtype=np.uint16)
+            b = np.array([int(r["bias"][0], 16), 0x3F80], dtype=np.uint16)
+            got = oracle.add_bias(y, b, lib=lib)
+            if int(got[0, 0]) != int(r["out"][0], 16) or int(got[0, 1]) != 0x3F80:
+                return False
+        return True
+
     for name, fn in [("pack_golden", pack_golden), ("unpack_roundtrip", unpack_roundtrip),
+                     ("quant_f32_golden", quant_f32_golden), ("bias_golden", bias_golden),
                      ("quant_golden", quant_golden), ("quant_absmax", quant_absmax),
                      ("gemm_hand", gemm_hand), ("gemm_brute", gemm_brute), ("epi_golden", epi_golden), ("epi_batch", epi_batch),
                      ("linear_k8", linear_k8), ("linear_shape", linear_shape)]:
@@ -116,13 +134,12 @@ MUTANTS = [
     ("pack_bit_order", "byte |= code << (2 * i);", "byte |= code << (6 - 2 * i);"),
     ("decode_offset", "return code - 2;", "return code - 1;"),
     ("decode_bit_order", "(byte >> (2 * (k % 4))) & 3", "(byte >> (2 * (3 - k % 4))) & 3"),
-    ("absmax_no_abs", "std::fabs(oracle_f32_from_bf16(x[k]))", "(oracle_f32_from_bf16(x[k]))"),
+    ("absmax_no_abs", "std::fabs(xf[k])", "(xf[k])"),
     ("scale_128", "const float s = a / 127.0f;", "const float s = a / 128.0f;"),
     ("eps_dropped", "if (a < eps) a = eps;", "(void)eps;"),
     ("round_half_away", "std::nearbyint(y)", "std::round(y)"),
-    ("mul_by_reciprocal", "oracle_f32_from_bf16(x[k]) / s;", "oracle_f32_from_bf16(x[k]) * (127.0f / a);"),
-    ("divide_by_bf16_scale", "oracle_f32_from_bf16(x[k]) / s;",
-     "oracle_f32_from_bf16(x[k]) / oracle_f32_from_bf16(oracle_bf16_from_f32(s));"),
+    ("mul_by_reciprocal", "xf[k] / s;", "xf[k] * (127.0f / a);"),
+    ("divide_by_bf16_scale", "xf[k] / s;", "xf[k] / oracle_f32_from_bf16(oracle_bf16_from_f32(s));"),
     ("scale_truncated", "*scale = oracle_bf16_from_f32(s);", "{ uint32_t u_; std::memcpy(&u_, &s, 4); *scale = (uint16_t)(u_ >> 16); }"),
     ("gemm_transposed_out", "acc[m * N + n] = (int32_t)s;", "acc[n * M + m] = (int32_t)s;"),
     ("gemm_dropped_term", "for (int64_t k = 0; k < K; ++k) s +=", "for (int64_t k = 1; k < K; ++k) s +="),
@@ -134,6 +151,12 @@ MUTANTS = [
     ("bf16_truncate", "if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;", "(void)lower;"),
     ("epi_scale_index", "oracle_epilogue_one(acc[m * N + n], sa[m], sw[n])",
      "oracle_epilogue_one(acc[m * N + n], sa[m], sw[m])"),
+    ("f32_via_bf16", "quantize_values(x, K, q, scale);  // the f32 values",
+     "for (int64_t k = 0; k < K; ++k) ((float*)x)[k] = oracle_f32_from_bf16(oracle_bf16_from_f32(x[k]));\n    quantize_values(x, K, q, scale);  // the f32 values"),
+    ("bf16_widen_wrong", "xf[k] = oracle_f32_from_bf16(x[k]);", "xf[k] = (float)(int16_t)x[k];"),
+    ("bias_double_round", "const float y = oracle_f32_from_bf16(out[m * N + n]) + oracle_f32_from_bf16(bias[n]);",
+     "const float y = oracle_f32_from_bf16(oracle_bf16_from_f32(oracle_f32_from_bf16(out[m * N + n]) + oracle_f32_from_bf16(bias[n]) * 0.5f)) + oracle_f32_from_bf16(bias[n]) * 0.5f;"),
+    ("bias_row_index", "oracle_f32_from_bf16(bias[n])", "oracle_f32_from_bf16(bias[m])"),
 ]
 
 

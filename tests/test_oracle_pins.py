@@ -257,3 +257,66 @@ def test_linear_is_composition_and_k8_example(orc):
     for m, n in ((0, 0), (4, 32), (2, 17)):
         o, a = orc.linear_one(q[m], sa[m], P, sw, n)
         assert o == r["out"][m, n] and a == r["acc"][m, n]
+
+
+# ----------------------------------------------------------------------------- f32 activations and bias
+
+def _f32_from_hex(tokens):
+    return np.array([int(t, 16) for t in tokens], dtype=np.uint32).view(np.float32)
+
+
+def test_quantize_f32_golden(orc):
+    for r in read_golden("quantize_f32_vectors.txt"):
+        q, sa = orc.quantize_f32(_f32_from_hex(r["x"])[None, :])
+        assert q[0].tolist() == [int(t) for t in r["q"]], r
+        assert int(sa[0]) == int(r["scale_bf16"][0], 16), r
+
+
+def test_quantize_f32_equals_bf16_path_on_bf16_values(orc):
+    """On values that are exactly bf16, the f32 path is the bf16 path."""
+    x = synth.activations_bf16(6, 640, seed=31, outlier_frac=0.02)
+    q16, s16 = orc.quantize(x)
+    q32, s32 = orc.quantize_f32(synth.bf16_bits_to_f32(x))
+    assert np.array_equal(q16, q32) and np.array_equal(s16, s32)
+
+
+def test_quantize_f32_absmax_and_double_division(orc):
+    g = synth.rng(33)
+    x = g.standard_normal((5, 300)).astype(np.float32) * np.float32(3.0)
+    q, sa = orc.quantize_f32(x)
+    am = np.argmax(np.abs(x), axis=1)
+    assert np.all(q[np.arange(5), am] == np.sign(x[np.arange(5), am]) * 127)
+    # independent quantiser: fp32 division emulated in double (exact rounding, 53 >= 2*24+2)
+    a = np.maximum(np.abs(x).max(axis=1), np.float32(1e-5)).astype(np.float32)
+    s = (a.astype(np.float64) / 127.0).astype(np.float32)
+    y = (x.astype(np.float64) / s.astype(np.float64)[:, None]).astype(np.float32)
+    assert np.array_equal(q, np.clip(np.rint(y), -127, 127).astype(np.int8))
+
+
+def test_add_bias_golden(orc):
+    for r in read_golden("bias_cases.txt"):
+        y = np.array([[int(r["y"][0], 16)]], dtype=np.uint16)
+        b = np.array([int(r["bias"][0], 16)], dtype=np.uint16)
+        assert int(orc.add_bias(y, b)[0, 0]) == int(r["out"][0], 16), r
+
+
+def test_add_bias_is_per_column_and_matches_torch(orc):
+    g = synth.rng(34)
+    y = torch.from_numpy(g.standard_normal((4, 9)).astype(np.float32)).to(torch.bfloat16)
+    b = torch.from_numpy(g.standard_normal((9,)).astype(np.float32)).to(torch.bfloat16)
+    want = (y + b).view(torch.int16).numpy().view(np.uint16)   # torch adds bf16 in fp32, rounds once
+    got = orc.add_bias(y.view(torch.int16).numpy().view(np.uint16), b.view(torch.int16).numpy().view(np.uint16))
+    assert np.array_equal(got, want)
+
+
+def test_linear_f32_is_composition(orc):
+    g = synth.rng(35)
+    x = g.standard_normal((3, 128)).astype(np.float32)
+    W = synth.ternary_weights(7, 128, seed=36)
+    P = orc.pack(W)
+    sw = synth.row_scales_bf16(7, seed=37)
+    r = orc.linear_f32(x, P, sw)
+    q, sa = orc.quantize_f32(x)
+    assert np.array_equal(r["q"], q) and np.array_equal(r["scale_act"], sa)
+    assert np.array_equal(r["acc"], q.astype(np.int64) @ W.astype(np.int64).T)
+    assert np.array_equal(r["out"], orc.epilogue(r["acc"], sa, sw))
