@@ -128,6 +128,47 @@ bitnet_status bitnet_linear(uint16_t* out, const uint16_t* x, const uint8_t* w_p
                             int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
                             bitnet_stream_t stream);
 
+/* Activation element types accepted by bitnet_linear_ex. */
+#define BITNET_DTYPE_BF16 0
+#define BITNET_DTYPE_F32 1
+
+/*
+ * Per-token absmax INT8 quantisation of f32 activations (quantize_activation
+ * of bitnet-cpu takes x in bf16 or f32): the formula of bitnet_quantize_act
+ * applied to the f32 values themselves, with no rounding to bf16 first:
+ *   a = max(max_k |x[m][k]|, 1e-5f);   s = a / 127.0f  (IEEE fp32 division)
+ *   x_int8[m][k] = clamp(round_half_even(x[m][k] / s), -127, 127)
+ *   scale_act[m] = bf16_round_nearest_even(s)
+ * x: f32 [M][K]; x_int8: int8 [M][K] (written); scale_act: bf16 [M] (written).
+ * Device pointers, enqueued on stream.  NaN/Inf inputs are outside the contract.
+ */
+bitnet_status bitnet_quantize_act_f32(int8_t* x_int8, uint16_t* scale_act, const float* x, int64_t M, int64_t K,
+                                      bitnet_stream_t stream);
+
+/*
+ * Device workspace (bytes) that bitnet_linear_ex needs: for bf16 activations
+ * the same as bitnet_linear_workspace_bytes; for f32 activations room for
+ * x_int8 [M][K] and scale_act [M] at every M (f32 input always takes the
+ * quantise-then-GEMM path).  Returns 0 for invalid sizes or dtypes.
+ */
+size_t bitnet_linear_ex_workspace_bytes(int64_t M, int64_t K, int x_dtype);
+
+/*
+ * BitLinear forward with the two options of bitnet-cpu's API: f32 or bf16
+ * activations (bitnet_linear and quantize_activation accept both) and an
+ * optional bias (class BitLinear adds its bf16 bias to the bf16 result).
+ *   y = bitnet_linear(x)   (for f32 x: bitnet_quantize_act_f32, then bitnet_gemm)
+ *   out[m][n] = bias ? bf16_rne( fp32(y[m][n]) + fp32(bias[n]) ) : y[m][n]
+ * out: bf16 [M][N] (written); x: [M][K] of x_dtype (BITNET_DTYPE_BF16 or
+ * BITNET_DTYPE_F32); w_packed: uint8 [N][K/4]; scale_wt: bf16 [N]; bias: bf16
+ * [N] or NULL; workspace: bitnet_linear_ex_workspace_bytes(M, K, x_dtype)
+ * bytes of device memory (256-byte aligned).  Device pointers, enqueued on stream.
+ * Errors: unknown x_dtype -> VALUE; workspace too small -> WORKSPACE.
+ */
+bitnet_status bitnet_linear_ex(uint16_t* out, const void* x, int x_dtype, const uint8_t* w_packed,
+                               const uint16_t* scale_wt, const uint16_t* bias, int64_t M, int64_t N, int64_t K,
+                               void* workspace, size_t workspace_bytes, bitnet_stream_t stream);
+
 /*
  * Debug: the raw int32 accumulators of the batched path,
  *   acc[m][n] = sum_k w[n][k] * x_int8[m][k],

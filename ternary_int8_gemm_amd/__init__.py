@@ -70,6 +70,8 @@ def load_library():
         "bitnet_gemm_i32": [_p, _p, _p, _i64, _i64, _i64, _p],
         "bitnet_gemv_fused_i32": [_p, _p, _p, _p, _i64, _i64, _i64, _p],
         "bitnet_scale_epilogue": [_p, _p, _p, _p, _i64, _i64, _p],
+        "bitnet_quantize_act_f32": [_p, _p, _p, _i64, _i64, _p],
+        "bitnet_linear_ex": [_p, _p, _st, _p, _p, _p, _i64, _i64, _i64, _p, _sz, _p],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -77,6 +79,8 @@ def load_library():
         fn.restype = _st
     lib.bitnet_linear_workspace_bytes.argtypes = [_i64, _i64]
     lib.bitnet_linear_workspace_bytes.restype = _sz
+    lib.bitnet_linear_ex_workspace_bytes.argtypes = [_i64, _i64, _st]
+    lib.bitnet_linear_ex_workspace_bytes.restype = _sz
     lib.bitnet_status_string.argtypes = [_st]
     lib.bitnet_status_string.restype = ctypes.c_char_p
     lib.bitnet_version.argtypes = []
@@ -130,14 +134,20 @@ def pack_weights(W):
 # ----------------------------------------------------------------------------- device calls
 
 def quantize_activation(x, out=None, scale=None):
-    """bf16 x[..., K] -> (int8 [M, K], bf16 scale [M]), M = prod of leading dims."""
-    _need(x, torch.bfloat16, "x")
+    """bf16 or f32 x[..., K] -> (int8 [M, K], bf16 scale [M]), M = prod of leading dims."""
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"x must be bfloat16 or float32, got {x.dtype}")
+    _need(x, x.dtype, "x")
     K = x.shape[-1]
     M = x.numel() // K if K else 0
     x2 = x.reshape(M, K)
     q = out if out is not None else torch.empty((M, K), dtype=torch.int8, device=x.device)
     s = scale if scale is not None else torch.empty((M,), dtype=torch.bfloat16, device=x.device)
-    _check(load_library().bitnet_quantize_act(_ptr(q), _ptr(s), _ptr(x2), M, K, _stream(x)), "bitnet_quantize_act")
+    if x.dtype == torch.float32:
+        _check(load_library().bitnet_quantize_act_f32(_ptr(q), _ptr(s), _ptr(x2), M, K, _stream(x)),
+               "bitnet_quantize_act_f32")
+    else:
+        _check(load_library().bitnet_quantize_act(_ptr(q), _ptr(s), _ptr(x2), M, K, _stream(x)), "bitnet_quantize_act")
     return q, s
 
 
@@ -176,23 +186,47 @@ def linear_workspace_bytes(M, K):
     return int(load_library().bitnet_linear_workspace_bytes(M, K))
 
 
-def bitnet_linear(x, w_packed, scale_wt, out=None, workspace=None):
-    """One-shot BitLinear forward: bf16 x[..., K] -> bf16 [..., N]; dispatches on M."""
-    _need(x, torch.bfloat16, "x")
+DTYPE_BF16, DTYPE_F32 = 0, 1
+
+
+def linear_ex_workspace_bytes(M, K, dtype=torch.bfloat16):
+    code = DTYPE_F32 if dtype == torch.float32 else DTYPE_BF16
+    return int(load_library().bitnet_linear_ex_workspace_bytes(M, K, code))
+
+
+def bitnet_linear(x, w_packed, scale_wt, out=None, workspace=None, bias=None):
+    """One-shot BitLinear forward: bf16 or f32 x[..., K] -> bf16 [..., N]; dispatches on M.
+
+    bias (bf16 [N], optional) is added to the bf16 result as BitLinear does.
+    bf16 input without bias calls bitnet_linear; anything else bitnet_linear_ex.
+    """
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"x must be bfloat16 or float32, got {x.dtype}")
+    _need(x, x.dtype, "x")
     _need(w_packed, torch.uint8, "w_packed")
     _need(scale_wt, torch.bfloat16, "scale_wt")
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias")
     K = x.shape[-1]
     M = x.numel() // K if K else 0
     N = w_packed.shape[0]
-    if w_packed.shape[1] * 4 != K or scale_wt.numel() != N:
+    if w_packed.shape[1] * 4 != K or scale_wt.numel() != N or (bias is not None and bias.numel() != N):
         raise ValueError("bitnet_linear: inconsistent shapes")
-    ws_bytes = linear_workspace_bytes(M, K)
+    plain = x.dtype == torch.bfloat16 and bias is None
+    ws_bytes = linear_workspace_bytes(M, K) if plain else linear_ex_workspace_bytes(M, K, x.dtype)
     ws = workspace
     if ws is None and ws_bytes > 0:
         ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=x.device)
     o = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-    _check(load_library().bitnet_linear(_ptr(o), _ptr(x), _ptr(w_packed), _ptr(scale_wt), M, N, K, _ptr(ws),
-                                        ws.numel() if ws is not None else 0, _stream(x)), "bitnet_linear")
+    lib = load_library()
+    ws_n = ws.numel() if ws is not None else 0
+    if plain:
+        _check(lib.bitnet_linear(_ptr(o), _ptr(x), _ptr(w_packed), _ptr(scale_wt), M, N, K, _ptr(ws), ws_n,
+                                 _stream(x)), "bitnet_linear")
+    else:
+        code = DTYPE_F32 if x.dtype == torch.float32 else DTYPE_BF16
+        _check(lib.bitnet_linear_ex(_ptr(o), _ptr(x), code, _ptr(w_packed), _ptr(scale_wt), _ptr(bias), M, N, K,
+                                    _ptr(ws), ws_n, _stream(x)), "bitnet_linear_ex")
     return o.view(*x.shape[:-1], N)
 
 

@@ -16,6 +16,8 @@ using bitnet::launch_epilogue;
 using bitnet::launch_gemm;
 using bitnet::launch_gemv_fused;
 using bitnet::launch_quantize;
+using bitnet::launch_quantize_f32;
+using bitnet::launch_add_bias;
 
 constexpr int kMaxDevices = 64;
 // 0 = unknown, 1 = gfx950, 2 = other
@@ -160,6 +162,51 @@ BITNET_API bitnet_status bitnet_linear(uint16_t* out, const uint16_t* x, const u
     hipStream_t s = (hipStream_t)stream;
     if (hipError_t e = launch_quantize(x_int8, scale_act, x, M, K, s)) return launched(e);
     return launched(launch_gemm(out, nullptr, x_int8, w_packed, scale_act, scale_wt, M, N, K, s));
+}
+
+BITNET_API bitnet_status bitnet_quantize_act_f32(int8_t* x_int8, uint16_t* scale_act, const float* x, int64_t M,
+                                                 int64_t K, bitnet_stream_t stream) {
+    if (!sizes_ok(M, 0)) return BITNET_ERR_SHAPE;
+    if (bitnet_status st = check_k(K)) return st;
+    if (M == 0) return BITNET_OK;
+    if (!x_int8 || !scale_act || !x) return BITNET_ERR_NULL;
+    if (bitnet_status st = check_device()) return st;
+    return launched(launch_quantize_f32(x_int8, scale_act, x, M, K, (hipStream_t)stream));
+}
+
+BITNET_API size_t bitnet_linear_ex_workspace_bytes(int64_t M, int64_t K, int x_dtype) {
+    if (x_dtype == BITNET_DTYPE_BF16) return bitnet_linear_workspace_bytes(M, K);
+    if (x_dtype != BITNET_DTYPE_F32) return 0;
+    if (M < 0 || K <= 0 || K % 4 != 0 || K > BITNET_MAX_K || !sizes_ok(M, 0)) return 0;
+    return round256((size_t)M * (size_t)K) + round256((size_t)M * 2);
+}
+
+BITNET_API bitnet_status bitnet_linear_ex(uint16_t* out, const void* x, int x_dtype, const uint8_t* w_packed,
+                                          const uint16_t* scale_wt, const uint16_t* bias, int64_t M, int64_t N,
+                                          int64_t K, void* workspace, size_t workspace_bytes,
+                                          bitnet_stream_t stream) {
+    if (x_dtype != BITNET_DTYPE_BF16 && x_dtype != BITNET_DTYPE_F32) return BITNET_ERR_VALUE;
+    if (!sizes_ok(M, N)) return BITNET_ERR_SHAPE;
+    if (bitnet_status st = check_k(K)) return st;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!out || !x || !w_packed || !scale_wt) return BITNET_ERR_NULL;
+    bitnet_status st;
+    if (x_dtype == BITNET_DTYPE_BF16) {
+        st = bitnet_linear(out, static_cast<const uint16_t*>(x), w_packed, scale_wt, M, N, K, workspace,
+                           workspace_bytes, stream);
+    } else {
+        const size_t need = bitnet_linear_ex_workspace_bytes(M, K, x_dtype);
+        if (workspace == nullptr || workspace_bytes < need) return BITNET_ERR_WORKSPACE;
+        if ((st = check_device())) return st;
+        int8_t* x_int8 = static_cast<int8_t*>(workspace);
+        uint16_t* scale_act = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + round256((size_t)M * K));
+        hipStream_t s = (hipStream_t)stream;
+        if (hipError_t e = launch_quantize_f32(x_int8, scale_act, static_cast<const float*>(x), M, K, s))
+            return launched(e);
+        st = launched(launch_gemm(out, nullptr, x_int8, w_packed, scale_act, scale_wt, M, N, K, s));
+    }
+    if (st != BITNET_OK || bias == nullptr) return st;
+    return launched(launch_add_bias(out, bias, M, N, (hipStream_t)stream));
 }
 
 BITNET_API bitnet_status bitnet_scale_epilogue(uint16_t* out, const int32_t* acc, const uint16_t* scale_act,

@@ -91,8 +91,17 @@ struct QuantScale {
     float r;  // fp32(1 / s): used only for a pre-rounding estimate
 };
 
-// From the row absmax (as bf16 magnitude bits): clamp below at fp32(1e-5), then
-// the IEEE fp32 quotient by 127 (the compiler's division is correctly rounded).
+// From the row absmax (quant_scale_f32: an fp32 value; quant_scale: bf16
+// magnitude bits): clamp below at fp32(1e-5), then the IEEE fp32 quotient by
+// 127 (the compiler's division is correctly rounded).
+__device__ __forceinline__ QuantScale quant_scale_f32(float a) {
+    a = a < 1e-5f ? 1e-5f : a;
+    QuantScale q;
+    q.s = a / 127.0f;
+    q.r = 1.0f / q.s;
+    return q;
+}
+
 __device__ __forceinline__ QuantScale quant_scale(uint32_t absmax_bits) {
     float a = bf16_to_f32(absmax_bits);
     a = a < 1e-5f ? 1e-5f : a;

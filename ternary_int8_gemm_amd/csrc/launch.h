@@ -25,6 +25,12 @@ hipError_t launch_gemv_fused(uint16_t* out, int32_t* acc, uint16_t* scale_act_ou
 hipError_t launch_epilogue(uint16_t* out, const int32_t* acc, const uint16_t* scale_act, const uint16_t* scale_wt,
                            int64_t M, int64_t N, hipStream_t s);
 
+// The same quantisation of f32 activations x [M][K].
+hipError_t launch_quantize_f32(int8_t* q, uint16_t* scale, const float* x, int64_t M, int64_t K, hipStream_t s);
+
+// In place: out[m][n] = bf16(fp32(out[m][n]) + fp32(bias[n])).
+hipError_t launch_add_bias(uint16_t* out, const uint16_t* bias, int64_t M, int64_t N, hipStream_t s);
+
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace bitnet

@@ -114,6 +114,64 @@ __global__ __launch_bounds__(256) void quantize_rows_plain(int8_t* __restrict__ 
     for (int64_t k = lane; k < K; k += 64) qr[k] = (int8_t)quantize_one(bf16_to_f32(xr[k]), qs);
 }
 
+// ---------------------------------------------------------------- f32 input
+//
+// The same quantisation on f32 activations (quantize_activation accepts bf16
+// or f32): the absmax is an integer max over the f32 magnitude bits (the
+// order of non-negative finite floats), and q comes from the same exact
+// division.  Lane l holds the 4-element groups g = c * 64 + l (c < CH).
+template <int CH>
+__global__ __launch_bounds__(256) void quantize_rows_f32_reg(int8_t* __restrict__ q, uint16_t* __restrict__ scale,
+                                                             const float* __restrict__ x, int64_t M, int64_t K) {
+    const int lane = threadIdx.x & 63;
+    const int64_t m = (int64_t)blockIdx.x * QUANT_ROWS_PER_BLOCK + (threadIdx.x >> 6);
+    if (m >= M) return;  // wave-uniform
+    const int groups = (int)(K >> 2);
+    const uint4* xv = reinterpret_cast<const uint4*>(x + m * K);
+    uint4 v[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int g = c * 64 + lane;
+        v[c] = g < groups ? xv[g] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    uint32_t amax = 0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+        amax = max(amax, max(max(v[c].x & 0x7FFFFFFFu, v[c].y & 0x7FFFFFFFu),
+                             max(v[c].z & 0x7FFFFFFFu, v[c].w & 0x7FFFFFFFu)));
+    amax = wave_max_u32(amax);
+    const QuantScale qs = quant_scale_f32(__builtin_bit_cast(float, amax));
+    if (lane == 0) scale[m] = f32_to_bf16(qs.s);
+    uint32_t* qv = reinterpret_cast<uint32_t*>(q + m * K);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int g = c * 64 + lane;
+        if (g < groups) {
+            const uint32_t b0 = (uint32_t)quantize_one(__builtin_bit_cast(float, v[c].x), qs) & 0xFFu;
+            const uint32_t b1 = (uint32_t)quantize_one(__builtin_bit_cast(float, v[c].y), qs) & 0xFFu;
+            const uint32_t b2 = (uint32_t)quantize_one(__builtin_bit_cast(float, v[c].z), qs) & 0xFFu;
+            const uint32_t b3 = (uint32_t)quantize_one(__builtin_bit_cast(float, v[c].w), qs) & 0xFFu;
+            qv[g] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        }
+    }
+}
+
+// Any K and alignment: one element per lane per iteration, two passes.
+__global__ __launch_bounds__(256) void quantize_rows_f32_plain(int8_t* __restrict__ q, uint16_t* __restrict__ scale,
+                                                               const float* __restrict__ x, int64_t M, int64_t K) {
+    const int lane = threadIdx.x & 63;
+    const int64_t m = (int64_t)blockIdx.x * QUANT_ROWS_PER_BLOCK + (threadIdx.x >> 6);
+    if (m >= M) return;
+    const float* xr = x + m * K;
+    uint32_t amax = 0;
+    for (int64_t k = lane; k < K; k += 64) amax = max(amax, __builtin_bit_cast(uint32_t, xr[k]) & 0x7FFFFFFFu);
+    amax = wave_max_u32(amax);
+    const QuantScale qs = quant_scale_f32(__builtin_bit_cast(float, amax));
+    if (lane == 0) scale[m] = f32_to_bf16(qs.s);
+    int8_t* qr = q + m * K;
+    for (int64_t k = lane; k < K; k += 64) qr[k] = (int8_t)quantize_one(xr[k], qs);
+}
+
 }  // namespace
 
 hipError_t launch_quantize(int8_t* q, uint16_t* scale, const uint16_t* x, int64_t M, int64_t K, hipStream_t s) {
@@ -140,6 +198,25 @@ hipError_t launch_quantize(int8_t* q, uint16_t* scale, const uint16_t* x, int64_
         hipLaunchKernelGGL(quantize_rows_vec, grid, block, 0, s, q, scale, x, M, K);
     } else {
         hipLaunchKernelGGL(quantize_rows_plain, grid, block, 0, s, q, scale, x, M, K);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_f32(int8_t* q, uint16_t* scale, const float* x, int64_t M, int64_t K, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((M + QUANT_ROWS_PER_BLOCK - 1) / QUANT_ROWS_PER_BLOCK)), block(256);
+    if (K % 4 == 0 && aligned16(x) && reinterpret_cast<uintptr_t>(q) % 4 == 0 && K <= 256 * 32) {
+        const int64_t ch = (K / 4 + 63) / 64;  // 16-byte groups per lane
+        if (ch <= 4)
+            hipLaunchKernelGGL(quantize_rows_f32_reg<4>, grid, block, 0, s, q, scale, x, M, K);
+        else if (ch <= 8)
+            hipLaunchKernelGGL(quantize_rows_f32_reg<8>, grid, block, 0, s, q, scale, x, M, K);
+        else if (ch <= 16)
+            hipLaunchKernelGGL(quantize_rows_f32_reg<16>, grid, block, 0, s, q, scale, x, M, K);
+        else
+            hipLaunchKernelGGL(quantize_rows_f32_reg<32>, grid, block, 0, s, q, scale, x, M, K);
+    } else {
+        hipLaunchKernelGGL(quantize_rows_f32_plain, grid, block, 0, s, q, scale, x, M, K);
     }
     return hipGetLastError();
 }

@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ["bitnet_pack_weights", "bitnet_quantize_act", "bitnet_gemm", "bitnet_gemv_fused",
                      "bitnet_linear", "bitnet_gemm_i32", "bitnet_gemv_fused_i32", "bitnet_scale_epilogue",
-                     "bitnet_linear_workspace_bytes", "bitnet_status_string", "bitnet_version"]:
+                     "bitnet_linear_workspace_bytes", "bitnet_status_string", "bitnet_version",
+                     "bitnet_quantize_act_f32", "bitnet_linear_ex", "bitnet_linear_ex_workspace_bytes"]:
         assert required in names
 
 
@@ -94,6 +95,12 @@ def test_shape_errors_precede_device_use():
     assert lib.bitnet_linear(d, d, d, d, 32, 8, 64, None, 0, None) == 4       # workspace missing
     assert lib.bitnet_linear(d, d, d, d, 32, 8, 64, d, 100, None) == 4        # workspace too small
     assert lib.bitnet_scale_epilogue(None, d, d, d, 2, 2, None) == 1
+    assert lib.bitnet_quantize_act_f32(d, d, d, 4, 10, None) == 2             # K % 4
+    assert lib.bitnet_quantize_act_f32(d, None, d, 4, 64, None) == 1
+    assert lib.bitnet_linear_ex(d, d, 7, d, d, None, 4, 8, 64, d, 1 << 20, None) == 3   # unknown dtype
+    assert lib.bitnet_linear_ex(d, d, 1, d, d, None, 1, 8, 64, None, 0, None) == 4      # f32 always needs it
+    assert lib.bitnet_linear_ex(d, d, 1, d, d, None, 4, 8, 62, d, 1 << 20, None) == 2   # K % 4
+    assert lib.bitnet_linear_ex(None, d, 0, d, d, None, 4, 8, 64, d, 1 << 20, None) == 1
 
 
 def test_workspace_size():
@@ -102,6 +109,11 @@ def test_workspace_size():
     assert tg.linear_workspace_bytes(16, 4096) == 16 * 4096 + 256
     assert tg.linear_workspace_bytes(17, 100) == 1792 + 256
     assert tg.linear_workspace_bytes(17, 6) == 0   # invalid K
+    # f32 activations always go through quantise + GEMM, so they need it at every M
+    assert tg.linear_ex_workspace_bytes(1, 2560, torch.float32) == 2560 + 256
+    assert tg.linear_ex_workspace_bytes(16, 4096, torch.float32) == 16 * 4096 + 256
+    assert tg.linear_ex_workspace_bytes(3, 2560, torch.bfloat16) == 0
+    assert tg.load_library().bitnet_linear_ex_workspace_bytes(4, 64, 9) == 0
 
 
 def test_status_strings():

@@ -288,3 +288,83 @@ def test_device_errors_raise():
         tg.bitnet_gemv_fused(x, P, sw)                   # M = 16 > 15
     with pytest.raises(tg.BitnetError):
         tg.bitnet_linear(x, P, sw, workspace=torch.empty((8,), dtype=torch.uint8, device=DEV))
+
+
+# ----------------------------------------------------------------------------- f32 activations and bias
+
+def dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+F32_QUANT_SHAPES = [(4, 256), (1, 4), (3, 12), (7, 100), (16, 2560), (33, 4096), (5, 6912), (2, 131072), (130, 64),
+                    (3, 8192), (2, 8196)]
+
+
+@pytest.mark.parametrize("M,K", F32_QUANT_SHAPES)
+def test_quantize_f32_parity(M, K):
+    g = synth.rng(6000 + M + K)
+    x = (g.standard_normal((M, K)) * 3.0).astype(np.float32)
+    if M > 2:
+        x[1, :] = 0.0                          # all-zero row: eps floor
+        x[2, : K // 2] = np.float32(2.0 ** -31)
+    q_ref, s_ref = oracle.quantize_f32(x)
+    q, s = tg.quantize_activation(dev_f32(x))
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(host_bf16(s), s_ref)
+
+
+def test_quantize_f32_golden_vectors_on_gpu():
+    from conftest import read_golden
+    for r in read_golden("quantize_f32_vectors.txt"):
+        x = np.array([int(t, 16) for t in r["x"]], dtype=np.uint32).view(np.float32)
+        K = (len(x) + 3) // 4 * 4
+        xp = np.zeros((1, K), dtype=np.float32)
+        xp[0, :len(x)] = x
+        q, s = tg.quantize_activation(dev_f32(xp))
+        assert q.cpu().numpy()[0, :len(x)].tolist() == [int(t) for t in r["q"]]
+        assert int(host_bf16(s)[0]) == int(r["scale_bf16"][0], 16)
+
+
+def test_quantize_f32_misaligned_plain_path():
+    g = synth.rng(61)
+    x = g.standard_normal((5, 96)).astype(np.float32)
+    q_ref, s_ref = oracle.quantize_f32(x)
+    q = torch.zeros((5, 96), dtype=torch.int8, device=DEV)
+    s = torch.empty((5,), dtype=torch.bfloat16, device=DEV)
+    tg.quantize_activation(misaligned(dev_f32(x)), out=q, scale=s)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(host_bf16(s), s_ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 3840, 2560), (5, 300, 1024), (16, 4096, 4096), (64, 1000, 640),
+                                   (300, 257, 320), (7, 33, 100)])
+def test_linear_f32_parity(M, N, K):
+    g = synth.rng(6100 + M + N + K)
+    x = g.standard_normal((M, K)).astype(np.float32)
+    W = synth.ternary_weights(N, K, seed=6200 + M)
+    P = oracle.pack(W)
+    sw = synth.row_scales_bf16(N, seed=6300 + M)
+    ref = oracle.linear_f32(x, P, sw)
+    out = tg.bitnet_linear(dev_f32(x), dev(P), dev_bf16(sw))
+    assert_bf16_parity(host_bf16(out), ref["out"], f"linear f32 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", [(1, 3840, 2560), (3, 130, 256), (40, 1000, 1024), (17, 33, 68), (2048, 64, 512)])
+def test_linear_bias_parity(dtype, M, N, K):
+    g = synth.rng(6400 + M + N + K)
+    W = synth.ternary_weights(N, K, seed=6500 + M)
+    P = oracle.pack(W)
+    sw = synth.row_scales_bf16(N, seed=6600 + M)
+    bias = synth.row_scales_bf16(N, seed=6700 + M, lo=-4.0, hi=4.0)
+    if dtype == "bf16":
+        x = synth.activations_bf16(M, K, seed=6800 + M)
+        ref = oracle.linear(x, P, sw)["out"]
+        xd = dev_bf16(x)
+    else:
+        x = g.standard_normal((M, K)).astype(np.float32)
+        ref = oracle.linear_f32(x, P, sw)["out"]
+        xd = dev_f32(x)
+    want = oracle.add_bias(ref, bias)
+    out = tg.bitnet_linear(xd, dev(P), dev_bf16(sw), bias=dev_bf16(bias))
+    assert_bf16_parity(host_bf16(out), want, f"linear+bias {dtype} {M}x{N}x{K}")
