@@ -315,6 +315,43 @@ def run_decode_full(device, stream, log, layers=30):
     return res
 
 
+# ----------------------------------------------------------------------------- f32 input and bias
+
+def run_options(device, stream, log):
+    """bitnet_linear_ex at the decode shapes (M = 1) and at M = 2048 on the
+    LLaMA-7B qkvo shape: f32 activations (quantise + GEMM) and bf16
+    activations with a bias, beside the plain bf16 call."""
+    out = {}
+    cases = [(name, N, K, 1) for name, N, K in synth.BITNET_2B_DECODE] + [("llama_qkvo", 4096, 4096, 2048)]
+    for i, (name, N, K, M) in enumerate(cases):
+        W = synth.ternary_weights(N, K, synth.seed_for(6, 16 * i + synth.T_WEIGHT))
+        P = tg.pack_weights(torch.from_numpy(W)).to(device)
+        del W
+        copies = max(2, -(-POOL_BYTES // P.numel()))
+        Ps = [P] + [P.clone() for _ in range(copies - 1)]
+        sw = dev_bf16(synth.weight_scale_bf16(N, K, synth.seed_for(6, 16 * i + synth.T_SCALE)), device)
+        bias = dev_bf16(synth.row_scales_bf16(N, synth.seed_for(6, 16 * i + synth.T_ROWSCALE)), device)
+        xb = dev_bf16(synth.activations_bf16(M, K, synth.seed_for(6, 16 * i + synth.T_ACT)), device)
+        xf = xb.float()
+        o = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+        ws = torch.empty((tg.linear_ex_workspace_bytes(M, K, torch.float32) + 256,), dtype=torch.uint8, device=device)
+        r = {"M": M, "N": N, "K": K}
+        for tag, x, b in (("bf16", xb, None), ("bf16_bias", xb, bias), ("f32", xf, None)):
+            def run(x=x, b=b):
+                for Pd in Ps:
+                    tg.bitnet_linear(x, Pd, sw, out=o, workspace=ws, bias=b)
+            g = capture(run, stream)
+            time_graph(g, 1, stream)
+            t = time_graph(g, 3, stream) / (3 * copies)
+            r[tag + "_us"] = round(t * 1e6, 2)
+        out[f"{name}_M{M}"] = r
+        log(f"  {name:10s} M={M:5d} N={N:6d} K={K:5d}: bf16 {r['bf16_us']:8.2f} us, +bias {r['bf16_bias_us']:8.2f} us, "
+            f"f32 input {r['f32_us']:8.2f} us")
+        del Ps, xb, xf, o, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 # ----------------------------------------------------------------------------- CPU oracle
 
 def run_cpu_baseline(host, shapes, budget_s, log):
@@ -549,12 +586,14 @@ def main():
         log(f"prefill GEMM M={args.gemm_m} (LLaMA-7B shapes):")
         gemm = run_gemm(device, stream, args.gemm_m, log)
 
-    small = full = None
+    small = full = options = None
     if not args.no_extra:
         log("small-batch GEMM M=8..256 (LLaMA-7B layer shapes, pre-quantised):")
         small = run_small_batch(device, stream, log)
         log("full BitNet-2B-4T decode step (30 layers x 4 + lm_head = 121 calls):")
         full = run_decode_full(device, stream, log)
+        log("bitnet_linear options (f32 activations, bias):")
+        options = run_options(device, stream, log)
 
     lm = dec["per_shape"]["lm_head"]
     traffic = load_traffic(lm["bytes"])
@@ -605,6 +644,7 @@ def main():
     if small is not None:
         line["small_batch_gemm"] = small
         line["decode_full_step"] = full
+        line["linear_options"] = options
     print(json.dumps(line), flush=True)
 
 

@@ -18,6 +18,8 @@ Parity status of each function (what pins it is listed in the tests):
   quantize_f32 / linear_f32       pinned (hand-worked f32 vector; equal to the bf16 path on
                                   bf16-representable inputs; composition)
   add_bias                        pinned (hand-worked round-to-even ties; zero bias; zero rows)
+  w8a16                           pinned (hand-worked example; zero weights; power-of-two scaling and
+                                  sign symmetry; brute force against an exact rational sum)
 """
 import ctypes
 import os
@@ -65,6 +67,8 @@ def load(path=None):
     lib.oracle_add_bias.restype = None
     lib.oracle_linear_f32.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p]
     lib.oracle_linear_f32.restype = ctypes.c_int
+    lib.oracle_w8a16.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p]
+    lib.oracle_w8a16.restype = None
     lib.oracle_dot_i64.argtypes = [_p, _p, _i64, _i64]
     lib.oracle_dot_i64.restype = ctypes.c_int64
     lib.oracle_gemm_i32.argtypes = [_p, _p, _i64, _i64, _i64, _p]
@@ -235,3 +239,18 @@ def linear_f32(x, P, sw, lib=None):
     _check(lib.oracle_linear_f32(_ptr(x), _ptr(P), _ptr(sw), M, N, K, _ptr(out), _ptr(q), _ptr(sa), _ptr(acc)),
            "linear_f32")
     return {"out": out, "q": q, "scale_act": sa, "acc": acc}
+
+
+def w8a16(x_bits, q, scale, lib=None):
+    """INT8 weight-only matmul: bf16 bits x[M,K], int8 q[N,K], float32 scale[N] ->
+    (float64 y[M,N], float64 bound[M,N] = sum_k |x*q| * |scale|)."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    scale = np.ascontiguousarray(scale, dtype=np.float32)
+    M, K = x.shape
+    N = q.shape[0]
+    y = np.zeros((M, N), dtype=np.float64)
+    bound = np.zeros((M, N), dtype=np.float64)
+    lib.oracle_w8a16(_ptr(x), _ptr(q), _ptr(scale), M, N, K, _ptr(y), _ptr(bound))
+    return y, bound

@@ -20,6 +20,8 @@
 //         and bitnet_linear)       -> oracle_quantize_row_f32, oracle_linear_f32
 //       - class BitLinear, the bias added to the layer's output
 //                                     -> oracle_add_bias
+//   * "CoolDip00/tiny-llm src/tinyllm/kernels/int8_gemv.py", the W8A16 decode
+//       matmul                     -> oracle_w8a16
 //   * "CoolDip00/tiny-llm src/tinyllm/kernels/int8_gemv.py", docstring of
 //       int8_matmul: the integer/matmul result is scaled without an
 //       intermediate rounding to bf16.
@@ -227,6 +229,33 @@ void oracle_epilogue(const int32_t* acc, const uint16_t* sa, const uint16_t* sw,
 // R6): quantise each row, contract, scale.  Fills q/scale_act/acc when the
 // caller passes buffers for them (NULL to skip).
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// INT8 weight-only decode matmul (W8A16), as in "CoolDip00/tiny-llm,
+// src/tinyllm/kernels/int8_gemv.py" (docstring of the module and of
+// int8_matmul): y[m][n] = scale[n] * sum_k x[m][k] * q[n][k], with bf16 x,
+// int8 q, fp32 scale, fp32 y.  The kernel accumulates in fp32 in an order of
+// its own, so the oracle gives the reference value in double (every product
+// x * q is exact in double, and so is the sum while it stays within 53 bits of
+// its smallest term) together with sum_k |x * q| * |scale|, from which the
+// tests bound the fp32 rounding of any summation order.
+// ---------------------------------------------------------------------------
+void oracle_w8a16(const uint16_t* x, const int8_t* q, const float* scale, int64_t M, int64_t N, int64_t K,
+                  double* y, double* absbound) {
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            double s = 0.0, a = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double t = (double)oracle_f32_from_bf16(x[m * K + k]) * (double)q[n * K + k];
+                s += t;
+                a += std::fabs(t);
+            }
+            y[m * N + n] = s * (double)scale[n];
+            absbound[m * N + n] = a * std::fabs((double)scale[n]);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // f32 activations.  bitnet-cpu's quantize_activation, bitnet_gemv_fused and
 // bitnet_linear accept x in bf16 or f32; for f32 the same per-token absmax

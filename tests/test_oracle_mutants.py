@@ -120,8 +120,15 @@ def _pin_battery(lib):
                 return False
         return True
 
+    def w8a16_hand():
+        x = _bf16([1.0, 2.0, -0.5, 0.25])[None, :]
+        q = np.array([[3, -1, 4, 8], [-127, 0, 127, 1]], dtype=np.int8)
+        y, bound = oracle.w8a16(x, q, np.array([0.5, 2.0], dtype=np.float32), lib=lib)
+        return y.tolist() == [[0.5, -380.5]] and bound.tolist() == [[4.5, 381.5]]
+
     for name, fn in [("pack_golden", pack_golden), ("unpack_roundtrip", unpack_roundtrip),
                      ("quant_f32_golden", quant_f32_golden), ("bias_golden", bias_golden),
+                     ("w8a16_hand", w8a16_hand),
                      ("quant_golden", quant_golden), ("quant_absmax", quant_absmax),
                      ("gemm_hand", gemm_hand), ("gemm_brute", gemm_brute), ("epi_golden", epi_golden), ("epi_batch", epi_batch),
                      ("linear_k8", linear_k8), ("linear_shape", linear_shape)]:
@@ -157,6 +164,10 @@ MUTANTS = [
     ("bias_double_round", "const float y = oracle_f32_from_bf16(out[m * N + n]) + oracle_f32_from_bf16(bias[n]);",
      "const float y = oracle_f32_from_bf16(oracle_bf16_from_f32(oracle_f32_from_bf16(out[m * N + n]) + oracle_f32_from_bf16(bias[n]) * 0.5f)) + oracle_f32_from_bf16(bias[n]) * 0.5f;"),
     ("bias_row_index", "oracle_f32_from_bf16(bias[n])", "oracle_f32_from_bf16(bias[m])"),
+    ("w8a16_scale_index", "y[m * N + n] = s * (double)scale[n];", "y[m * N + n] = s * (double)scale[0];"),
+    ("w8a16_dropped_term", "for (int64_t k = 0; k < K; ++k) {\n                const double t",
+     "for (int64_t k = 1; k < K; ++k) {\n                const double t"),
+    ("w8a16_abs_bound", "a += std::fabs(t);", "a += t;"),
 ]
 
 

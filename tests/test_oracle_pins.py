@@ -320,3 +320,42 @@ def test_linear_f32_is_composition(orc):
     assert np.array_equal(r["q"], q) and np.array_equal(r["scale_act"], sa)
     assert np.array_equal(r["acc"], q.astype(np.int64) @ W.astype(np.int64).T)
     assert np.array_equal(r["out"], orc.epilogue(r["acc"], sa, sw))
+
+
+# ----------------------------------------------------------------------------- W8A16 decode matmul
+
+def test_w8a16_hand_example(orc):
+    # x = [1, 2, -0.5, 0.25] (bf16-exact), q rows [3, -1, 4, 8] and [-127, 0, 127, 1]:
+    #   row 0: 3 - 2 - 2 + 2 = 1, times scale 0.5 -> 0.5
+    #   row 1: -127 + 0 - 63.5 + 0.25 = -190.25, times scale 2 -> -380.5
+    x = bf16_bits([1.0, 2.0, -0.5, 0.25])[None, :]
+    q = np.array([[3, -1, 4, 8], [-127, 0, 127, 1]], dtype=np.int8)
+    y, bound = orc.w8a16(x, q, np.array([0.5, 2.0], dtype=np.float32))
+    assert y.tolist() == [[0.5, -380.5]]
+    assert bound.tolist() == [[0.5 * (3 + 2 + 2 + 2), 2.0 * (127 + 0 + 63.5 + 0.25)]]
+
+
+def test_w8a16_zero_weights_and_symmetries(orc):
+    x = synth.activations_bf16(3, 256, seed=41)
+    g = synth.rng(42)
+    q = g.integers(-127, 128, size=(5, 256)).astype(np.int8)
+    sc = g.uniform(0.001, 0.1, size=5).astype(np.float32)
+    y, _ = orc.w8a16(x, q, sc)
+    assert np.all(orc.w8a16(x, np.zeros_like(q), sc)[0] == 0.0)
+    assert np.array_equal(orc.w8a16(x, -q, sc)[0], -y)
+    x2 = bf16_bits(synth.bf16_bits_to_f32(x) * 2.0)          # exact doubling in bf16
+    assert np.array_equal(orc.w8a16(x2, q, sc)[0], 2.0 * y)
+
+
+def test_w8a16_brute_force_exact(orc):
+    from fractions import Fraction
+    x = synth.activations_bf16(2, 40, seed=43)
+    g = synth.rng(44)
+    q = g.integers(-127, 128, size=(3, 40)).astype(np.int8)
+    sc = g.uniform(0.01, 1.0, size=3).astype(np.float32)
+    y, _ = orc.w8a16(x, q, sc)
+    xf = synth.bf16_bits_to_f32(x)
+    for m in range(2):
+        for n in range(3):
+            exact = sum(Fraction(float(xf[m, k])) * int(q[n, k]) for k in range(40)) * Fraction(float(sc[n]))
+            assert y[m, n] == float(exact)
