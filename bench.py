@@ -352,6 +352,43 @@ def run_options(device, stream, log):
     return out
 
 
+def w8a16_bytes(M, N, K):
+    """Algorithmic bytes of the INT8 weight-only matmul: int8 W + fp32 scale + bf16 x + fp32 y."""
+    return N * K + 4 * N + 2 * M * K + 4 * M * N
+
+
+def run_w8a16(device, stream, log):
+    """bitnet_w8a16_gemv (int8 weights, bf16 activations) at the BitNet-2B-4T and
+    LLaMA-7B decode shapes, M = 1 and 16, weights rotated through a 1 GiB pool."""
+    out = {}
+    cases = [("bitnet_" + n, N, K) for n, N, K in synth.BITNET_2B_DECODE] + \
+            [("llama_" + n, N, K) for n, N, K in synth.LLAMA7B_SHAPES]
+    for i, (name, N, K) in enumerate(cases):
+        q = torch.from_numpy(synth.random_int8((N, K), synth.seed_for(7, 16 * i + synth.T_WEIGHT))).to(device)
+        copies = max(2, -(-POOL_BYTES // q.numel()))
+        qs = [q] + [q.clone() for _ in range(copies - 1)]
+        sc = torch.full((N,), 1.0 / 127.0, dtype=torch.float32, device=device)
+        r = {"N": N, "K": K}
+        for M in (1, 16):
+            x = dev_bf16(synth.activations_bf16(M, K, synth.seed_for(7, 16 * i + synth.T_ACT) + M), device)
+            y = torch.empty((M, N), dtype=torch.float32, device=device)
+
+            def run(x=x, y=y):
+                for qd in qs:
+                    tg.w8a16_gemv(x, qd, sc, out=y)
+            g = capture(run, stream)
+            time_graph(g, 1, stream)
+            t = time_graph(g, 3, stream) / (3 * copies)
+            r[f"M{M}_us"] = round(t * 1e6, 2)
+            r[f"M{M}_gbs"] = round(w8a16_bytes(M, N, K) / t / 1e9, 1)
+        out[name] = r
+        log(f"  {name:16s} N={N:6d} K={K:5d}: M=1 {r['M1_us']:8.2f} us {r['M1_gbs']:7.1f} GB/s, "
+            f"M=16 {r['M16_us']:8.2f} us {r['M16_gbs']:7.1f} GB/s")
+        del qs, q
+        torch.cuda.empty_cache()
+    return out
+
+
 # ----------------------------------------------------------------------------- CPU oracle
 
 def run_cpu_baseline(host, shapes, budget_s, log):
@@ -586,7 +623,7 @@ def main():
         log(f"prefill GEMM M={args.gemm_m} (LLaMA-7B shapes):")
         gemm = run_gemm(device, stream, args.gemm_m, log)
 
-    small = full = options = None
+    small = full = options = w8 = None
     if not args.no_extra:
         log("small-batch GEMM M=8..256 (LLaMA-7B layer shapes, pre-quantised):")
         small = run_small_batch(device, stream, log)
@@ -594,6 +631,8 @@ def main():
         full = run_decode_full(device, stream, log)
         log("bitnet_linear options (f32 activations, bias):")
         options = run_options(device, stream, log)
+        log("INT8 weight-only matmul (W8A16), decode shapes:")
+        w8 = run_w8a16(device, stream, log)
 
     lm = dec["per_shape"]["lm_head"]
     traffic = load_traffic(lm["bytes"])
@@ -645,6 +684,7 @@ def main():
         line["small_batch_gemm"] = small
         line["decode_full_step"] = full
         line["linear_options"] = options
+        line["w8a16_gemv"] = w8
     print(json.dumps(line), flush=True)
 
 

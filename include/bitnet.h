@@ -169,6 +169,26 @@ bitnet_status bitnet_linear_ex(uint16_t* out, const void* x, int x_dtype, const 
                                const uint16_t* scale_wt, const uint16_t* bias, int64_t M, int64_t N, int64_t K,
                                void* workspace, size_t workspace_bytes, bitnet_stream_t stream);
 
+/* Largest activation row count bitnet_w8a16_gemv takes (decode batches). */
+#define BITNET_W8A16_MAX_M 64
+
+/*
+ * INT8 weight-only decode matmul (int8_matmul of "CoolDip00/tiny-llm,
+ * src/tinyllm/kernels/int8_gemv.py"): each int8 weight is read once, converted
+ * exactly to bf16 in registers, multiplied with bf16 activations and summed in
+ * fp32; the per-row scale is applied to the fp32 sum:
+ *   y[m][n] = scale[n] * sum_k x[m][k] * q[n][k].
+ * y: fp32 [M][N] (written); x: bf16 [M][K]; q: int8 [N][K]; scale: fp32 [N].
+ * 0 <= M <= BITNET_W8A16_MAX_M, 0 < K <= BITNET_MAX_K (any K; K % 64 == 0 and
+ * 16-byte aligned x and q take the fast kernel).  The fp32 summation order is
+ * the library's own (fixed for a given shape, so results are deterministic);
+ * it differs from an exact sum by at most K * 2^-24 * sum_k |x * q| * |scale|
+ * plus the final rounding.  Device pointers, enqueued on stream.
+ * Errors: M > BITNET_W8A16_MAX_M, K <= 0 or K > BITNET_MAX_K -> SHAPE.
+ */
+bitnet_status bitnet_w8a16_gemv(float* y, const uint16_t* x, const int8_t* q, const float* scale, int64_t M,
+                                int64_t N, int64_t K, bitnet_stream_t stream);
+
 /*
  * Debug: the raw int32 accumulators of the batched path,
  *   acc[m][n] = sum_k w[n][k] * x_int8[m][k],

@@ -72,6 +72,7 @@ def load_library():
         "bitnet_scale_epilogue": [_p, _p, _p, _p, _i64, _i64, _p],
         "bitnet_quantize_act_f32": [_p, _p, _p, _i64, _i64, _p],
         "bitnet_linear_ex": [_p, _p, _st, _p, _p, _p, _i64, _i64, _i64, _p, _sz, _p],
+        "bitnet_w8a16_gemv": [_p, _p, _p, _p, _i64, _i64, _i64, _p],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -268,4 +269,22 @@ def bitnet_scale_epilogue(acc, scale_act, scale_wt, out=None):
     o = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=acc.device)
     _check(load_library().bitnet_scale_epilogue(_ptr(o), _ptr(acc), _ptr(scale_act), _ptr(scale_wt), M, N,
                                                 _stream(acc)), "bitnet_scale_epilogue")
+    return o
+
+
+W8A16_MAX_M = 64
+
+
+def w8a16_gemv(x, q, scale, out=None):
+    """INT8 weight-only matmul: bf16 x[M, K] (M <= 64), int8 q[N, K], fp32 scale[N] -> fp32 [M, N]."""
+    _need(x, torch.bfloat16, "x")
+    _need(q, torch.int8, "q")
+    _need(scale, torch.float32, "scale")
+    M, K = x.shape
+    N = q.shape[0]
+    if q.shape[1] != K or scale.numel() != N:
+        raise ValueError("w8a16_gemv: inconsistent shapes")
+    o = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check(load_library().bitnet_w8a16_gemv(_ptr(o), _ptr(x), _ptr(q), _ptr(scale), M, N, K, _stream(x)),
+           "bitnet_w8a16_gemv")
     return o

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbitnet_hip.so")
-SOURCES = ["api.hip", "quant.hip", "gemv.hip", "gemm.hip", "epilogue.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemv.hip", "gemm.hip", "epilogue.hip", "w8a16.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -18,6 +18,7 @@ using bitnet::launch_gemv_fused;
 using bitnet::launch_quantize;
 using bitnet::launch_quantize_f32;
 using bitnet::launch_add_bias;
+using bitnet::launch_w8a16;
 
 constexpr int kMaxDevices = 64;
 // 0 = unknown, 1 = gfx950, 2 = other
@@ -207,6 +208,15 @@ BITNET_API bitnet_status bitnet_linear_ex(uint16_t* out, const void* x, int x_dt
     }
     if (st != BITNET_OK || bias == nullptr) return st;
     return launched(launch_add_bias(out, bias, M, N, (hipStream_t)stream));
+}
+
+BITNET_API bitnet_status bitnet_w8a16_gemv(float* y, const uint16_t* x, const int8_t* q, const float* scale,
+                                           int64_t M, int64_t N, int64_t K, bitnet_stream_t stream) {
+    if (!sizes_ok(M, N) || M > BITNET_W8A16_MAX_M || K <= 0 || K > BITNET_MAX_K) return BITNET_ERR_SHAPE;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!y || !x || !q || !scale) return BITNET_ERR_NULL;
+    if (bitnet_status st = check_device()) return st;
+    return launched(launch_w8a16(y, x, q, scale, M, N, K, (hipStream_t)stream));
 }
 
 BITNET_API bitnet_status bitnet_scale_epilogue(uint16_t* out, const int32_t* acc, const uint16_t* scale_act,

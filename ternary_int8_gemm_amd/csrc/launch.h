@@ -31,6 +31,11 @@ hipError_t launch_quantize_f32(int8_t* q, uint16_t* scale, const float* x, int64
 // In place: out[m][n] = bf16(fp32(out[m][n]) + fp32(bias[n])).
 hipError_t launch_add_bias(uint16_t* out, const uint16_t* bias, int64_t M, int64_t N, hipStream_t s);
 
+// INT8 weight-only matmul: y [M][N] (fp32) = scale[n] * sum_k x[m][k] * q[n][k],
+// x bf16 [M][K] (M <= 64), q int8 [N][K], scale fp32 [N].
+hipError_t launch_w8a16(float* y, const uint16_t* x, const int8_t* q, const float* scale, int64_t M, int64_t N,
+                        int64_t K, hipStream_t s);
+
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace bitnet

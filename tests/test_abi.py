@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
     for required in ["bitnet_pack_weights", "bitnet_quantize_act", "bitnet_gemm", "bitnet_gemv_fused",
                      "bitnet_linear", "bitnet_gemm_i32", "bitnet_gemv_fused_i32", "bitnet_scale_epilogue",
                      "bitnet_linear_workspace_bytes", "bitnet_status_string", "bitnet_version",
-                     "bitnet_quantize_act_f32", "bitnet_linear_ex", "bitnet_linear_ex_workspace_bytes"]:
+                     "bitnet_quantize_act_f32", "bitnet_linear_ex", "bitnet_linear_ex_workspace_bytes",
+                     "bitnet_w8a16_gemv"]:
         assert required in names
 
 
@@ -101,6 +102,11 @@ def test_shape_errors_precede_device_use():
     assert lib.bitnet_linear_ex(d, d, 1, d, d, None, 1, 8, 64, None, 0, None) == 4      # f32 always needs it
     assert lib.bitnet_linear_ex(d, d, 1, d, d, None, 4, 8, 62, d, 1 << 20, None) == 2   # K % 4
     assert lib.bitnet_linear_ex(None, d, 0, d, d, None, 4, 8, 64, d, 1 << 20, None) == 1
+    assert lib.bitnet_w8a16_gemv(d, d, d, d, 65, 8, 64, None) == 2           # M > 64
+    assert lib.bitnet_w8a16_gemv(d, d, d, d, 4, 8, 0, None) == 2             # K == 0
+    assert lib.bitnet_w8a16_gemv(d, d, d, d, 4, 8, 131072 + 1, None) == 2   # K > MAX_K
+    assert lib.bitnet_w8a16_gemv(d, d, d, d, 0, 8, 64, None) == 0            # M == 0: no-op
+    assert lib.bitnet_w8a16_gemv(d, None, d, d, 4, 8, 64, None) == 1
 
 
 def test_workspace_size():

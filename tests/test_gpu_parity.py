@@ -368,3 +368,76 @@ def test_linear_bias_parity(dtype, M, N, K):
     want = oracle.add_bias(ref, bias)
     out = tg.bitnet_linear(xd, dev(P), dev_bf16(sw), bias=dev_bf16(bias))
     assert_bf16_parity(host_bf16(out), want, f"linear+bias {dtype} {M}x{N}x{K}")
+
+
+# ----------------------------------------------------------------------------- INT8 weight-only (W8A16)
+
+def w8a16_problem(M, N, K, seed, int_x=False):
+    g = synth.rng(seed)
+    if int_x:
+        # integer activations in [-8, 8]: every product and partial sum is an
+        # integer below 2^24, so any fp32 summation order gives the exact sum
+        x = synth._to_bf16_bits(g.integers(-8, 9, size=(M, K)).astype(np.float32))
+    else:
+        x = synth.activations_bf16(M, K, seed=seed + 1)
+    q = synth.random_int8((N, K), seed=seed + 2)
+    scale = (g.uniform(0.5, 2.0, size=N) * np.where(g.random(N) < 0.5, -1.0, 1.0) / 127.0).astype(np.float32)
+    return x, q, scale
+
+
+def assert_w8a16_close(got, y, bound, K, what):
+    # fp32 summation of K exact products (bf16 x int8 fits 24 bits): each partial
+    # sum rounds once, so |error| <= (K - 1) * 2^-24 * sum|x*q| * |scale| (to first
+    # order; 1% slack covers the higher-order terms), plus one rounding of the
+    # final product with the scale, 2^-24 * |y| (doubled for the fp32 input to it)
+    tol = bound * (K * 2.0 ** -24) * 1.01 + np.abs(y) * 2.0 ** -23 + 1e-30
+    err = np.abs(got.astype(np.float64) - y)
+    worst = np.unravel_index(np.argmax(err / tol), err.shape)
+    assert np.all(err <= tol), f"{what}: |err| {err[worst]:.3e} > tol {tol[worst]:.3e} at {worst}"
+
+
+W8A16_EXACT_SHAPES = [(1, 64, 256), (5, 100, 4096), (32, 33, 1024), (33, 4096, 4096), (64, 96, 2560),
+                      (3, 7, 200), (2, 4, 64)]
+
+
+@pytest.mark.parametrize("M,N,K", W8A16_EXACT_SHAPES)
+def test_w8a16_exact_integer_activations(M, N, K):
+    """Exact sums make the output bit-checkable: this pins the MFMA operand and
+    result layouts (a swapped row, column or k index changes some output)."""
+    x, q, scale = w8a16_problem(M, N, K, seed=7000 + M + N + K, int_x=True)
+    y, _ = oracle.w8a16(x, q, scale)
+    got = tg.w8a16_gemv(dev_bf16(x), dev(q), dev(scale)).cpu().numpy()
+    assert np.array_equal(got, y.astype(np.float32)), f"w8a16 exact {M}x{N}x{K}"
+
+
+W8A16_SHAPES = [(1, 4096, 4096), (1, 1, 256), (1, 32000, 4096), (3, 100, 256), (16, 4096, 4096), (16, 31, 11008),
+                (33, 1000, 1024), (64, 257, 11008), (7, 300, 11072), (2, 64, 131072), (5, 300, 200), (4, 3, 68)]
+
+
+@pytest.mark.parametrize("M,N,K", W8A16_SHAPES)
+def test_w8a16_parity(M, N, K):
+    x, q, scale = w8a16_problem(M, N, K, seed=7100 + M + N + K)
+    y, bound = oracle.w8a16(x, q, scale)
+    got = tg.w8a16_gemv(dev_bf16(x), dev(q), dev(scale)).cpu().numpy()
+    assert_w8a16_close(got, y, bound, K, f"w8a16 {M}x{N}x{K}")
+
+
+def test_w8a16_misaligned_plain_path_and_determinism():
+    M, N, K = 6, 130, 1024
+    x, q, scale = w8a16_problem(M, N, K, seed=7200)
+    y, bound = oracle.w8a16(x, q, scale)
+    xd, qd, sd = dev_bf16(x), dev(q), dev(scale)
+    fast = tg.w8a16_gemv(xd, qd, sd)
+    assert torch.equal(fast, tg.w8a16_gemv(xd, qd, sd)), "fast path: repeated calls differ"
+    plain = tg.w8a16_gemv(misaligned(xd), qd, sd)
+    assert_w8a16_close(plain.cpu().numpy(), y, bound, K, "w8a16 misaligned x")
+    assert_w8a16_close(fast.cpu().numpy(), y, bound, K, "w8a16 fast")
+
+
+def test_w8a16_shape_errors():
+    x = torch.zeros((65, 64), dtype=torch.bfloat16, device=DEV)
+    q = torch.zeros((8, 64), dtype=torch.int8, device=DEV)
+    s = torch.ones((8,), dtype=torch.float32, device=DEV)
+    with pytest.raises(RuntimeError):
+        tg.w8a16_gemv(x, q, s)                      # M > 64
+    assert tg.w8a16_gemv(x[:0], q, s).shape == (0, 8)
