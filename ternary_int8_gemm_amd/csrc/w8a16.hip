@@ -18,8 +18,20 @@
 // chunks keeps loads in flight.  The waves' partial fp32 tiles are summed in
 // LDS in a fixed order (deterministic results), scaled and stored.
 //
-// Fast path: K % 64 == 0 and 16-byte aligned x and q; otherwise w8a16_plain,
-// one wave per output column.
+// w8a16_stream_kernel (M <= 4, the decode case).  Padding M to an MFMA tile
+// forces the lanes of one load onto 32 different weight rows; for a handful of
+// activation rows the multiply-adds are cheap on the vector ALUs instead, so
+// the weights are streamed the way the ternary decode GEMV streams them: units
+// of 8 rows, 8 lanes per row, each lane 16 contiguous int8 weights per step, so
+// one wave instruction reads 8 whole 128-byte lines, with a ring of D loads in
+// flight per wave.  The activations are widened to fp32 once per workgroup into
+// LDS; each weight is converted exactly to fp32 and fed to one fp32 FMA per
+// activation row (every product exact, one rounding per add).  A row's eight
+// lane sums are combined by a fixed DPP tree.
+//
+// Fast paths need 16-byte aligned x and q; the stream kernel K % 16 == 0 and
+// M * K small enough for LDS, the MFMA kernel K % 64 == 0.  Anything else goes
+// to w8a16_plain, one wave per output column.
 #include "bitnet_device.h"
 #include "launch.h"
 
@@ -142,6 +154,194 @@ __global__ __launch_bounds__(64 * KW) void w8a16_kernel(float* __restrict__ y, c
     }
 }
 
+// ---------------------------------------------------------------- stream kernel (M <= 4)
+
+constexpr int W8_STEP = 128;                // weights of a row per wave step (8 lanes x 16)
+constexpr int W8_LDS_BYTES = 65536;         // fp32 activations held per workgroup
+constexpr int W8_MAX_STEPS = W8_LDS_BYTES / (W8_STEP * 4);
+constexpr int W8_STREAM_MAX_BLOCKS = 1024;
+
+// Loads past a wave's work read this small, always-cached pad instead of
+// weight lines (every ring slot is issued unconditionally).
+__device__ __align__(256) uint8_t w8_pad[W8_MAX_STEPS * W8_STEP + 64 * 16];
+
+// LDS float index of activation (m, k): 16-element pieces of 64 bytes, whose
+// four 16-byte quarters are swapped pairwise in every other group of four
+// pieces, so that the eight lanes of a row read eight distinct bank groups.
+__device__ __forceinline__ int w8_lds_index(int m, int k, int row_floats) {
+    const int p = k >> 4;
+    const int i = (k >> 2) & 3;
+    return m * row_floats + p * 16 + 4 * (i ^ ((p >> 2) & 1)) + (k & 3);
+}
+
+__device__ __forceinline__ float group8_sum_f32(float v) {
+    v += __builtin_bit_cast(float, dpp_mov<DPP_QUAD_XOR1>(__builtin_bit_cast(int, v)));
+    v += __builtin_bit_cast(float, dpp_mov<DPP_QUAD_XOR2>(__builtin_bit_cast(int, v)));
+    v += __builtin_bit_cast(float, dpp_mov<DPP_ROW_HALF_MIRROR>(__builtin_bit_cast(int, v)));
+    return v;
+}
+
+template <int MT, int D>
+__global__ __launch_bounds__(256) void w8a16_stream_kernel(float* __restrict__ y, const uint16_t* __restrict__ x,
+                                                           const int8_t* __restrict__ q,
+                                                           const float* __restrict__ scale, int M, int N, int K,
+                                                           int steps, int units, int upb) {
+    constexpr int WAVES = 4;
+    constexpr int NT = WAVES * 64;
+    extern __shared__ __align__(16) float lds_xf[];  // [MT][steps * W8_STEP], zero past K
+    __shared__ float sc_lds[NT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 3;   // row of the unit
+    const int sl = lane & 7;   // 16-weight piece of the step
+    const int row_floats = steps * W8_STEP;
+
+    const int ub0 = blockIdx.x * upb;
+    const int ub1 = min(ub0 + upb, units);
+    const int my_units = (ub0 + wave < ub1) ? (ub1 - 1 - ub0 - wave) / WAVES + 1 : 0;
+    const int items = my_units * steps;
+
+    // ---- the weight ring (first loads go out before the activation prologue)
+    const int last_step = steps - 1;
+    const bool ktail = (K % W8_STEP) != 0;
+    const uint32_t piece = (uint32_t)(sl * 16);
+    // in a partial last step, lanes past the row's end re-read its last 16
+    // bytes; their activations in LDS are zero
+    const uint32_t piece_last = (uint32_t)min(sl * 16, K - last_step * W8_STEP - 16);
+    int lj = 0, lt = 0;
+    const int8_t* unit_ptr;
+    uint32_t voff, voff_last;
+    auto set_unit = [&]() {
+        const bool live = lj < my_units;  // wave-uniform
+        const int u = min(ub0 + wave + WAVES * min(lj, max(my_units - 1, 0)), units - 1);
+        const uint32_t lane_row = (uint32_t)((min(u * 8 + g, N - 1) - u * 8) * K);
+        unit_ptr = live ? q + (int64_t)u * 8 * K : reinterpret_cast<const int8_t*>(w8_pad);
+        voff = live ? lane_row + piece : (uint32_t)(lane * 16);
+        voff_last = live ? lane_row + piece_last : (uint32_t)(lane * 16);
+    };
+    set_unit();
+    auto issue = [&](uint4& dst) {
+        const int8_t* b = unit_ptr + lt * W8_STEP;
+        dst = load_stream16(b + ((ktail && lt == last_step) ? voff_last : voff));
+        if (++lt == steps) {
+            lt = 0;
+            ++lj;
+            set_unit();
+        }
+    };
+    uint4 buf[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) issue(buf[i]);
+
+    // ---- activations to LDS as fp32 (8 per thread and pass), weight scales
+    const int per_row8 = steps * (W8_STEP / 8);
+    for (int idx = tid; idx < MT * per_row8; idx += NT) {
+        const int m = idx / per_row8;
+        const int k = (idx - m * per_row8) * 8;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (m < M && k < K) v = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + k);
+        const float4 lo = make_float4(bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xFFFFu),
+                                      bf16_to_f32(v.y >> 16));
+        const float4 hi = make_float4(bf16_to_f32(v.z & 0xFFFFu), bf16_to_f32(v.z >> 16), bf16_to_f32(v.w & 0xFFFFu),
+                                      bf16_to_f32(v.w >> 16));
+        *reinterpret_cast<float4*>(lds_xf + w8_lds_index(m, k, row_floats)) = lo;
+        *reinterpret_cast<float4*>(lds_xf + w8_lds_index(m, k + 4, row_floats)) = hi;
+    }
+    const int row0 = ub0 * 8;
+    const int nrows = min(ub1 * 8, N) - row0;
+    sc_lds[tid] = tid < nrows ? scale[row0 + tid] : 0.0f;
+    __syncthreads();
+
+    // ---- stream
+    float acc0[MT], acc1[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc0[m] = acc1[m] = 0.0f;
+    const int swz = 4 * ((sl >> 2) & 1);
+    const float* lds_a = lds_xf + sl * 16 + swz;       // quarters 0 and 2 of this lane's piece
+    const float* lds_b = lds_xf + sl * 16 + 4 - swz;   // quarters 1 and 3
+    int cj = 0, ct = 0;
+    auto consume = [&](const uint4& v) {
+        float wf[16];
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) wf[j] = (float)(int8_t)(wd[j >> 2] >> (8 * (j & 3)));
+        const int off = ct * (8 * 16);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const float4 x0 = *reinterpret_cast<const float4*>(lds_a + m * row_floats + off);
+            const float4 x1 = *reinterpret_cast<const float4*>(lds_b + m * row_floats + off);
+            const float4 x2 = *reinterpret_cast<const float4*>(lds_a + m * row_floats + off + 8);
+            const float4 x3 = *reinterpret_cast<const float4*>(lds_b + m * row_floats + off + 8);
+            acc0[m] = __builtin_fmaf(x0.x, wf[0], acc0[m]);
+            acc1[m] = __builtin_fmaf(x0.y, wf[1], acc1[m]);
+            acc0[m] = __builtin_fmaf(x0.z, wf[2], acc0[m]);
+            acc1[m] = __builtin_fmaf(x0.w, wf[3], acc1[m]);
+            acc0[m] = __builtin_fmaf(x1.x, wf[4], acc0[m]);
+            acc1[m] = __builtin_fmaf(x1.y, wf[5], acc1[m]);
+            acc0[m] = __builtin_fmaf(x1.z, wf[6], acc0[m]);
+            acc1[m] = __builtin_fmaf(x1.w, wf[7], acc1[m]);
+            acc0[m] = __builtin_fmaf(x2.x, wf[8], acc0[m]);
+            acc1[m] = __builtin_fmaf(x2.y, wf[9], acc1[m]);
+            acc0[m] = __builtin_fmaf(x2.z, wf[10], acc0[m]);
+            acc1[m] = __builtin_fmaf(x2.w, wf[11], acc1[m]);
+            acc0[m] = __builtin_fmaf(x3.x, wf[12], acc0[m]);
+            acc1[m] = __builtin_fmaf(x3.y, wf[13], acc1[m]);
+            acc0[m] = __builtin_fmaf(x3.z, wf[14], acc0[m]);
+            acc1[m] = __builtin_fmaf(x3.w, wf[15], acc1[m]);
+        }
+        if (++ct == steps) {  // unit complete: combine the row's 8 lanes, scale, write
+            const int ul = wave + WAVES * cj;
+            const int n = (ub0 + ul) * 8 + g;
+            const float sc = sc_lds[ul * 8 + g];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const float tot = group8_sum_f32(acc0[m] + acc1[m]);
+                acc0[m] = acc1[m] = 0.0f;
+                if (m == sl && n < N && m < M) y[(int64_t)m * N + n] = tot * sc;
+            }
+            ct = 0;
+            ++cj;
+        }
+    };
+
+    int base = 0;
+    for (; base + D <= items; base += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            consume(buf[i]);
+            issue(buf[i]);
+        }
+    }
+    const int rem = items - base;
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        if (i < rem) consume(buf[i]);
+}
+
+template <int MT>
+hipError_t launch_w8a16_stream(float* y, const uint16_t* x, const int8_t* q, const float* scale, int M, int N, int K,
+                               hipStream_t s) {
+    const int steps = (K + W8_STEP - 1) / W8_STEP;
+    const int units = (N + 7) / 8;
+    // at most 32 units (256 rows, one scale per thread) per workgroup;
+    // otherwise as few workgroups as keep the GPU full
+    int blocks = (units + 3) / 4;
+    if (blocks > W8_STREAM_MAX_BLOCKS) blocks = W8_STREAM_MAX_BLOCKS;
+    if (blocks < (units + 31) / 32) blocks = (units + 31) / 32;
+    const int upb = (units + blocks - 1) / blocks;
+    blocks = (units + upb - 1) / upb;
+    const size_t lds = (size_t)MT * steps * W8_STEP * 4;
+    if (steps >= 12)
+        hipLaunchKernelGGL((w8a16_stream_kernel<MT, MT == 1 ? 16 : 8>), dim3(blocks), dim3(256), lds, s, y, x, q,
+                           scale, M, N, K, steps, units, upb);
+    else
+        hipLaunchKernelGGL((w8a16_stream_kernel<MT, 8>), dim3(blocks), dim3(256), lds, s, y, x, q, scale, M, N, K,
+                           steps, units, upb);
+    return hipGetLastError();
+}
+
 // Any shape: one wave per output column, fp32 partial sums per lane, a fixed
 // DPP/readlane tree across the wave.
 __global__ __launch_bounds__(64) void w8a16_plain(float* __restrict__ y, const uint16_t* __restrict__ x,
@@ -170,6 +370,13 @@ __global__ __launch_bounds__(64) void w8a16_plain(float* __restrict__ y, const u
 hipError_t launch_w8a16(float* y, const uint16_t* x, const int8_t* q, const float* scale, int64_t M, int64_t N,
                         int64_t K, hipStream_t s) {
     if (M <= 0 || N <= 0) return hipSuccess;
+    const int64_t steps = (K + W8_STEP - 1) / W8_STEP;
+    const int mt = M == 1 ? 1 : (M == 2 ? 2 : 4);
+    if (M <= 4 && K % 16 == 0 && mt * steps <= W8_MAX_STEPS && aligned16(x) && aligned16(q)) {
+        if (mt == 1) return launch_w8a16_stream<1>(y, x, q, scale, (int)M, (int)N, (int)K, s);
+        if (mt == 2) return launch_w8a16_stream<2>(y, x, q, scale, (int)M, (int)N, (int)K, s);
+        return launch_w8a16_stream<4>(y, x, q, scale, (int)M, (int)N, (int)K, s);
+    }
     constexpr int KW = 4;
     const int64_t nc = K / WQ_CHUNK;
     // 32-bit buffer offsets: weights and activations below 2 GiB
