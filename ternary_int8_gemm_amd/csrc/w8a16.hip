@@ -18,7 +18,7 @@
 // chunks keeps loads in flight.  The waves' partial fp32 tiles are summed in
 // LDS in a fixed order (deterministic results), scaled and stored.
 //
-// w8a16_stream_kernel (M <= 4, the decode case).  Padding M to an MFMA tile
+// w8a16_stream_kernel (M <= 2, the decode case).  Padding M to an MFMA tile
 // forces the lanes of one load onto 32 different weight rows; for a handful of
 // activation rows the multiply-adds are cheap on the vector ALUs instead, so
 // the weights are streamed the way the ternary decode GEMV streams them: units
@@ -27,7 +27,10 @@
 // flight per wave.  The activations are widened to fp32 once per workgroup into
 // LDS; each weight is converted exactly to fp32 and fed to one fp32 FMA per
 // activation row (every product exact, one rounding per add).  A row's eight
-// lane sums are combined by a fixed DPP tree.
+// lane sums are combined by a fixed DPP tree.  When there are too few units of
+// rows to fill the GPU (the smaller projections), groups of 2 or 4 waves share
+// each unit, every wave taking a contiguous range of its steps, and the groups'
+// row sums are added in LDS in a fixed order before the scale.
 //
 // Fast paths need 16-byte aligned x and q; the stream kernel K % 16 == 0 and
 // M * K small enough for LDS, the MFMA kernel K % 64 == 0.  Anything else goes
@@ -154,12 +157,22 @@ __global__ __launch_bounds__(64 * KW) void w8a16_kernel(float* __restrict__ y, c
     }
 }
 
-// ---------------------------------------------------------------- stream kernel (M <= 4)
+// ---------------------------------------------------------------- stream kernel (M <= 2)
 
 constexpr int W8_STEP = 128;                // weights of a row per wave step (8 lanes x 16)
 constexpr int W8_LDS_BYTES = 65536;         // fp32 activations held per workgroup
 constexpr int W8_MAX_STEPS = W8_LDS_BYTES / (W8_STEP * 4);
+// Workgroup cap: every workgroup stages all activations, so mid-sized split
+// problems run best with fewer, longer workgroups (measured on the BitNet and
+// LLaMA decode shapes).
 constexpr int W8_STREAM_MAX_BLOCKS = 1024;
+constexpr int W8_STREAM_MAX_BLOCKS_SPLIT = 512;  // when units x K parts <= W8_SPLIT_WORK
+constexpr int W8_SPLIT_WORK = 8192;
+constexpr int W8_STREAM_MAX_M = 2;          // from 3 rows on the MFMA kernel is as fast or faster
+// Split K further while (units x K parts) stays below this (fewer for two
+// activation rows, whose LDS staging costs twice as much per workgroup).
+constexpr int W8_SPLIT_UNITS_M1 = 16384;
+constexpr int W8_SPLIT_UNITS_M2 = 4096;
 
 // Loads past a wave's work read this small, always-cached pad instead of
 // weight lines (every ring slot is issued unconditionally).
@@ -181,27 +194,33 @@ __device__ __forceinline__ float group8_sum_f32(float v) {
     return v;
 }
 
-template <int MT, int D>
+template <int MT, int D, int KS>
 __global__ __launch_bounds__(256) void w8a16_stream_kernel(float* __restrict__ y, const uint16_t* __restrict__ x,
                                                            const int8_t* __restrict__ q,
                                                            const float* __restrict__ scale, int M, int N, int K,
                                                            int steps, int units, int upb) {
     constexpr int WAVES = 4;
     constexpr int NT = WAVES * 64;
+    constexpr int WG = WAVES / KS;  // wave groups; the KS waves of a group split K
     extern __shared__ __align__(16) float lds_xf[];  // [MT][steps * W8_STEP], zero past K
     __shared__ float sc_lds[NT];
+    __shared__ float part[KS > 1 ? KS : 1][KS > 1 ? NT * MT : 1];  // per-wave row sums when K is split
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wg = wave / KS;  // the wave's group: units wg, wg + WG, ... of the workgroup
+    const int kp = wave % KS;  // the wave's part of K: steps [s_begin, s_end)
     const int g = lane >> 3;   // row of the unit
     const int sl = lane & 7;   // 16-weight piece of the step
     const int row_floats = steps * W8_STEP;
+    const int s_begin = kp * steps / KS;
+    const int s_end = (kp + 1) * steps / KS;  // the host guarantees steps >= KS
 
     const int ub0 = blockIdx.x * upb;
     const int ub1 = min(ub0 + upb, units);
-    const int my_units = (ub0 + wave < ub1) ? (ub1 - 1 - ub0 - wave) / WAVES + 1 : 0;
-    const int items = my_units * steps;
+    const int my_units = (ub0 + wg < ub1) ? (ub1 - 1 - ub0 - wg) / WG + 1 : 0;
+    const int items = my_units * (s_end - s_begin);
 
     // ---- the weight ring (first loads go out before the activation prologue)
     const int last_step = steps - 1;
@@ -210,12 +229,12 @@ __global__ __launch_bounds__(256) void w8a16_stream_kernel(float* __restrict__ y
     // in a partial last step, lanes past the row's end re-read its last 16
     // bytes; their activations in LDS are zero
     const uint32_t piece_last = (uint32_t)min(sl * 16, K - last_step * W8_STEP - 16);
-    int lj = 0, lt = 0;
+    int lj = 0, lt = s_begin;
     const int8_t* unit_ptr;
     uint32_t voff, voff_last;
     auto set_unit = [&]() {
         const bool live = lj < my_units;  // wave-uniform
-        const int u = min(ub0 + wave + WAVES * min(lj, max(my_units - 1, 0)), units - 1);
+        const int u = min(ub0 + wg + WG * min(lj, max(my_units - 1, 0)), units - 1);
         const uint32_t lane_row = (uint32_t)((min(u * 8 + g, N - 1) - u * 8) * K);
         unit_ptr = live ? q + (int64_t)u * 8 * K : reinterpret_cast<const int8_t*>(w8_pad);
         voff = live ? lane_row + piece : (uint32_t)(lane * 16);
@@ -225,8 +244,8 @@ __global__ __launch_bounds__(256) void w8a16_stream_kernel(float* __restrict__ y
     auto issue = [&](uint4& dst) {
         const int8_t* b = unit_ptr + lt * W8_STEP;
         dst = load_stream16(b + ((ktail && lt == last_step) ? voff_last : voff));
-        if (++lt == steps) {
-            lt = 0;
+        if (++lt == s_end) {
+            lt = s_begin;
             ++lj;
             set_unit();
         }
@@ -261,7 +280,7 @@ __global__ __launch_bounds__(256) void w8a16_stream_kernel(float* __restrict__ y
     const int swz = 4 * ((sl >> 2) & 1);
     const float* lds_a = lds_xf + sl * 16 + swz;       // quarters 0 and 2 of this lane's piece
     const float* lds_b = lds_xf + sl * 16 + 4 - swz;   // quarters 1 and 3
-    int cj = 0, ct = 0;
+    int cj = 0, ct = s_begin;
     auto consume = [&](const uint4& v) {
         float wf[16];
         const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
@@ -291,17 +310,21 @@ __global__ __launch_bounds__(256) void w8a16_stream_kernel(float* __restrict__ y
             acc0[m] = __builtin_fmaf(x3.z, wf[14], acc0[m]);
             acc1[m] = __builtin_fmaf(x3.w, wf[15], acc1[m]);
         }
-        if (++ct == steps) {  // unit complete: combine the row's 8 lanes, scale, write
-            const int ul = wave + WAVES * cj;
+        if (++ct == s_end) {  // unit complete: combine the row's 8 lanes, then scale and write
+            const int ul = wg + WG * cj;
             const int n = (ub0 + ul) * 8 + g;
             const float sc = sc_lds[ul * 8 + g];
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 const float tot = group8_sum_f32(acc0[m] + acc1[m]);
                 acc0[m] = acc1[m] = 0.0f;
-                if (m == sl && n < N && m < M) y[(int64_t)m * N + n] = tot * sc;
+                if (KS == 1) {
+                    if (m == sl && n < N && m < M) y[(int64_t)m * N + n] = tot * sc;
+                } else if (m == sl) {
+                    part[kp][(ul * 8 + g) * MT + m] = tot;  // combined below
+                }
             }
-            ct = 0;
+            ct = s_begin;
             ++cj;
         }
     };
@@ -318,6 +341,34 @@ __global__ __launch_bounds__(256) void w8a16_stream_kernel(float* __restrict__ y
 #pragma unroll
     for (int i = 0; i < D; ++i)
         if (i < rem) consume(buf[i]);
+
+    if (KS > 1) {  // the parts of K in a fixed order, then the scale
+        __syncthreads();
+        for (int idx = tid; idx < nrows * MT; idx += NT) {
+            const int r = idx / MT;
+            const int m = idx - r * MT;
+            float v = part[0][idx];
+#pragma unroll
+            for (int p = 1; p < KS; ++p) v += part[p][idx];
+            if (m < M) y[(int64_t)m * N + row0 + r] = v * sc_lds[r];
+        }
+    }
+}
+
+template <int MT, int D>
+hipError_t launch_w8a16_stream_ks(int ks, dim3 grid, size_t lds, hipStream_t s, float* y, const uint16_t* x,
+                                  const int8_t* q, const float* scale, int M, int N, int K, int steps, int units,
+                                  int upb) {
+    if (ks == 4)
+        hipLaunchKernelGGL((w8a16_stream_kernel<MT, D, 4>), grid, dim3(256), lds, s, y, x, q, scale, M, N, K, steps,
+                           units, upb);
+    else if (ks == 2)
+        hipLaunchKernelGGL((w8a16_stream_kernel<MT, D, 2>), grid, dim3(256), lds, s, y, x, q, scale, M, N, K, steps,
+                           units, upb);
+    else
+        hipLaunchKernelGGL((w8a16_stream_kernel<MT, D, 1>), grid, dim3(256), lds, s, y, x, q, scale, M, N, K, steps,
+                           units, upb);
+    return hipGetLastError();
 }
 
 template <int MT>
@@ -325,21 +376,25 @@ hipError_t launch_w8a16_stream(float* y, const uint16_t* x, const int8_t* q, con
                                hipStream_t s) {
     const int steps = (K + W8_STEP - 1) / W8_STEP;
     const int units = (N + 7) / 8;
+    // Split K inside the workgroup when there are too few units to give every
+    // CU several waves of whole rows.
+    int ks = 1;
+    const int split_units = MT == 1 ? W8_SPLIT_UNITS_M1 : W8_SPLIT_UNITS_M2;
+    while (ks < 4 && units * ks < split_units && steps >= 4 * ks) ks *= 2;
+    const int groups = 4 / ks;
     // at most 32 units (256 rows, one scale per thread) per workgroup;
     // otherwise as few workgroups as keep the GPU full
-    int blocks = (units + 3) / 4;
-    if (blocks > W8_STREAM_MAX_BLOCKS) blocks = W8_STREAM_MAX_BLOCKS;
+    int blocks = (units + groups - 1) / groups;
+    const int max_blocks = units * ks <= W8_SPLIT_WORK ? W8_STREAM_MAX_BLOCKS_SPLIT : W8_STREAM_MAX_BLOCKS;
+    if (blocks > max_blocks) blocks = max_blocks;
     if (blocks < (units + 31) / 32) blocks = (units + 31) / 32;
     const int upb = (units + blocks - 1) / blocks;
     blocks = (units + upb - 1) / upb;
     const size_t lds = (size_t)MT * steps * W8_STEP * 4;
-    if (steps >= 12)
-        hipLaunchKernelGGL((w8a16_stream_kernel<MT, MT == 1 ? 16 : 8>), dim3(blocks), dim3(256), lds, s, y, x, q,
-                           scale, M, N, K, steps, units, upb);
-    else
-        hipLaunchKernelGGL((w8a16_stream_kernel<MT, 8>), dim3(blocks), dim3(256), lds, s, y, x, q, scale, M, N, K,
-                           steps, units, upb);
-    return hipGetLastError();
+    if (steps / ks >= 12)
+        return launch_w8a16_stream_ks<MT, MT == 1 ? 16 : 8>(ks, dim3(blocks), lds, s, y, x, q, scale, M, N, K, steps,
+                                                            units, upb);
+    return launch_w8a16_stream_ks<MT, 8>(ks, dim3(blocks), lds, s, y, x, q, scale, M, N, K, steps, units, upb);
 }
 
 // Any shape: one wave per output column, fp32 partial sums per lane, a fixed
@@ -371,11 +426,9 @@ hipError_t launch_w8a16(float* y, const uint16_t* x, const int8_t* q, const floa
                         int64_t K, hipStream_t s) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const int64_t steps = (K + W8_STEP - 1) / W8_STEP;
-    const int mt = M == 1 ? 1 : (M == 2 ? 2 : 4);
-    if (M <= 4 && K % 16 == 0 && mt * steps <= W8_MAX_STEPS && aligned16(x) && aligned16(q)) {
-        if (mt == 1) return launch_w8a16_stream<1>(y, x, q, scale, (int)M, (int)N, (int)K, s);
-        if (mt == 2) return launch_w8a16_stream<2>(y, x, q, scale, (int)M, (int)N, (int)K, s);
-        return launch_w8a16_stream<4>(y, x, q, scale, (int)M, (int)N, (int)K, s);
+    if (M <= W8_STREAM_MAX_M && K % 16 == 0 && M * steps <= W8_MAX_STEPS && aligned16(x) && aligned16(q)) {
+        if (M == 1) return launch_w8a16_stream<1>(y, x, q, scale, (int)M, (int)N, (int)K, s);
+        return launch_w8a16_stream<2>(y, x, q, scale, (int)M, (int)N, (int)K, s);
     }
     constexpr int KW = 4;
     const int64_t nc = K / WQ_CHUNK;
