@@ -18,6 +18,9 @@ Parity status of each function (what pins it is listed in the tests):
   quantize_f32 / linear_f32       pinned (hand-worked f32 vector; equal to the bf16 path on
                                   bf16-representable inputs; composition)
   add_bias                        pinned (hand-worked round-to-even ties; zero bias; zero rows)
+  rmsnorm_quantize / linear_rms   pinned (bit-equal to torch's F.rms_norm on rows whose sums are exact;
+                                  closed forms: constant rows, zero rows; sign, power-of-two scale
+                                  and gain symmetries; the ambiguity flag on constructed ties)
   w8a16                           pinned (hand-worked example; zero weights; power-of-two scaling and
                                   sign symmetry; brute force against an exact rational sum)
 """
@@ -68,6 +71,8 @@ def load(path=None):
     lib.oracle_linear_f32.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p]
     lib.oracle_linear_f32.restype = ctypes.c_int
     lib.oracle_w8a16.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p]
+    lib.oracle_rmsnorm_quantize.argtypes = [_p, _p, ctypes.c_float, _i64, _i64, _p, _p, _p, _p, _p, _p]
+    lib.oracle_rmsnorm_quantize.restype = ctypes.c_int
     lib.oracle_w8a16.restype = None
     lib.oracle_dot_i64.argtypes = [_p, _p, _i64, _i64]
     lib.oracle_dot_i64.restype = ctypes.c_int64
@@ -254,3 +259,38 @@ def w8a16(x_bits, q, scale, lib=None):
     bound = np.zeros((M, N), dtype=np.float64)
     lib.oracle_w8a16(_ptr(x), _ptr(q), _ptr(scale), M, N, K, _ptr(y), _ptr(bound))
     return y, bound
+
+
+FP32_EPS = 2.0 ** -23   # torch's default rms_norm eps for bf16 and f32 input
+
+
+def rmsnorm_quantize(x_bits, gain_bits=None, eps=FP32_EPS, means=None, lib=None):
+    """RMSNorm then per-token quantisation: bf16 bits x[M,K], optional bf16 gain[K].
+
+    Returns a dict with xn (bf16 bits), q, scale_act, mean (fp32 per row),
+    mean_alt (the other fp32 mean a different summation order could give;
+    equal to mean when the row is unambiguous) and ambiguous (bool per row).
+    means (fp32 [M]) forces the mean used for every row."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    M, K = x.shape
+    g = None if gain_bits is None else np.ascontiguousarray(gain_bits, dtype=np.uint16)
+    mi = None if means is None else np.ascontiguousarray(means, dtype=np.float32)
+    xn = np.zeros((M, K), dtype=np.uint16)
+    q = np.zeros((M, K), dtype=np.int8)
+    sa = np.zeros(M, dtype=np.uint16)
+    mean = np.zeros(M, dtype=np.float32)
+    alt = np.zeros(M, dtype=np.float32)
+    _check(lib.oracle_rmsnorm_quantize(_ptr(x), None if g is None else _ptr(g), ctypes.c_float(eps), M, K,
+                                       None if mi is None else _ptr(mi), _ptr(xn), _ptr(q), _ptr(sa), _ptr(mean),
+                                       _ptr(alt)), "oracle_rmsnorm_quantize")
+    return {"xn": xn, "q": q, "scale_act": sa, "mean": mean, "mean_alt": alt, "ambiguous": mean != alt}
+
+
+def linear_rms(x_bits, P, sw, gain_bits=None, eps=FP32_EPS, means=None, lib=None):
+    """RMSNorm, quantise, ternary contraction, epilogue: bf16 bits out[M,N] and the intermediates."""
+    r = rmsnorm_quantize(x_bits, gain_bits, eps, means, lib)
+    acc = gemm_i32(r["q"], P, lib)
+    r["acc"] = acc
+    r["out"] = epilogue(acc, r["scale_act"], sw, lib)
+    return r

@@ -22,6 +22,10 @@
 //                                     -> oracle_add_bias
 //   * "CoolDip00/tiny-llm src/tinyllm/kernels/int8_gemv.py", the W8A16 decode
 //       matmul                     -> oracle_w8a16
+//   * "kyegomez/BitNet issue #77", activation_norm_quant (RMSNorm, then the
+//       per-token quantisation; a fused kernel is suggested there), and
+//       bitnet-cpu's BitLinearKernel (its rms_norm module runs before
+//       bitnet_linear)              -> oracle_rmsnorm_row, oracle_rmsnorm_quantize
 //   * "CoolDip00/tiny-llm src/tinyllm/kernels/int8_gemv.py", docstring of
 //       int8_matmul: the integer/matmul result is scaled without an
 //       intermediate rounding to bf16.
@@ -281,6 +285,71 @@ void oracle_add_bias(uint16_t* out, const uint16_t* bias, int64_t M, int64_t N) 
             const float y = oracle_f32_from_bf16(out[m * N + n]) + oracle_f32_from_bf16(bias[n]);
             out[m * N + n] = oracle_bf16_from_f32(y);
         }
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm before the quantisation ("kyegomez/BitNet issue #77",
+// activation_norm_quant: F.rms_norm over the last dimension, then the int8
+// quantisation; bitnet-cpu's BitLinearKernel applies its rms_norm module the
+// same way before bitnet_linear).  Reading R22, torch's rms_norm on bf16 input,
+// computed in fp32:
+//   mean = fp32( sum_k x_k^2 / K )
+//   r    = fp32( 1 / fp32( sqrt( fp32(mean + eps) ) ) )
+//   xn_k = bf16_rne( fp32( fp32(x_k * r) * g_k ) )     (no multiply without a gain)
+// with eps given in fp32 (torch's default is the fp32 epsilon, 2^-23).  Every
+// square of a bf16 value is exact in double; the sum is taken in double, so an
+// implementation may add the squares in any order.  Different orders can round
+// the double sum differently, and in rare rows that moves the fp32 mean by one
+// step: the oracle then returns both fp32 candidates (mean_out, mean_alt_out;
+// equal when the row is unambiguous), and mean_in (when given) forces the mean
+// used, so that each candidate's result can be formed.
+// ---------------------------------------------------------------------------
+void oracle_rmsnorm_row(const uint16_t* x, const uint16_t* gain, float eps, int64_t K, const float* mean_in,
+                        uint16_t* xn, float* mean_out, float* mean_alt_out) {
+    double S = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        const double v = (double)oracle_f32_from_bf16(x[k]);
+        S += v * v;  // exact product
+    }
+    const double m64 = S / (double)K;
+    // Any summation order of K non-negative terms lies within (K - 1) * 2^-53
+    // (relative, to first order) of the exact sum, as does this one; with the
+    // division's rounding, an implementation's double mean lies within
+    // delta of m64 (relative).
+    const double delta = (2.0 * (double)(K - 1) + 4.0) * std::ldexp(1.0, -53) * 1.01;
+    const float lo = (float)(m64 * (1.0 - delta));
+    const float hi = (float)(m64 * (1.0 + delta));
+    float mean = (float)m64;
+    float alt = (lo != mean) ? lo : hi;
+    if (mean_in) {
+        mean = *mean_in;
+        alt = mean;
+    }
+    if (mean_out) *mean_out = mean;
+    if (mean_alt_out) *mean_alt_out = alt;
+    const float v = mean + eps;
+    const float sd = std::sqrt(v);
+    const float r = 1.0f / sd;
+    for (int64_t k = 0; k < K; ++k) {
+        float t = oracle_f32_from_bf16(x[k]) * r;
+        if (gain) t = t * oracle_f32_from_bf16(gain[k]);
+        xn[k] = oracle_bf16_from_f32(t);
+    }
+}
+
+// RMSNorm then quantise, row by row.  xn (bf16, [M][K]) receives the
+// normalised activations the quantiser sees; mean_in may be NULL.
+int oracle_rmsnorm_quantize(const uint16_t* x, const uint16_t* gain, float eps, int64_t M, int64_t K,
+                            const float* mean_in, uint16_t* xn, int8_t* q, uint16_t* scale, float* mean_out,
+                            float* mean_alt_out) {
+    if (M < 0 || K <= 0) return ORC_ERR_SHAPE;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        oracle_rmsnorm_row(x + m * K, gain, eps, K, mean_in ? mean_in + m : nullptr, xn + m * K, mean_out + m,
+                           mean_alt_out + m);
+        oracle_quantize_row(xn + m * K, K, q + m * K, scale + m);
+    }
+    return ORC_OK;
 }
 
 int oracle_linear(const uint16_t* x, const uint8_t* P, const uint16_t* sw, int64_t M, int64_t N, int64_t K,

@@ -126,7 +126,35 @@ def _pin_battery(lib):
         y, bound = oracle.w8a16(x, q, np.array([0.5, 2.0], dtype=np.float32), lib=lib)
         return y.tolist() == [[0.5, -380.5]] and bound.tolist() == [[4.5, 381.5]]
 
+    def rms_torch_exact():
+        # integer rows: exact sums in any order, so torch's F.rms_norm is matched bit for bit
+        import torch.nn.functional as F
+        g = synth.rng(77)
+        x = _bf16(g.integers(-8, 9, size=(6, 256)).astype(np.float32).tolist())
+        gain = _bf16(g.uniform(0.5, 1.5, size=256).astype(np.float32).tolist())
+        r = oracle.rmsnorm_quantize(x, gain, lib=lib)
+        xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+        gt = torch.from_numpy(gain.view(np.int16)).view(torch.bfloat16)
+        want = F.rms_norm(xt, [256], gt).view(torch.int16).numpy().view(np.uint16)
+        # small rows (x 2^-12, sums still exact): the mean is comparable to eps
+        xs = _bf16((g.integers(-8, 9, size=(6, 256)) * 2.0 ** -12).astype(np.float32).tolist())
+        rs = oracle.rmsnorm_quantize(xs, eps=1e-6, lib=lib)
+        xst = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16)
+        wants = F.rms_norm(xst, [256], None, 1e-6).view(torch.int16).numpy().view(np.uint16)
+        return np.array_equal(r["xn"], want) and np.array_equal(rs["xn"], wants)
+
+    def rms_tie_flagged():
+        x = _bf16([[2.0, 0.0, 0.0, 2.0 ** -11]])
+        r = oracle.rmsnorm_quantize(x, eps=0.0, lib=lib)
+        return bool(r["ambiguous"][0]) and float(r["mean_alt"][0]) == 1.0 + 2.0 ** -23
+
+    def rms_constant_row():
+        r = oracle.rmsnorm_quantize(_bf16([[-3.0] * 64]), lib=lib)
+        return bool(np.all(r["xn"] == 0xBF80)) and bool(np.all(r["q"] == -127))
+
     for name, fn in [("pack_golden", pack_golden), ("unpack_roundtrip", unpack_roundtrip),
+                     ("rms_torch_exact", rms_torch_exact), ("rms_tie_flagged", rms_tie_flagged),
+                     ("rms_constant_row", rms_constant_row),
                      ("quant_f32_golden", quant_f32_golden), ("bias_golden", bias_golden),
                      ("w8a16_hand", w8a16_hand),
                      ("quant_golden", quant_golden), ("quant_absmax", quant_absmax),
@@ -168,6 +196,16 @@ MUTANTS = [
     ("w8a16_dropped_term", "for (int64_t k = 0; k < K; ++k) {\n                const double t",
      "for (int64_t k = 1; k < K; ++k) {\n                const double t"),
     ("w8a16_abs_bound", "a += std::fabs(t);", "a += t;"),
+    ("rms_eps_after_sqrt", "const float v = mean + eps;\n    const float sd = std::sqrt(v);",
+     "const float v = mean;\n    const float sd = std::sqrt(v) + eps;"),
+    ("rms_sum_not_mean", "const double m64 = S / (double)K;", "const double m64 = S;"),
+    ("rms_gain_after_round", "if (gain) t = t * oracle_f32_from_bf16(gain[k]);",
+     "if (gain) t = oracle_f32_from_bf16(oracle_bf16_from_f32(t)) * oracle_f32_from_bf16(gain[k]);"),
+    ("rms_gain_index", "oracle_f32_from_bf16(gain[k])", "oracle_f32_from_bf16(gain[0])"),
+    ("rms_no_inverse", "const float r = 1.0f / sd;", "const float r = sd;"),
+    ("rms_signed_square", "S += v * v;  // exact product", "S += v * std::fabs(v);  // exact product"),
+    ("rms_no_margin", "const double delta = (2.0 * (double)(K - 1) + 4.0) * std::ldexp(1.0, -53) * 1.01;",
+     "const double delta = 0.0;"),
 ]
 
 

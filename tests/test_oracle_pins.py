@@ -359,3 +359,111 @@ def test_w8a16_brute_force_exact(orc):
         for n in range(3):
             exact = sum(Fraction(float(xf[m, k])) * int(q[n, k]) for k in range(40)) * Fraction(float(sc[n]))
             assert y[m, n] == float(exact)
+
+
+# ----------------------------------------------------------------------------- RMSNorm before quantisation
+
+def _torch_rms_norm_bits(x_bits, gain_bits, eps):
+    """torch's own F.rms_norm on the same bf16 input (the library routine the reading follows)."""
+    import torch
+    import torch.nn.functional as F
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16)
+    g = None if gain_bits is None else torch.from_numpy(gain_bits.view(np.int16)).view(torch.bfloat16)
+    y = F.rms_norm(x, [x.shape[-1]], g, eps)
+    return y.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("K", [256, 2560, 6912])
+@pytest.mark.parametrize("with_gain", [False, True])
+@pytest.mark.parametrize("eps", [None, 1e-5])
+@pytest.mark.parametrize("magnitude", [1.0, 2.0 ** -12])
+def test_rmsnorm_equals_torch_on_exact_rows(orc, K, with_gain, eps, magnitude):
+    # Integer activations in [-8, 8] (times a power of two): every sum of squares
+    # is an integer below 2^24 (times a power of two), exact in torch's fp32
+    # reduction in any order, so the normalised values must agree bit for bit.
+    # At 2^-12 the mean is comparable to eps, which makes eps's place visible.
+    g = synth.rng(900 + K)
+    x = bf16_bits((g.integers(-8, 9, size=(32, K)) * magnitude).astype(np.float32))
+    gain = bf16_bits(g.uniform(0.5, 1.5, size=K).astype(np.float32)) if with_gain else None
+    r = orc.rmsnorm_quantize(x, gain, orc.FP32_EPS if eps is None else eps)
+    assert not r["ambiguous"].any()
+    assert np.array_equal(r["xn"], _torch_rms_norm_bits(x, gain, eps))
+
+
+def test_rmsnorm_close_to_torch_on_random_rows(orc):
+    # Random bf16 rows: torch sums the squares in fp32, the oracle in double, so
+    # an fp32 mean can differ in its last bit; the normalised values then differ
+    # by at most one bf16 step, and rarely.
+    x = synth.activations_bf16(64, 2560, seed=910)
+    r = orc.rmsnorm_quantize(x)
+    want = _torch_rms_norm_bits(x, None, None)
+    a = r["xn"].astype(np.int32)
+    b = want.astype(np.int32)
+    oa = np.where(a & 0x8000, -(a & 0x7FFF), a & 0x7FFF)
+    ob = np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    assert np.abs(oa - ob).max() <= 1
+    assert (a != b).mean() < 1e-3
+
+
+def test_rmsnorm_constant_and_zero_rows(orc):
+    K = 512
+    x = np.zeros((4, K), dtype=np.uint16)
+    x[0] = bf16_bits(np.full(K, 0.5, dtype=np.float32))
+    x[1] = bf16_bits(np.full(K, -3.0, dtype=np.float32))
+    x[2] = bf16_bits(np.where(np.arange(K) % 2 == 0, 7.0, -7.0).astype(np.float32))
+    r = orc.rmsnorm_quantize(x)
+    # a row of constant magnitude c normalises to sign(x) * c / sqrt(c^2 + eps), i.e. +-1 in bf16
+    assert np.all(r["xn"][0] == 0x3F80) and np.all(r["xn"][1] == 0xBF80)
+    assert np.array_equal(r["xn"][2], np.where(np.arange(K) % 2 == 0, 0x3F80, 0xBF80))
+    assert np.all(np.abs(r["q"][:3]) == 127)
+    # all-zero row: zeros out, the quantiser's eps floor for the scale
+    assert np.all(r["xn"][3] == 0) and np.all(r["q"][3] == 0) and r["mean"][3] == 0.0
+    assert r["scale_act"][3] == 0x33A9
+
+
+def test_rmsnorm_symmetries(orc):
+    x = synth.activations_bf16(8, 1024, seed=920)
+    xf = synth.bf16_bits_to_f32(x)
+    base = orc.rmsnorm_quantize(x, eps=0.0)
+    neg = orc.rmsnorm_quantize(bf16_bits(-xf), eps=0.0)
+    assert np.array_equal(neg["xn"], base["xn"] ^ np.uint16(0x8000) * (base["xn"] != 0))
+    for j in (-6, 5):                                        # exact power-of-two scaling, eps = 0
+        sc = orc.rmsnorm_quantize(bf16_bits(xf * np.float32(2.0 ** j)), eps=0.0)
+        assert np.array_equal(sc["xn"], base["xn"]) and np.array_equal(sc["q"], base["q"])
+    two = orc.rmsnorm_quantize(x, bf16_bits(np.full(1024, 2.0, dtype=np.float32)), eps=0.0)
+    assert np.array_equal(synth.bf16_bits_to_f32(two["xn"]), 2.0 * synth.bf16_bits_to_f32(base["xn"]))
+    perm = synth.rng(921).permutation(1024)
+    xi = bf16_bits(synth.rng(922).integers(-8, 9, size=(8, 1024)).astype(np.float32))   # exact sums
+    a = orc.rmsnorm_quantize(xi)
+    b = orc.rmsnorm_quantize(xi[:, perm])
+    assert np.array_equal(b["xn"], a["xn"][:, perm]) and np.array_equal(b["q"], a["q"][:, perm])
+
+
+def test_rmsnorm_unit_mean_square(orc):
+    x = synth.activations_bf16(16, 4096, seed=930, outlier_frac=0.01)
+    xn = synth.bf16_bits_to_f32(orc.rmsnorm_quantize(x)["xn"]).astype(np.float64)
+    assert np.allclose((xn * xn).mean(axis=1), 1.0, rtol=2.0 ** -7)
+
+
+def test_rmsnorm_ambiguous_mean_is_flagged(orc):
+    # [2, 0, 0, 2^-11]: sum of squares 4 + 2^-22, mean 1 + 2^-24, exactly halfway
+    # between the fp32 values 1 and 1 + 2^-23.  [2, 0, 0, 0]: mean exactly 1.
+    x = bf16_bits(np.array([[2.0, 0.0, 0.0, 2.0 ** -11], [2.0, 0.0, 0.0, 0.0]], dtype=np.float32))
+    r = orc.rmsnorm_quantize(x, eps=0.0)
+    assert r["ambiguous"].tolist() == [True, False]
+    assert r["mean"].tolist() == [1.0, 1.0]
+    assert float(r["mean_alt"][0]) == 1.0 + 2.0 ** -23
+    forced = orc.rmsnorm_quantize(x, eps=0.0, means=np.array([1.0 + 2.0 ** -23, 1.0], dtype=np.float32))
+    assert forced["mean"].tolist() == [1.0 + 2.0 ** -23, 1.0] and not forced["ambiguous"].any()
+
+
+def test_linear_rms_is_the_composition(orc):
+    x = synth.activations_bf16(5, 512, seed=940)
+    gain = synth.row_scales_bf16(512, seed=941, lo=0.5, hi=2.0)
+    W = synth.ternary_weights(33, 512, seed=942)
+    P = orc.pack(W)
+    sw = synth.row_scales_bf16(33, seed=943)
+    r = orc.linear_rms(x, P, sw, gain, 1e-6)
+    ref = orc.linear(r["xn"], P, sw)
+    assert np.array_equal(r["out"], ref["out"]) and np.array_equal(r["q"], ref["q"])
+    assert np.array_equal(r["acc"], r["q"].astype(np.int64) @ W.astype(np.int64).T)
