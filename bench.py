@@ -266,7 +266,9 @@ def run_decode_full(device, stream, log, layers=30):
     projections per layer) plus the LM head: 121 calls on 121 distinct weight
     buffers (603 MB).  The layers hold copies of one synthetic layer's packed
     weights (distinct memory, same values).  M = 1 (fused GEMV) and M = 16
-    (quantise + GEMM), each step captured as one graph."""
+    (quantise + GEMM), each step captured as one graph; then the same with the
+    RMSNorm that precedes every BitLinear fused in (bitnet_linear_rms: the
+    decode GEMV's prologue at M = 1, RMSNorm-quantise + GEMM at M = 16)."""
     shapes = synth.BITNET_2B_DECODE
     layer_shapes = [s for s in shapes if s[0] != "lm_head"]
     head = [s for s in shapes if s[0] == "lm_head"]
@@ -284,17 +286,20 @@ def run_decode_full(device, stream, log, layers=30):
         calls.append((name, N, K, base[name][0], base[name][1]))
     total_w = sum(c[3].numel() for c in calls)
     res = {"calls": len(calls), "weight_bytes": total_w}
-    for M in (1, 16):
+    for M, rms in ((1, False), (16, False), (1, True), (16, True)):
         xs, outs = [], []
         for j, (name, N, K, _, _) in enumerate(calls):
             xs.append(dev_bf16(synth.activations_bf16(M, K, synth.seed_for(5, j) + M), device))
             outs.append(torch.empty((M, N), dtype=torch.bfloat16, device=device))
-        ws = torch.empty((max(tg.linear_workspace_bytes(M, c[2]) for c in calls) + 256,), dtype=torch.uint8,
+        ws = torch.empty((max(tg.linear_rms_workspace_bytes(M, c[2]) for c in calls) + 256,), dtype=torch.uint8,
                          device=device)
 
         def step():
             for (name, N, K, Pd, swd), xd, od in zip(calls, xs, outs):
-                tg.bitnet_linear(xd, Pd, swd, out=od, workspace=ws)
+                if rms:
+                    tg.bitnet_linear_rms(xd, Pd, swd, out=od, workspace=ws)
+                else:
+                    tg.bitnet_linear(xd, Pd, swd, out=od, workspace=ws)
 
         g = capture(step, stream)
         time_graph(g, 2, stream)
@@ -304,10 +309,11 @@ def run_decode_full(device, stream, log, layers=30):
             nbytes = sum(gemv_bytes(M, N, K) for _, N, K, _, _ in calls)
         else:  # quantise (2MK in, MK + 2M out) + GEMM
             nbytes = sum(gemm_bytes(M, N, K) + 3 * M * K + 2 * M for _, N, K, _, _ in calls)
-        res[f"M{M}"] = {"us_per_step": round(t * 1e6, 2), "tokens_per_s": round(M / t, 1),
-                        "gbs": round(nbytes / t / 1e9, 1), "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
-                        "step_bytes": nbytes}
-        log(f"  full decode step M={M:2d}: {t * 1e6:8.1f} us/step, {M / t:9.1f} tok/s, "
+        key = f"M{M}_rmsnorm" if rms else f"M{M}"
+        res[key] = {"us_per_step": round(t * 1e6, 2), "tokens_per_s": round(M / t, 1),
+                    "gbs": round(nbytes / t / 1e9, 1), "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                    "step_bytes": nbytes}
+        log(f"  full decode step M={M:2d}{' +RMSNorm' if rms else '         '}: {t * 1e6:8.1f} us/step, {M / t:9.1f} tok/s, "
             f"{nbytes / t / 1e9:7.1f} GB/s ({100 * nbytes / t / 1e9 / HBM_PEAK_GBS:.1f}% of HBM peak)")
         del xs, outs, ws
     del calls, base

@@ -169,6 +169,56 @@ bitnet_status bitnet_linear_ex(uint16_t* out, const void* x, int x_dtype, const 
                                const uint16_t* scale_wt, const uint16_t* bias, int64_t M, int64_t N, int64_t K,
                                void* workspace, size_t workspace_bytes, bitnet_stream_t stream);
 
+/*
+ * RMSNorm, then the per-token quantisation of the normalised rows
+ * (activation_norm_quant of "kyegomez/BitNet issue #77": F.rms_norm over the
+ * last dimension before the int8 quantisation, which that page notes can be
+ * one fused kernel; bitnet-cpu's BitLinearKernel likewise runs its rms_norm
+ * module before bitnet_linear).  Per row m, in fp32 as torch's rms_norm
+ * computes on bf16 input:
+ *   mean = fp32( sum_k x[m][k]^2 / K )      (exact squares summed in double)
+ *   r    = fp32( 1 / fp32( sqrt( fp32(mean + eps) ) ) )   (IEEE sqrt, division)
+ *   xn[m][k] = bf16_round_nearest_even( fp32( fp32(x[m][k] * r) * gain[k] ) )
+ * (no gain multiply when gain is NULL), then bitnet_quantize_act on xn.
+ * The double sum's order is the library's; a different order could move the
+ * fp32 mean by one step only where the double mean lies within about
+ * K * 2^-52 (relative) of an fp32 rounding boundary.
+ * x: bf16 [M][K]; gain: bf16 [K] or NULL; eps: finite, >= 0 (torch's default is
+ * the fp32 epsilon 2^-23); x_int8: int8 [M][K] (written); scale_act: bf16 [M]
+ * (written); x_norm: bf16 [M][K] (written when not NULL).  Device pointers,
+ * enqueued on stream.  Errors: eps negative or not finite -> VALUE.
+ */
+bitnet_status bitnet_rmsnorm_quantize(int8_t* x_int8, uint16_t* scale_act, uint16_t* x_norm, const uint16_t* x,
+                                      const uint16_t* gain, float eps, int64_t M, int64_t K, bitnet_stream_t stream);
+
+/*
+ * Device workspace (bytes) that bitnet_linear_rms needs: room for x_int8
+ * [M][K] and scale_act [M] (each rounded up to 256 bytes) at every M.
+ * Returns 0 for invalid sizes.
+ */
+size_t bitnet_linear_rms_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * BitLinear forward preceded by RMSNorm (the rms_norm step of bitnet-cpu's
+ * BitLinearKernel, fused as "kyegomez/BitNet issue #77" suggests):
+ *   out = bitnet_linear( rms_norm(x) )  with rms_norm as in
+ *   bitnet_rmsnorm_quantize.
+ * For 1 <= M <= 4 (K % 64 == 0, 16-byte aligned x, w_packed and gain) the
+ * normalisation runs in the prologue of the fused decode GEMV and the
+ * workspace is not touched; otherwise bitnet_rmsnorm_quantize into the
+ * workspace, then bitnet_gemm.  The two paths add the squares in different
+ * orders; they give the same bits except in the rare rows whose fp32 mean is
+ * ambiguous in the sense of bitnet_rmsnorm_quantize.
+ * out: bf16 [M][N]; x: bf16 [M][K]; gain: bf16 [K] or NULL; w_packed: uint8
+ * [N][K/4]; scale_wt: bf16 [N]; workspace: device memory of at least
+ * bitnet_linear_rms_workspace_bytes(M, K) bytes, 256-byte aligned (always
+ * required).  Errors: workspace too small -> WORKSPACE; eps negative or not
+ * finite -> VALUE.
+ */
+bitnet_status bitnet_linear_rms(uint16_t* out, const uint16_t* x, const uint16_t* gain, float eps,
+                                const uint8_t* w_packed, const uint16_t* scale_wt, int64_t M, int64_t N, int64_t K,
+                                void* workspace, size_t workspace_bytes, bitnet_stream_t stream);
+
 /* Largest activation row count bitnet_w8a16_gemv takes (decode batches). */
 #define BITNET_W8A16_MAX_M 64
 

@@ -73,6 +73,8 @@ def load_library():
         "bitnet_quantize_act_f32": [_p, _p, _p, _i64, _i64, _p],
         "bitnet_linear_ex": [_p, _p, _st, _p, _p, _p, _i64, _i64, _i64, _p, _sz, _p],
         "bitnet_w8a16_gemv": [_p, _p, _p, _p, _i64, _i64, _i64, _p],
+        "bitnet_rmsnorm_quantize": [_p, _p, _p, _p, _p, ctypes.c_float, _i64, _i64, _p],
+        "bitnet_linear_rms": [_p, _p, _p, ctypes.c_float, _p, _p, _i64, _i64, _i64, _p, _sz, _p],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -82,6 +84,8 @@ def load_library():
     lib.bitnet_linear_workspace_bytes.restype = _sz
     lib.bitnet_linear_ex_workspace_bytes.argtypes = [_i64, _i64, _st]
     lib.bitnet_linear_ex_workspace_bytes.restype = _sz
+    lib.bitnet_linear_rms_workspace_bytes.argtypes = [_i64, _i64]
+    lib.bitnet_linear_rms_workspace_bytes.restype = _sz
     lib.bitnet_status_string.argtypes = [_st]
     lib.bitnet_status_string.restype = ctypes.c_char_p
     lib.bitnet_version.argtypes = []
@@ -288,3 +292,51 @@ def w8a16_gemv(x, q, scale, out=None):
     _check(load_library().bitnet_w8a16_gemv(_ptr(o), _ptr(x), _ptr(q), _ptr(scale), M, N, K, _stream(x)),
            "bitnet_w8a16_gemv")
     return o
+
+
+RMS_EPS_DEFAULT = 2.0 ** -23   # torch's rms_norm default eps (the fp32 epsilon)
+
+
+def linear_rms_workspace_bytes(M, K):
+    return load_library().bitnet_linear_rms_workspace_bytes(M, K)
+
+
+def rmsnorm_quantize(x, gain=None, eps=RMS_EPS_DEFAULT, out=None, scale=None, x_norm=None):
+    """RMSNorm then quantise: bf16 x[..., K], optional bf16 gain[K] -> (int8 [M, K], bf16 scale [M]).
+
+    When x_norm (bf16 [M, K]) is given it receives the normalised activations."""
+    _need(x, torch.bfloat16, "x")
+    if gain is not None:
+        _need(gain, torch.bfloat16, "gain")
+    if x_norm is not None:
+        _need(x_norm, torch.bfloat16, "x_norm")
+    K = x.shape[-1]
+    M = x.numel() // K if K else 0
+    if gain is not None and gain.numel() != K:
+        raise ValueError("rmsnorm_quantize: gain must have K elements")
+    q = out if out is not None else torch.empty((M, K), dtype=torch.int8, device=x.device)
+    sa = scale if scale is not None else torch.empty((M,), dtype=torch.bfloat16, device=x.device)
+    _check(load_library().bitnet_rmsnorm_quantize(_ptr(q), _ptr(sa), _ptr(x_norm), _ptr(x), _ptr(gain), eps, M, K,
+                                                  _stream(x)), "bitnet_rmsnorm_quantize")
+    return q, sa
+
+
+def bitnet_linear_rms(x, w_packed, scale_wt, gain=None, eps=RMS_EPS_DEFAULT, out=None, workspace=None):
+    """RMSNorm then the BitLinear forward: bf16 x[..., K] -> bf16 [..., N]."""
+    _need(x, torch.bfloat16, "x")
+    _need(w_packed, torch.uint8, "w_packed")
+    _need(scale_wt, torch.bfloat16, "scale_wt")
+    if gain is not None:
+        _need(gain, torch.bfloat16, "gain")
+    K = x.shape[-1]
+    M = x.numel() // K if K else 0
+    N = w_packed.shape[0]
+    if w_packed.shape[1] * 4 != K or scale_wt.numel() != N or (gain is not None and gain.numel() != K):
+        raise ValueError("bitnet_linear_rms: inconsistent shapes")
+    ws = workspace
+    if ws is None:
+        ws = torch.empty((max(linear_rms_workspace_bytes(M, K), 1),), dtype=torch.uint8, device=x.device)
+    o = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(load_library().bitnet_linear_rms(_ptr(o), _ptr(x), _ptr(gain), eps, _ptr(w_packed), _ptr(scale_wt), M, N,
+                                            K, _ptr(ws), ws.numel(), _stream(x)), "bitnet_linear_rms")
+    return o.view(*x.shape[:-1], N)

@@ -19,6 +19,9 @@ using bitnet::launch_quantize;
 using bitnet::launch_quantize_f32;
 using bitnet::launch_add_bias;
 using bitnet::launch_w8a16;
+using bitnet::launch_quantize_rms;
+using bitnet::launch_gemv_fused_rms;
+using bitnet::gemv_rms_fusable;
 
 constexpr int kMaxDevices = 64;
 // 0 = unknown, 1 = gfx950, 2 = other
@@ -208,6 +211,46 @@ BITNET_API bitnet_status bitnet_linear_ex(uint16_t* out, const void* x, int x_dt
     }
     if (st != BITNET_OK || bias == nullptr) return st;
     return launched(launch_add_bias(out, bias, M, N, (hipStream_t)stream));
+}
+
+static bool eps_ok(float eps) { return eps >= 0.0f && eps <= 3.4028234e38f; }  // false for NaN and +inf
+
+BITNET_API bitnet_status bitnet_rmsnorm_quantize(int8_t* x_int8, uint16_t* scale_act, uint16_t* x_norm,
+                                                 const uint16_t* x, const uint16_t* gain, float eps, int64_t M,
+                                                 int64_t K, bitnet_stream_t stream) {
+    if (!sizes_ok(M, 0)) return BITNET_ERR_SHAPE;
+    if (bitnet_status st = check_k(K)) return st;
+    if (!eps_ok(eps)) return BITNET_ERR_VALUE;
+    if (M == 0) return BITNET_OK;
+    if (!x_int8 || !scale_act || !x) return BITNET_ERR_NULL;
+    if (bitnet_status st = check_device()) return st;
+    return launched(launch_quantize_rms(x_int8, scale_act, x_norm, x, gain, eps, M, K, (hipStream_t)stream));
+}
+
+BITNET_API size_t bitnet_linear_rms_workspace_bytes(int64_t M, int64_t K) {
+    if (M < 0 || K <= 0 || K % 4 != 0 || K > BITNET_MAX_K || !sizes_ok(M, 0)) return 0;
+    return round256((size_t)M * (size_t)K) + round256((size_t)M * 2);
+}
+
+BITNET_API bitnet_status bitnet_linear_rms(uint16_t* out, const uint16_t* x, const uint16_t* gain, float eps,
+                                           const uint8_t* w_packed, const uint16_t* scale_wt, int64_t M, int64_t N,
+                                           int64_t K, void* workspace, size_t workspace_bytes,
+                                           bitnet_stream_t stream) {
+    if (!sizes_ok(M, N)) return BITNET_ERR_SHAPE;
+    if (bitnet_status st = check_k(K)) return st;
+    if (!eps_ok(eps)) return BITNET_ERR_VALUE;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!out || !x || !w_packed || !scale_wt) return BITNET_ERR_NULL;
+    const size_t need = bitnet_linear_rms_workspace_bytes(M, K);
+    if (workspace == nullptr || workspace_bytes < need) return BITNET_ERR_WORKSPACE;
+    if (bitnet_status st = check_device()) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (gemv_rms_fusable(M, K, x, w_packed, gain))
+        return launched(launch_gemv_fused_rms(out, nullptr, x, gain, eps, w_packed, scale_wt, M, N, K, s));
+    int8_t* x_int8 = static_cast<int8_t*>(workspace);
+    uint16_t* scale_act = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + round256((size_t)M * K));
+    if (hipError_t e = launch_quantize_rms(x_int8, scale_act, nullptr, x, gain, eps, M, K, s)) return launched(e);
+    return launched(launch_gemm(out, nullptr, x_int8, w_packed, scale_act, scale_wt, M, N, K, s));
 }
 
 BITNET_API bitnet_status bitnet_w8a16_gemv(float* y, const uint16_t* x, const int8_t* q, const float* scale,

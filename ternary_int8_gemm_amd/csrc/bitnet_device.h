@@ -79,6 +79,76 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
            __builtin_amdgcn_readlane(v, 48);
 }
 
+template <int CTRL>
+__device__ __forceinline__ double dpp_mov_f64(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)dpp_mov<CTRL>((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)dpp_mov<CTRL>((int)(uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the whole wave in double, in a fixed order; the result is wave-uniform.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v += dpp_mov_f64<DPP_QUAD_XOR1>(v);
+    v += dpp_mov_f64<DPP_QUAD_XOR2>(v);
+    v += dpp_mov_f64<DPP_ROW_HALF_MIRROR>(v);
+    v += dpp_mov_f64<DPP_ROW_MIRROR>(v);
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// ----------------------------------------------------------------- RMSNorm
+//
+// RMSNorm before the quantisation (F.rms_norm over the row, as the BitNet
+// activation_norm_quant function of "kyegomez/BitNet issue #77" applies it),
+// computed as torch computes it on bf16 input, in fp32:
+//   mean = fp32( sum_k x_k^2 / K )     (squares exact, summed in double)
+//   r    = fp32( 1 / fp32( sqrt( fp32(mean + eps) ) ) )
+//   xn_k = bf16_rne( fp32( fp32(x_k * r) * g_k ) )
+// The square root and the division are the correctly rounded IEEE operations
+// (hipcc's default lowering of sqrtf and of '/').
+
+__device__ __forceinline__ float rms_inv(double sum_sq, int K, float eps) {
+    const float mean = (float)(sum_sq / (double)K);
+    const float v = mean + eps;
+    return 1.0f / __builtin_sqrtf(v);
+}
+
+// Sum of the squares of the eight bf16 values of a 16-byte group, in double.
+__device__ __forceinline__ double sum_sq_bf16x8(const uint4& v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const double a = (double)bf16_to_f32(w[i] & 0xFFFFu);
+        const double b = (double)bf16_to_f32(w[i] >> 16);
+        s += a * a;
+        s += b * b;
+    }
+    return s;
+}
+
+// Two normalised bf16 values from two bf16 inputs and their two bf16 gains.
+__device__ __forceinline__ uint32_t rms_apply_bf16x2(uint32_t xw, uint32_t gw, float r) {
+    const float t0 = (bf16_to_f32(xw & 0xFFFFu) * r) * bf16_to_f32(gw & 0xFFFFu);
+    const float t1 = (bf16_to_f32(xw >> 16) * r) * bf16_to_f32(gw >> 16);
+    return (uint32_t)f32_to_bf16(t0) | ((uint32_t)f32_to_bf16(t1) << 16);
+}
+
+__device__ __forceinline__ uint4 rms_apply_bf16x8(const uint4& x, const uint4& g, float r) {
+    return make_uint4(rms_apply_bf16x2(x.x, g.x, r), rms_apply_bf16x2(x.y, g.y, r), rms_apply_bf16x2(x.z, g.z, r),
+                      rms_apply_bf16x2(x.w, g.w, r));
+}
+
+// bf16 1.0 in both halves: the gain used when there is none (x * 1 is exact).
+constexpr uint32_t BF16X2_ONE = 0x3F803F80u;
+
 // ----------------------------------------------------------------- quantisation
 
 // |x| of a bf16 value as an unsigned integer: for non-NaN inputs the order of

@@ -34,6 +34,13 @@
 //  * Reduction.  A row's eight partial sums are combined with three DPP adds
 //    (quad_perm xor 1, quad_perm xor 2, row_half_mirror); the epilogue is fused.
 //
+// With RMS (the fused RMSNorm prologue of "kyegomez/BitNet issue #77"'s
+// activation_norm_quant), every workgroup first normalises its activation rows:
+// the exact squares are summed in double (per thread, then per wave with DPP,
+// then the four waves in a fixed order through LDS), and each thread turns its
+// bf16 words into the normalised bf16 values before the absmax and quantisation
+// above.  The weight loads are already in flight meanwhile.
+//
 // gemv_chunked_kernel (longer activations): each wave owns 8*RB rows and K is
 // processed in LDS-sized chunks, with the same unpack and reduction.
 //
@@ -248,13 +255,14 @@ __device__ __forceinline__ void dot_piece_padded(const uint4& wv, const uint8_t*
     }
 }
 
-template <int MT, int D, int XW, bool OUT_I32>
+template <int MT, int D, int XW, bool OUT_I32, bool RMS>
 __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
                                                           uint16_t* __restrict__ sa_out,
                                                           const uint16_t* __restrict__ x,
                                                           const uint8_t* __restrict__ w,
                                                           const uint16_t* __restrict__ sw, int M, int N, int K,
-                                                          int steps, int units, int upb) {
+                                                          int steps, int units, int upb,
+                                                          const uint16_t* __restrict__ gain, float eps) {
     constexpr int WAVES = 4;
     constexpr int NT = WAVES * 64;
     extern __shared__ __align__(16) uint8_t lds_x[];  // [MT][steps * 8 segments of GV_SEG bytes]
@@ -330,6 +338,46 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
     uint4 buf[D];
 #pragma unroll
     for (int i = 0; i < D; ++i) issue(buf[i]);
+
+    // ---- RMSNorm of the activation rows, in registers
+    if constexpr (RMS) {
+        __shared__ double red_d[WAVES][MT];
+        double ss[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) ss[m] = 0.0;
+        uint4 gr[XW][2];
+#pragma unroll
+        for (int i = 0; i < XW; ++i) {
+            const double t = sum_sq_bf16x8(xr[i][0]) + sum_sq_bf16x8(xr[i][1]);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) ss[m] += (xm[i] == m) ? t : 0.0;
+            const bool live = gain != nullptr && xm[i] < M && xm[i] < MT && xw[i] * 16 < K;
+            if (live) {
+                const uint4* src = reinterpret_cast<const uint4*>(gain + xw[i] * 16);
+                gr[i][0] = src[0];
+                gr[i][1] = src[1];
+            } else {
+                gr[i][0] = gr[i][1] = make_uint4(BF16X2_ONE, BF16X2_ONE, BF16X2_ONE, BF16X2_ONE);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const double v = wave_sum_f64(ss[m]);
+            if (lane == 0) red_d[wave][m] = v;
+        }
+        __syncthreads();
+        float rr[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) rr[m] = rms_inv(((red_d[0][m] + red_d[1][m]) + red_d[2][m]) + red_d[3][m], K, eps);
+#pragma unroll
+        for (int i = 0; i < XW; ++i) {
+            float r = rr[0];
+#pragma unroll
+            for (int m = 1; m < MT; ++m) r = (xm[i] == m) ? rr[m] : r;
+            xr[i][0] = rms_apply_bf16x8(xr[i][0], gr[i][0], r);  // zero words stay zero
+            xr[i][1] = rms_apply_bf16x8(xr[i][1], gr[i][1], r);
+        }
+    }
 
     // ---- absmax of every activation row over the block
     uint32_t am[MT];
@@ -706,28 +754,29 @@ __global__ __launch_bounds__(64) void gemv_fused_plain(uint16_t* __restrict__ ou
 // over, never more than there are 4-wave groups of units.
 constexpr int GV_STREAM_MAX_BLOCKS = 512;
 
-template <int MT, int D, bool OUT_I32>
+template <int MT, int D, bool OUT_I32, bool RMS>
 hipError_t launch_stream_xw(int xw, dim3 grid, size_t lds, hipStream_t s, uint16_t* out, int32_t* acc, uint16_t* sa_out,
                             const uint16_t* x, const uint8_t* w, const uint16_t* sw, int M, int N, int K, int steps,
-                            int units, int upb) {
+                            int units, int upb, const uint16_t* gain, float eps) {
     if (xw <= 1)
-        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 1, OUT_I32>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
-                           sw, M, N, K, steps, units, upb);
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 1, OUT_I32, RMS>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
+                           sw, M, N, K, steps, units, upb, gain, eps);
     else if (xw <= 2)
-        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 2, OUT_I32>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
-                           sw, M, N, K, steps, units, upb);
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 2, OUT_I32, RMS>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
+                           sw, M, N, K, steps, units, upb, gain, eps);
     else if (xw <= 4)
-        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 4, OUT_I32>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
-                           sw, M, N, K, steps, units, upb);
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 4, OUT_I32, RMS>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
+                           sw, M, N, K, steps, units, upb, gain, eps);
     else
-        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 8, OUT_I32>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
-                           sw, M, N, K, steps, units, upb);
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 8, OUT_I32, RMS>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
+                           sw, M, N, K, steps, units, upb, gain, eps);
     return hipGetLastError();
 }
 
-template <int MT, bool OUT_I32>
+template <int MT, bool OUT_I32, bool RMS = false>
 hipError_t launch_stream(uint16_t* out, int32_t* acc, uint16_t* sa_out, const uint16_t* x, const uint8_t* w,
-                         const uint16_t* sw, int M, int N, int K, hipStream_t s) {
+                         const uint16_t* sw, int M, int N, int K, hipStream_t s, const uint16_t* gain = nullptr,
+                         float eps = 0.0f) {
     const int steps = (K + GV_STEP - 1) / GV_STEP;
     const int units = (N + 7) / 8;
     // At most 32 units (256 rows, one weight scale per thread) per workgroup;
@@ -744,10 +793,10 @@ hipError_t launch_stream(uint16_t* out, int32_t* acc, uint16_t* sa_out, const ui
     constexpr int D_SHORT = MT >= 8 ? 4 : 8;
     constexpr int D_LONG = MT == 1 ? 16 : D_SHORT;
     if (steps >= 12)
-        return launch_stream_xw<MT, D_LONG, OUT_I32>(xw, dim3(blocks), lds, s, out, acc, sa_out, x, w, sw, M, N, K,
-                                                     steps, units, upb);
-    return launch_stream_xw<MT, D_SHORT, OUT_I32>(xw, dim3(blocks), lds, s, out, acc, sa_out, x, w, sw, M, N, K, steps,
-                                                  units, upb);
+        return launch_stream_xw<MT, D_LONG, OUT_I32, RMS>(xw, dim3(blocks), lds, s, out, acc, sa_out, x, w, sw, M, N, K,
+                                                     steps, units, upb, gain, eps);
+    return launch_stream_xw<MT, D_SHORT, OUT_I32, RMS>(xw, dim3(blocks), lds, s, out, acc, sa_out, x, w, sw, M, N, K, steps,
+                                                  units, upb, gain, eps);
 }
 
 template <int MT, bool OUT_I32>
@@ -798,6 +847,31 @@ hipError_t launch_gemv_fused(uint16_t* out, int32_t* acc, uint16_t* scale_act_ou
     if (M <= 0 || N <= 0) return hipSuccess;
     if (acc != nullptr) return dispatch<true>(nullptr, acc, scale_act_out, x, w, scale_wt, (int)M, (int)N, (int)K, s);
     return dispatch<false>(out, nullptr, scale_act_out, x, w, scale_wt, (int)M, (int)N, (int)K, s);
+}
+
+// The fused RMSNorm prologue exists for the streaming kernel at 1, 2 and 4
+// (padded) activation rows; other shapes take RMSNorm-quantise + GEMM.
+bool gemv_rms_fusable(int64_t M, int64_t K, const void* x, const void* w, const void* gain) {
+    if (M < 1 || M > 4 || K % 64 != 0 || !aligned16(x) || !aligned16(w) || (gain != nullptr && !aligned16(gain)))
+        return false;
+    const int64_t mt = M == 1 ? 1 : (M == 2 ? 2 : 4);
+    const int64_t kpad = (K + GV_STEP - 1) / GV_STEP * GV_STEP;
+    return mt * kpad <= GV_LDS_BUDGET;
+}
+
+hipError_t launch_gemv_fused_rms(uint16_t* out, uint16_t* scale_act_out, const uint16_t* x, const uint16_t* gain,
+                                 float eps, const uint8_t* w, const uint16_t* scale_wt, int64_t M, int64_t N,
+                                 int64_t K, hipStream_t s) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    if (!gemv_rms_fusable(M, K, x, w, gain)) return hipErrorInvalidValue;
+    if (M == 1)
+        return launch_stream<1, false, true>(out, nullptr, scale_act_out, x, w, scale_wt, (int)M, (int)N, (int)K, s,
+                                             gain, eps);
+    if (M == 2)
+        return launch_stream<2, false, true>(out, nullptr, scale_act_out, x, w, scale_wt, (int)M, (int)N, (int)K, s,
+                                             gain, eps);
+    return launch_stream<4, false, true>(out, nullptr, scale_act_out, x, w, scale_wt, (int)M, (int)N, (int)K, s, gain,
+                                         eps);
 }
 
 }  // namespace bitnet

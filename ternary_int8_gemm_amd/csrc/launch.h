@@ -31,6 +31,18 @@ hipError_t launch_quantize_f32(int8_t* q, uint16_t* scale, const float* x, int64
 // In place: out[m][n] = bf16(fp32(out[m][n]) + fp32(bias[n])).
 hipError_t launch_add_bias(uint16_t* out, const uint16_t* bias, int64_t M, int64_t N, hipStream_t s);
 
+// Fused decode GEMV with the RMSNorm prologue (1 <= M <= 4, K % 64 == 0,
+// aligned operands, activations within the LDS budget: gemv_rms_fusable).
+bool gemv_rms_fusable(int64_t M, int64_t K, const void* x, const void* w, const void* gain);
+hipError_t launch_gemv_fused_rms(uint16_t* out, uint16_t* scale_act_out, const uint16_t* x, const uint16_t* gain,
+                                 float eps, const uint8_t* w, const uint16_t* scale_wt, int64_t M, int64_t N,
+                                 int64_t K, hipStream_t s);
+
+// RMSNorm over each row of bf16 x [M][K] (optional bf16 gain [K]), then the
+// per-token quantisation of the normalised row; xn (optional) receives it.
+hipError_t launch_quantize_rms(int8_t* q, uint16_t* scale, uint16_t* xn, const uint16_t* x, const uint16_t* gain,
+                               float eps, int64_t M, int64_t K, hipStream_t s);
+
 // INT8 weight-only matmul: y [M][N] (fp32) = scale[n] * sum_k x[m][k] * q[n][k],
 // x bf16 [M][K] (M <= 64), q int8 [N][K], scale fp32 [N].
 hipError_t launch_w8a16(float* y, const uint16_t* x, const int8_t* q, const float* scale, int64_t M, int64_t N,

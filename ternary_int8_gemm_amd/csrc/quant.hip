@@ -16,6 +16,13 @@
 //  * quantize_rows_vec (longer rows, K % 16 == 0): two passes over the row, the
 //    second re-reading it from L2.
 //  * quantize_rows_plain: any K and alignment, one element per lane.
+//
+// RMSNorm variants (the RMS flag of quantize_rows_reg, and
+// quantize_rows_rms_plain) normalise the row first, as the BitNet
+// activation_norm_quant of "kyegomez/BitNet issue #77" does before quantising:
+// the wave sums the exact squares of its row in double, every lane forms the
+// normalised bf16 values of its registers (fp32 x * r, times the gain), and
+// the absmax and quantisation then run on those values.
 #include "bitnet_device.h"
 #include "launch.h"
 
@@ -62,10 +69,14 @@ __global__ __launch_bounds__(256) void quantize_rows_vec(int8_t* __restrict__ q,
 
 // Register-resident path: lane l holds the 8-element groups g = c * 64 + l
 // (c < CH) of its row.  Needs K % 8 == 0, K <= 512 * CH, 16-byte aligned x rows
-// and 8-byte aligned q rows.
-template <int CH>
+// (and gain, xn_out) and 8-byte aligned q rows.  With RMS, xn_out (when not
+// NULL) receives the normalised bf16 row.
+template <int CH, bool RMS>
 __global__ __launch_bounds__(256) void quantize_rows_reg(int8_t* __restrict__ q, uint16_t* __restrict__ scale,
-                                                         const uint16_t* __restrict__ x, int64_t M, int64_t K) {
+                                                         uint16_t* __restrict__ xn_out,
+                                                         const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ gain, float eps, int64_t M,
+                                                         int64_t K) {
     const int lane = threadIdx.x & 63;
     const int64_t m = (int64_t)blockIdx.x * QUANT_ROWS_PER_BLOCK + (threadIdx.x >> 6);
     if (m >= M) return;  // wave-uniform
@@ -76,6 +87,28 @@ __global__ __launch_bounds__(256) void quantize_rows_reg(int8_t* __restrict__ q,
     for (int c = 0; c < CH; ++c) {
         const int g = c * 64 + lane;
         v[c] = g < groups ? xv[g] : make_uint4(0u, 0u, 0u, 0u);  // zeros do not change the absmax
+    }
+    if constexpr (RMS) {
+        double ss = 0.0;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) ss += sum_sq_bf16x8(v[c]);
+        const float r = rms_inv(wave_sum_f64(ss), (int)K, eps);
+        // the gain row is shared by every row (cached); it is read only now,
+        // so that it does not hold registers across the reduction
+        const uint4* gv = reinterpret_cast<const uint4*>(gain);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int g = c * 64 + lane;
+            const uint4 gw = (gain != nullptr && g < groups) ? gv[g]
+                                                             : make_uint4(BF16X2_ONE, BF16X2_ONE, BF16X2_ONE, BF16X2_ONE);
+            v[c] = rms_apply_bf16x8(v[c], gw, r);  // zero padding stays zero
+        }
+        if (xn_out != nullptr) {
+            uint4* xo = reinterpret_cast<uint4*>(xn_out + m * K);
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                if (c * 64 + lane < groups) xo[c * 64 + lane] = v[c];
+        }
     }
     uint32_t amax = 0;
 #pragma unroll
@@ -112,6 +145,41 @@ __global__ __launch_bounds__(256) void quantize_rows_plain(int8_t* __restrict__ 
     if (lane == 0) scale[m] = f32_to_bf16(qs.s);
     int8_t* qr = q + m * K;
     for (int64_t k = lane; k < K; k += 64) qr[k] = (int8_t)quantize_one(bf16_to_f32(xr[k]), qs);
+}
+
+// RMSNorm then quantise, any K and alignment: the sum of squares, then the
+// absmax of the normalised values, then the quantisation (each recomputing the
+// normalised element, which is a pure function of x, r and the gain).
+__global__ __launch_bounds__(256) void quantize_rows_rms_plain(int8_t* __restrict__ q, uint16_t* __restrict__ scale,
+                                                               uint16_t* __restrict__ xn_out,
+                                                               const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ gain, float eps,
+                                                               int64_t M, int64_t K) {
+    const int lane = threadIdx.x & 63;
+    const int64_t m = (int64_t)blockIdx.x * QUANT_ROWS_PER_BLOCK + (threadIdx.x >> 6);
+    if (m >= M) return;
+    const uint16_t* xr = x + m * K;
+    double ss = 0.0;
+    for (int64_t k = lane; k < K; k += 64) {
+        const double d = (double)bf16_to_f32(xr[k]);
+        ss += d * d;
+    }
+    const float r = rms_inv(wave_sum_f64(ss), (int)K, eps);
+    auto norm = [&](int64_t k) -> uint32_t {
+        const uint32_t g = gain != nullptr ? (uint32_t)gain[k] : 0x3F80u;
+        return rms_apply_bf16x2((uint32_t)xr[k], g, r) & 0xFFFFu;
+    };
+    uint32_t amax = 0;
+    for (int64_t k = lane; k < K; k += 64) amax = max(amax, norm(k) & 0x7FFFu);
+    amax = wave_max_u32(amax);
+    const QuantScale qs = quant_scale(amax);
+    if (lane == 0) scale[m] = f32_to_bf16(qs.s);
+    int8_t* qr = q + m * K;
+    for (int64_t k = lane; k < K; k += 64) {
+        const uint32_t h = norm(k);
+        qr[k] = (int8_t)quantize_one(bf16_to_f32(h), qs);
+        if (xn_out != nullptr) xn_out[m * K + k] = (uint16_t)h;
+    }
 }
 
 // ---------------------------------------------------------------- f32 input
@@ -174,31 +242,55 @@ __global__ __launch_bounds__(256) void quantize_rows_f32_plain(int8_t* __restric
 
 }  // namespace
 
+namespace {
+
+template <bool RMS>
+void launch_rows_reg(int64_t ch, dim3 grid, hipStream_t s, int8_t* q, uint16_t* scale, uint16_t* xn,
+                     const uint16_t* x, const uint16_t* gain, float eps, int64_t M, int64_t K) {
+    const dim3 block(256);
+    if (ch <= 2)
+        hipLaunchKernelGGL((quantize_rows_reg<2, RMS>), grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
+    else if (ch <= 4)
+        hipLaunchKernelGGL((quantize_rows_reg<4, RMS>), grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
+    else if (ch <= 8)
+        hipLaunchKernelGGL((quantize_rows_reg<8, RMS>), grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
+    else if (ch <= 12)
+        hipLaunchKernelGGL((quantize_rows_reg<12, RMS>), grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
+    else if (ch <= 16)
+        hipLaunchKernelGGL((quantize_rows_reg<16, RMS>), grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
+    else if (ch <= 24)
+        hipLaunchKernelGGL((quantize_rows_reg<24, RMS>), grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
+    else
+        hipLaunchKernelGGL((quantize_rows_reg<32, RMS>), grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
+}
+
+}  // namespace
+
 hipError_t launch_quantize(int8_t* q, uint16_t* scale, const uint16_t* x, int64_t M, int64_t K, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     const int64_t blocks = (M + QUANT_ROWS_PER_BLOCK - 1) / QUANT_ROWS_PER_BLOCK;
     const dim3 grid((unsigned)blocks), block(256);
     if (K % 8 == 0 && aligned16(x) && reinterpret_cast<uintptr_t>(q) % 8 == 0 && K <= 512 * 32) {
-        const int64_t ch = (K / 8 + 63) / 64;  // 16-byte groups per lane
-        if (ch <= 2)
-            hipLaunchKernelGGL(quantize_rows_reg<2>, grid, block, 0, s, q, scale, x, M, K);
-        else if (ch <= 4)
-            hipLaunchKernelGGL(quantize_rows_reg<4>, grid, block, 0, s, q, scale, x, M, K);
-        else if (ch <= 8)
-            hipLaunchKernelGGL(quantize_rows_reg<8>, grid, block, 0, s, q, scale, x, M, K);
-        else if (ch <= 12)
-            hipLaunchKernelGGL(quantize_rows_reg<12>, grid, block, 0, s, q, scale, x, M, K);
-        else if (ch <= 16)
-            hipLaunchKernelGGL(quantize_rows_reg<16>, grid, block, 0, s, q, scale, x, M, K);
-        else if (ch <= 24)
-            hipLaunchKernelGGL(quantize_rows_reg<24>, grid, block, 0, s, q, scale, x, M, K);
-        else
-            hipLaunchKernelGGL(quantize_rows_reg<32>, grid, block, 0, s, q, scale, x, M, K);
+        launch_rows_reg<false>((K / 8 + 63) / 64, grid, s, q, scale, nullptr, x, nullptr, 0.0f, M, K);
     } else if (K % 16 == 0 && aligned16(x) && aligned16(q)) {
         hipLaunchKernelGGL(quantize_rows_vec, grid, block, 0, s, q, scale, x, M, K);
     } else {
         hipLaunchKernelGGL(quantize_rows_plain, grid, block, 0, s, q, scale, x, M, K);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_rms(int8_t* q, uint16_t* scale, uint16_t* xn, const uint16_t* x, const uint16_t* gain,
+                               float eps, int64_t M, int64_t K, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    const int64_t blocks = (M + QUANT_ROWS_PER_BLOCK - 1) / QUANT_ROWS_PER_BLOCK;
+    const dim3 grid((unsigned)blocks), block(256);
+    const bool vec = K % 8 == 0 && K <= 512 * 32 && aligned16(x) && (gain == nullptr || aligned16(gain)) &&
+                     (xn == nullptr || aligned16(xn)) && reinterpret_cast<uintptr_t>(q) % 8 == 0;
+    if (vec)
+        launch_rows_reg<true>((K / 8 + 63) / 64, grid, s, q, scale, xn, x, gain, eps, M, K);
+    else
+        hipLaunchKernelGGL(quantize_rows_rms_plain, grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
     return hipGetLastError();
 }
 

@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
                      "bitnet_linear", "bitnet_gemm_i32", "bitnet_gemv_fused_i32", "bitnet_scale_epilogue",
                      "bitnet_linear_workspace_bytes", "bitnet_status_string", "bitnet_version",
                      "bitnet_quantize_act_f32", "bitnet_linear_ex", "bitnet_linear_ex_workspace_bytes",
-                     "bitnet_w8a16_gemv"]:
+                     "bitnet_w8a16_gemv", "bitnet_rmsnorm_quantize", "bitnet_linear_rms",
+                     "bitnet_linear_rms_workspace_bytes"]:
         assert required in names
 
 
@@ -107,6 +108,18 @@ def test_shape_errors_precede_device_use():
     assert lib.bitnet_w8a16_gemv(d, d, d, d, 4, 8, 131072 + 1, None) == 2   # K > MAX_K
     assert lib.bitnet_w8a16_gemv(d, d, d, d, 0, 8, 64, None) == 0            # M == 0: no-op
     assert lib.bitnet_w8a16_gemv(d, None, d, d, 4, 8, 64, None) == 1
+    nan, inf = float("nan"), float("inf")
+    assert lib.bitnet_rmsnorm_quantize(d, d, None, d, None, -1e-6, 4, 64, None) == 3     # eps < 0
+    assert lib.bitnet_rmsnorm_quantize(d, d, None, d, None, nan, 4, 64, None) == 3       # eps NaN
+    assert lib.bitnet_rmsnorm_quantize(d, d, None, d, None, inf, 4, 64, None) == 3       # eps inf
+    assert lib.bitnet_rmsnorm_quantize(d, d, None, d, None, 1e-5, 4, 62, None) == 2      # K % 4
+    assert lib.bitnet_rmsnorm_quantize(d, None, None, d, None, 1e-5, 4, 64, None) == 1
+    assert lib.bitnet_rmsnorm_quantize(d, d, None, d, None, 1e-5, 0, 64, None) == 0      # M == 0: no-op
+    assert lib.bitnet_linear_rms(d, d, None, 1e-5, d, d, 1, 8, 64, None, 0, None) == 4   # always needs it
+    assert lib.bitnet_linear_rms(d, d, None, 1e-5, d, d, 1, 8, 64, d, 100, None) == 4    # too small
+    assert lib.bitnet_linear_rms(d, d, None, -1.0, d, d, 1, 8, 64, d, 1 << 20, None) == 3
+    assert lib.bitnet_linear_rms(None, d, None, 1e-5, d, d, 1, 8, 64, d, 1 << 20, None) == 1
+    assert lib.bitnet_linear_rms(d, d, None, 1e-5, d, d, 1, 0, 64, None, 0, None) == 0   # N == 0: no-op
 
 
 def test_workspace_size():
@@ -120,6 +133,14 @@ def test_workspace_size():
     assert tg.linear_ex_workspace_bytes(16, 4096, torch.float32) == 16 * 4096 + 256
     assert tg.linear_ex_workspace_bytes(3, 2560, torch.bfloat16) == 0
     assert tg.load_library().bitnet_linear_ex_workspace_bytes(4, 64, 9) == 0
+
+
+def test_rms_workspace_size():
+    lib = tg.load_library()
+    assert lib.bitnet_linear_rms_workspace_bytes(1, 2560) == 2560 + 256
+    assert lib.bitnet_linear_rms_workspace_bytes(3, 100) == 512 + 256
+    assert lib.bitnet_linear_rms_workspace_bytes(16, 4096) == 16 * 4096 + 256
+    assert lib.bitnet_linear_rms_workspace_bytes(4, 62) == 0
 
 
 def test_status_strings():

@@ -445,3 +445,90 @@ def test_w8a16_shape_errors():
     with pytest.raises(RuntimeError):
         tg.w8a16_gemv(x, q, s)                      # M > 64
     assert tg.w8a16_gemv(x[:0], q, s).shape == (0, 8)
+
+
+# ----------------------------------------------------------------------------- RMSNorm + quantise
+
+def rms_references(x, gain, eps):
+    """The oracle's result and, for rows whose fp32 mean a different double
+    summation order could round the other way, the result with that other mean."""
+    ref = oracle.rmsnorm_quantize(x, gain, eps)
+    alt = ref
+    if ref["ambiguous"].any():
+        alt = oracle.rmsnorm_quantize(x, gain, eps, means=ref["mean_alt"])
+    return ref, alt
+
+
+def rows_match(got, ref, alt, amb):
+    """Per row: equal to the oracle's row, or (ambiguous rows only) to the alternative."""
+    got = got.reshape(got.shape[0], -1)
+    ok = np.all(got == ref.reshape(got.shape), axis=1)
+    ok_alt = np.all(got == alt.reshape(got.shape), axis=1) & amb
+    return ok | ok_alt
+
+
+def check_rms_quantize(x, gain, eps, q, sa, xn, what):
+    ref, alt = rms_references(x, gain, eps)
+    amb = ref["ambiguous"]
+    for name, got in (("x_norm", host_bf16(xn)), ("q", q.cpu().numpy()), ("scale_act", host_bf16(sa)[:, None])):
+        want = ref["xn"] if name == "x_norm" else (ref["q"] if name == "q" else ref["scale_act"][:, None])
+        want_alt = alt["xn"] if name == "x_norm" else (alt["q"] if name == "q" else alt["scale_act"][:, None])
+        ok = rows_match(got, want, want_alt, amb)
+        assert ok.all(), f"{what} {name}: rows {np.nonzero(~ok)[0][:8].tolist()} differ (ambiguous rows: {int(amb.sum())})"
+
+
+RMS_QUANT_SHAPES = [(1, 2560), (4, 6912), (16, 4096), (33, 11008), (5, 100), (3, 20000), (2049, 2560), (7, 8)]
+
+
+@pytest.mark.parametrize("with_gain", [False, True])
+@pytest.mark.parametrize("M,K", RMS_QUANT_SHAPES)
+def test_rmsnorm_quantize_parity(M, K, with_gain):
+    x = synth.activations_bf16(M, K, seed=8000 + M + K, outlier_frac=0.01)
+    if M > 2:
+        x[1, :] = 0                                          # zero row: eps alone
+        x[2, :] = synth.activations_bf16(1, K, seed=8001)[0] & np.uint16(0x83FF)   # tiny magnitudes
+    gain = synth.row_scales_bf16(K, seed=8002 + K, lo=0.25, hi=2.0) if with_gain else None
+    eps = 1e-5 if with_gain else oracle.FP32_EPS
+    xn = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    q, sa = tg.rmsnorm_quantize(dev_bf16(x), None if gain is None else dev_bf16(gain), eps, x_norm=xn)
+    check_rms_quantize(x, gain, eps, q, sa, xn, f"rmsnorm_quantize {M}x{K} gain={with_gain}")
+
+
+def test_rmsnorm_quantize_misaligned_plain_path():
+    M, K = 5, 1024
+    x = synth.activations_bf16(M, K, seed=8100)
+    gain = synth.row_scales_bf16(K, seed=8101, lo=0.5, hi=1.5)
+    xn = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    q, sa = tg.rmsnorm_quantize(misaligned(dev_bf16(x)), misaligned(dev_bf16(gain)), 1e-6, x_norm=xn)
+    check_rms_quantize(x, gain, 1e-6, q, sa, xn, "rmsnorm_quantize misaligned")
+
+
+@pytest.mark.parametrize("with_gain", [False, True])
+@pytest.mark.parametrize("M,N,K", [(1, 3840, 2560), (2, 2560, 6912), (3, 130, 4096), (4, 13824, 2560), (1, 100, 1024),
+                                   (5, 300, 2560), (16, 4096, 4096), (64, 1000, 1024), (300, 257, 512), (2, 33, 68)])
+def test_linear_rms_parity(M, N, K, with_gain):
+    x = synth.activations_bf16(M, K, seed=8200 + M + N + K)
+    W = synth.ternary_weights(N, K, seed=8300 + M)
+    P = oracle.pack(W)
+    sw = synth.row_scales_bf16(N, seed=8400 + M)
+    gain = synth.row_scales_bf16(K, seed=8500 + K, lo=0.5, hi=1.5) if with_gain else None
+    eps = oracle.FP32_EPS
+    ref = oracle.linear_rms(x, P, sw, gain, eps)
+    alt = oracle.linear_rms(x, P, sw, gain, eps, means=ref["mean_alt"]) if ref["ambiguous"].any() else ref
+    out = tg.bitnet_linear_rms(dev_bf16(x), dev(P), dev_bf16(sw), None if gain is None else dev_bf16(gain), eps)
+    ok = rows_match(host_bf16(out), ref["out"], alt["out"], ref["ambiguous"])
+    assert ok.all(), f"linear_rms {M}x{N}x{K}: rows {np.nonzero(~ok)[0][:8].tolist()} differ"
+
+
+def test_linear_rms_fused_equals_split_on_unambiguous_rows():
+    M, N, K = 4, 4096, 2560
+    x = synth.activations_bf16(M, K, seed=8600)
+    W = synth.ternary_weights(N, K, seed=8601)
+    Pd, swd = dev(oracle.pack(W)), dev_bf16(synth.row_scales_bf16(N, seed=8602))
+    xd = dev_bf16(x)
+    fused = tg.bitnet_linear_rms(xd, Pd, swd)                 # fused decode GEMV with the prologue
+    q, sa = tg.rmsnorm_quantize(xd)
+    split = tg.bitnet_gemm(q, Pd, sa, swd)
+    amb = oracle.rmsnorm_quantize(x)["ambiguous"]
+    same = np.all(host_bf16(fused) == host_bf16(split), axis=1)
+    assert np.all(same | amb)
