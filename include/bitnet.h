@@ -110,16 +110,19 @@ bitnet_status bitnet_gemv_fused(uint16_t* out, const uint16_t* x, const uint8_t*
 
 /*
  * Device workspace (bytes) that bitnet_linear needs for an [M][K] input:
- * 0 when M <= BITNET_FUSED_MAX_M, else room for x_int8 [M][K] and
- * scale_act [M] (each rounded up to 256 bytes).  Returns 0 for invalid sizes.
+ * 0 when it takes the fused GEMV (M <= 2, or M <= 4 with K <= 8192), else
+ * room for x_int8 [M][K] and scale_act [M] (each rounded up to 256 bytes).
+ * Returns 0 for invalid sizes.
  */
 size_t bitnet_linear_workspace_bytes(int64_t M, int64_t K);
 
 /*
  * One-shot BitLinear forward (bitnet_linear of bitnet-cpu): dispatches on M.
- * M <= BITNET_FUSED_MAX_M -> bitnet_gemv_fused; otherwise bitnet_quantize_act
- * into the workspace, then bitnet_gemm.  The result is bit-identical on both
- * paths.  out: bf16 [M][N]; x: bf16 [M][K]; w_packed: uint8 [N][K/4];
+ * bitnet-cpu sends M < 16 to its fused GEMV; here both paths give identical
+ * bits, so the choice is made for speed: bitnet_gemv_fused for M <= 2 (and for
+ * M <= 4 when K <= 8192), otherwise bitnet_quantize_act into the workspace,
+ * then bitnet_gemm (one quantisation pass is cheaper than the fused kernel's
+ * per-workgroup quantisation once there are more rows).  out: bf16 [M][N]; x: bf16 [M][K]; w_packed: uint8 [N][K/4];
  * scale_wt: bf16 [N]; workspace: device memory of workspace_bytes bytes, 256-byte
  * aligned, used as scratch (may be NULL when bitnet_linear_workspace_bytes is 0).
  * Errors: workspace_bytes too small -> WORKSPACE.

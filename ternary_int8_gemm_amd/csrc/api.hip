@@ -144,9 +144,23 @@ BITNET_API bitnet_status bitnet_gemv_fused_i32(int32_t* acc, uint16_t* scale_act
     return launched(launch_gemv_fused(nullptr, acc, scale_act, x, w_packed, nullptr, M, N, K, (hipStream_t)stream));
 }
 
+// Which path bitnet_linear takes.  Both give the same bits; the fused GEMV
+// quantises the activations in every workgroup, which is cheapest for one or
+// two rows (or up to four that fit its LDS budget), while from there on one
+// quantisation pass plus the GEMM is faster (measured on the BitNet-2B-4T and
+// LLaMA-7B projection shapes).
+// Longest K for which three or four rows stay on the fused GEMV (its streaming
+// kernel holds 4 x K int8 activations in 32 KB of LDS).
+constexpr int64_t LINEAR_FUSED_K_MAX_M4 = 8192;
+
+static bool linear_takes_fused(int64_t M, int64_t K) {
+    if (M <= 2) return true;
+    return M <= 4 && K <= LINEAR_FUSED_K_MAX_M4;
+}
+
 BITNET_API size_t bitnet_linear_workspace_bytes(int64_t M, int64_t K) {
     if (M < 0 || K <= 0 || K % 4 != 0 || K > BITNET_MAX_K || !sizes_ok(M, 0)) return 0;
-    if (M <= BITNET_FUSED_MAX_M) return 0;
+    if (linear_takes_fused(M, K)) return 0;
     return round256((size_t)M * (size_t)K) + round256((size_t)M * 2);
 }
 
@@ -156,7 +170,7 @@ BITNET_API bitnet_status bitnet_linear(uint16_t* out, const uint16_t* x, const u
     if (!sizes_ok(M, N)) return BITNET_ERR_SHAPE;
     if (bitnet_status st = check_k(K)) return st;
     if (M == 0 || N == 0) return BITNET_OK;
-    if (M <= BITNET_FUSED_MAX_M) return bitnet_gemv_fused(out, x, w_packed, scale_wt, M, N, K, stream);
+    if (linear_takes_fused(M, K)) return bitnet_gemv_fused(out, x, w_packed, scale_wt, M, N, K, stream);
     if (!out || !x || !w_packed || !scale_wt) return BITNET_ERR_NULL;
     const size_t need = bitnet_linear_workspace_bytes(M, K);
     if (workspace == nullptr || workspace_bytes < need) return BITNET_ERR_WORKSPACE;

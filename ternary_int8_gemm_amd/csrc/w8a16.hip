@@ -45,7 +45,12 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int WQ_CHUNK = 64;  // K elements per chunk (four MFMA k-steps of 16)
+// MFMA kernel: 16-byte weight loads per lane and chunk (4: a wave reads whole
+// 128-byte lines of its 32 rows), and the chunk ring depth for one and two
+// 32-row activation tiles.
+constexpr int W8_MFMA_NB = 4;
+constexpr int W8_MFMA_D = 2;
+constexpr int W8_MFMA_D2 = 1;
 // Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format;
 // stride 0, so bounds are checked against the byte count in word 2).
 constexpr int BUFFER_RSRC_WORD3_W8 = 0x00020000;
@@ -64,19 +69,21 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t p0, uint32_t p1) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int MT, int KW, int D>
+template <int MT, int KW, int D, int NB>
 __global__ __launch_bounds__(64 * KW) void w8a16_kernel(float* __restrict__ y, const uint16_t* __restrict__ x,
                                                         const int8_t* __restrict__ q, const float* __restrict__ scale,
                                                         int M, int N, int K) {
     constexpr int BM = 32 * MT;
     constexpr int LDC = 33;  // padded LDS row of a partial tile
+    constexpr int CK = 32 * NB;  // K elements per chunk: NB 16-byte weight loads per lane
+    constexpr int NS = 2 * NB;   // MFMA k-steps of 16 per chunk
     __shared__ float part[KW][BM * LDC];
 
     const int n0 = blockIdx.x * 32;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nc = K / WQ_CHUNK;
+    const int nc = K / CK;
     const int r = lane & 31, h = lane >> 5;
 
     // rows past M and columns past N lie past the end of their buffers: zeros
@@ -84,24 +91,25 @@ __global__ __launch_bounds__(64 * KW) void w8a16_kernel(float* __restrict__ y, c
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), (short)0, M * K * 2, BUFFER_RSRC_WORD3_W8);
     const __amdgpu_buffer_rsrc_t q_rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(q), (short)0, N * K, BUFFER_RSRC_WORD3_W8);
+    // lane half h owns the chunk's weights 16 * NB * h .. 16 * NB * (h + 1) - 1
     int a_voff[MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) a_voff[t] = ((32 * t + r) * K + 32 * h) * 2;
-    const int b_voff = (n0 + r) * K + 32 * h;
+    for (int t = 0; t < MT; ++t) a_voff[t] = ((32 * t + r) * K + 16 * NB * h) * 2;
+    const int b_voff = (n0 + r) * K + 16 * NB * h;
 
     struct Chunk {
-        v4u a[MT][4];
-        v4u b[2];
+        v4u a[MT][NS];
+        v4u b[NB];
     };
     auto load = [&](int j, Chunk& C) {
         const int c = min(wave + KW * j, nc - 1);  // clamped repeats past the end are never used
 #pragma unroll
+        for (int i = 0; i < NB; ++i) C.b[i] = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, b_voff, c * CK + 16 * i, 0);
+#pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                C.a[t][s] = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, a_voff[t], (c * WQ_CHUNK + 8 * s) * 2, 0);
-        C.b[0] = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, b_voff, c * WQ_CHUNK, 0);
-        C.b[1] = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, b_voff, c * WQ_CHUNK + 16, 0);
+            for (int s = 0; s < NS; ++s)
+                C.a[t][s] = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, a_voff[t], (c * CK + 8 * s) * 2, 0);
     };
 
     f32x16 acc[MT];
@@ -109,7 +117,7 @@ __global__ __launch_bounds__(64 * KW) void w8a16_kernel(float* __restrict__ y, c
     for (int t = 0; t < MT; ++t) acc[t] = f32x16{};
     auto compute = [&](const Chunk& C) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < NS; ++s) {
             const v4u& bw = C.b[s >> 1];
             const bf16x8 bop = (s & 1) ? i8x8_to_bf16x8(bw.z, bw.w) : i8x8_to_bf16x8(bw.x, bw.y);
 #pragma unroll
@@ -431,19 +439,27 @@ hipError_t launch_w8a16(float* y, const uint16_t* x, const int8_t* q, const floa
         return launch_w8a16_stream<2>(y, x, q, scale, (int)M, (int)N, (int)K, s);
     }
     constexpr int KW = 4;
-    const int64_t nc = K / WQ_CHUNK;
     // 32-bit buffer offsets: weights and activations below 2 GiB
-    const bool fast = K % WQ_CHUNK == 0 && nc >= KW && aligned16(x) && aligned16(q) &&
-                      (N + 31) * K < ((int64_t)1 << 31) && 64 * K * 2 < ((int64_t)1 << 31);
-    if (!fast) {
-        hipLaunchKernelGGL(w8a16_plain, dim3((unsigned)N), dim3(64), 0, s, y, x, q, scale, (int)M, (int)N, (int)K);
+    const bool fits = aligned16(x) && aligned16(q) && (N + 31) * K < ((int64_t)1 << 31) && 64 * K * 2 < ((int64_t)1 << 31);
+    const dim3 grid((unsigned)((N + 31) / 32)), block(64 * KW);
+    if (fits && K % (32 * W8_MFMA_NB) == 0 && K / (32 * W8_MFMA_NB) >= KW) {
+        // whole 128-byte weight lines per wave and chunk
+        if (M <= 32)
+            hipLaunchKernelGGL((w8a16_kernel<1, KW, W8_MFMA_D, W8_MFMA_NB>), grid, block, 0, s, y, x, q, scale, (int)M,
+                               (int)N, (int)K);
+        else
+            hipLaunchKernelGGL((w8a16_kernel<2, KW, W8_MFMA_D2, W8_MFMA_NB>), grid, block, 0, s, y, x, q, scale,
+                               (int)M, (int)N, (int)K);
         return hipGetLastError();
     }
-    const dim3 grid((unsigned)((N + 31) / 32)), block(64 * KW);
-    if (M <= 32)
-        hipLaunchKernelGGL((w8a16_kernel<1, KW, 2>), grid, block, 0, s, y, x, q, scale, (int)M, (int)N, (int)K);
-    else
-        hipLaunchKernelGGL((w8a16_kernel<2, KW, 2>), grid, block, 0, s, y, x, q, scale, (int)M, (int)N, (int)K);
+    if (fits && K % 64 == 0 && K / 64 >= KW) {
+        if (M <= 32)
+            hipLaunchKernelGGL((w8a16_kernel<1, KW, 2, 2>), grid, block, 0, s, y, x, q, scale, (int)M, (int)N, (int)K);
+        else
+            hipLaunchKernelGGL((w8a16_kernel<2, KW, 2, 2>), grid, block, 0, s, y, x, q, scale, (int)M, (int)N, (int)K);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(w8a16_plain, dim3((unsigned)N), dim3(64), 0, s, y, x, q, scale, (int)M, (int)N, (int)K);
     return hipGetLastError();
 }
 

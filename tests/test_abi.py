@@ -124,7 +124,11 @@ def test_shape_errors_precede_device_use():
 
 def test_workspace_size():
     assert tg.linear_workspace_bytes(1, 2560) == 0
-    assert tg.linear_workspace_bytes(15, 2560) == 0
+    assert tg.linear_workspace_bytes(2, 131072) == 0          # one or two rows: always the fused GEMV
+    assert tg.linear_workspace_bytes(4, 8192) == 0            # up to four rows while K <= 8192
+    assert tg.linear_workspace_bytes(4, 8196) == 33024 + 256
+    assert tg.linear_workspace_bytes(5, 2560) == 12800 + 256  # from five rows: quantise + GEMM
+    assert tg.linear_workspace_bytes(15, 2560) == 38400 + 256
     assert tg.linear_workspace_bytes(16, 4096) == 16 * 4096 + 256
     assert tg.linear_workspace_bytes(17, 100) == 1792 + 256
     assert tg.linear_workspace_bytes(17, 6) == 0   # invalid K

@@ -195,14 +195,16 @@ def test_gemv_fused_misaligned_plain_path():
 
 # ----------------------------------------------------------------------------- dispatch
 
-@pytest.mark.parametrize("M", [1, 2, 15, 16, 17, 64])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 15, 16, 17, 64])
 def test_linear_dispatch_neutral(M):
     N, K = 192, 1024
     x, W, P, sw = problem(M, N, K, seed=5000 + M, outliers=0.01, row_scales=True)
     ref = oracle.linear(x, P, sw)
     out = tg.bitnet_linear(dev_bf16(x), dev(P), dev_bf16(sw))
     assert_bf16_parity(host_bf16(out), ref["out"], f"linear M={M}")
-    if M <= tg.FUSED_MAX_M:   # the split path gives the same bits too
+    if M <= tg.FUSED_MAX_M:   # the fused GEMV and the split path give the same bits too
+        fused = tg.bitnet_gemv_fused(dev_bf16(x), dev(P), dev_bf16(sw))
+        assert np.array_equal(host_bf16(fused), host_bf16(out))
         q, sa = tg.quantize_activation(dev_bf16(x))
         out2 = tg.bitnet_gemm(q, dev(P), sa, dev_bf16(sw))
         assert np.array_equal(host_bf16(out2), host_bf16(out))
