@@ -570,6 +570,180 @@ hipError_t launch_mfma(uint16_t* out, int32_t* acc, const int8_t* x, const uint8
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- skinny kernel, LDS-staged operands
+//
+// The same split-K tiling as gemm_skinny_kernel, but each wave stages its
+// 256-element chunk of both operands through its own LDS region, so that the
+// global loads read whole row segments: the weights as 16 rows x 64 bytes and
+// the activations as 4 rows x 256 bytes per wave instruction, instead of the
+// 32 rows x 32 bytes that loading MFMA fragments directly touches.  The
+// fragments are then read from LDS (rows padded so that the reads hit distinct
+// banks) in the same k order as the direct kernel: lane (r, h), k-step s, holds
+// elements 128h + 16s .. 128h + 16s + 15 of the chunk.  The region is private
+// to the wave (LDS operations of one wave complete in order), so no barrier is
+// needed until the split-K reduction; the next chunk's global loads are in
+// flight while the current one is multiplied.
+constexpr int GS_KS = 256;            // K elements per chunk
+constexpr int GS_XROW = GS_KS + 16;   // bytes per staged activation row (padded)
+constexpr int GS_WROW = GS_KS / 4 + 16;  // bytes per staged weight row (padded)
+
+template <int MT, int NT, int KW, bool OUT_I32>
+__global__ __launch_bounds__(64 * KW) void gemm_skinny_lds_kernel(uint16_t* __restrict__ out,
+                                                                  int32_t* __restrict__ acc_out,
+                                                                  const int8_t* __restrict__ x,
+                                                                  const uint8_t* __restrict__ w,
+                                                                  const uint16_t* __restrict__ sa,
+                                                                  const uint16_t* __restrict__ sw, int M, int N, int K,
+                                                                  int tiles_n) {
+    constexpr int BM = 32 * MT, BN = 32 * NT;
+    constexpr int LDN = BN + 8;
+    constexpr int THREADS = 64 * KW;
+    constexpr int XB = BM * GS_XROW;  // staged activation bytes per wave
+    constexpr int WB = BN * GS_WROW;  // staged weight bytes per wave
+    __shared__ __align__(16) uint8_t stage[KW][XB + WB];
+    __shared__ int red[BM * LDN];
+    __shared__ int rsum[BM];
+    __shared__ float rscale[BM];
+    __shared__ float cscale[BN];
+
+    const int tm = blockIdx.x / tiles_n;
+    const int tn = blockIdx.x - tm * tiles_n;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int KB = K >> 2;
+    const int nc = K / GS_KS;
+    const int r = lane & 31, h = lane >> 5;
+
+    for (int i = tid; i < BM * LDN; i += THREADS) red[i] = 0;
+    for (int i = tid; i < BM; i += THREADS) {
+        rsum[i] = 0;
+        rscale[i] = (!OUT_I32 && m0 + i < M) ? bf16_to_f32(sa[m0 + i]) : 0.0f;
+    }
+    for (int i = tid; i < BN; i += THREADS) cscale[i] = (!OUT_I32 && n0 + i < N) ? bf16_to_f32(sw[n0 + i]) : 0.0f;
+
+    const __amdgpu_buffer_rsrc_t x_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(x), (short)0, M * K, BUFFER_RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t w_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w), (short)0, N * KB, BUFFER_RSRC_WORD3);
+    // global pieces of this lane: activation rows 4i + lane/16 (16 bytes at
+    // lane%16), weight rows 16i + lane/4 (16 bytes at lane%4); rows past M or N
+    // read zeros
+    const int xr_l = lane >> 4, xp_l = lane & 15;
+    const int wr_l = lane >> 2, wp_l = lane & 3;
+    uint8_t* const xs = stage[wave];
+    uint8_t* const ws = stage[wave] + XB;
+
+    constexpr int XI = BM / 4;   // activation load instructions per chunk
+    constexpr int WI = BN / 16;  // weight load instructions per chunk
+    v4u xg[XI], wg[WI];
+    auto load = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < XI; ++i)
+            xg[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, (m0 + 4 * i + xr_l) * K + 16 * xp_l, c * GS_KS, 0);
+#pragma unroll
+        for (int i = 0; i < WI; ++i)
+            wg[i] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, (n0 + 16 * i + wr_l) * KB + 16 * wp_l,
+                                                          c * (GS_KS / 4), 0);
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int i = 0; i < XI; ++i)
+            *reinterpret_cast<v4u*>(xs + (4 * i + xr_l) * GS_XROW + 16 * xp_l) = xg[i];
+#pragma unroll
+        for (int i = 0; i < WI; ++i)
+            *reinterpret_cast<v4u*>(ws + (16 * i + wr_l) * GS_WROW + 16 * wp_l) = wg[i];
+    };
+
+    v16i acc[MT][NT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int u = 0; u < NT; ++u) acc[t][u] = v16i{};
+    int rs[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) rs[t] = 0;
+
+    auto compute = [&]() {
+        v4u bw[NT][2];  // this lane's 32 weight bytes of each column tile (8 k-steps)
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                bw[u][i] = *reinterpret_cast<const v4u*>(ws + (32 * u + r) * GS_WROW + 32 * h + 16 * i);
+#pragma unroll
+        for (int s = 0; s < GS_KS / 32; ++s) {
+            v4i af[MT];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const v4u v = *reinterpret_cast<const v4u*>(xs + (32 * t + r) * GS_XROW + 128 * h + 16 * s);
+                const uint4 tt = transpose4x4(v.x, v.y, v.z, v.w);
+                af[t] = v4i{(int)tt.x, (int)tt.y, (int)tt.z, (int)tt.w};
+                int sum = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, rs[t], false);
+                sum = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, sum, false);
+                sum = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, sum, false);
+                rs[t] = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, sum, false);
+            }
+#pragma unroll
+            for (int u = 0; u < NT; ++u) {
+                const uint32_t p = bw[u][s >> 2][s & 3];
+                const v4i bf = {(int)(p & CODE_MASK), (int)((p >> 2) & CODE_MASK), (int)((p >> 4) & CODE_MASK),
+                                (int)((p >> 6) & CODE_MASK)};
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    acc[t][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[t], bf, acc[t][u], 0, 0, 0);
+            }
+        }
+    };
+
+    // chunks wave, wave + KW, ...: the next chunk's loads are issued (clamped,
+    // so always in bounds) before the current chunk is multiplied
+    const int nj = (nc - 1 - wave) / KW + 1;  // the host guarantees nc >= KW
+    load(wave);
+    for (int j = 0; j < nj; ++j) {
+        store();  // after the previous chunk's fragment reads (same wave: in order)
+        load(min(wave + KW * (j + 1), nc - 1));
+        compute();
+    }
+
+    // ---- split-K reduction in LDS, then the epilogue
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int row = 32 * t + 8 * (q >> 2) + 4 * h + (q & 3);
+                atomicAdd(&red[row * LDN + 32 * u + r], acc[t][u][q]);
+            }
+        atomicAdd(&rsum[32 * t + r], rs[t]);
+    }
+    __syncthreads();
+    for (int e = tid; e < BM * BN; e += THREADS) {
+        const int row = e / BN, col = e - row * BN;
+        const int gm = m0 + row, gn = n0 + col;
+        if (gm < M && gn < N) {
+            const int v = red[row * LDN + col] - 2 * rsum[row];
+            if (OUT_I32)
+                acc_out[(int64_t)gm * N + gn] = v;
+            else
+                out[(int64_t)gm * N + gn] = epilogue_bf16(v, rscale[row], cscale[col]);
+        }
+    }
+}
+
+template <int MT, int NT, int KW, bool OUT_I32>
+hipError_t launch_skinny_lds(uint16_t* out, int32_t* acc, const int8_t* x, const uint8_t* w, const uint16_t* sa,
+                             const uint16_t* sw, int M, int N, int K, hipStream_t s) {
+    const int tiles_m = (M + 32 * MT - 1) / (32 * MT);
+    const int tiles_n = (N + 32 * NT - 1) / (32 * NT);
+    hipLaunchKernelGGL((gemm_skinny_lds_kernel<MT, NT, KW, OUT_I32>), dim3((unsigned)(tiles_m * tiles_n)),
+                       dim3(64 * KW), 0, s, out, acc, x, w, sa, sw, M, N, K, tiles_n);
+    return hipGetLastError();
+}
+
 template <int MT, int NT, int KW, int D, bool OUT_I32>
 hipError_t launch_skinny(uint16_t* out, int32_t* acc, const int8_t* x, const uint8_t* w, const uint16_t* sa,
                          const uint16_t* sw, int M, int N, int K, hipStream_t s) {
@@ -588,13 +762,40 @@ hipError_t launch_tiles(uint16_t* out, int32_t* acc, const int8_t* x, const uint
     // spend the least VALU per MFMA; they are used when there are enough of them
     // to give every CU at least two.  Otherwise 128 x 256 blocks (eight 64 x 64
     // wave tiles), which keep two waves per SIMD busy on N = 4096-sized shapes.
-    // Too few 128 x 256 tiles to give every CU one: the split-K skinny kernel
-    // (each wave needs at least one 128-element chunk of K).  Configurations
-    // measured on the LLaMA-7B layer shapes: short rings and more resident
-    // waves beat deep per-wave prefetch here.
+    // Too few 128 x 256 tiles to give every CU one: a split-K skinny kernel
+    // (each wave needs at least one chunk of K): the LDS-staged one when
+    // K % 256 == 0, else the direct one.  Configurations measured on the
+    // LLaMA-7B layer shapes: short rings and more resident waves beat deep
+    // per-wave prefetch here.
     const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 255) / 256);
     const int nc = K / GM_KS;
-    if (tiles < 256 && nc >= 4) {
+    if (tiles < 256 && K % GS_KS == 0 && K / GS_KS >= 4) {
+        // LDS-staged skinny kernel (configurations measured on the LLaMA-7B
+        // layer shapes at M = 8 ... 256; wide layers take two column tiles)
+        const int ncs = K / GS_KS;
+        const bool wide = N >= 8192;
+        if (ncs >= 8) {
+            if (M <= 32) {
+                if (wide) return launch_skinny_lds<1, 2, 8, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+                return launch_skinny_lds<1, 1, 8, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+            }
+            if (M <= 64) {
+                if (wide) return launch_skinny_lds<1, 2, 4, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+                return launch_skinny_lds<1, 1, 8, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+            }
+            if (M <= 128) {
+                if (wide) return launch_skinny_lds<1, 2, 4, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+                return launch_skinny_lds<1, 2, 8, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+            }
+            return launch_skinny_lds<2, 2, 4, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+        }
+        if (M <= 64) return launch_skinny_lds<1, 1, 4, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+        if (M <= 128) return launch_skinny_lds<1, 2, 4, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+        return launch_skinny_lds<2, 2, 4, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+    }
+    if (tiles < 256 && nc >= 4) {  // K % 256 != 0: the direct kernel
+        // wide layers: two column tiles per block halve the activation re-reads
+        if (M <= 64 && N >= 8192 && nc >= 8) return launch_skinny<1, 2, 8, 1, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
         if (M <= 16 && nc >= 8) return launch_skinny<1, 1, 8, 1, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
         if (M <= 64) return launch_skinny<1, 1, 4, 1, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
         if (M <= 128) return launch_skinny<1, 2, 4, 1, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);

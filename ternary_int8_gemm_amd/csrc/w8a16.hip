@@ -45,12 +45,14 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// MFMA kernel: 16-byte weight loads per lane and chunk (4: a wave reads whole
-// 128-byte lines of its 32 rows), and the chunk ring depth for one and two
-// 32-row activation tiles.
-constexpr int W8_MFMA_NB = 4;
+// MFMA kernel: 16-byte weight loads per lane and chunk, and the chunk ring
+// depth for one and two 32-row activation tiles.  (Chunks of 128 elements, so
+// that a wave reads whole 128-byte weight lines, measured slower from M = 8 on:
+// the loads are bound by the 32 rows each instruction touches, not by lines
+// shared between waves.)
+constexpr int W8_MFMA_NB = 2;
 constexpr int W8_MFMA_D = 2;
-constexpr int W8_MFMA_D2 = 1;
+constexpr int W8_MFMA_D2 = 2;
 // Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format;
 // stride 0, so bounds are checked against the byte count in word 2).
 constexpr int BUFFER_RSRC_WORD3_W8 = 0x00020000;

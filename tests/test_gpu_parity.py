@@ -114,6 +114,9 @@ GEMM_SHAPES = [
     (16, 4096, 4096), (64, 512, 2560), (255, 129, 6912), (8, 64, 68), (5, 7, 100), (3, 3, 4),
     # split-K path for few rows: every configuration, ragged N, K of 4..9 chunks of 128
     (9, 100, 1152), (20, 777, 1024), (100, 1000, 640), (130, 70, 512), (1, 33, 4096), (64, 31, 512),
+    # LDS-staged split-K kernel (K % 256 == 0): every configuration, wide and ragged N, ragged M
+    (32, 8200, 2048), (33, 300, 2048), (64, 9000, 1024), (100, 8192, 2048), (128, 500, 2048),
+    (200, 9001, 2048), (250, 300, 1024), (5, 4096, 768), (77, 2000, 1280),
 ]
 
 
