@@ -50,6 +50,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // that a wave reads whole 128-byte weight lines, measured slower from M = 8 on:
 // the loads are bound by the 32 rows each instruction touches, not by lines
 // shared between waves.)
+constexpr int64_t W8_LDS_KW8_MAX_N = 8192;  // eight waves per column block up to this N
 constexpr int W8_MFMA_NB = 2;
 constexpr int W8_MFMA_D = 2;
 constexpr int W8_MFMA_D2 = 2;
@@ -144,6 +145,121 @@ __global__ __launch_bounds__(64 * KW) void w8a16_kernel(float* __restrict__ y, c
 #pragma unroll
     for (int i = 0; i < D; ++i)
         if (j + i < nj) compute(ring[i]);
+
+    // ---- partial tiles to LDS (register q of lane l: row 8(q/4) + 4(l/32) + q%4,
+    //      column l%32), then a fixed-order sum over the waves, the scale, the store
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int qq = 0; qq < 16; ++qq) {
+            const int row = 32 * t + 8 * (qq >> 2) + 4 * h + (qq & 3);
+            part[wave][row * LDC + r] = acc[t][qq];
+        }
+    __syncthreads();
+    for (int e = tid; e < BM * 32; e += 64 * KW) {
+        const int row = e >> 5, col = e & 31;
+        const int gn = n0 + col;
+        if (row < M && gn < N) {
+            float v = part[0][row * LDC + col];
+#pragma unroll
+            for (int w = 1; w < KW; ++w) v += part[w][row * LDC + col];
+            y[(int64_t)row * N + gn] = v * scale[gn];
+        }
+    }
+}
+
+// ---------------------------------------------------------------- MFMA kernel, LDS-staged operands
+//
+// Loading MFMA fragments straight from memory makes each 16-byte-per-lane
+// instruction touch 32 rows; that, not the bytes, bounds w8a16_kernel.  Here
+// each wave stages its 128-element chunk of both operands in a private LDS
+// region, loading the weights as 8 whole 128-byte rows and the activations as
+// 4 rows x 256 bytes per instruction, and reads the fragments from padded LDS
+// rows (distinct banks): lane (r, h), k-step s, holds elements 64h + 8s ..
+// 64h + 8s + 7 of the chunk for both operands.  The next chunk's loads are in
+// flight while the current one is multiplied; no barrier is needed until the
+// fixed-order sum over the waves.
+constexpr int WL_KS = 128;                 // K elements per chunk
+constexpr int WL_XROW = WL_KS * 2 + 16;    // bytes per staged activation row (bf16, padded)
+constexpr int WL_WROW = WL_KS + 16;        // bytes per staged weight row (int8, padded)
+
+template <int MT, int KW>
+__global__ __launch_bounds__(64 * KW) void w8a16_lds_kernel(float* __restrict__ y, const uint16_t* __restrict__ x,
+                                                            const int8_t* __restrict__ q,
+                                                            const float* __restrict__ scale, int M, int N, int K) {
+    constexpr int BM = 32 * MT;
+    constexpr int LDC = 33;
+    constexpr int XB = BM * WL_XROW;
+    constexpr int WB = 32 * WL_WROW;
+    __shared__ __align__(16) uint8_t stage[KW][XB + WB];
+    __shared__ float part[KW][BM * LDC];
+
+    const int n0 = blockIdx.x * 32;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nc = K / WL_KS;
+    const int r = lane & 31, h = lane >> 5;
+
+    // rows past M and columns past N lie past the end of their buffers: zeros
+    const __amdgpu_buffer_rsrc_t x_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), (short)0, M * K * 2, BUFFER_RSRC_WORD3_W8);
+    const __amdgpu_buffer_rsrc_t q_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(q), (short)0, N * K, BUFFER_RSRC_WORD3_W8);
+    // this lane's global pieces: activation rows 4i + lane/16 (16 bytes at
+    // lane%16 of the row's 256), weight rows 8i + lane/8 (16 bytes at lane%8)
+    const int xr_l = lane >> 4, xp_l = lane & 15;
+    const int wr_l = lane >> 3, wp_l = lane & 7;
+    uint8_t* const xs = stage[wave];
+    uint8_t* const ws = stage[wave] + XB;
+
+    constexpr int XI = BM / 4;
+    constexpr int WI = 4;
+    v4u xg[XI], wg[WI];
+    auto load = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < XI; ++i)
+            xg[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, ((4 * i + xr_l) * K) * 2 + 16 * xp_l,
+                                                          c * WL_KS * 2, 0);
+#pragma unroll
+        for (int i = 0; i < WI; ++i)
+            wg[i] = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, (n0 + 8 * i + wr_l) * K + 16 * wp_l, c * WL_KS, 0);
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int i = 0; i < XI; ++i)
+            *reinterpret_cast<v4u*>(xs + (4 * i + xr_l) * WL_XROW + 16 * xp_l) = xg[i];
+#pragma unroll
+        for (int i = 0; i < WI; ++i)
+            *reinterpret_cast<v4u*>(ws + (8 * i + wr_l) * WL_WROW + 16 * wp_l) = wg[i];
+    };
+
+    f32x16 acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = f32x16{};
+    auto compute = [&]() {
+        v4u bw[4];  // this lane's 64 weights of the chunk: elements 64h .. 64h + 63
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bw[i] = *reinterpret_cast<const v4u*>(ws + r * WL_WROW + 64 * h + 16 * i);
+#pragma unroll
+        for (int s = 0; s < WL_KS / 16; ++s) {
+            const v4u& b = bw[s >> 1];
+            const bf16x8 bop = (s & 1) ? i8x8_to_bf16x8(b.z, b.w) : i8x8_to_bf16x8(b.x, b.y);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const v4u a = *reinterpret_cast<const v4u*>(xs + (32 * t + r) * WL_XROW + 128 * h + 16 * s);
+                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), bop, acc[t], 0, 0, 0);
+            }
+        }
+    };
+
+    const int nj = (nc - 1 - wave) / KW + 1;  // the host guarantees nc >= KW
+    load(wave);
+    for (int j = 0; j < nj; ++j) {
+        store();  // after the previous chunk's fragment reads (same wave: in order)
+        load(min(wave + KW * (j + 1), nc - 1));
+        compute();
+    }
 
     // ---- partial tiles to LDS (register q of lane l: row 8(q/4) + 4(l/32) + q%4,
     //      column l%32), then a fixed-order sum over the waves, the scale, the store
@@ -444,6 +560,17 @@ hipError_t launch_w8a16(float* y, const uint16_t* x, const int8_t* q, const floa
     // 32-bit buffer offsets: weights and activations below 2 GiB
     const bool fits = aligned16(x) && aligned16(q) && (N + 31) * K < ((int64_t)1 << 31) && 64 * K * 2 < ((int64_t)1 << 31);
     const dim3 grid((unsigned)((N + 31) / 32)), block(64 * KW);
+    if (fits && K % WL_KS == 0 && K / WL_KS >= KW) {
+        constexpr int KW8 = 8;
+        if (M <= 32 && N <= W8_LDS_KW8_MAX_N && K / WL_KS >= KW8)
+            hipLaunchKernelGGL((w8a16_lds_kernel<1, KW8>), grid, dim3(64 * KW8), 0, s, y, x, q, scale, (int)M, (int)N,
+                               (int)K);
+        else if (M <= 32)
+            hipLaunchKernelGGL((w8a16_lds_kernel<1, KW>), grid, block, 0, s, y, x, q, scale, (int)M, (int)N, (int)K);
+        else
+            hipLaunchKernelGGL((w8a16_lds_kernel<2, KW>), grid, block, 0, s, y, x, q, scale, (int)M, (int)N, (int)K);
+        return hipGetLastError();
+    }
     if (fits && K % (32 * W8_MFMA_NB) == 0 && K / (32 * W8_MFMA_NB) >= KW) {
         // whole 128-byte weight lines per wave and chunk
         if (M <= 32)
