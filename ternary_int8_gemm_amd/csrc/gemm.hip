@@ -288,14 +288,17 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
     load_stage(NS, sets[0]);
     __syncthreads();
     read_first(lds, pb, af0);
+    // stage k + i sits in LDS buffer (k + i) % 3; k advances by NS, so with
+    // NS a multiple of 3 that is the constant i % 3
     int k = 0;
     for (; k + NS <= nk; k += NS) {
 #pragma unroll
-        for (int i = 0; i < NS; ++i) step(i % 3, k + i, sets[(i + 2) % NS], sets[(i + LEAD) % NS]);
+        for (int i = 0; i < NS; ++i)
+            step(NS % 3 == 0 ? i % 3 : (k + i) % 3, k + i, sets[(i + 2) % NS], sets[(i + LEAD) % NS]);
     }
 #pragma unroll
     for (int i = 0; i < NS - 1; ++i)
-        if (k + i < nk) step(i % 3, k + i, sets[(i + 2) % NS], sets[(i + LEAD) % NS]);
+        if (k + i < nk) step(NS % 3 == 0 ? i % 3 : (k + i) % 3, k + i, sets[(i + 2) % NS], sets[(i + LEAD) % NS]);
 
     // ---- row sums (the 8 threads of a row are aligned lanes) and row scales to LDS
 #pragma unroll
