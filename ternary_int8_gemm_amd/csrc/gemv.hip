@@ -41,6 +41,11 @@
 // bf16 words into the normalised bf16 values before the absmax and quantisation
 // above.  The weight loads are already in flight meanwhile.
 //
+// With one activation row and few units of long rows (fewer than 4096 units x
+// parts, at least 4 steps a part), groups of 2 or 4 waves share each unit, each
+// wave taking a contiguous range of its steps; the exact int32 partial sums
+// meet in LDS before the correction and the epilogue.
+//
 // gemv_chunked_kernel (longer activations): each wave owns 8*RB rows and K is
 // processed in LDS-sized chunks, with the same unpack and reduction.
 //
@@ -55,6 +60,8 @@ namespace bitnet {
 namespace {
 
 constexpr int GV_STEP = 512;            // weights per row per wave step (8 lanes x 64)
+constexpr int GV_MAX_KS = 4;            // waves that can share one unit's K range
+constexpr int GV_SPLIT_UNITS = 4096;    // split K while units x parts stays below this
 constexpr int GV_LDS_BUDGET = 32768;    // bytes of quantised activations held per chunk
 
 __device__ __forceinline__ int lds_word_offset(int word) {
@@ -255,7 +262,7 @@ __device__ __forceinline__ void dot_piece_padded(const uint4& wv, const uint8_t*
     }
 }
 
-template <int MT, int D, int XW, bool OUT_I32, bool RMS>
+template <int MT, int D, int XW, bool OUT_I32, bool RMS, int KS>
 __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
                                                           uint16_t* __restrict__ sa_out,
                                                           const uint16_t* __restrict__ x,
@@ -279,10 +286,17 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
     const int row_stride = steps * 8 * GV_SEG;
     const int wpr = steps * (GV_STEP / 16);  // 16-element words per activation row in LDS
 
+    // With KS > 1 (one activation row), groups of KS waves share each unit,
+    // wave kp of a group taking the contiguous steps [s_begin, s_end).
+    constexpr int wg_n = WAVES / KS;  // wave groups
+    const int wg = wave / KS;
+    const int kp = wave - wg * KS;
+    const int s_begin = KS == 1 ? 0 : kp * steps / KS;
+    const int s_end = KS == 1 ? steps : (kp + 1) * steps / KS;  // the host guarantees steps >= KS
     const int ub0 = blockIdx.x * upb;
     const int ub1 = min(ub0 + upb, units);
-    const int my_units = (ub0 + wave < ub1) ? (ub1 - 1 - ub0 - wave) / WAVES + 1 : 0;
-    const int items = my_units * steps;
+    const int my_units = (ub0 + wg < ub1) ? (ub1 - 1 - ub0 - wg) / wg_n + 1 : 0;
+    const int items = my_units * (s_end - s_begin);
 
     // ---- prologue reads, before any weight load
     uint4 xr[XW][2];
@@ -310,7 +324,7 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
     // this lane's 16-byte piece in a step, clamped into the row for the last step
     const uint32_t piece = (uint32_t)(sl * 16);
     const uint32_t piece_last = (uint32_t)min(sl * 16, KB - last_step * (GV_STEP / 4) - 16);
-    int lj = 0, lt = 0;         // load cursor: unit index (of this wave) and step
+    int lj = 0, lt = s_begin;   // load cursor: unit index (of this wave group) and step
     const uint8_t* unit_ptr;    // row 0 of the unit being loaded (wave-uniform)
     uint32_t voff, voff_last;   // this lane's byte offset from unit_ptr (normal / last step)
     auto set_unit = [&]() {
@@ -319,7 +333,7 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
         // streaming loads have already evicted.  Selects, not branches, so the
         // ring's loads stay in straight-line code.
         const bool live = lj < my_units;  // wave-uniform
-        const int u = min(ub0 + wave + WAVES * min(lj, max(my_units - 1, 0)), units - 1);
+        const int u = min(ub0 + wg + wg_n * min(lj, max(my_units - 1, 0)), units - 1);
         const uint32_t lane_row = (uint32_t)((min(u * 8 + g, N - 1) - u * 8) * KB);
         unit_ptr = live ? w + (int64_t)u * 8 * KB : gv_pad;
         voff = live ? lane_row + piece : (uint32_t)(lane * 16);
@@ -329,8 +343,8 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
     auto issue = [&](uint4& dst) {
         const uint8_t* b = unit_ptr + lt * (GV_STEP / 4);
         dst = load_stream16(b + ((ktail && lt == last_step) ? voff_last : voff));
-        if (++lt == steps) {
-            lt = 0;
+        if (++lt == s_end) {
+            lt = s_begin;
             ++lj;
             set_unit();
         }
@@ -465,25 +479,30 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
     for (int m = 0; m < MT; ++m) a0[m] = a1[m] = a2[m] = 0;
 
     const uint8_t* lds_lane = lds_x + sl * GV_SEG;
-    int cj = 0, ct = 0;  // consume cursor
+    // partial sums of the K parts (exact int32), combined after the stream
+    __shared__ int part[KS][KS > 1 ? NT * MT : 1];
+    int cj = 0, ct = s_begin;  // consume cursor
     auto consume = [&](const uint4& piece) {
         dot_piece_padded<MT>(piece, lds_lane + ct * (8 * GV_SEG), row_stride, a0, a1, a2);
-        if (++ct == steps) {  // unit complete: reduce its 8 lanes per row and write
-            const int ul = wave + WAVES * cj;  // unit index within the workgroup
+        if (++ct == s_end) {  // unit complete: reduce its 8 lanes per row and write
+            const int ul = wg + wg_n * cj;  // unit index within the workgroup
             const int n = (ub0 + ul) * 8 + g;
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 int tot = a0[m] + (a1[m] >> 2) + (a2[m] >> 4);
-                tot = group8_sum(tot) - sumq2[m];
+                tot = group8_sum(tot);
                 a0[m] = a1[m] = a2[m] = 0;
-                if ((m & 7) == sl && n < N && m < M) {
+                if (KS > 1) {
+                    if ((m & 7) == sl) part[kp][(ul * 8 + g) * MT + m] = tot;
+                } else if ((m & 7) == sl && n < N && m < M) {
+                    tot -= sumq2[m];
                     if (OUT_I32)
                         acc_out[(int64_t)m * N + n] = tot;
                     else
                         out[(int64_t)m * N + n] = epilogue_bf16(tot, sa_f[m], bf16_to_f32(sw_lds[ul * 8 + g]));
                 }
             }
-            ct = 0;
+            ct = s_begin;
             ++cj;
         }
     };
@@ -500,6 +519,25 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
 #pragma unroll
     for (int i = 0; i < D; ++i)
         if (i < rem) consume(buf[i]);
+
+    if constexpr (KS > 1) {  // add the K parts, then the correction and the epilogue
+        __syncthreads();
+        for (int idx = tid; idx < nrows * MT; idx += NT) {
+            const int rr = idx / MT;
+            const int m = idx - rr * MT;
+            int tot = part[0][idx];
+#pragma unroll
+            for (int p = 1; p < KS; ++p) tot += part[p][idx];
+            tot -= sumq2[m];
+            const int n = row0 + rr;
+            if (m < M) {
+                if (OUT_I32)
+                    acc_out[(int64_t)m * N + n] = tot;
+                else
+                    out[(int64_t)m * N + n] = epilogue_bf16(tot, sa_f[m], bf16_to_f32(sw_lds[rr]));
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------- chunked kernel
@@ -754,21 +792,21 @@ __global__ __launch_bounds__(64) void gemv_fused_plain(uint16_t* __restrict__ ou
 // over, never more than there are 4-wave groups of units.
 constexpr int GV_STREAM_MAX_BLOCKS = 512;
 
-template <int MT, int D, bool OUT_I32, bool RMS>
+template <int MT, int D, bool OUT_I32, bool RMS, int KS>
 hipError_t launch_stream_xw(int xw, dim3 grid, size_t lds, hipStream_t s, uint16_t* out, int32_t* acc, uint16_t* sa_out,
                             const uint16_t* x, const uint8_t* w, const uint16_t* sw, int M, int N, int K, int steps,
                             int units, int upb, const uint16_t* gain, float eps) {
     if (xw <= 1)
-        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 1, OUT_I32, RMS>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 1, OUT_I32, RMS, KS>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
                            sw, M, N, K, steps, units, upb, gain, eps);
     else if (xw <= 2)
-        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 2, OUT_I32, RMS>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 2, OUT_I32, RMS, KS>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
                            sw, M, N, K, steps, units, upb, gain, eps);
     else if (xw <= 4)
-        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 4, OUT_I32, RMS>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 4, OUT_I32, RMS, KS>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
                            sw, M, N, K, steps, units, upb, gain, eps);
     else
-        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 8, OUT_I32, RMS>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 8, OUT_I32, RMS, KS>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
                            sw, M, N, K, steps, units, upb, gain, eps);
     return hipGetLastError();
 }
@@ -779,9 +817,15 @@ hipError_t launch_stream(uint16_t* out, int32_t* acc, uint16_t* sa_out, const ui
                          float eps = 0.0f) {
     const int steps = (K + GV_STEP - 1) / GV_STEP;
     const int units = (N + 7) / 8;
+    // Split K inside the workgroup (one or two activation rows) when there are
+    // too few units to give every CU several waves of whole rows.
+    int ks = 1;
+    if (MT == 1)
+        while (ks < GV_MAX_KS && units * ks < GV_SPLIT_UNITS && steps >= 8 * ks) ks *= 2;  // >= 4 steps a part
+    const int groups = 4 / ks;
     // At most 32 units (256 rows, one weight scale per thread) per workgroup;
     // otherwise as few workgroups as keep the GPU full.
-    int blocks = (units + 3) / 4;
+    int blocks = (units + groups - 1) / groups;
     if (blocks > GV_STREAM_MAX_BLOCKS) blocks = GV_STREAM_MAX_BLOCKS;
     if (blocks < (units + 31) / 32) blocks = (units + 31) / 32;
     const int upb = (units + blocks - 1) / blocks;
@@ -792,11 +836,28 @@ hipError_t launch_stream(uint16_t* out, int32_t* acc, uint16_t* sa_out, const ui
     // accumulators already take most of the register file.
     constexpr int D_SHORT = MT >= 8 ? 4 : 8;
     constexpr int D_LONG = MT == 1 ? 16 : D_SHORT;
+    const dim3 grid(blocks);
+    if constexpr (MT == 1) {
+        if (ks == 4) {
+            if (steps / 4 >= 12)
+                return launch_stream_xw<MT, D_LONG, OUT_I32, RMS, 4>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N,
+                                                                     K, steps, units, upb, gain, eps);
+            return launch_stream_xw<MT, D_SHORT, OUT_I32, RMS, 4>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N, K,
+                                                                  steps, units, upb, gain, eps);
+        }
+        if (ks == 2) {
+            if (steps / 2 >= 12)
+                return launch_stream_xw<MT, D_LONG, OUT_I32, RMS, 2>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N,
+                                                                     K, steps, units, upb, gain, eps);
+            return launch_stream_xw<MT, D_SHORT, OUT_I32, RMS, 2>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N, K,
+                                                                  steps, units, upb, gain, eps);
+        }
+    }
     if (steps >= 12)
-        return launch_stream_xw<MT, D_LONG, OUT_I32, RMS>(xw, dim3(blocks), lds, s, out, acc, sa_out, x, w, sw, M, N, K,
-                                                     steps, units, upb, gain, eps);
-    return launch_stream_xw<MT, D_SHORT, OUT_I32, RMS>(xw, dim3(blocks), lds, s, out, acc, sa_out, x, w, sw, M, N, K, steps,
-                                                  units, upb, gain, eps);
+        return launch_stream_xw<MT, D_LONG, OUT_I32, RMS, 1>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N, K,
+                                                             steps, units, upb, gain, eps);
+    return launch_stream_xw<MT, D_SHORT, OUT_I32, RMS, 1>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N, K, steps,
+                                                          units, upb, gain, eps);
 }
 
 template <int MT, bool OUT_I32>

@@ -173,6 +173,9 @@ def test_gemm_bf16_parity(M, N, K):
 GEMV_SHAPES = [
     (1, 1, 64), (1, 7, 256), (4, 128, 256), (2, 1000, 512), (3, 129, 576), (5, 64, 2560), (8, 3840, 2560),
     (9, 100, 6912), (15, 256, 4096), (1, 2560, 6912), (16 - 1, 33, 40960), (1, 300, 68), (7, 50, 100),
+    # K split across the waves of a workgroup (one row, few units, long rows): 4 parts, 4 parts
+    # with a partial last step, 2 parts with a partial last step; two rows are never split
+    (1, 1000, 16384), (1, 300, 8256), (1, 520, 7232), (2, 520, 7232),
 ]
 
 
@@ -510,6 +513,7 @@ def test_rmsnorm_quantize_misaligned_plain_path():
 
 @pytest.mark.parametrize("with_gain", [False, True])
 @pytest.mark.parametrize("M,N,K", [(1, 3840, 2560), (2, 2560, 6912), (3, 130, 4096), (4, 13824, 2560), (1, 100, 1024),
+                                   (1, 2560, 6912), (1, 4096, 11008),
                                    (5, 300, 2560), (16, 4096, 4096), (64, 1000, 1024), (300, 257, 512), (2, 33, 68)])
 def test_linear_rms_parity(M, N, K, with_gain):
     x = synth.activations_bf16(M, K, seed=8200 + M + N + K)
