@@ -353,7 +353,33 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
 #pragma unroll
     for (int i = 0; i < D; ++i) issue(buf[i]);
 
-    // ---- RMSNorm of the activation rows, in registers
+    // ---- absmax of every activation row, per wave (of x itself)
+    uint32_t am[MT];
+    auto wave_absmax = [&]() {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) am[m] = 0u;
+#pragma unroll
+        for (int i = 0; i < XW; ++i) {
+            uint32_t a = 0u;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                a = max(a, max(max(absmax_bf16x2(xr[i][h].x), absmax_bf16x2(xr[i][h].y)),
+                               max(absmax_bf16x2(xr[i][h].z), absmax_bf16x2(xr[i][h].w))));
+#pragma unroll
+            for (int m = 0; m < MT; ++m) am[m] = (xm[i] == m) ? max(am[m], a) : am[m];
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint32_t a = wave_max_u32(am[m]);
+            if (lane == 0) red_u[wave][m] = a;
+        }
+    };
+
+    // ---- RMSNorm of the activation rows, in registers.  Without a gain the
+    // normalised absmax is bf16(fp32(max|x| * r)) (both roundings are
+    // monotonic and r > 0), so the absmax of x is reduced in the same round as
+    // the sum of squares; with a gain the normalised values are scanned again.
+    float rr[MT];
     if constexpr (RMS) {
         __shared__ double red_d[WAVES][MT];
         double ss[MT];
@@ -379,8 +405,11 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
             const double v = wave_sum_f64(ss[m]);
             if (lane == 0) red_d[wave][m] = v;
         }
+        if (gain == nullptr) {  // wave-uniform
+            wave_absmax();
+            sw_lds[tid] = sw_mine;
+        }
         __syncthreads();
-        float rr[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) rr[m] = rms_inv(((red_d[0][m] + red_d[1][m]) + red_d[2][m]) + red_d[3][m], K, eps);
 #pragma unroll
@@ -392,28 +421,11 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
             xr[i][1] = rms_apply_bf16x8(xr[i][1], gr[i][1], r);
         }
     }
-
-    // ---- absmax of every activation row over the block
-    uint32_t am[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) am[m] = 0u;
-#pragma unroll
-    for (int i = 0; i < XW; ++i) {
-        uint32_t a = 0u;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-            a = max(a, max(max(absmax_bf16x2(xr[i][h].x), absmax_bf16x2(xr[i][h].y)),
-                           max(absmax_bf16x2(xr[i][h].z), absmax_bf16x2(xr[i][h].w))));
-#pragma unroll
-        for (int m = 0; m < MT; ++m) am[m] = (xm[i] == m) ? max(am[m], a) : am[m];
+    if (!RMS || gain != nullptr) {
+        wave_absmax();
+        sw_lds[tid] = sw_mine;
+        __syncthreads();
     }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        const uint32_t a = wave_max_u32(am[m]);
-        if (lane == 0) red_u[wave][m] = a;
-    }
-    sw_lds[tid] = sw_mine;
-    __syncthreads();
 
     // ---- scales (every thread), quantise own words into LDS, sum_k q
     QuantScale qsc[MT];
@@ -423,6 +435,7 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
         uint32_t a = red_u[0][m];
 #pragma unroll
         for (int wv = 1; wv < WAVES; ++wv) a = max(a, red_u[wv][m]);
+        if (RMS && gain == nullptr) a = (uint32_t)f32_to_bf16(bf16_to_f32(a) * rr[m]) & 0x7FFFu;
         qsc[m] = quant_scale(a);
         sa_f[m] = bf16_to_f32(f32_to_bf16(qsc[m].s));
     }
