@@ -541,3 +541,26 @@ def test_linear_rms_fused_equals_split_on_unambiguous_rows():
     amb = oracle.rmsnorm_quantize(x)["ambiguous"]
     same = np.all(host_bf16(fused) == host_bf16(split), axis=1)
     assert np.all(same | amb)
+
+
+@pytest.mark.parametrize("M", [1, 8])
+@pytest.mark.parametrize("kind", ["denormal", "tiny_normal", "mixed"])
+def test_w8a16_denormal_activations(M, kind):
+    """bf16 subnormal and smallest-normal activations: both the vector (M = 1)
+    and the matrix-unit (M = 8) paths keep them (no flush to zero)."""
+    K, N = 1024, 96
+    g = synth.rng(7300 + M)
+    if kind == "denormal":
+        bits = g.integers(1, 0x80, size=(M, K)).astype(np.uint16)
+    elif kind == "tiny_normal":
+        bits = g.integers(0x0080, 0x0100, size=(M, K)).astype(np.uint16)
+    else:
+        bits = synth.activations_bf16(M, K, seed=7301)
+        bits[:, ::2] = g.integers(1, 0x80, size=(M, K // 2)).astype(np.uint16)
+    bits |= g.integers(0, 2, size=(M, K)).astype(np.uint16) << 15
+    q = synth.random_int8((N, K), seed=7302)
+    scale = np.ones(N, dtype=np.float32)
+    y, bound = oracle.w8a16(bits, q, scale)
+    got = tg.w8a16_gemv(dev_bf16(bits), dev(q), dev(scale)).cpu().numpy()
+    assert_w8a16_close(got, y, bound, K, f"w8a16 {kind} M={M}")
+    assert np.all((got != 0) | (y == 0)), "an output was flushed to zero"
