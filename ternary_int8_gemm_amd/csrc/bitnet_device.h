@@ -189,10 +189,10 @@ __device__ __forceinline__ QuantScale quant_scale(uint32_t absmax_bits) {
 // half-integer, round(y) == round(fp32(x / s)); in that rare case the correctly
 // rounded quotient is computed and used instead.
 __device__ __forceinline__ int quantize_one(float x, const QuantScale& q) {
-    float y = x * q.r;
-    float d = y - __builtin_floorf(y);
-    if (__builtin_expect(__builtin_fabsf(d - 0.5f) < 0x1p-12f, 0)) y = x / q.s;
+    const float y = x * q.r;
     float t = __builtin_rintf(y);
+    // y within 2^-12 of a half-integer <=> |y - rint(y)| > 1/2 - 2^-12
+    if (__builtin_expect(__builtin_fabsf(y - t) > 0.5f - 0x1p-12f, 0)) t = __builtin_rintf(x / q.s);
     t = __builtin_fminf(__builtin_fmaxf(t, -127.0f), 127.0f);
     return (int)t;
 }
