@@ -197,6 +197,46 @@ __device__ __forceinline__ int quantize_one(float x, const QuantScale& q) {
     return (int)t;
 }
 
+// Quantise eight bf16 values (one 16-byte group) with the arithmetic of
+// quantize_one; returns the eight int8 in two words, low element first.
+//  * Rounding by addition: for |y| <= 2^22, y + 1.5 * 2^23 lands in [2^23,
+//    2^24), where the spacing is 1, so the sum is 1.5 * 2^23 + rint(y) with
+//    ties to even, and its low byte is rint(y) as a two's-complement int8.
+//  * No clamp is needed: |x| <= absmax and r = fp32(1 / fp32(absmax / 127)),
+//    so |y| <= 127 * (1 + 3 * 2^-24) < 127.5 (also when absmax is clamped to
+//    1e-5, since then |x| < 1e-5).
+//  * The near-half-integer test is taken once for the group: one branch per
+//    eight elements; the rare elements it finds get the correctly rounded x / s.
+// Needs FP contraction off (y must be the rounded product before the add).
+__device__ __forceinline__ uint2 quantize_bf16x8(const uint4& v, const QuantScale& q) {
+    constexpr float RND = 12582912.0f;  // 1.5 * 2^23
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float x[8], m[8], dev = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        x[e] = bf16_to_f32((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu));
+        const float y = x[e] * q.r;
+        m[e] = y + RND;
+        dev = __builtin_fmaxf(dev, __builtin_fabsf(y - (m[e] - RND)));
+    }
+    if (__builtin_expect(dev > 0.5f - 0x1p-12f, 0)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float y = x[e] * q.r;
+            if (__builtin_fabsf(y - (m[e] - RND)) > 0.5f - 0x1p-12f) m[e] = x[e] / q.s + RND;
+        }
+    }
+    uint32_t u[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u[e] = __builtin_bit_cast(uint32_t, m[e]);
+    // byte 0 of each value: perm selects bytes 0 (second operand) and 4 (first)
+    const uint32_t p01 = __builtin_amdgcn_perm(u[1], u[0], 0x0C0C0400u);
+    const uint32_t p23 = __builtin_amdgcn_perm(u[3], u[2], 0x0C0C0400u);
+    const uint32_t p45 = __builtin_amdgcn_perm(u[5], u[4], 0x0C0C0400u);
+    const uint32_t p67 = __builtin_amdgcn_perm(u[7], u[6], 0x0C0C0400u);
+    return make_uint2(p01 | (p23 << 16), p45 | (p67 << 16));
+}
+
 // Quantise two bf16 values held in one 32-bit word; returns them in the low
 // two bytes (low element first).
 __device__ __forceinline__ uint32_t quantize_bf16x2(uint32_t w, const QuantScale& q) {

@@ -143,10 +143,9 @@ __device__ __forceinline__ void block_quantize_to_lds(uint8_t* lds_x, int ldsz, 
                 const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)m * K + k0 + wd * 16);
                 const uint4 lo = src[0];
                 const uint4 hi = src[1];
-                const uint32_t n0 = quantize_bf16x2(lo.x, qsc[m]) | (quantize_bf16x2(lo.y, qsc[m]) << 16);
-                const uint32_t n1 = quantize_bf16x2(lo.z, qsc[m]) | (quantize_bf16x2(lo.w, qsc[m]) << 16);
-                const uint32_t n2 = quantize_bf16x2(hi.x, qsc[m]) | (quantize_bf16x2(hi.y, qsc[m]) << 16);
-                const uint32_t n3 = quantize_bf16x2(hi.z, qsc[m]) | (quantize_bf16x2(hi.w, qsc[m]) << 16);
+                const uint2 qlo = quantize_bf16x8(lo, qsc[m]);
+                const uint2 qhi = quantize_bf16x8(hi, qsc[m]);
+                const uint32_t n0 = qlo.x, n1 = qlo.y, n2 = qhi.x, n3 = qhi.y;
                 int s = __builtin_amdgcn_sdot4((int)n0, 0x01010101, 0, false);
                 s = __builtin_amdgcn_sdot4((int)n1, 0x01010101, s, false);
                 s = __builtin_amdgcn_sdot4((int)n2, 0x01010101, s, false);
@@ -456,10 +455,9 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
                 if (xm[i] == m) qs = qsc[m];
             const uint4 lo = xr[i][0];
             const uint4 hi = xr[i][1];
-            const uint32_t n0 = quantize_bf16x2(lo.x, qs) | (quantize_bf16x2(lo.y, qs) << 16);
-            const uint32_t n1 = quantize_bf16x2(lo.z, qs) | (quantize_bf16x2(lo.w, qs) << 16);
-            const uint32_t n2 = quantize_bf16x2(hi.x, qs) | (quantize_bf16x2(hi.y, qs) << 16);
-            const uint32_t n3 = quantize_bf16x2(hi.z, qs) | (quantize_bf16x2(hi.w, qs) << 16);
+            const uint2 qlo = quantize_bf16x8(lo, qs);
+            const uint2 qhi = quantize_bf16x8(hi, qs);
+            const uint32_t n0 = qlo.x, n1 = qlo.y, n2 = qhi.x, n3 = qhi.y;
             int t = __builtin_amdgcn_sdot4((int)n0, 0x01010101, 0, false);
             t = __builtin_amdgcn_sdot4((int)n1, 0x01010101, t, false);
             t = __builtin_amdgcn_sdot4((int)n2, 0x01010101, t, false);
@@ -675,10 +673,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_chunked_kernel(uint16_t* __re
                     const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)m * K + k0 + wd * 16);
                     const uint4 lo = src[0];
                     const uint4 hi = src[1];
-                    const uint32_t n0 = quantize_bf16x2(lo.x, qsc[m]) | (quantize_bf16x2(lo.y, qsc[m]) << 16);
-                    const uint32_t n1 = quantize_bf16x2(lo.z, qsc[m]) | (quantize_bf16x2(lo.w, qsc[m]) << 16);
-                    const uint32_t n2 = quantize_bf16x2(hi.x, qsc[m]) | (quantize_bf16x2(hi.y, qsc[m]) << 16);
-                    const uint32_t n3 = quantize_bf16x2(hi.z, qsc[m]) | (quantize_bf16x2(hi.w, qsc[m]) << 16);
+                    const uint2 qlo = quantize_bf16x8(lo, qsc[m]);
+                    const uint2 qhi = quantize_bf16x8(hi, qsc[m]);
+                    const uint32_t n0 = qlo.x, n1 = qlo.y, n2 = qhi.x, n3 = qhi.y;
                     int s = __builtin_amdgcn_sdot4((int)n0, 0x01010101, 0, false);
                     s = __builtin_amdgcn_sdot4((int)n1, 0x01010101, s, false);
                     s = __builtin_amdgcn_sdot4((int)n2, 0x01010101, s, false);

@@ -32,8 +32,6 @@ namespace {
 
 constexpr int QUANT_ROWS_PER_BLOCK = 4;
 
-__device__ __forceinline__ uint32_t pack4(uint32_t lo2, uint32_t hi2) { return lo2 | (hi2 << 16); }
-
 // Vector path: K % 16 == 0, x and q 16-byte aligned.
 __global__ __launch_bounds__(256) void quantize_rows_vec(int8_t* __restrict__ q, uint16_t* __restrict__ scale,
                                                          const uint16_t* __restrict__ x, int64_t M, int64_t K) {
@@ -59,10 +57,12 @@ __global__ __launch_bounds__(256) void quantize_rows_vec(int8_t* __restrict__ q,
         const uint4 a = xv[2 * i];
         const uint4 b = xv[2 * i + 1];
         uint4 o;
-        o.x = pack4(quantize_bf16x2(a.x, qs), quantize_bf16x2(a.y, qs));
-        o.y = pack4(quantize_bf16x2(a.z, qs), quantize_bf16x2(a.w, qs));
-        o.z = pack4(quantize_bf16x2(b.x, qs), quantize_bf16x2(b.y, qs));
-        o.w = pack4(quantize_bf16x2(b.z, qs), quantize_bf16x2(b.w, qs));
+        const uint2 qa = quantize_bf16x8(a, qs);
+        const uint2 qb = quantize_bf16x8(b, qs);
+        o.x = qa.x;
+        o.y = qa.y;
+        o.z = qb.x;
+        o.w = qb.y;
         qv[i] = o;
     }
 }
@@ -122,12 +122,7 @@ __global__ __launch_bounds__(256) void quantize_rows_reg(int8_t* __restrict__ q,
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int g = c * 64 + lane;
-        if (g < groups) {
-            uint2 o;
-            o.x = pack4(quantize_bf16x2(v[c].x, qs), quantize_bf16x2(v[c].y, qs));
-            o.y = pack4(quantize_bf16x2(v[c].z, qs), quantize_bf16x2(v[c].w, qs));
-            qv[g] = o;
-        }
+        if (g < groups) qv[g] = quantize_bf16x8(v[c], qs);
     }
 }
 
