@@ -201,7 +201,7 @@ def test_gemv_fused_misaligned_plain_path():
 
 # ----------------------------------------------------------------------------- dispatch
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 15, 16, 17, 64])
+@pytest.mark.parametrize("M", list(range(1, 18)) + [64])
 def test_linear_dispatch_neutral(M):
     N, K = 192, 1024
     x, W, P, sw = problem(M, N, K, seed=5000 + M, outliers=0.01, row_scales=True)
