@@ -51,6 +51,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // the loads are bound by the 32 rows each instruction touches, not by lines
 // shared between waves.)
 constexpr int64_t W8_LDS_KW8_MAX_N = 8192;  // eight waves per column block up to this N
+// Two column tiles per workgroup halve the activation staging per weight byte,
+// which dominates once M is large; they pay while there are still enough column
+// blocks to fill the chip (measured on the BitNet-2B and LLaMA-7B decode shapes).
+constexpr int64_t W8_LDS_NT2_MIN_N = 16384;      // from this N at any M
+constexpr int64_t W8_LDS_NT2_MIN_N_M16 = 10240;  // from this N at M >= 16
 constexpr int W8_MFMA_NB = 2;
 constexpr int W8_MFMA_D = 2;
 constexpr int W8_MFMA_D2 = 2;
@@ -183,18 +188,26 @@ constexpr int WL_KS = 128;                 // K elements per chunk
 constexpr int WL_XROW = WL_KS * 2 + 16;    // bytes per staged activation row (bf16, padded)
 constexpr int WL_WROW = WL_KS + 16;        // bytes per staged weight row (int8, padded)
 
-template <int MT, int KW>
+template <int MT, int NT, int KW>
 __global__ __launch_bounds__(64 * KW) void w8a16_lds_kernel(float* __restrict__ y, const uint16_t* __restrict__ x,
                                                             const int8_t* __restrict__ q,
                                                             const float* __restrict__ scale, int M, int N, int K) {
     constexpr int BM = 32 * MT;
-    constexpr int LDC = 33;
+    constexpr int BN = 32 * NT;  // NT column tiles share each staged activation chunk
+    constexpr int LDC = BN + 1;
     constexpr int XB = BM * WL_XROW;
-    constexpr int WB = 32 * WL_WROW;
-    __shared__ __align__(16) uint8_t stage[KW][XB + WB];
-    __shared__ float part[KW][BM * LDC];
+    constexpr int WB = BN * WL_WROW;
+    // With two column tiles the partial tiles reuse the stages' memory after the K
+    // loop (two workgroups per CU rather than one); otherwise they have their own.
+    constexpr bool OVERLAY = NT > 1;
+    constexpr int STAGE_BYTES = KW * (XB + WB);
+    constexpr int PART_BYTES = KW * BM * LDC * 4;
+    __shared__ __align__(16) uint8_t
+        smem[OVERLAY ? (STAGE_BYTES > PART_BYTES ? STAGE_BYTES : PART_BYTES) : STAGE_BYTES + PART_BYTES];
+    auto stage = reinterpret_cast<uint8_t(*)[XB + WB]>(smem);
+    auto part = reinterpret_cast<float(*)[BM * LDC]>(smem + (OVERLAY ? 0 : STAGE_BYTES));
 
-    const int n0 = blockIdx.x * 32;
+    const int n0 = blockIdx.x * BN;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -214,7 +227,7 @@ __global__ __launch_bounds__(64 * KW) void w8a16_lds_kernel(float* __restrict__ 
     uint8_t* const ws = stage[wave] + XB;
 
     constexpr int XI = BM / 4;
-    constexpr int WI = 4;
+    constexpr int WI = BN / 8;
     v4u xg[XI], wg[WI];
     auto load = [&](int c) {
 #pragma unroll
@@ -234,21 +247,32 @@ __global__ __launch_bounds__(64 * KW) void w8a16_lds_kernel(float* __restrict__ 
             *reinterpret_cast<v4u*>(ws + (8 * i + wr_l) * WL_WROW + 16 * wp_l) = wg[i];
     };
 
-    f32x16 acc[MT];
+    f32x16 acc[MT][NT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = f32x16{};
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int u = 0; u < NT; ++u) acc[t][u] = f32x16{};
     auto compute = [&]() {
-        v4u bw[4];  // this lane's 64 weights of the chunk: elements 64h .. 64h + 63
+        v4u bw[NT][4];  // this lane's 64 weights of the chunk per column tile: elements 64h .. 64h + 63
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bw[i] = *reinterpret_cast<const v4u*>(ws + r * WL_WROW + 64 * h + 16 * i);
+        for (int u = 0; u < NT; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                bw[u][i] = *reinterpret_cast<const v4u*>(ws + (32 * u + r) * WL_WROW + 64 * h + 16 * i);
 #pragma unroll
         for (int s = 0; s < WL_KS / 16; ++s) {
-            const v4u& b = bw[s >> 1];
-            const bf16x8 bop = (s & 1) ? i8x8_to_bf16x8(b.z, b.w) : i8x8_to_bf16x8(b.x, b.y);
+            bf16x8 af[MT];
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const v4u a = *reinterpret_cast<const v4u*>(xs + (32 * t + r) * WL_XROW + 128 * h + 16 * s);
-                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), bop, acc[t], 0, 0, 0);
+            for (int t = 0; t < MT; ++t)
+                af[t] = __builtin_bit_cast(bf16x8,
+                                           *reinterpret_cast<const v4u*>(xs + (32 * t + r) * WL_XROW + 128 * h + 16 * s));
+#pragma unroll
+            for (int u = 0; u < NT; ++u) {
+                const v4u& b = bw[u][s >> 1];
+                const bf16x8 bop = (s & 1) ? i8x8_to_bf16x8(b.z, b.w) : i8x8_to_bf16x8(b.x, b.y);
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t], bop, acc[t][u], 0, 0, 0);
             }
         }
     };
@@ -263,16 +287,19 @@ __global__ __launch_bounds__(64 * KW) void w8a16_lds_kernel(float* __restrict__ 
 
     // ---- partial tiles to LDS (register q of lane l: row 8(q/4) + 4(l/32) + q%4,
     //      column l%32), then a fixed-order sum over the waves, the scale, the store
+    if constexpr (OVERLAY) __syncthreads();  // every wave is done with its stage before the tiles overwrite it
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int qq = 0; qq < 16; ++qq) {
-            const int row = 32 * t + 8 * (qq >> 2) + 4 * h + (qq & 3);
-            part[wave][row * LDC + r] = acc[t][qq];
-        }
+        for (int u = 0; u < NT; ++u)
+#pragma unroll
+            for (int qq = 0; qq < 16; ++qq) {
+                const int row = 32 * t + 8 * (qq >> 2) + 4 * h + (qq & 3);
+                part[wave][row * LDC + 32 * u + r] = acc[t][u][qq];
+            }
     __syncthreads();
-    for (int e = tid; e < BM * 32; e += 64 * KW) {
-        const int row = e >> 5, col = e & 31;
+    for (int e = tid; e < BM * BN; e += 64 * KW) {
+        const int row = e / BN, col = e - row * BN;
         const int gn = n0 + col;
         if (row < M && gn < N) {
             float v = part[0][row * LDC + col];
@@ -562,13 +589,24 @@ hipError_t launch_w8a16(float* y, const uint16_t* x, const int8_t* q, const floa
     const dim3 grid((unsigned)((N + 31) / 32)), block(64 * KW);
     if (fits && K % WL_KS == 0 && K / WL_KS >= KW) {
         constexpr int KW8 = 8;
-        if (M <= 32 && N <= W8_LDS_KW8_MAX_N && K / WL_KS >= KW8)
-            hipLaunchKernelGGL((w8a16_lds_kernel<1, KW8>), grid, dim3(64 * KW8), 0, s, y, x, q, scale, (int)M, (int)N,
+        const dim3 grid2((unsigned)((N + 63) / 64));
+        if (N >= W8_LDS_NT2_MIN_N || (M >= 16 && N >= W8_LDS_NT2_MIN_N_M16)) {
+            if (M <= 32)
+                hipLaunchKernelGGL((w8a16_lds_kernel<1, 2, KW>), grid2, block, 0, s, y, x, q, scale, (int)M, (int)N,
+                                   (int)K);
+            else
+                hipLaunchKernelGGL((w8a16_lds_kernel<2, 2, KW>), grid2, block, 0, s, y, x, q, scale, (int)M, (int)N,
+                                   (int)K);
+        } else if (M <= 32 && N <= W8_LDS_KW8_MAX_N && K / WL_KS >= KW8) {
+            hipLaunchKernelGGL((w8a16_lds_kernel<1, 1, KW8>), grid, dim3(64 * KW8), 0, s, y, x, q, scale, (int)M,
+                               (int)N, (int)K);
+        } else if (M <= 32) {
+            hipLaunchKernelGGL((w8a16_lds_kernel<1, 1, KW>), grid, block, 0, s, y, x, q, scale, (int)M, (int)N,
                                (int)K);
-        else if (M <= 32)
-            hipLaunchKernelGGL((w8a16_lds_kernel<1, KW>), grid, block, 0, s, y, x, q, scale, (int)M, (int)N, (int)K);
-        else
-            hipLaunchKernelGGL((w8a16_lds_kernel<2, KW>), grid, block, 0, s, y, x, q, scale, (int)M, (int)N, (int)K);
+        } else {
+            hipLaunchKernelGGL((w8a16_lds_kernel<2, 1, KW>), grid, block, 0, s, y, x, q, scale, (int)M, (int)N,
+                               (int)K);
+        }
         return hipGetLastError();
     }
     if (fits && K % (32 * W8_MFMA_NB) == 0 && K / (32 * W8_MFMA_NB) >= KW) {

@@ -408,7 +408,9 @@ W8A16_EXACT_SHAPES = [(1, 64, 256), (5, 100, 4096), (32, 33, 1024), (33, 4096, 4
                       (3, 7, 200), (2, 4, 64),
                       # M <= 4 streaming kernel: partial last step, tiny K, the LDS limit, ragged N
                       (1, 13, 2576), (2, 130, 1040), (3, 257, 4096), (4, 9, 4096), (1, 8, 16), (1, 5, 16384),
-                      (2, 3, 8192), (4, 1000, 2560)]
+                      (2, 3, 8192), (4, 1000, 2560),
+                      # two column tiles per workgroup on wide layers: ragged N, one and two row tiles
+                      (8, 16400, 512), (40, 16385, 1024), (17, 20000, 384), (3, 16392, 256), (20, 11000, 640)]
 
 
 @pytest.mark.parametrize("M,N,K", W8A16_EXACT_SHAPES)
@@ -423,7 +425,8 @@ def test_w8a16_exact_integer_activations(M, N, K):
 
 W8A16_SHAPES = [(1, 4096, 4096), (1, 1, 256), (1, 32000, 4096), (3, 100, 256), (16, 4096, 4096), (16, 31, 11008),
                 (33, 1000, 1024), (64, 257, 11008), (7, 300, 11072), (2, 64, 131072), (5, 300, 200), (4, 3, 68),
-                (1, 128256, 2560), (2, 3840, 2560), (4, 13824, 2560), (1, 4096, 11008), (3, 2560, 6912)]
+                (1, 128256, 2560), (2, 3840, 2560), (4, 13824, 2560), (1, 4096, 11008), (3, 2560, 6912),
+                (16, 32000, 4096), (64, 16448, 2560), (32, 13824, 2560), (5, 128256, 2560)]
 
 
 @pytest.mark.parametrize("M,N,K", W8A16_SHAPES)
