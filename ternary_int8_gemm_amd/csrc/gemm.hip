@@ -58,6 +58,8 @@ namespace {
 constexpr int GM_KS = 128;     // K elements per pipeline stage (4 MFMA k-steps of 32)
 constexpr int GROUP_M = 8;     // row panels swept per column tile (tile order)
 constexpr int GM_FRAG = 1024;  // bytes of one 32 x 32 int8 A operand fragment (64 lanes x 16 B)
+constexpr int64_t GM_MID_MN = (int64_t)1 << 21;  // M * N from which few tiles still beat split-K
+constexpr int64_t GM_MID_BLOCKS = 160;           // blocks a mid-M block tile should give
 // Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format;
 // stride 0, so bounds are checked against the byte count in word 2).
 constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
@@ -230,8 +232,13 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
     v4i af0[MT];
     auto step = [&](const int bi, int k, const StageRegs<A_CH, B_CH>& SS, StageRegs<A_CH, B_CH>& SL) {
         __syncthreads();  // stage k+1 visible; buffer (k+2) % 3 no longer read
+        // The global loads go out at raised wave priority, so that a wave leaving
+        // the barrier issues them ahead of the MFMA and LDS work of the other
+        // wave on its SIMD (measured: about one point of MFMA utilisation at M = 2048).
+        __builtin_amdgcn_s_setprio(1);
         load_stage(k + NS + 1, SL);
         __builtin_amdgcn_sched_barrier(0);  // keep the loads at the top
+        __builtin_amdgcn_s_setprio(0);
         const uint8_t* cur = lds + bi * S::STAGE;
         uint8_t* later = lds + ((bi + 2) % 3) * S::STAGE;
         const uint8_t* next = lds + ((bi + 1) % 3) * S::STAGE;
@@ -772,6 +779,16 @@ hipError_t launch_tiles(uint16_t* out, int32_t* acc, const int8_t* x, const uint
     // per-wave prefetch here.
     const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 255) / 256);
     const int nc = K / GM_KS;
+    if (tiles < 256 && (int64_t)M * N >= GM_MID_MN) {
+        // Mid-sized M: the split-K kernels re-read the activations once per 64
+        // output columns, which costs more than leaving CUs idle in a block-tiled
+        // kernel.  Take the largest block tile that still gives GM_MID_BLOCKS
+        // blocks (measured on the LLaMA-7B shapes at M = 128 ... 1024).
+        if (tiles >= GM_MID_BLOCKS) return launch_mfma<128, 256, 2, 4, 2, 3, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+        if ((int64_t)((M + 127) / 128) * ((N + 127) / 128) >= GM_MID_BLOCKS)
+            return launch_mfma<128, 128, 2, 2, 2, 3, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+        return launch_mfma<64, 128, 1, 2, 2, 3, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+    }
     if (tiles < 256 && K % GS_KS == 0 && K / GS_KS >= 4) {
         // LDS-staged skinny kernel (configurations measured on the LLaMA-7B
         // layer shapes at M = 8 ... 256; wide layers take two column tiles)

@@ -117,6 +117,8 @@ GEMM_SHAPES = [
     # LDS-staged split-K kernel (K % 256 == 0): every configuration, wide and ragged N, ragged M
     (32, 8200, 2048), (33, 300, 2048), (64, 9000, 1024), (100, 8192, 2048), (128, 500, 2048),
     (200, 9001, 2048), (250, 300, 1024), (5, 4096, 768), (77, 2000, 1280),
+    # mid-sized M (M * N >= 2^21 with few 128 x 256 tiles): 128 x 256, 128 x 128 and 64 x 128 blocks
+    (513, 10000, 256), (300, 13000, 384), (1000, 2200, 512),
 ]
 
 
@@ -158,7 +160,8 @@ def test_gemm_i32_misaligned_plain_path():
 
 # ----------------------------------------------------------------------------- bf16 GEMM
 
-@pytest.mark.parametrize("M,N,K", [(4, 128, 256), (16, 4096, 4096), (200, 300, 1024), (33, 65, 68)])
+@pytest.mark.parametrize("M,N,K", [(4, 128, 256), (16, 4096, 4096), (200, 300, 1024), (33, 65, 68),
+                                   (513, 10000, 256), (300, 13000, 384), (1000, 2200, 512)])
 def test_gemm_bf16_parity(M, N, K):
     x, W, P, _ = problem(M, N, K, seed=3000 + M)
     sw = synth.row_scales_bf16(N, seed=3100 + M)
