@@ -87,6 +87,20 @@ def time_graph(graph, replays, stream):
     return start.elapsed_time(end) * 1e-3  # seconds
 
 
+RAMP_SECONDS = 0.03
+
+
+def ramp(graph, stream, seconds=RAMP_SECONDS):
+    """Untimed replays of `graph` until `seconds` of GPU time have passed.  The
+    GPU's clocks take several milliseconds of sustained work to settle (about
+    10 ms measured on MI355X after an idle gap), so a warm-up of one or two short
+    replays would leave the timed replays inside that ramp."""
+    spent, n = 0.0, 1
+    while spent < seconds:
+        spent += time_graph(graph, n, stream)
+        n = min(2 * n, 1024)
+
+
 def capture(fn, stream):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
@@ -155,7 +169,7 @@ def run_decode(shapes, dev_sets, steps, warmup, stream, log):
                 Pd, swd, xd, od = d[name]
                 tg.bitnet_linear(xd, Pd, swd, out=od)
         gs = capture(launches, stream)
-        time_graph(gs, 2, stream)
+        ramp(gs, stream)
         r = 30
         t = time_graph(gs, r, stream) / (r * copies)
         per_shape[name] = {"N": N, "K": K, "us": t * 1e6, "gbs": gemv_bytes(1, N, K) / t / 1e9,
@@ -197,7 +211,7 @@ def run_gemm(device, stream, M, log, rotate=4):
         res = {"N": N, "K": K}
         for tag, fn in (("gemm", gemm_only), ("linear", linear_full), ("quant", quant_only)):
             g = capture(fn, stream)
-            time_graph(g, 2, stream)
+            ramp(g, stream)
             reps = 10
             t = time_graph(g, reps, stream) / (reps * rotate)
             res[tag + "_us"] = t * 1e6
@@ -246,7 +260,7 @@ def run_small_batch(device, stream, log):
                     tg.bitnet_gemm(q, Pd, sa, sw, out=o)
 
             g = capture(run, stream)
-            time_graph(g, 1, stream)
+            ramp(g, stream)
             t = time_graph(g, 3, stream) / (3 * copies)
             ops, nbytes = 2.0 * M * N * K, gemm_bytes(M, N, K)
             r = {"us": round(t * 1e6, 2), "gbs": round(nbytes / t / 1e9, 1), "tops": round(ops / t / 1e12, 1),
@@ -302,7 +316,7 @@ def run_decode_full(device, stream, log, layers=30):
                     tg.bitnet_linear(xd, Pd, swd, out=od, workspace=ws)
 
         g = capture(step, stream)
-        time_graph(g, 2, stream)
+        ramp(g, stream)
         reps = 20
         t = time_graph(g, reps, stream) / reps
         if M == 1:
@@ -347,7 +361,7 @@ def run_options(device, stream, log):
                 for Pd in Ps:
                     tg.bitnet_linear(x, Pd, sw, out=o, workspace=ws, bias=b)
             g = capture(run, stream)
-            time_graph(g, 1, stream)
+            ramp(g, stream)
             t = time_graph(g, 3, stream) / (3 * copies)
             r[tag + "_us"] = round(t * 1e6, 2)
         out[f"{name}_M{M}"] = r
@@ -383,7 +397,7 @@ def run_w8a16(device, stream, log):
                 for qd in qs:
                     tg.w8a16_gemv(x, qd, sc, out=y)
             g = capture(run, stream)
-            time_graph(g, 1, stream)
+            ramp(g, stream)
             t = time_graph(g, 3, stream) / (3 * copies)
             r[f"M{M}_us"] = round(t * 1e6, 2)
             r[f"M{M}_gbs"] = round(w8a16_bytes(M, N, K) / t / 1e9, 1)
@@ -579,8 +593,8 @@ def summarize_pmc(fetch_dir, write_dir):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=220)
-    ap.add_argument("--warmup", type=int, default=22)
+    ap.add_argument("--steps", type=int, default=2200)
+    ap.add_argument("--warmup", type=int, default=660)
     ap.add_argument("--gemm-m", type=int, default=2048)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
