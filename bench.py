@@ -26,6 +26,7 @@ Profiling helpers (not part of the timed benchmark):
 """
 import argparse
 import csv
+import gzip
 import glob
 import hashlib
 import json
@@ -481,9 +482,13 @@ def run_pmc_target(device, reps=3):
 
 
 def _csv_rows(folder, suffix):
+    """Rows of every *suffix (or gzip-compressed *suffix.gz) file under folder."""
     rows = []
-    for path in sorted(glob.glob(os.path.join(folder, "**", "*" + suffix), recursive=True)):
-        with open(path, newline="") as f:
+    paths = glob.glob(os.path.join(folder, "**", "*" + suffix), recursive=True) + \
+        glob.glob(os.path.join(folder, "**", "*" + suffix + ".gz"), recursive=True)
+    for path in sorted(paths):
+        opener = gzip.open if path.endswith(".gz") else open
+        with opener(path, "rt", newline="") as f:
             rows.extend(csv.DictReader(f))
     if not rows:
         raise SystemExit(f"no *{suffix} under {folder}")
@@ -513,6 +518,7 @@ def summarize_trace(folder):
            "Command (from the repository root, after `cd /tmp && export TMPDIR=/tmp`):", "",
            "    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_bench -o bench -- "
            "python3 bench.py --steps 22 --warmup 5 --no-cpu-baseline",
+           "    gzip gpurun_out/trace_bench/*kernel_trace.csv   # the per-dispatch trace, compressed for transfer",
            f"    python bench.py --summarize-trace gpurun_out/trace_bench", "",
            "## --stats (kernel_stats.csv)", "",
            "| kernel | calls | total ms | avg us | min us | max us | % |", "|---|---:|---:|---:|---:|---:|---:|"]
