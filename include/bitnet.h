@@ -151,8 +151,9 @@ bitnet_status bitnet_quantize_act_f32(int8_t* x_int8, uint16_t* scale_act, const
 /*
  * Device workspace (bytes) that bitnet_linear_ex needs: for bf16 activations
  * the same as bitnet_linear_workspace_bytes; for f32 activations room for
- * x_int8 [M][K] and scale_act [M] at every M (f32 input always takes the
- * quantise-then-GEMM path).  Returns 0 for invalid sizes or dtypes.
+ * x_int8 [M][K] and scale_act [M] at every M (required even when the call
+ * takes the one-launch path below and leaves it untouched).  Returns 0 for
+ * invalid sizes or dtypes.
  */
 size_t bitnet_linear_ex_workspace_bytes(int64_t M, int64_t K, int x_dtype);
 
@@ -162,6 +163,10 @@ size_t bitnet_linear_ex_workspace_bytes(int64_t M, int64_t K, int x_dtype);
  * optional bias (class BitLinear adds its bf16 bias to the bf16 result).
  *   y = bitnet_linear(x)   (for f32 x: bitnet_quantize_act_f32, then bitnet_gemm)
  *   out[m][n] = bias ? bf16_rne( fp32(y[m][n]) + fp32(bias[n]) ) : y[m][n]
+ * Where bitnet_linear takes the fused GEMV (small M) and x and w_packed are
+ * 16-byte aligned with K % 64 == 0 and M <= 4, the whole call is one kernel:
+ * either activation type quantised in the GEMV's prologue, the bias added in
+ * its epilogue, with the same bits as the separate steps.
  * out: bf16 [M][N] (written); x: [M][K] of x_dtype (BITNET_DTYPE_BF16 or
  * BITNET_DTYPE_F32); w_packed: uint8 [N][K/4]; scale_wt: bf16 [N]; bias: bf16
  * [N] or NULL; workspace: bitnet_linear_ex_workspace_bytes(M, K, x_dtype)

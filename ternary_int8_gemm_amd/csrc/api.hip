@@ -22,6 +22,8 @@ using bitnet::launch_w8a16;
 using bitnet::launch_quantize_rms;
 using bitnet::launch_gemv_fused_rms;
 using bitnet::gemv_rms_fusable;
+using bitnet::gemv_ex_fusable;
+using bitnet::launch_gemv_fused_ex;
 
 constexpr int kMaxDevices = 64;
 // 0 = unknown, 1 = gfx950, 2 = other
@@ -209,12 +211,19 @@ BITNET_API bitnet_status bitnet_linear_ex(uint16_t* out, const void* x, int x_dt
     if (M == 0 || N == 0) return BITNET_OK;
     if (!out || !x || !w_packed || !scale_wt) return BITNET_ERR_NULL;
     bitnet_status st;
+    const size_t need = bitnet_linear_ex_workspace_bytes(M, K, x_dtype);
+    if (x_dtype == BITNET_DTYPE_F32 && (workspace == nullptr || workspace_bytes < need)) return BITNET_ERR_WORKSPACE;
+    if (linear_takes_fused(M, K) && gemv_ex_fusable(M, K, x, w_packed)) {
+        // one launch: the activations (either type) quantised in the GEMV's
+        // prologue, the bias in its epilogue; the workspace is not touched
+        if ((st = check_device())) return st;
+        return launched(launch_gemv_fused_ex(out, x, x_dtype == BITNET_DTYPE_F32, bias, w_packed, scale_wt, M, N, K,
+                                             (hipStream_t)stream));
+    }
     if (x_dtype == BITNET_DTYPE_BF16) {
         st = bitnet_linear(out, static_cast<const uint16_t*>(x), w_packed, scale_wt, M, N, K, workspace,
                            workspace_bytes, stream);
     } else {
-        const size_t need = bitnet_linear_ex_workspace_bytes(M, K, x_dtype);
-        if (workspace == nullptr || workspace_bytes < need) return BITNET_ERR_WORKSPACE;
         if ((st = check_device())) return st;
         int8_t* x_int8 = static_cast<int8_t*>(workspace);
         uint16_t* scale_act = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + round256((size_t)M * K));

@@ -197,6 +197,21 @@ __device__ __forceinline__ int quantize_one(float x, const QuantScale& q) {
     return (int)t;
 }
 
+// Quantise four f32 values (one 16-byte group) with quantize_one; returns the
+// four int8 in one word, low element first.
+__device__ __forceinline__ uint32_t quantize_f32x4(const uint4& v, const QuantScale& q) {
+    const uint32_t b0 = (uint32_t)quantize_one(__builtin_bit_cast(float, v.x), q) & 0xFFu;
+    const uint32_t b1 = (uint32_t)quantize_one(__builtin_bit_cast(float, v.y), q) & 0xFFu;
+    const uint32_t b2 = (uint32_t)quantize_one(__builtin_bit_cast(float, v.z), q) & 0xFFu;
+    const uint32_t b3 = (uint32_t)quantize_one(__builtin_bit_cast(float, v.w), q) & 0xFFu;
+    return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+}
+
+// Largest f32 magnitude bits of four values (the order of non-negative finite floats).
+__device__ __forceinline__ uint32_t absmax_f32x4(const uint4& v) {
+    return max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu));
+}
+
 // Quantise eight bf16 values (one 16-byte group) with the arithmetic of
 // quantize_one; returns the eight int8 in two words, low element first.
 //  * Rounding by addition: for |y| <= 2^22, y + 1.5 * 2^23 lands in [2^23,
@@ -251,6 +266,11 @@ __device__ __forceinline__ uint32_t quantize_bf16x2(uint32_t w, const QuantScale
 // bf16 significands fit in fp32), (float)acc is exact for |acc| < 2^24, so the
 // result has a single fp32 rounding followed by the bf16 rounding.  There is
 // no addition, so no contraction can change it.
+// The bias on a bf16 layer output: bf16_rne(fp32(y) + fp32(bias)).
+__device__ __forceinline__ uint16_t add_bias_bf16(uint32_t y, uint32_t b) {
+    return f32_to_bf16(bf16_to_f32(y) + bf16_to_f32(b));
+}
+
 __device__ __forceinline__ uint16_t epilogue_bf16(int acc, float sa, float sw) {
     const float scale = sa * sw;
     const float y = (float)acc * scale;

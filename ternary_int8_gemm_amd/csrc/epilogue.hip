@@ -56,8 +56,8 @@ __global__ __launch_bounds__(256) void epilogue_plain(uint16_t* __restrict__ out
 }
 
 __device__ __forceinline__ uint32_t add_bias_pair(uint32_t y2, uint32_t b2) {
-    const uint32_t lo = f32_to_bf16(bf16_to_f32(y2 & 0xFFFFu) + bf16_to_f32(b2 & 0xFFFFu));
-    const uint32_t hi = f32_to_bf16(bf16_to_f32(y2 >> 16) + bf16_to_f32(b2 >> 16));
+    const uint32_t lo = add_bias_bf16(y2 & 0xFFFFu, b2 & 0xFFFFu);
+    const uint32_t hi = add_bias_bf16(y2 >> 16, b2 >> 16);
     return lo | (hi << 16);
 }
 
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void add_bias_plain(uint16_t* __restrict__ out
     const int64_t total = M * N;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x)
-        out[i] = f32_to_bf16(bf16_to_f32(out[i]) + bf16_to_f32(bias[i % N]));
+        out[i] = add_bias_bf16(out[i], bias[i % N]);
 }
 
 int64_t grid_for(int64_t work) {

@@ -261,20 +261,26 @@ __device__ __forceinline__ void dot_piece_padded(const uint4& wv, const uint8_t*
     }
 }
 
-template <int MT, int D, int XW, bool OUT_I32, bool RMS, int KS>
+// XF32: x holds f32 activations (quantised as they are, with the f32 absmax),
+// else bf16.  BIAS: bias [N] is added to the bf16 outputs.
+template <int MT, int D, int XW, bool OUT_I32, bool RMS, int KS, bool XF32, bool BIAS>
 __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
                                                           uint16_t* __restrict__ sa_out,
-                                                          const uint16_t* __restrict__ x,
+                                                          const void* __restrict__ x,
                                                           const uint8_t* __restrict__ w,
                                                           const uint16_t* __restrict__ sw, int M, int N, int K,
                                                           int steps, int units, int upb,
-                                                          const uint16_t* __restrict__ gain, float eps) {
+                                                          const uint16_t* __restrict__ gain, float eps,
+                                                          const uint16_t* __restrict__ bias) {
+    static_assert(!(RMS && XF32), "the RMSNorm prologue takes bf16 activations");
+    static_assert(!(BIAS && OUT_I32), "the bias applies to the bf16 outputs");
     constexpr int WAVES = 4;
     constexpr int NT = WAVES * 64;
     extern __shared__ __align__(16) uint8_t lds_x[];  // [MT][steps * 8 segments of GV_SEG bytes]
     __shared__ uint32_t red_u[WAVES][MT];
     __shared__ int red_i[WAVES][MT];
     __shared__ uint16_t sw_lds[NT];
+    __shared__ uint16_t bias_lds[BIAS ? NT : 1];  // the workgroup's bias values
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -297,8 +303,11 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
     const int my_units = (ub0 + wg < ub1) ? (ub1 - 1 - ub0 - wg) / wg_n + 1 : 0;
     const int items = my_units * (s_end - s_begin);
 
-    // ---- prologue reads, before any weight load
-    uint4 xr[XW][2];
+    // ---- prologue reads, before any weight load: 16 elements a word, as two
+    //      (bf16) or four (f32) 16-byte pieces
+    constexpr int XV = XF32 ? 4 : 2;
+    constexpr int XES = XF32 ? 4 : 2;  // bytes per activation element
+    uint4 xr[XW][XV];
     int xm[XW], xw[XW];
 #pragma unroll
     for (int i = 0; i < XW; ++i) {
@@ -306,16 +315,19 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
         xm[i] = idx / wpr;
         xw[i] = idx - xm[i] * wpr;
         if (xm[i] < M && xm[i] < MT && xw[i] * 16 < K) {
-            const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)xm[i] * K + xw[i] * 16);
-            xr[i][0] = src[0];
-            xr[i][1] = src[1];
+            const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(x) +
+                                                              ((int64_t)xm[i] * K + xw[i] * 16) * XES);
+#pragma unroll
+            for (int v = 0; v < XV; ++v) xr[i][v] = src[v];
         } else {
-            xr[i][0] = xr[i][1] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int v = 0; v < XV; ++v) xr[i][v] = make_uint4(0u, 0u, 0u, 0u);
         }
     }
     const int row0 = ub0 * 8;
     const int nrows = min(ub1 * 8, N) - row0;
     const uint16_t sw_mine = (tid < nrows && sw != nullptr) ? sw[row0 + tid] : (uint16_t)0;
+    const uint16_t bias_mine = (BIAS && tid < nrows) ? bias[row0 + tid] : (uint16_t)0;
 
     // ---- the weight ring
     const int last_step = steps - 1;
@@ -361,9 +373,13 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
         for (int i = 0; i < XW; ++i) {
             uint32_t a = 0u;
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-                a = max(a, max(max(absmax_bf16x2(xr[i][h].x), absmax_bf16x2(xr[i][h].y)),
-                               max(absmax_bf16x2(xr[i][h].z), absmax_bf16x2(xr[i][h].w))));
+            for (int h = 0; h < XV; ++h) {
+                if constexpr (XF32)
+                    a = max(a, absmax_f32x4(xr[i][h]));
+                else
+                    a = max(a, max(max(absmax_bf16x2(xr[i][h].x), absmax_bf16x2(xr[i][h].y)),
+                                   max(absmax_bf16x2(xr[i][h].z), absmax_bf16x2(xr[i][h].w))));
+            }
 #pragma unroll
             for (int m = 0; m < MT; ++m) am[m] = (xm[i] == m) ? max(am[m], a) : am[m];
         }
@@ -407,6 +423,7 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
         if (gain == nullptr) {  // wave-uniform
             wave_absmax();
             sw_lds[tid] = sw_mine;
+            if constexpr (BIAS) bias_lds[tid] = bias_mine;
         }
         __syncthreads();
 #pragma unroll
@@ -423,6 +440,7 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
     if (!RMS || gain != nullptr) {
         wave_absmax();
         sw_lds[tid] = sw_mine;
+        if constexpr (BIAS) bias_lds[tid] = bias_mine;
         __syncthreads();
     }
 
@@ -435,7 +453,7 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
 #pragma unroll
         for (int wv = 1; wv < WAVES; ++wv) a = max(a, red_u[wv][m]);
         if (RMS && gain == nullptr) a = (uint32_t)f32_to_bf16(bf16_to_f32(a) * rr[m]) & 0x7FFFu;
-        qsc[m] = quant_scale(a);
+        qsc[m] = XF32 ? quant_scale_f32(__builtin_bit_cast(float, a)) : quant_scale(a);
         sa_f[m] = bf16_to_f32(f32_to_bf16(qsc[m].s));
     }
     if (sa_out != nullptr && blockIdx.x == 0 && tid < M && tid < MT) {
@@ -453,11 +471,17 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
 #pragma unroll
             for (int m = 1; m < MT; ++m)
                 if (xm[i] == m) qs = qsc[m];
-            const uint4 lo = xr[i][0];
-            const uint4 hi = xr[i][1];
-            const uint2 qlo = quantize_bf16x8(lo, qs);
-            const uint2 qhi = quantize_bf16x8(hi, qs);
-            const uint32_t n0 = qlo.x, n1 = qlo.y, n2 = qhi.x, n3 = qhi.y;
+            uint32_t n0, n1, n2, n3;
+            if constexpr (XF32) {
+                n0 = quantize_f32x4(xr[i][0], qs);
+                n1 = quantize_f32x4(xr[i][1], qs);
+                n2 = quantize_f32x4(xr[i][2], qs);
+                n3 = quantize_f32x4(xr[i][3], qs);
+            } else {
+                const uint2 qlo = quantize_bf16x8(xr[i][0], qs);
+                const uint2 qhi = quantize_bf16x8(xr[i][1], qs);
+                n0 = qlo.x, n1 = qlo.y, n2 = qhi.x, n3 = qhi.y;
+            }
             int t = __builtin_amdgcn_sdot4((int)n0, 0x01010101, 0, false);
             t = __builtin_amdgcn_sdot4((int)n1, 0x01010101, t, false);
             t = __builtin_amdgcn_sdot4((int)n2, 0x01010101, t, false);
@@ -507,10 +531,13 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
                     if ((m & 7) == sl) part[kp][(ul * 8 + g) * MT + m] = tot;
                 } else if ((m & 7) == sl && n < N && m < M) {
                     tot -= sumq2[m];
-                    if (OUT_I32)
+                    if (OUT_I32) {
                         acc_out[(int64_t)m * N + n] = tot;
-                    else
-                        out[(int64_t)m * N + n] = epilogue_bf16(tot, sa_f[m], bf16_to_f32(sw_lds[ul * 8 + g]));
+                    } else {
+                        uint16_t o = epilogue_bf16(tot, sa_f[m], bf16_to_f32(sw_lds[ul * 8 + g]));
+                        if constexpr (BIAS) o = add_bias_bf16(o, bias_lds[ul * 8 + g]);
+                        out[(int64_t)m * N + n] = o;
+                    }
                 }
             }
             ct = s_begin;
@@ -542,10 +569,13 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
             tot -= sumq2[m];
             const int n = row0 + rr;
             if (m < M) {
-                if (OUT_I32)
+                if (OUT_I32) {
                     acc_out[(int64_t)m * N + n] = tot;
-                else
-                    out[(int64_t)m * N + n] = epilogue_bf16(tot, sa_f[m], bf16_to_f32(sw_lds[rr]));
+                } else {
+                    uint16_t o = epilogue_bf16(tot, sa_f[m], bf16_to_f32(sw_lds[rr]));
+                    if constexpr (BIAS) o = add_bias_bf16(o, bias_lds[rr]);
+                    out[(int64_t)m * N + n] = o;
+                }
             }
         }
     }
@@ -802,29 +832,29 @@ __global__ __launch_bounds__(64) void gemv_fused_plain(uint16_t* __restrict__ ou
 // over, never more than there are 4-wave groups of units.
 constexpr int GV_STREAM_MAX_BLOCKS = 512;
 
-template <int MT, int D, bool OUT_I32, bool RMS, int KS>
+template <int MT, int D, bool OUT_I32, bool RMS, int KS, bool XF32, bool BIAS>
 hipError_t launch_stream_xw(int xw, dim3 grid, size_t lds, hipStream_t s, uint16_t* out, int32_t* acc, uint16_t* sa_out,
-                            const uint16_t* x, const uint8_t* w, const uint16_t* sw, int M, int N, int K, int steps,
-                            int units, int upb, const uint16_t* gain, float eps) {
+                            const void* x, const uint8_t* w, const uint16_t* sw, int M, int N, int K, int steps,
+                            int units, int upb, const uint16_t* gain, float eps, const uint16_t* bias) {
     if (xw <= 1)
-        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 1, OUT_I32, RMS, KS>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
-                           sw, M, N, K, steps, units, upb, gain, eps);
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 1, OUT_I32, RMS, KS, XF32, BIAS>), grid, dim3(256), lds, s, out, acc,
+                           sa_out, x, w, sw, M, N, K, steps, units, upb, gain, eps, bias);
     else if (xw <= 2)
-        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 2, OUT_I32, RMS, KS>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
-                           sw, M, N, K, steps, units, upb, gain, eps);
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 2, OUT_I32, RMS, KS, XF32, BIAS>), grid, dim3(256), lds, s, out, acc,
+                           sa_out, x, w, sw, M, N, K, steps, units, upb, gain, eps, bias);
     else if (xw <= 4)
-        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 4, OUT_I32, RMS, KS>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
-                           sw, M, N, K, steps, units, upb, gain, eps);
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 4, OUT_I32, RMS, KS, XF32, BIAS>), grid, dim3(256), lds, s, out, acc,
+                           sa_out, x, w, sw, M, N, K, steps, units, upb, gain, eps, bias);
     else
-        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 8, OUT_I32, RMS, KS>), grid, dim3(256), lds, s, out, acc, sa_out, x, w,
-                           sw, M, N, K, steps, units, upb, gain, eps);
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 8, OUT_I32, RMS, KS, XF32, BIAS>), grid, dim3(256), lds, s, out, acc,
+                           sa_out, x, w, sw, M, N, K, steps, units, upb, gain, eps, bias);
     return hipGetLastError();
 }
 
-template <int MT, bool OUT_I32, bool RMS = false>
-hipError_t launch_stream(uint16_t* out, int32_t* acc, uint16_t* sa_out, const uint16_t* x, const uint8_t* w,
+template <int MT, bool OUT_I32, bool RMS = false, bool XF32 = false, bool BIAS = false>
+hipError_t launch_stream(uint16_t* out, int32_t* acc, uint16_t* sa_out, const void* x, const uint8_t* w,
                          const uint16_t* sw, int M, int N, int K, hipStream_t s, const uint16_t* gain = nullptr,
-                         float eps = 0.0f) {
+                         float eps = 0.0f, const uint16_t* bias = nullptr) {
     const int steps = (K + GV_STEP - 1) / GV_STEP;
     const int units = (N + 7) / 8;
     // Split K inside the workgroup (one or two activation rows) when there are
@@ -850,24 +880,24 @@ hipError_t launch_stream(uint16_t* out, int32_t* acc, uint16_t* sa_out, const ui
     if constexpr (MT == 1) {
         if (ks == 4) {
             if (steps / 4 >= 12)
-                return launch_stream_xw<MT, D_LONG, OUT_I32, RMS, 4>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N,
-                                                                     K, steps, units, upb, gain, eps);
-            return launch_stream_xw<MT, D_SHORT, OUT_I32, RMS, 4>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N, K,
-                                                                  steps, units, upb, gain, eps);
+                return launch_stream_xw<MT, D_LONG, OUT_I32, RMS, 4, XF32, BIAS>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N,
+                                                                     K, steps, units, upb, gain, eps, bias);
+            return launch_stream_xw<MT, D_SHORT, OUT_I32, RMS, 4, XF32, BIAS>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N, K,
+                                                                  steps, units, upb, gain, eps, bias);
         }
         if (ks == 2) {
             if (steps / 2 >= 12)
-                return launch_stream_xw<MT, D_LONG, OUT_I32, RMS, 2>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N,
-                                                                     K, steps, units, upb, gain, eps);
-            return launch_stream_xw<MT, D_SHORT, OUT_I32, RMS, 2>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N, K,
-                                                                  steps, units, upb, gain, eps);
+                return launch_stream_xw<MT, D_LONG, OUT_I32, RMS, 2, XF32, BIAS>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N,
+                                                                     K, steps, units, upb, gain, eps, bias);
+            return launch_stream_xw<MT, D_SHORT, OUT_I32, RMS, 2, XF32, BIAS>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N, K,
+                                                                  steps, units, upb, gain, eps, bias);
         }
     }
     if (steps >= 12)
-        return launch_stream_xw<MT, D_LONG, OUT_I32, RMS, 1>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N, K,
-                                                             steps, units, upb, gain, eps);
-    return launch_stream_xw<MT, D_SHORT, OUT_I32, RMS, 1>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N, K, steps,
-                                                          units, upb, gain, eps);
+        return launch_stream_xw<MT, D_LONG, OUT_I32, RMS, 1, XF32, BIAS>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N, K,
+                                                             steps, units, upb, gain, eps, bias);
+    return launch_stream_xw<MT, D_SHORT, OUT_I32, RMS, 1, XF32, BIAS>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N, K,
+                                                                steps, units, upb, gain, eps, bias);
 }
 
 template <int MT, bool OUT_I32>
@@ -918,6 +948,39 @@ hipError_t launch_gemv_fused(uint16_t* out, int32_t* acc, uint16_t* scale_act_ou
     if (M <= 0 || N <= 0) return hipSuccess;
     if (acc != nullptr) return dispatch<true>(nullptr, acc, scale_act_out, x, w, scale_wt, (int)M, (int)N, (int)K, s);
     return dispatch<false>(out, nullptr, scale_act_out, x, w, scale_wt, (int)M, (int)N, (int)K, s);
+}
+
+// The streaming kernel with f32 activations or a bias epilogue exists at 1, 2
+// and 4 (padded) activation rows whose quantised values fit in LDS.
+bool gemv_ex_fusable(int64_t M, int64_t K, const void* x, const void* w) {
+    if (M < 1 || M > 4 || K % 64 != 0 || !aligned16(x) || !aligned16(w)) return false;
+    const int64_t mt = M == 1 ? 1 : (M == 2 ? 2 : 4);
+    const int64_t kpad = (K + GV_STEP - 1) / GV_STEP * GV_STEP;
+    return mt * kpad <= GV_LDS_BUDGET;
+}
+
+template <bool XF32, bool BIAS>
+hipError_t launch_ex_m(uint16_t* out, const void* x, const uint16_t* bias, const uint8_t* w, const uint16_t* scale_wt,
+                       int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    const int m = (int)M, n = (int)N, k = (int)K;
+    if (M == 1)
+        return launch_stream<1, false, false, XF32, BIAS>(out, nullptr, nullptr, x, w, scale_wt, m, n, k, s, nullptr,
+                                                           0.0f, bias);
+    if (M == 2)
+        return launch_stream<2, false, false, XF32, BIAS>(out, nullptr, nullptr, x, w, scale_wt, m, n, k, s, nullptr,
+                                                           0.0f, bias);
+    return launch_stream<4, false, false, XF32, BIAS>(out, nullptr, nullptr, x, w, scale_wt, m, n, k, s, nullptr, 0.0f,
+                                                       bias);
+}
+
+hipError_t launch_gemv_fused_ex(uint16_t* out, const void* x, bool x_f32, const uint16_t* bias, const uint8_t* w,
+                                const uint16_t* scale_wt, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    if (!gemv_ex_fusable(M, K, x, w)) return hipErrorInvalidValue;
+    if (x_f32 && bias != nullptr) return launch_ex_m<true, true>(out, x, bias, w, scale_wt, M, N, K, s);
+    if (x_f32) return launch_ex_m<true, false>(out, x, nullptr, w, scale_wt, M, N, K, s);
+    if (bias != nullptr) return launch_ex_m<false, true>(out, x, bias, w, scale_wt, M, N, K, s);
+    return launch_ex_m<false, false>(out, x, nullptr, w, scale_wt, M, N, K, s);
 }
 
 // The fused RMSNorm prologue exists for the streaming kernel at 1, 2 and 4

@@ -38,6 +38,12 @@ hipError_t launch_gemv_fused_rms(uint16_t* out, uint16_t* scale_act_out, const u
                                  float eps, const uint8_t* w, const uint16_t* scale_wt, int64_t M, int64_t N,
                                  int64_t K, hipStream_t s);
 
+// The fused GEMV for bitnet_linear_ex: bf16 or f32 (x_f32) activations, an
+// optional bf16 bias on the outputs; M <= 4, shapes gemv_ex_fusable accepts.
+bool gemv_ex_fusable(int64_t M, int64_t K, const void* x, const void* w);
+hipError_t launch_gemv_fused_ex(uint16_t* out, const void* x, bool x_f32, const uint16_t* bias, const uint8_t* w,
+                                const uint16_t* scale_wt, int64_t M, int64_t N, int64_t K, hipStream_t s);
+
 // RMSNorm over each row of bf16 x [M][K] (optional bf16 gain [K]), then the
 // per-token quantisation of the normalised row; xn (optional) receives it.
 hipError_t launch_quantize_rms(int8_t* q, uint16_t* scale, uint16_t* xn, const uint16_t* x, const uint16_t* gain,

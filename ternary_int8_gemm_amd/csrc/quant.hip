@@ -199,9 +199,7 @@ __global__ __launch_bounds__(256) void quantize_rows_f32_reg(int8_t* __restrict_
     }
     uint32_t amax = 0;
 #pragma unroll
-    for (int c = 0; c < CH; ++c)
-        amax = max(amax, max(max(v[c].x & 0x7FFFFFFFu, v[c].y & 0x7FFFFFFFu),
-                             max(v[c].z & 0x7FFFFFFFu, v[c].w & 0x7FFFFFFFu)));
+    for (int c = 0; c < CH; ++c) amax = max(amax, absmax_f32x4(v[c]));
     amax = wave_max_u32(amax);
     const QuantScale qs = quant_scale_f32(__builtin_bit_cast(float, amax));
     if (lane == 0) scale[m] = f32_to_bf16(qs.s);
@@ -209,13 +207,7 @@ __global__ __launch_bounds__(256) void quantize_rows_f32_reg(int8_t* __restrict_
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int g = c * 64 + lane;
-        if (g < groups) {
-            const uint32_t b0 = (uint32_t)quantize_one(__builtin_bit_cast(float, v[c].x), qs) & 0xFFu;
-            const uint32_t b1 = (uint32_t)quantize_one(__builtin_bit_cast(float, v[c].y), qs) & 0xFFu;
-            const uint32_t b2 = (uint32_t)quantize_one(__builtin_bit_cast(float, v[c].z), qs) & 0xFFu;
-            const uint32_t b3 = (uint32_t)quantize_one(__builtin_bit_cast(float, v[c].w), qs) & 0xFFu;
-            qv[g] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-        }
+        if (g < groups) qv[g] = quantize_f32x4(v[c], qs);
     }
 }
 

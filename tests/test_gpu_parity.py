@@ -348,7 +348,11 @@ def test_quantize_f32_misaligned_plain_path():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 3840, 2560), (5, 300, 1024), (16, 4096, 4096), (64, 1000, 640),
-                                   (300, 257, 320), (7, 33, 100)])
+                                   (300, 257, 320), (7, 33, 100),
+                                   # M <= 4: f32 quantised in the GEMV's prologue (one to three K parts,
+                                   # one step, the LDS limit at 1, 2 and 4 rows, ragged N)
+                                   (2, 1000, 4096), (4, 257, 8192), (1, 20000, 2560), (3, 64, 64), (2, 5, 16384),
+                                   (1, 700, 32768), (1, 2560, 6912)])
 def test_linear_f32_parity(M, N, K):
     g = synth.rng(6100 + M + N + K)
     x = g.standard_normal((M, K)).astype(np.float32)
@@ -361,7 +365,8 @@ def test_linear_f32_parity(M, N, K):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("M,N,K", [(1, 3840, 2560), (3, 130, 256), (40, 1000, 1024), (17, 33, 68), (2048, 64, 512)])
+@pytest.mark.parametrize("M,N,K", [(1, 3840, 2560), (3, 130, 256), (40, 1000, 1024), (17, 33, 68), (2048, 64, 512),
+                                   (2, 1000, 6912), (4, 37, 8192)])
 def test_linear_bias_parity(dtype, M, N, K):
     g = synth.rng(6400 + M + N + K)
     W = synth.ternary_weights(N, K, seed=6500 + M)
@@ -379,6 +384,50 @@ def test_linear_bias_parity(dtype, M, N, K):
     want = oracle.add_bias(ref, bias)
     out = tg.bitnet_linear(xd, dev(P), dev_bf16(sw), bias=dev_bf16(bias))
     assert_bf16_parity(host_bf16(out), want, f"linear+bias {dtype} {M}x{N}x{K}")
+
+
+def test_linear_f32_fused_special_rows():
+    """The GEMV prologue's f32 absmax and rounding on the rows that stress them:
+    all zeros (the eps floor), values far below the floor, and one outlier."""
+    M, N, K = 4, 300, 1024
+    g = synth.rng(6900)
+    x = g.standard_normal((M, K)).astype(np.float32)
+    x[1, :] = 0.0
+    x[2, :] = np.float32(2.0 ** -31)
+    x[3, 17] = np.float32(3.0e4)
+    W = synth.ternary_weights(N, K, seed=6901)
+    P = oracle.pack(W)
+    sw = synth.row_scales_bf16(N, seed=6902)
+    ref = oracle.linear_f32(x, P, sw)
+    out = tg.bitnet_linear(dev_f32(x), dev(P), dev_bf16(sw))
+    assert_bf16_parity(host_bf16(out), ref["out"], "linear f32 special rows")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", [(1, 3840, 2560), (2, 1000, 4096), (4, 300, 512)])
+def test_linear_ex_fused_equals_split(dtype, M, N, K):
+    """The one-launch path (quantise in the GEMV prologue, bias in its epilogue)
+    and the quantise + GEMM + bias path give the same bits: a misaligned x
+    sends the same call down the second."""
+    W = synth.ternary_weights(N, K, seed=7000 + M)
+    P = dev(oracle.pack(W))
+    sw = dev_bf16(synth.row_scales_bf16(N, seed=7001 + M))
+    bias = dev_bf16(synth.row_scales_bf16(N, seed=7002 + M, lo=-4.0, hi=4.0))
+    if dtype == "bf16":
+        xd = dev_bf16(synth.activations_bf16(M, K, seed=7003 + M))
+    else:
+        xd = dev_f32(synth.rng(7004 + M).standard_normal((M, K)).astype(np.float32))
+    for b in (None, bias):
+        fused = tg.bitnet_linear(xd, P, sw, bias=b)
+        split = tg.bitnet_linear(misaligned(xd), P, sw, bias=b)
+        assert torch.equal(fused.view(torch.int16), split.view(torch.int16)), f"{dtype} {M}x{N}x{K} bias={b is not None}"
+    if dtype == "bf16":  # bitnet_linear_ex itself with bf16 and no bias (the binding calls bitnet_linear there)
+        lib = tg.load_library()
+        o = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        st = lib.bitnet_linear_ex(o.data_ptr(), xd.data_ptr(), tg.DTYPE_BF16, P.data_ptr(), sw.data_ptr(), None,
+                                  M, N, K, None, 0, torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+        assert torch.equal(o.view(torch.int16), tg.bitnet_linear(xd, P, sw).view(torch.int16))
 
 
 # ----------------------------------------------------------------------------- INT8 weight-only (W8A16)
