@@ -5,22 +5,22 @@
 // absmax per row clamped below at 1e-5, s = absmax / 127 (IEEE fp32 division),
 // q = clamp(round_half_even(x / s), -127, 127), scale stored as bf16(s).
 //
-// Layout on gfx950: one wave64 per row, four rows per 256-thread workgroup.
-// The kernel is HBM-bound at 3 bytes per element, so what matters is keeping
-// enough bytes in flight:
-//  * quantize_rows_reg<CH> (rows of up to 512 * CH elements, K % 8 == 0): each
-//    lane loads its CH 16-byte groups of the row up front (consecutive lanes,
-//    consecutive groups), reduces the absmax on the bf16 magnitude bits (an
-//    integer max; DPP inside each 16-lane row, readlane across rows), and
-//    quantises from registers: one read of x, 8-byte int8 stores.
-//  * quantize_rows_vec (longer rows, K % 16 == 0): two passes over the row, the
-//    second re-reading it from L2.
+// Layout on gfx950.  The kernel is HBM-bound at 3 bytes per element, so what
+// matters is keeping enough bytes in flight and the per-row work short:
+//  * quantize_rows_block<CH> (rows of up to 2048 * CH elements, K % 8 == 0):
+//    one 256-thread workgroup per row; each thread loads its CH 16-byte groups
+//    of the row up front (consecutive threads, consecutive groups), the absmax
+//    is reduced on the bf16 magnitude bits (an integer max; DPP inside each
+//    wave, LDS across the four), and the row is quantised from registers: one
+//    read of x, 8-byte int8 stores.
+//  * quantize_rows_vec (longer rows, K % 16 == 0): one wave per row, two
+//    passes over the row, the second re-reading it from L2.
 //  * quantize_rows_plain: any K and alignment, one element per lane.
 //
-// RMSNorm variants (the RMS flag of quantize_rows_reg, and
+// RMSNorm variants (the RMS flag of quantize_rows_block, and
 // quantize_rows_rms_plain) normalise the row first, as the BitNet
 // activation_norm_quant of "kyegomez/BitNet issue #77" does before quantising:
-// the wave sums the exact squares of its row in double, every lane forms the
+// the exact squares of the row are summed in double, every thread forms the
 // normalised bf16 values of its registers (fp32 x * r, times the gain), and
 // the absmax and quantisation then run on those values.
 #include "bitnet_device.h"
@@ -67,38 +67,65 @@ __global__ __launch_bounds__(256) void quantize_rows_vec(int8_t* __restrict__ q,
     }
 }
 
-// Register-resident path: lane l holds the 8-element groups g = c * 64 + l
-// (c < CH) of its row.  Needs K % 8 == 0, K <= 512 * CH, 16-byte aligned x rows
-// (and gain, xn_out) and 8-byte aligned q rows.  With RMS, xn_out (when not
-// NULL) receives the normalised bf16 row.
+// Register-resident path, one workgroup per row: the 256 threads of workgroup
+// m hold the 8-element groups g = c * 256 + tid (c < CH) of row m, so a row's
+// arithmetic is spread over four waves and its loads are all in flight at
+// once.  (One wave per row, measured against it, was 1.3-2x slower at every M
+// from 5 to 4096 on the BitNet-2B-4T and LLaMA-7B widths.)  The sum of squares
+// and the absmax are reduced per wave (DPP), then over the four waves through
+// LDS in a fixed order.  Needs K % 8 == 0, K <= 2048 * CH, 16-byte aligned x
+// rows (and gain, xn_out) and 8-byte aligned q rows.  With RMS, xn_out (when
+// not NULL) receives the normalised bf16 row; without a gain the absmax of
+// the normalised row is bf16(fp32(max|x| * r)) (both roundings are monotonic,
+// r > 0), so it is reduced together with the sum of squares.
 template <int CH, bool RMS>
-__global__ __launch_bounds__(256) void quantize_rows_reg(int8_t* __restrict__ q, uint16_t* __restrict__ scale,
-                                                         uint16_t* __restrict__ xn_out,
-                                                         const uint16_t* __restrict__ x,
-                                                         const uint16_t* __restrict__ gain, float eps, int64_t M,
-                                                         int64_t K) {
-    const int lane = threadIdx.x & 63;
-    const int64_t m = (int64_t)blockIdx.x * QUANT_ROWS_PER_BLOCK + (threadIdx.x >> 6);
-    if (m >= M) return;  // wave-uniform
+__global__ __launch_bounds__(256) void quantize_rows_block(int8_t* __restrict__ q, uint16_t* __restrict__ scale,
+                                                           uint16_t* __restrict__ xn_out,
+                                                           const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ gain, float eps, int64_t M,
+                                                           int64_t K) {
+    constexpr int WAVES = 4;
+    __shared__ double red_d[WAVES];
+    __shared__ uint32_t red_a[WAVES];  // absmax of x (RMS without a gain)
+    __shared__ uint32_t red_b[WAVES];  // absmax of the values to quantise
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t m = blockIdx.x;
     const int groups = (int)(K >> 3);
     const uint4* xv = reinterpret_cast<const uint4*>(x + m * K);
     uint4 v[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int g = c * 64 + lane;
-        v[c] = g < groups ? xv[g] : make_uint4(0u, 0u, 0u, 0u);  // zeros do not change the absmax
+        const int g = c * 256 + tid;
+        v[c] = g < groups ? xv[g] : make_uint4(0u, 0u, 0u, 0u);  // zeros change neither sum nor absmax
     }
+    auto absmax = [&]() {
+        uint32_t a = 0u;
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+            a = max(a, max(max(absmax_bf16x2(v[c].x), absmax_bf16x2(v[c].y)),
+                           max(absmax_bf16x2(v[c].z), absmax_bf16x2(v[c].w))));
+        return wave_max_u32(a);
+    };
+    uint32_t amax = 0u;
+    bool have_amax = false;
     if constexpr (RMS) {
         double ss = 0.0;
 #pragma unroll
         for (int c = 0; c < CH; ++c) ss += sum_sq_bf16x8(v[c]);
-        const float r = rms_inv(wave_sum_f64(ss), (int)K, eps);
-        // the gain row is shared by every row (cached); it is read only now,
-        // so that it does not hold registers across the reduction
+        ss = wave_sum_f64(ss);
+        const uint32_t a = gain == nullptr ? absmax() : 0u;  // wave-uniform
+        if (lane == 0) {
+            red_d[wave] = ss;
+            red_a[wave] = a;
+        }
+        __syncthreads();
+        const float r = rms_inv(((red_d[0] + red_d[1]) + red_d[2]) + red_d[3], (int)K, eps);
         const uint4* gv = reinterpret_cast<const uint4*>(gain);
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int g = c * 64 + lane;
+            const int g = c * 256 + tid;
             const uint4 gw = (gain != nullptr && g < groups) ? gv[g]
                                                              : make_uint4(BF16X2_ONE, BF16X2_ONE, BF16X2_ONE, BF16X2_ONE);
             v[c] = rms_apply_bf16x8(v[c], gw, r);  // zero padding stays zero
@@ -107,21 +134,26 @@ __global__ __launch_bounds__(256) void quantize_rows_reg(int8_t* __restrict__ q,
             uint4* xo = reinterpret_cast<uint4*>(xn_out + m * K);
 #pragma unroll
             for (int c = 0; c < CH; ++c)
-                if (c * 64 + lane < groups) xo[c * 64 + lane] = v[c];
+                if (c * 256 + tid < groups) xo[c * 256 + tid] = v[c];
+        }
+        if (gain == nullptr) {
+            const uint32_t ax = max(max(red_a[0], red_a[1]), max(red_a[2], red_a[3]));
+            amax = (uint32_t)f32_to_bf16(bf16_to_f32(ax) * r) & 0x7FFFu;
+            have_amax = true;
         }
     }
-    uint32_t amax = 0;
-#pragma unroll
-    for (int c = 0; c < CH; ++c)
-        amax = max(amax, max(max(absmax_bf16x2(v[c].x), absmax_bf16x2(v[c].y)),
-                             max(absmax_bf16x2(v[c].z), absmax_bf16x2(v[c].w))));
-    amax = wave_max_u32(amax);
+    if (!have_amax) {  // workgroup-uniform
+        const uint32_t a = absmax();
+        if (lane == 0) red_b[wave] = a;
+        __syncthreads();
+        amax = max(max(red_b[0], red_b[1]), max(red_b[2], red_b[3]));
+    }
     const QuantScale qs = quant_scale(amax);
-    if (lane == 0) scale[m] = f32_to_bf16(qs.s);
+    if (tid == 0) scale[m] = f32_to_bf16(qs.s);
     uint2* qv = reinterpret_cast<uint2*>(q + m * K);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int g = c * 64 + lane;
+        const int g = c * 256 + tid;
         if (g < groups) qv[g] = quantize_bf16x8(v[c], qs);
     }
 }
@@ -232,24 +264,20 @@ __global__ __launch_bounds__(256) void quantize_rows_f32_plain(int8_t* __restric
 namespace {
 
 template <bool RMS>
-void launch_rows_reg(int64_t ch, dim3 grid, hipStream_t s, int8_t* q, uint16_t* scale, uint16_t* xn,
-                     const uint16_t* x, const uint16_t* gain, float eps, int64_t M, int64_t K) {
-    const dim3 block(256);
-    if (ch <= 2)
-        hipLaunchKernelGGL((quantize_rows_reg<2, RMS>), grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
+void launch_rows_block(hipStream_t s, int8_t* q, uint16_t* scale, uint16_t* xn, const uint16_t* x,
+                       const uint16_t* gain, float eps, int64_t M, int64_t K) {
+    const int64_t ch = (K / 8 + 255) / 256;
+    const dim3 grid((unsigned)M), block(256);
+    if (ch <= 1)
+        hipLaunchKernelGGL((quantize_rows_block<1, RMS>), grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
+    else if (ch <= 2)
+        hipLaunchKernelGGL((quantize_rows_block<2, RMS>), grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
     else if (ch <= 4)
-        hipLaunchKernelGGL((quantize_rows_reg<4, RMS>), grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
-    else if (ch <= 8)
-        hipLaunchKernelGGL((quantize_rows_reg<8, RMS>), grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
-    else if (ch <= 12)
-        hipLaunchKernelGGL((quantize_rows_reg<12, RMS>), grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
-    else if (ch <= 16)
-        hipLaunchKernelGGL((quantize_rows_reg<16, RMS>), grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
-    else if (ch <= 24)
-        hipLaunchKernelGGL((quantize_rows_reg<24, RMS>), grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
+        hipLaunchKernelGGL((quantize_rows_block<4, RMS>), grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
     else
-        hipLaunchKernelGGL((quantize_rows_reg<32, RMS>), grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
+        hipLaunchKernelGGL((quantize_rows_block<8, RMS>), grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
 }
+
 
 }  // namespace
 
@@ -257,8 +285,8 @@ hipError_t launch_quantize(int8_t* q, uint16_t* scale, const uint16_t* x, int64_
     if (M <= 0) return hipSuccess;
     const int64_t blocks = (M + QUANT_ROWS_PER_BLOCK - 1) / QUANT_ROWS_PER_BLOCK;
     const dim3 grid((unsigned)blocks), block(256);
-    if (K % 8 == 0 && aligned16(x) && reinterpret_cast<uintptr_t>(q) % 8 == 0 && K <= 512 * 32) {
-        launch_rows_reg<false>((K / 8 + 63) / 64, grid, s, q, scale, nullptr, x, nullptr, 0.0f, M, K);
+    if (K % 8 == 0 && aligned16(x) && reinterpret_cast<uintptr_t>(q) % 8 == 0 && K <= 2048 * 8) {
+        launch_rows_block<false>(s, q, scale, nullptr, x, nullptr, 0.0f, M, K);
     } else if (K % 16 == 0 && aligned16(x) && aligned16(q)) {
         hipLaunchKernelGGL(quantize_rows_vec, grid, block, 0, s, q, scale, x, M, K);
     } else {
@@ -272,10 +300,10 @@ hipError_t launch_quantize_rms(int8_t* q, uint16_t* scale, uint16_t* xn, const u
     if (M <= 0) return hipSuccess;
     const int64_t blocks = (M + QUANT_ROWS_PER_BLOCK - 1) / QUANT_ROWS_PER_BLOCK;
     const dim3 grid((unsigned)blocks), block(256);
-    const bool vec = K % 8 == 0 && K <= 512 * 32 && aligned16(x) && (gain == nullptr || aligned16(gain)) &&
+    const bool vec = K % 8 == 0 && K <= 2048 * 8 && aligned16(x) && (gain == nullptr || aligned16(gain)) &&
                      (xn == nullptr || aligned16(xn)) && reinterpret_cast<uintptr_t>(q) % 8 == 0;
     if (vec)
-        launch_rows_reg<true>((K / 8 + 63) / 64, grid, s, q, scale, xn, x, gain, eps, M, K);
+        launch_rows_block<true>(s, q, scale, xn, x, gain, eps, M, K);
     else
         hipLaunchKernelGGL(quantize_rows_rms_plain, grid, block, 0, s, q, scale, xn, x, gain, eps, M, K);
     return hipGetLastError();

@@ -68,8 +68,11 @@ def problem(M, N, K, seed, outliers=0.0, row_scales=False):
 # ----------------------------------------------------------------------------- quantisation
 
 QUANT_SHAPES = [(4, 256), (1, 4), (3, 12), (7, 100), (16, 2560), (33, 4096), (5, 6912), (2, 131072), (130, 64),
-                # two rows per wave (M >= 2048), with an odd last wave
-                (2049, 4096), (2051, 6912), (2053, 520)]
+                # many rows (one workgroup each)
+                (2049, 4096), (2051, 6912), (2053, 520),
+                # each register depth of the workgroup-per-row kernel, full and ragged last chunks, and the
+                # first lengths past it (two-pass and plain kernels)
+                (1, 2048), (1, 2056), (3, 8192), (9, 12000), (3, 16384), (5, 16400), (2, 16392)]
 
 
 @pytest.mark.parametrize("M,K", QUANT_SHAPES)
@@ -540,7 +543,8 @@ def check_rms_quantize(x, gain, eps, q, sa, xn, what):
         assert ok.all(), f"{what} {name}: rows {np.nonzero(~ok)[0][:8].tolist()} differ (ambiguous rows: {int(amb.sum())})"
 
 
-RMS_QUANT_SHAPES = [(1, 2560), (4, 6912), (16, 4096), (33, 11008), (5, 100), (3, 20000), (2049, 2560), (7, 8)]
+RMS_QUANT_SHAPES = [(1, 2560), (4, 6912), (16, 4096), (33, 11008), (5, 100), (3, 20000), (2049, 2560), (7, 8),
+                    (2, 2048), (3, 16384), (65, 640)]
 
 
 @pytest.mark.parametrize("with_gain", [False, True])
