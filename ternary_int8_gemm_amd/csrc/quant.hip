@@ -214,31 +214,36 @@ __global__ __launch_bounds__(256) void quantize_rows_rms_plain(int8_t* __restric
 // The same quantisation on f32 activations (quantize_activation accepts bf16
 // or f32): the absmax is an integer max over the f32 magnitude bits (the
 // order of non-negative finite floats), and q comes from the same exact
-// division.  Lane l holds the 4-element groups g = c * 64 + l (c < CH).
+// division.  One 256-thread workgroup per row, as quantize_rows_block: thread
+// t holds the 4-element groups g = c * 256 + t (c < CH).
 template <int CH>
-__global__ __launch_bounds__(256) void quantize_rows_f32_reg(int8_t* __restrict__ q, uint16_t* __restrict__ scale,
-                                                             const float* __restrict__ x, int64_t M, int64_t K) {
-    const int lane = threadIdx.x & 63;
-    const int64_t m = (int64_t)blockIdx.x * QUANT_ROWS_PER_BLOCK + (threadIdx.x >> 6);
-    if (m >= M) return;  // wave-uniform
+__global__ __launch_bounds__(256) void quantize_rows_f32_block(int8_t* __restrict__ q, uint16_t* __restrict__ scale,
+                                                               const float* __restrict__ x, int64_t M, int64_t K) {
+    constexpr int WAVES = 4;
+    __shared__ uint32_t red[WAVES];
+    const int tid = threadIdx.x;
+    const int64_t m = blockIdx.x;
     const int groups = (int)(K >> 2);
     const uint4* xv = reinterpret_cast<const uint4*>(x + m * K);
     uint4 v[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int g = c * 64 + lane;
+        const int g = c * 256 + tid;
         v[c] = g < groups ? xv[g] : make_uint4(0u, 0u, 0u, 0u);
     }
     uint32_t amax = 0;
 #pragma unroll
     for (int c = 0; c < CH; ++c) amax = max(amax, absmax_f32x4(v[c]));
     amax = wave_max_u32(amax);
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = max(max(red[0], red[1]), max(red[2], red[3]));
     const QuantScale qs = quant_scale_f32(__builtin_bit_cast(float, amax));
-    if (lane == 0) scale[m] = f32_to_bf16(qs.s);
+    if (tid == 0) scale[m] = f32_to_bf16(qs.s);
     uint32_t* qv = reinterpret_cast<uint32_t*>(q + m * K);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int g = c * 64 + lane;
+        const int g = c * 256 + tid;
         if (g < groups) qv[g] = quantize_f32x4(v[c], qs);
     }
 }
@@ -311,18 +316,22 @@ hipError_t launch_quantize_rms(int8_t* q, uint16_t* scale, uint16_t* xn, const u
 
 hipError_t launch_quantize_f32(int8_t* q, uint16_t* scale, const float* x, int64_t M, int64_t K, hipStream_t s) {
     if (M <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((M + QUANT_ROWS_PER_BLOCK - 1) / QUANT_ROWS_PER_BLOCK)), block(256);
-    if (K % 4 == 0 && aligned16(x) && reinterpret_cast<uintptr_t>(q) % 4 == 0 && K <= 256 * 32) {
-        const int64_t ch = (K / 4 + 63) / 64;  // 16-byte groups per lane
-        if (ch <= 4)
-            hipLaunchKernelGGL(quantize_rows_f32_reg<4>, grid, block, 0, s, q, scale, x, M, K);
+    const dim3 block(256);
+    if (K % 4 == 0 && aligned16(x) && reinterpret_cast<uintptr_t>(q) % 4 == 0 && K <= 1024 * 16) {
+        const dim3 grid((unsigned)M);
+        const int64_t ch = (K / 4 + 255) / 256;  // 16-byte groups per thread
+        if (ch <= 1)
+            hipLaunchKernelGGL(quantize_rows_f32_block<1>, grid, block, 0, s, q, scale, x, M, K);
+        else if (ch <= 2)
+            hipLaunchKernelGGL(quantize_rows_f32_block<2>, grid, block, 0, s, q, scale, x, M, K);
+        else if (ch <= 4)
+            hipLaunchKernelGGL(quantize_rows_f32_block<4>, grid, block, 0, s, q, scale, x, M, K);
         else if (ch <= 8)
-            hipLaunchKernelGGL(quantize_rows_f32_reg<8>, grid, block, 0, s, q, scale, x, M, K);
-        else if (ch <= 16)
-            hipLaunchKernelGGL(quantize_rows_f32_reg<16>, grid, block, 0, s, q, scale, x, M, K);
+            hipLaunchKernelGGL(quantize_rows_f32_block<8>, grid, block, 0, s, q, scale, x, M, K);
         else
-            hipLaunchKernelGGL(quantize_rows_f32_reg<32>, grid, block, 0, s, q, scale, x, M, K);
+            hipLaunchKernelGGL(quantize_rows_f32_block<16>, grid, block, 0, s, q, scale, x, M, K);
     } else {
+        const dim3 grid((unsigned)((M + QUANT_ROWS_PER_BLOCK - 1) / QUANT_ROWS_PER_BLOCK));
         hipLaunchKernelGGL(quantize_rows_f32_plain, grid, block, 0, s, q, scale, x, M, K);
     }
     return hipGetLastError();

@@ -311,6 +311,7 @@ def dev_f32(a):
 
 
 F32_QUANT_SHAPES = [(4, 256), (1, 4), (3, 12), (7, 100), (16, 2560), (33, 4096), (5, 6912), (2, 131072), (130, 64),
+                    (1, 1024), (1, 1028), (3, 16384), (2, 16388), (2049, 4096),
                     (3, 8192), (2, 8196)]
 
 
