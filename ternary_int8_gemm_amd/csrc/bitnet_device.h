@@ -120,18 +120,19 @@ __device__ __forceinline__ float rms_inv(double sum_sq, int K, float eps) {
     return 1.0f / __builtin_sqrtf(v);
 }
 
-// Sum of the squares of the eight bf16 values of a 16-byte group, in double.
+// Sum of the squares of the eight bf16 values of a 16-byte group, in double,
+// as a tree (each square is exact in double; the order of the additions is
+// free within the bound the oracle allows for any order).
 __device__ __forceinline__ double sum_sq_bf16x8(const uint4& v) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    double s = 0.0;
+    double p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const double a = (double)bf16_to_f32(w[i] & 0xFFFFu);
         const double b = (double)bf16_to_f32(w[i] >> 16);
-        s += a * a;
-        s += b * b;
+        p[i] = a * a + b * b;
     }
-    return s;
+    return (p[0] + p[1]) + (p[2] + p[3]);
 }
 
 // Two normalised bf16 values from two bf16 inputs and their two bf16 gains.
@@ -139,6 +140,19 @@ __device__ __forceinline__ uint32_t rms_apply_bf16x2(uint32_t xw, uint32_t gw, f
     const float t0 = (bf16_to_f32(xw & 0xFFFFu) * r) * bf16_to_f32(gw & 0xFFFFu);
     const float t1 = (bf16_to_f32(xw >> 16) * r) * bf16_to_f32(gw >> 16);
     return (uint32_t)f32_to_bf16(t0) | ((uint32_t)f32_to_bf16(t1) << 16);
+}
+
+// The same without a gain: bf16(fp32(x * r)), which is what multiplying by a
+// gain of exactly 1 gives.
+__device__ __forceinline__ uint32_t rms_scale_bf16x2(uint32_t xw, float r) {
+    const float t0 = bf16_to_f32(xw & 0xFFFFu) * r;
+    const float t1 = bf16_to_f32(xw >> 16) * r;
+    return (uint32_t)f32_to_bf16(t0) | ((uint32_t)f32_to_bf16(t1) << 16);
+}
+
+__device__ __forceinline__ uint4 rms_scale_bf16x8(const uint4& x, float r) {
+    return make_uint4(rms_scale_bf16x2(x.x, r), rms_scale_bf16x2(x.y, r), rms_scale_bf16x2(x.z, r),
+                      rms_scale_bf16x2(x.w, r));
 }
 
 __device__ __forceinline__ uint4 rms_apply_bf16x8(const uint4& x, const uint4& g, float r) {

@@ -433,8 +433,13 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
             float r = rr[0];
 #pragma unroll
             for (int m = 1; m < MT; ++m) r = (xm[i] == m) ? rr[m] : r;
-            xr[i][0] = rms_apply_bf16x8(xr[i][0], gr[i][0], r);  // zero words stay zero
-            xr[i][1] = rms_apply_bf16x8(xr[i][1], gr[i][1], r);
+            if (gain == nullptr) {  // wave-uniform; the same bits as a gain of 1
+                xr[i][0] = rms_scale_bf16x8(xr[i][0], r);  // zero words stay zero
+                xr[i][1] = rms_scale_bf16x8(xr[i][1], r);
+            } else {
+                xr[i][0] = rms_apply_bf16x8(xr[i][0], gr[i][0], r);
+                xr[i][1] = rms_apply_bf16x8(xr[i][1], gr[i][1], r);
+            }
         }
     }
     if (!RMS || gain != nullptr) {

@@ -123,12 +123,16 @@ __global__ __launch_bounds__(256) void quantize_rows_block(int8_t* __restrict__ 
         __syncthreads();
         const float r = rms_inv(((red_d[0] + red_d[1]) + red_d[2]) + red_d[3], (int)K, eps);
         const uint4* gv = reinterpret_cast<const uint4*>(gain);
+        if (gain == nullptr) {  // the same bits as a gain of 1
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int g = c * 256 + tid;
-            const uint4 gw = (gain != nullptr && g < groups) ? gv[g]
-                                                             : make_uint4(BF16X2_ONE, BF16X2_ONE, BF16X2_ONE, BF16X2_ONE);
-            v[c] = rms_apply_bf16x8(v[c], gw, r);  // zero padding stays zero
+            for (int c = 0; c < CH; ++c) v[c] = rms_scale_bf16x8(v[c], r);  // zero padding stays zero
+        } else {
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int g = c * 256 + tid;
+                const uint4 gw = g < groups ? gv[g] : make_uint4(BF16X2_ONE, BF16X2_ONE, BF16X2_ONE, BF16X2_ONE);
+                v[c] = rms_apply_bf16x8(v[c], gw, r);
+            }
         }
         if (xn_out != nullptr) {
             uint4* xo = reinterpret_cast<uint4*>(xn_out + m * K);
