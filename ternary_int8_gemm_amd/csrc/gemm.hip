@@ -113,6 +113,10 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
                       const uint16_t* __restrict__ sw, int M, int N, int K, int tiles_m, int tiles_n) {
     using S = GemmShape<BM, BN, WAVES_M, WAVES_N>;
     constexpr int MT = S::MT, NT = S::NT, A_CH = S::A_CH, B_CH = S::B_CH;
+    // k-steps by which A fragment reads run ahead of their MFMAs: two for
+    // 64-row wave tiles (measured: 0.3-1.5% at M = 2048 on two boxes), one for 128-row tiles,
+    // whose register budget the extra fragments would exceed
+    constexpr int A_AHEAD = MT <= 2 ? 2 : 1;
     extern __shared__ __align__(16) uint8_t lds[];
     int* rowsum = reinterpret_cast<int*>(lds + 3 * S::STAGE);
     float* rowscale = reinterpret_cast<float*>(lds + 3 * S::STAGE + 4 * BM);
@@ -208,15 +212,19 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
         rs[i] += live * sum;
     };
 
-    // Fragments a step needs first: the packed B dwords of the whole stage and
-    // the A fragments of its first k-step.  The previous step reads them.
-    auto read_first = [&](const uint8_t* base, v4u (&pb)[NT], v4i (&af)[MT]) {
-        const uint8_t* A = base + (wm * MT) * 4 * GM_FRAG;
+    // Fragment reads: the packed B dwords of a whole stage, and the A
+    // fragments of k-step s.  A reads run A_AHEAD k-steps ahead of their
+    // MFMAs; the previous step reads the B dwords and the first A_AHEAD
+    // k-steps' A fragments of the next stage.
+    auto read_b = [&](const uint8_t* base, v4u (&pb)[NT]) {
         const uint8_t* B = base + S::A_STAGE + (wn * NT) * GM_FRAG;
 #pragma unroll
         for (int u = 0; u < NT; ++u) pb[u] = *reinterpret_cast<const v4u*>(B + u * GM_FRAG + b_rd);
+    };
+    auto read_a = [&](const uint8_t* base, int s, v4i (&af)[MT]) {
+        const uint8_t* A = base + (wm * MT) * 4 * GM_FRAG;
 #pragma unroll
-        for (int t = 0; t < MT; ++t) af[t] = *reinterpret_cast<const v4i*>(A + (t * 4) * GM_FRAG + a_rd[0]);
+        for (int t = 0; t < MT; ++t) af[t] = *reinterpret_cast<const v4i*>(A + (t * 4 + s) * GM_FRAG + a_rd[s]);
     };
 
     // One pipeline step k, between two barriers, with LDS buffer bi = k % 3:
@@ -229,7 +237,7 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
     // reads are issued before the MFMAs of the previous k-step, and the stores
     // of stage k+2 are spread over the k-steps.
     v4u pb[NT];
-    v4i af0[MT];
+    v4i afn[A_AHEAD][MT];  // the next stage's first A_AHEAD k-steps
     auto step = [&](const int bi, int k, const StageRegs<A_CH, B_CH>& SS, StageRegs<A_CH, B_CH>& SL) {
         __syncthreads();  // stage k+1 visible; buffer (k+2) % 3 no longer read
         // The global loads go out at raised wave priority, so that a wave leaving
@@ -243,19 +251,23 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
         uint8_t* later = lds + ((bi + 2) % 3) * S::STAGE;
         const uint8_t* next = lds + ((bi + 1) % 3) * S::STAGE;
         const int live = (k + 2 < nk) ? 1 : 0;
-        const uint8_t* A = cur + (wm * MT) * 4 * GM_FRAG;
-        v4i af[2][MT];
+        constexpr int R = A_AHEAD + 1;  // A fragment sets in flight
+        v4i af[R][MT];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) af[0][t] = af0[t];
+        for (int j = 0; j < A_AHEAD; ++j)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) af[j][t] = afn[j][t];
         v4u pbc[NT];
 #pragma unroll
         for (int u = 0; u < NT; ++u) pbc[u] = pb[u];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            if (s < 3) {
-#pragma unroll
-                for (int t = 0; t < MT; ++t)
-                    af[(s + 1) & 1][t] = *reinterpret_cast<const v4i*>(A + (t * 4 + s + 1) * GM_FRAG + a_rd[s + 1]);
+            if (s + A_AHEAD < 4) {
+                read_a(cur, s + A_AHEAD, af[(s + A_AHEAD) % R]);
+            } else {  // k-step sn of the next stage (written during step k - 1)
+                const int sn = s + A_AHEAD - 4;
+                if (sn == 0) read_b(next, pb);
+                read_a(next, sn, afn[sn]);
             }
 #pragma unroll
             for (int i = 0; i < A_CH; ++i)
@@ -264,7 +276,6 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
 #pragma unroll
                 for (int j = 0; j < B_CH; ++j) *reinterpret_cast<v4u*>(later + b_off[j]) = SS.b[j];
             }
-            if (s == 3) read_first(next, pb, af0);
 #pragma unroll
             for (int u = 0; u < NT; ++u) {
                 const uint32_t p = pbc[u][s];
@@ -272,7 +283,7 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
                                 (int)((p >> 6) & CODE_MASK)};
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
-                    acc[t][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s & 1][t], bf, acc[t][u], 0, 0, 0);
+                    acc[t][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s % R][t], bf, acc[t][u], 0, 0, 0);
             }
         }
     };
@@ -294,7 +305,9 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
     for (int j = 0; j < B_CH; ++j) *reinterpret_cast<v4u*>(lds + S::STAGE + b_off[j]) = sets[1].b[j];
     load_stage(NS, sets[0]);
     __syncthreads();
-    read_first(lds, pb, af0);
+    read_b(lds, pb);
+#pragma unroll
+    for (int j = 0; j < A_AHEAD; ++j) read_a(lds, j, afn[j]);
     // stage k + i sits in LDS buffer (k + i) % 3; k advances by NS, so with
     // NS a multiple of 3 that is the constant i % 3
     int k = 0;
