@@ -23,6 +23,9 @@ Profiling helpers (not part of the timed benchmark):
                                           output folders into profiles/gemv_lm_head_m1_traffic.{json,md}
   python bench.py --summarize-trace T     turn a rocprofv3 --kernel-trace --stats csv output folder
                                           into a per-kernel, per-grid table on stdout
+  python bench.py --pmc-target-gemm       eager launches for the counter passes over the M=2048 GEMM
+  python bench.py --summarize-gemm-pmc A B F W
+                                          turn those four passes into profiles/gemm_m2048_qkvo_counters.md
 """
 import argparse
 import csv
@@ -596,6 +599,105 @@ def summarize_pmc(fetch_dir, write_dir):
     print(json.dumps(out))
 
 
+GEMM_PMC_FILE = os.path.join(ROOT, "profiles", "gemm_m2048_qkvo_counters.md")
+GEMM_PMC_PASSES = {  # pass name -> counters (each pass a run of its own)
+    "a": "SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_VALU_MFMA_COEXEC_CYCLES",
+    "b": "SQ_WAIT_INST_ANY SQ_WAVE_CYCLES SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS SQ_BUSY_CYCLES",
+    "fetch": "FETCH_SIZE",
+    "write": "WRITE_SIZE",
+}
+GEMM_PMC_WARM, GEMM_PMC_REPS = 300, 20
+
+
+def run_pmc_target_gemm(device):
+    """Eager launches for counter passes over the prefill GEMM: a plain copy of
+    CALIB_COPY_BYTES (byte-counter calibration), then GEMM_PMC_WARM +
+    GEMM_PMC_REPS launches of bitnet_gemm on the LLaMA-7B qkvo shape at M=2048
+    (pre-quantised activations); the summary keeps the last GEMM_PMC_REPS, when
+    the clocks have settled."""
+    a = torch.full((CALIB_COPY_BYTES,), 7, dtype=torch.uint8, device=device)
+    b = torch.empty_like(a)
+    i, (name, N, K) = next((i, sh) for i, sh in enumerate(synth.LLAMA7B_SHAPES) if sh[0] == "qkvo")
+    M = 2048
+    P = tg.pack_weights(torch.from_numpy(synth.ternary_weights(N, K, synth.seed_for(3, 16 * i + synth.T_WEIGHT)))).to(device)
+    sw = dev_bf16(synth.weight_scale_bf16(N, K, synth.seed_for(3, 16 * i + synth.T_SCALE)), device)
+    x = dev_bf16(synth.activations_bf16(M, K, synth.seed_for(3, 16 * i + synth.T_ACT), outlier_frac=0.01), device)
+    q, sa = tg.quantize_activation(x)
+    o = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    for _ in range(GEMM_PMC_WARM + GEMM_PMC_REPS):
+        tg.bitnet_gemm(q, P, sa, sw, out=o)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_target_gemm": "done", "M": M, "N": N, "K": K,
+                      "launches": GEMM_PMC_WARM + GEMM_PMC_REPS}), flush=True)
+
+
+def summarize_gemm_pmc(dirs):
+    """Markdown summary of the four counter passes of run_pmc_target_gemm (the
+    directories in GEMM_PMC_PASSES order): per-launch averages over the last
+    GEMM_PMC_REPS GEMM dispatches of each pass."""
+    vals, durs, calib = {}, [], {}
+    for (pname, counters), folder in zip(GEMM_PMC_PASSES.items(), dirs):
+        rows = _csv_rows(folder, "counter_collection.csv")
+        gemm_ids = sorted({int(_col(r, "Dispatch_Id")) for r in rows if "gemm_mfma_kernel" in _col(r, "Kernel_Name")})
+        keep = set(gemm_ids[-GEMM_PMC_REPS:])
+        if len(keep) < GEMM_PMC_REPS:
+            raise SystemExit(f"pass {pname}: only {len(keep)} GEMM dispatches in {folder}")
+        seen_dur = set()
+        for r in rows:
+            did = int(_col(r, "Dispatch_Id"))
+            cname = _col(r, "Counter_Name")
+            v = float(_col(r, "Counter_Value"))
+            if did in keep:
+                vals.setdefault(cname, []).append(v)
+                if pname == "a" and did not in seen_dur:
+                    seen_dur.add(did)
+                    durs.append(float(_col(r, "End_Timestamp")) - float(_col(r, "Start_Timestamp")))
+            elif "copyBuffer" in _col(r, "Kernel_Name") and cname in ("FETCH_SIZE", "WRITE_SIZE"):
+                calib.setdefault(cname, []).append(v)
+    avg = {k: sum(v) / len(v) for k, v in vals.items()}
+    dur_ns = sum(durs) / len(durs)
+    i, (name, N, K) = next((i, sh) for i, sh in enumerate(synth.LLAMA7B_SHAPES) if sh[0] == "qkvo")
+    M = 2048
+    simds, clk = 256 * 4, 2.4e9
+    mfma_cycles = 32.0  # v_mfma_i32_32x32x32_i8 per SIMD
+    busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"]
+    factor = {c: CALIB_COPY_BYTES / (1024.0 * max(v)) for c, v in calib.items()}
+    fetch_b = avg["FETCH_SIZE"] * 1024.0 * factor["FETCH_SIZE"]
+    write_b = avg["WRITE_SIZE"] * 1024.0 * factor["WRITE_SIZE"]
+    algo = gemm_bytes(M, N, K)
+    cmds = [f"timeout -s KILL 90 rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_gemm_{p} -o run -- "
+            "python3 bench.py --pmc-target-gemm" for p, c in GEMM_PMC_PASSES.items()]
+    cmds.append("python bench.py --summarize-gemm-pmc " + " ".join(f"gpurun_out/pmc_gemm_{p}" for p in GEMM_PMC_PASSES))
+    md = [f"# Counters of the prefill GEMM (bitnet_gemm, LLaMA-7B qkvo, M={M}, N={N}, K={K})", "",
+          "Commands (each pass a run of its own, from the repository root after `cd /tmp && export TMPDIR=/tmp`):", ""]
+    md += ["    " + c for c in cmds]
+    md += ["", f"Per-launch averages over the last {GEMM_PMC_REPS} of {GEMM_PMC_WARM + GEMM_PMC_REPS} eager launches "
+           "(`gemm_mfma_kernel<128, 256, 2, 4, 2, 3, false>`, 256 workgroups of 8 waves).", "",
+           "| quantity | value |", "|---|---:|",
+           f"| dispatch duration (profiled) | {dur_ns / 1e3:.2f} µs |",
+           f"| SQ_INSTS_MFMA | {avg['SQ_INSTS_MFMA']:.0f} (2MNK / 65536 = {2 * M * N * K // 65536}) |",
+           f"| SQ_VALU_MFMA_BUSY_CYCLES | {busy:.4g} ({busy / avg['SQ_INSTS_MFMA']:.1f} per MFMA) |",
+           f"| MFMA busy / (duration × 2.4 GHz × {simds} SIMDs) | {busy / (dur_ns * 1e-9 * clk * simds):.3f} |",
+           f"| VALU instructions per MFMA | {avg['SQ_INSTS_VALU'] / avg['SQ_INSTS_MFMA']:.2f} |",
+           f"| MFMA cycles with VALU co-issued (COEXEC / MFMA busy) | {avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / busy:.3f} |",
+           f"| LDS instructions per MFMA | {avg['SQ_INSTS_LDS'] / avg['SQ_INSTS_MFMA']:.2f} |",
+           f"| LDS bank-conflict cycles per LDS instruction | {avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_INSTS_LDS']:.2f} |",
+           f"| SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES | {avg['SQ_WAIT_INST_ANY'] / avg['SQ_WAVE_CYCLES']:.3f} |",
+           f"| SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES | {avg['SQ_WAIT_INST_LDS'] / avg['SQ_WAVE_CYCLES']:.3f} |",
+           f"| HBM bytes (FETCH_SIZE × {factor['FETCH_SIZE']:.3f} + WRITE_SIZE × {factor['WRITE_SIZE']:.3f}) | "
+           f"{fetch_b + write_b:.4g} ({(fetch_b + write_b) / algo:.2f} × the {algo} algorithmic bytes) |"]
+    md += ["", "The byte counters are scaled by what they read for a plain device copy of 256 MiB in the same run.",
+           "The MFMA peak used for the fraction is the dense int8 rate at 2.4 GHz: 1024 SIMDs × 32768 MACs per",
+           "32 cycles = 5.0 POPS."]
+    with open(GEMM_PMC_FILE, "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -610,6 +712,8 @@ def main():
     ap.add_argument("--pmc-target", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
+    ap.add_argument("--pmc-target-gemm", action="store_true")
+    ap.add_argument("--summarize-gemm-pmc", nargs=4, metavar=("A_DIR", "B_DIR", "FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -618,10 +722,12 @@ def main():
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
         return
+    if args.summarize_gemm_pmc:
+        summarize_gemm_pmc(args.summarize_gemm_pmc)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: there is no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     def log(msg):
@@ -633,6 +739,9 @@ def main():
     tg.load_library()
     if args.pmc_target:
         run_pmc_target(device)
+        return
+    if args.pmc_target_gemm:
+        run_pmc_target_gemm(device)
         return
     stream = torch.cuda.Stream(device)
 

@@ -34,7 +34,8 @@
 //    mean fewer LDS bytes per MAC; the register file bounds them.
 //  * LDS slots are XOR-swizzled so that the staging writes (8 rows x 8 groups
 //    per instruction for A; 32 columns x 2 halves for B) and the fragment reads
-//    (lane-contiguous) both keep every 16 lanes on distinct 16-byte bank groups.
+//    (lane-contiguous) keep every 8 and every 16 consecutive lanes on distinct
+//    16-byte bank groups.
 //  * Global loads are issued four stages ahead into three register sets; LDS
 //    holds three stages, so a stage is stored two steps before it is multiplied
 //    and the first fragments of the next stage are read at the end of each step
@@ -89,11 +90,14 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 }
 
 // Byte offset, within a 1 KB A fragment of k-step s, of the 16-byte slot of
-// fragment lane l (row l % 32, lane half h = l / 32).  Staging writes: 16
-// consecutive lanes are two rows x the eight groups 2h' + ... of a 128-byte row
-// chunk, which the XOR with 2 * (4h + s) spreads over 16 distinct slots mod 16;
-// fragment reads: 16 consecutive lanes share h, so an XOR keeps them distinct.
-__device__ __forceinline__ int a_slot(int l, int s) { return (l ^ (2 * (4 * (l >> 5) + s))) * 16; }
+// fragment lane l (row l % 32, lane half h = l / 32).  Staging writes: eight
+// consecutive lanes are one row's eight (h, s) groups, which the XOR with
+// 2s + 9h sends to eight distinct slots mod 8, and sixteen consecutive lanes
+// (two rows) to sixteen distinct slots mod 16; fragment reads: 16 consecutive
+// lanes share h and s, so the XOR keeps them distinct.  (The counters read no
+// LDS bank conflicts with it; an XOR with 2s + 8h left 1.2 conflict cycles per
+// LDS instruction, at the same speed.)
+__device__ __forceinline__ int a_slot(int l, int s) { return (l ^ (2 * s + 9 * (l >> 5))) * 16; }
 
 // Byte offset, within the 1 KB packed B tile of 32 columns, of half h of
 // column n (n < 32): 16 consecutive columns of one half fall on 16 distinct
