@@ -46,6 +46,12 @@
 // wave taking a contiguous range of its steps; the exact int32 partial sums
 // meet in LDS before the correction and the epilogue.
 //
+// For bitnet_linear_ex the same kernel takes f32 activations (XF32: the f32
+// rows quantised as they are, with the f32 absmax) and a bias on the bf16
+// outputs (BIAS: each workgroup stages its rows' bias values in LDS beside the
+// weight scales); both are template variants, so a plain call runs the
+// unchanged kernel.
+//
 // gemv_chunked_kernel (longer activations): each wave owns 8*RB rows and K is
 // processed in LDS-sized chunks, with the same unpack and reduction.
 //

@@ -6,6 +6,9 @@
   graph, the benchmark's launch mode.
 * The same shapes at M=16 (split quantise + GEMM path of bitnet_linear): every
   output against the oracle.
+* The same shapes with RMSNorm fused before the call (bitnet_linear_rms, M=1
+  and 16), and at M=1 with f32 activations and a bias (bitnet_linear_ex's one
+  launch): every output against the oracle.
 * Small-batch GEMM, M in {8..256}, LLaMA-7B shapes, pre-quantised activations:
   the int32 accumulators over the whole output against an exact float64 product
   (every partial sum is an integer below 2^53, so any summation order is exact),
@@ -141,6 +144,36 @@ def test_decode_m16_full(i):
     ref = oracle.linear(x, P, sw)
     out = tg.bitnet_linear(dev_bf16(x), dev(P), dev_bf16(sw))   # M=16: quantise + GEMM
     assert_bf16_equal(host_bf16(out), ref["out"], f"{name} M=16")
+
+
+@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("i", range(len(synth.BITNET_2B_DECODE)), ids=DECODE_IDS)
+def test_decode_rmsnorm_full(i, M):
+    """The decode step with the RMSNorm that precedes every BitLinear call fused
+    in (no gain, torch's default eps), launched as the benchmark launches it:
+    every output against the oracle, where rows whose fp32 mean another double
+    summation order could round the other way may match the alternative."""
+    name, N, K, P, sw, _ = decode_problem(i)
+    x = synth.activations_bf16(M, K, synth.seed_for(6, 16 * i + synth.T_ACT) + M)
+    ref = oracle.linear_rms(x, P, sw)
+    amb = ref["ambiguous"]
+    alt = oracle.linear_rms(x, P, sw, means=ref["mean_alt"]) if amb.any() else ref
+    got = host_bf16(tg.bitnet_linear_rms(dev_bf16(x), dev(P), dev_bf16(sw)))
+    ok = np.all(got == ref["out"], axis=1) | (np.all(got == alt["out"], axis=1) & amb)
+    assert ok.all(), f"{name} M={M}: rows {np.nonzero(~ok)[0][:8].tolist()} differ (ambiguous: {int(amb.sum())})"
+
+
+@pytest.mark.parametrize("i", range(len(synth.BITNET_2B_DECODE)), ids=DECODE_IDS)
+def test_decode_f32_bias_full(i):
+    """bitnet_linear_ex at M=1 with f32 activations and a bias (one launch: the
+    f32 row quantised in the GEMV prologue, the bias in its epilogue): every
+    output against the oracle."""
+    name, N, K, P, sw, _ = decode_problem(i)
+    x = synth.rng(synth.seed_for(7, 16 * i + synth.T_ACT)).standard_normal((1, K)).astype(np.float32)
+    bias = synth.row_scales_bf16(N, synth.seed_for(7, 16 * i + synth.T_ROWSCALE), lo=-4.0, hi=4.0)
+    want = oracle.add_bias(oracle.linear_f32(x, P, sw)["out"], bias)
+    out = tg.bitnet_linear(torch.from_numpy(x).to(DEV), dev(P), dev_bf16(sw), bias=dev_bf16(bias))
+    assert_bf16_equal(host_bf16(out), want, f"{name} f32 + bias")
 
 
 # ----------------------------------------------------------------------------- LLaMA-7B GEMMs
