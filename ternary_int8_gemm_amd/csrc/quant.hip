@@ -82,8 +82,8 @@ template <int CH, bool RMS>
 __global__ __launch_bounds__(256) void quantize_rows_block(int8_t* __restrict__ q, uint16_t* __restrict__ scale,
                                                            uint16_t* __restrict__ xn_out,
                                                            const uint16_t* __restrict__ x,
-                                                           const uint16_t* __restrict__ gain, float eps, int64_t M,
-                                                           int64_t K) {
+                                                           const uint16_t* __restrict__ gain, float eps,
+                                                           int64_t /*M: one workgroup per row*/, int64_t K) {
     constexpr int WAVES = 4;
     __shared__ double red_d[WAVES];
     __shared__ uint32_t red_a[WAVES];  // absmax of x (RMS without a gain)
@@ -222,7 +222,8 @@ __global__ __launch_bounds__(256) void quantize_rows_rms_plain(int8_t* __restric
 // t holds the 4-element groups g = c * 256 + t (c < CH).
 template <int CH>
 __global__ __launch_bounds__(256) void quantize_rows_f32_block(int8_t* __restrict__ q, uint16_t* __restrict__ scale,
-                                                               const float* __restrict__ x, int64_t M, int64_t K) {
+                                                               const float* __restrict__ x,
+                                                               int64_t /*M: one workgroup per row*/, int64_t K) {
     constexpr int WAVES = 4;
     __shared__ uint32_t red[WAVES];
     const int tid = threadIdx.x;

@@ -585,7 +585,8 @@ hipError_t launch_w8a16(float* y, const uint16_t* x, const int8_t* q, const floa
     }
     constexpr int KW = 4;
     // 32-bit buffer offsets: weights and activations below 2 GiB
-    const bool fits = aligned16(x) && aligned16(q) && (N + 31) * K < ((int64_t)1 << 31) && 64 * K * 2 < ((int64_t)1 << 31);
+    // 32-bit buffer offsets: weight rows up to the last 64-column block's padding, activation rows up to 64
+    const bool fits = aligned16(x) && aligned16(q) && (N + 63) * K < ((int64_t)1 << 31) && 64 * K * 2 < ((int64_t)1 << 31);
     const dim3 grid((unsigned)((N + 31) / 32)), block(64 * KW);
     if (fits && K % WL_KS == 0 && K / WL_KS >= KW) {
         constexpr int KW8 = 8;
