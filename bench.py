@@ -34,6 +34,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -639,7 +640,7 @@ def summarize_gemm_pmc(dirs):
     """Markdown summary of the four counter passes of run_pmc_target_gemm (the
     directories in GEMM_PMC_PASSES order): per-launch averages over the last
     GEMM_PMC_REPS GEMM dispatches of each pass."""
-    vals, durs, calib = {}, [], {}
+    vals, durs, calib, kname = {}, [], {}, set()
     for (pname, counters), folder in zip(GEMM_PMC_PASSES.items(), dirs):
         rows = _csv_rows(folder, "counter_collection.csv")
         gemm_ids = sorted({int(_col(r, "Dispatch_Id")) for r in rows if "gemm_mfma_kernel" in _col(r, "Kernel_Name")})
@@ -653,6 +654,8 @@ def summarize_gemm_pmc(dirs):
             v = float(_col(r, "Counter_Value"))
             if did in keep:
                 vals.setdefault(cname, []).append(v)
+                m = re.search(r"gemm_mfma_kernel<[^>]*>", _col(r, "Kernel_Name"))
+                kname.add(m.group(0) if m else _col(r, "Kernel_Name"))
                 if pname == "a" and did not in seen_dur:
                     seen_dur.add(did)
                     durs.append(float(_col(r, "End_Timestamp")) - float(_col(r, "Start_Timestamp")))
@@ -676,7 +679,7 @@ def summarize_gemm_pmc(dirs):
           "Commands (each pass a run of its own, from the repository root after `cd /tmp && export TMPDIR=/tmp`):", ""]
     md += ["    " + c for c in cmds]
     md += ["", f"Per-launch averages over the last {GEMM_PMC_REPS} of {GEMM_PMC_WARM + GEMM_PMC_REPS} eager launches "
-           "(`gemm_mfma_kernel<128, 256, 2, 4, 2, 3, false>`, 256 workgroups of 8 waves).", "",
+           f"(`{', '.join(sorted(kname))}`, 256 workgroups of 8 waves).", "",
            "| quantity | value |", "|---|---:|",
            f"| dispatch duration (profiled) | {dur_ns / 1e3:.2f} µs |",
            f"| SQ_INSTS_MFMA | {avg['SQ_INSTS_MFMA']:.0f} (2MNK / 65536 = {2 * M * N * K // 65536}) |",

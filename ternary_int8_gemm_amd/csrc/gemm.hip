@@ -42,6 +42,11 @@
 //    (one barrier per stage).  Every step issues the same loads (stage indices
 //    past the end are clamped and never multiplied), so the waits the compiler
 //    derives are exact.
+//  * On the larger blocks (BDMA) the packed weights skip the registers: LDS
+//    DMA loads (16 bytes per lane) put each stage into a ring of NS + 1 weight
+//    stages, issued with that stage's activation loads, and each wave counts
+//    its own outstanding loads down (vmcnt) before the barrier that publishes
+//    the stage.
 //
 // Tiles are assigned XCD-aware: the hardware deals workgroups round-robin to
 // the 8 XCDs, so the block index is remapped to give each XCD a contiguous run
@@ -65,7 +70,7 @@ constexpr int64_t GM_MID_BLOCKS = 160;           // blocks a mid-M block tile sh
 // stride 0, so bounds are checked against the byte count in word 2).
 constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool BDMA, int NS>
 struct GemmShape {
     static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
     static constexpr int MT = BM / WAVES_M / 32;  // MFMA row tiles per wave
@@ -75,7 +80,15 @@ struct GemmShape {
     static constexpr int STAGE = A_STAGE + B_STAGE;
     static constexpr int A_CH = BM * (GM_KS / 16) / THREADS;  // 16-byte A groups per thread per stage
     static constexpr int B_CH = BN * 2 / THREADS;             // 16-byte B halves per thread per stage
-    static constexpr size_t LDS = 3 * (size_t)STAGE + 8 * BM + 4 * BN;  // three stages, row sums, scales
+    // LDS: three A (or A and B) stage buffers; with BDMA a separate ring of
+    // NB = NS + 1 B stages after them; then row sums and scales.
+    static constexpr int NB = NS + 1;
+    static constexpr int A_BUF = BDMA ? A_STAGE : STAGE;
+    static constexpr int B_RING = 3 * A_BUF;
+    static constexpr int DATA = BDMA ? 3 * A_STAGE + NB * B_STAGE : 3 * STAGE;
+    static constexpr int B_DMA = BN / 32 / (WAVES_M * WAVES_N);  // 1 KB B tiles each wave loads per stage
+    static constexpr size_t LDS = (size_t)DATA + 8 * BM + 4 * BN;
+    static_assert(!BDMA || B_DMA * 32 * WAVES_M * WAVES_N == BN, "whole B tiles per wave");
     static_assert(THREADS >= BM && THREADS >= BN, "one thread per block row / column fetches its scale");
     static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "wave tiles are whole MFMA tiles");
     static_assert(A_CH * THREADS == BM * 8 && B_CH * THREADS == BN * 2, "staging splits evenly");
@@ -109,22 +122,56 @@ struct StageRegs {
     v4u a[A_CH];
     v4u b[B_CH];
 };
+template <int A_CH>
+struct StageRegs<A_CH, 0> {  // weights loaded straight into LDS: no B registers
+    v4u a[A_CH];
+};
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int WAVES_PER_EU, int NS, bool OUT_I32>
+// s_waitcnt on the vector-memory counter alone (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt and lgkmcnt at their maxima, i.e. not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l writes
+// lds_dst + 16 l (lds_dst wave-uniform).  A device-only function: a lambda in
+// a kernel is also compiled for the host, where this builtin does not exist.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_dst, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, soff, 0, 0);
+}
+
+// Workgroup barrier for LDS written by this wave's ds_write and by LDS DMA
+// loads that have been waited for explicitly.  __syncthreads() would wait for
+// every LDS DMA in flight (its release fence covers them), including those of
+// stages far ahead; here each wave waits for its own LDS writes (lgkmcnt 0), the
+// s_barrier joins the waves, and the wavefront-scope fences only keep the
+// compiler from moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int WAVES_PER_EU, int NS, bool BDMA, bool OUT_I32>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out, const int8_t* __restrict__ x,
                       const uint8_t* __restrict__ w, const uint16_t* __restrict__ sa,
                       const uint16_t* __restrict__ sw, int M, int N, int K, int tiles_m, int tiles_n) {
-    using S = GemmShape<BM, BN, WAVES_M, WAVES_N>;
+    using S = GemmShape<BM, BN, WAVES_M, WAVES_N, BDMA, NS>;
     constexpr int MT = S::MT, NT = S::NT, A_CH = S::A_CH, B_CH = S::B_CH;
+    constexpr int B_REG = BDMA ? 0 : B_CH;  // B halves staged through registers
+    using Regs = StageRegs<A_CH, B_REG>;
     // k-steps by which A fragment reads run ahead of their MFMAs: two for
     // 64-row wave tiles (measured: 0.3-1.5% at M = 2048 on two boxes), one for 128-row tiles,
     // whose register budget the extra fragments would exceed
     constexpr int A_AHEAD = MT <= 2 ? 2 : 1;
     extern __shared__ __align__(16) uint8_t lds[];
-    int* rowsum = reinterpret_cast<int*>(lds + 3 * S::STAGE);
-    float* rowscale = reinterpret_cast<float*>(lds + 3 * S::STAGE + 4 * BM);
-    float* colscale = reinterpret_cast<float*>(lds + 3 * S::STAGE + 8 * BM);
+    int* rowsum = reinterpret_cast<int*>(lds + S::DATA);
+    float* rowscale = reinterpret_cast<float*>(lds + S::DATA + 4 * BM);
+    float* colscale = reinterpret_cast<float*>(lds + S::DATA + 8 * BM);
 
     // Block -> tile: consecutive logical tiles land on one XCD (xcd_remap) and
     // sweep GROUP_M row panels per column tile, so an XCD's concurrent tiles
@@ -168,7 +215,7 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
         a_voff[i] = (m0 + r) * K + ac * 16;
         a_off[i] = ((r >> 5) * 4 + (ac & 3)) * GM_FRAG + a_slot((r & 31) + 32 * (ac >> 2), ac & 3);
     }
-    // B staging: half g % 2 (= tid % 2) of column g / 2.
+    // B staging through registers: half g % 2 (= tid % 2) of column g / 2.
     const int bh = tid & 1;
     int b_voff[B_CH], b_off[B_CH];
 #pragma unroll
@@ -176,6 +223,15 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
         const int n = (tid >> 1) + (S::THREADS / 2) * j;
         b_voff[j] = (n0 + n) * KB + bh * 16;
         b_off[j] = S::A_STAGE + (n >> 5) * GM_FRAG + b_slot(n & 31, bh);
+    }
+    // B straight into LDS (BDMA): the d-th load of wave w fills 32-column tile
+    // w + WAVES * d, lane l writing slot l, i.e. column l / 2, half
+    // (l % 2) ^ bit 3 of the column (the inverse of b_slot).
+    int bd_voff[S::B_DMA];
+#pragma unroll
+    for (int d = 0; d < S::B_DMA; ++d) {
+        const int n = (wave + WAVES_M * WAVES_N * d) * 32 + (lane >> 1);
+        bd_voff[d] = (n0 + n) * KB + ((lane & 1) ^ ((lane >> 4) & 1)) * 16;
     }
     // Scales for the epilogue, fetched now so that their latency hides under
     // the K loop, and parked in LDS until then.
@@ -186,13 +242,32 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) rs[i] = 0;
 
-    auto load_stage = [&](int st, StageRegs<A_CH, B_CH>& R) {
+    // Global loads of stage st (clamped to the last stage past the end).  With
+    // BDMA the B part goes straight into ring slot st % NB.
+    auto load_stage = [&](int st, Regs& R) {
         const int kb = min(st, nk - 1) * GM_KS;  // wave-uniform
+        if constexpr (BDMA) {
+            uint8_t* ring = lds + S::B_RING + (st % S::NB) * S::B_STAGE;
+#pragma unroll
+            for (int d = 0; d < S::B_DMA; ++d)
+                buffer_load_lds16(w_rsrc, ring + (wave + WAVES_M * WAVES_N * d) * GM_FRAG, bd_voff[d], kb >> 2);
+        }
 #pragma unroll
         for (int i = 0; i < A_CH; ++i) R.a[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, a_voff[i], kb, 0);
+        if constexpr (!BDMA) {
 #pragma unroll
-        for (int j = 0; j < B_CH; ++j) R.b[j] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, b_voff[j], kb >> 2, 0);
+            for (int j = 0; j < B_CH; ++j) R.b[j] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, b_voff[j], kb >> 2, 0);
+        }
     };
+    // The B tiles of stage k + 1 are issued with the loads of stage k + 1 (in
+    // whatever order the compiler picks within that group); each of the NS - 1
+    // later groups up to the barrier of step k issues B_DMA + A_CH more loads,
+    // and vector-memory loads complete in issue order, so at most B_WAIT loads
+    // may still be in flight when they have landed.  (The A loads of stage k + 1
+    // have to complete a step earlier anyway, for their LDS store.)  The groups
+    // stay apart: the loop steps are separated by barriers, the prologue's
+    // groups by scheduling barriers.
+    constexpr int B_WAIT = (NS - 1) * (S::B_DMA + A_CH);
     v16i acc[MT][NT];
 #pragma unroll
     for (int t = 0; t < MT; ++t)
@@ -220,8 +295,8 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
     // fragments of k-step s.  A reads run A_AHEAD k-steps ahead of their
     // MFMAs; the previous step reads the B dwords and the first A_AHEAD
     // k-steps' A fragments of the next stage.
-    auto read_b = [&](const uint8_t* base, v4u (&pb)[NT]) {
-        const uint8_t* B = base + S::A_STAGE + (wn * NT) * GM_FRAG;
+    auto read_b = [&](const uint8_t* bbase, v4u (&pb)[NT]) {
+        const uint8_t* B = bbase + (wn * NT) * GM_FRAG;
 #pragma unroll
         for (int u = 0; u < NT; ++u) pb[u] = *reinterpret_cast<const v4u*>(B + u * GM_FRAG + b_rd);
     };
@@ -242,8 +317,18 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
     // of stage k+2 are spread over the k-steps.
     v4u pb[NT];
     v4i afn[A_AHEAD][MT];  // the next stage's first A_AHEAD k-steps
-    auto step = [&](const int bi, int k, const StageRegs<A_CH, B_CH>& SS, StageRegs<A_CH, B_CH>& SL) {
-        __syncthreads();  // stage k+1 visible; buffer (k+2) % 3 no longer read
+    auto b_of = [&](const uint8_t* abuf, int st) -> const uint8_t* {  // B tiles of stage st
+        if constexpr (BDMA) return lds + S::B_RING + (st % S::NB) * S::B_STAGE;
+        return abuf + S::A_STAGE;
+    };
+    auto step = [&](const int bi, int k, const Regs& SS, Regs& SL) {
+        // stage k+1 visible; buffer (k+2) % 3 no longer read
+        if constexpr (BDMA) {
+            wait_vmcnt<B_WAIT>();  // this wave's B tiles of stage k+1 have landed
+            lds_barrier();
+        } else {
+            __syncthreads();
+        }
         // The global loads go out at raised wave priority, so that a wave leaving
         // the barrier issues them ahead of the MFMA and LDS work of the other
         // wave on its SIMD (measured: about one point of MFMA utilisation at M = 2048).
@@ -251,9 +336,9 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
         load_stage(k + NS + 1, SL);
         __builtin_amdgcn_sched_barrier(0);  // keep the loads at the top
         __builtin_amdgcn_s_setprio(0);
-        const uint8_t* cur = lds + bi * S::STAGE;
-        uint8_t* later = lds + ((bi + 2) % 3) * S::STAGE;
-        const uint8_t* next = lds + ((bi + 1) % 3) * S::STAGE;
+        const uint8_t* cur = lds + bi * S::A_BUF;
+        uint8_t* later = lds + ((bi + 2) % 3) * S::A_BUF;
+        const uint8_t* next = lds + ((bi + 1) % 3) * S::A_BUF;
         const int live = (k + 2 < nk) ? 1 : 0;
         constexpr int R = A_AHEAD + 1;  // A fragment sets in flight
         v4i af[R][MT];
@@ -270,15 +355,17 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
                 read_a(cur, s + A_AHEAD, af[(s + A_AHEAD) % R]);
             } else {  // k-step sn of the next stage (written during step k - 1)
                 const int sn = s + A_AHEAD - 4;
-                if (sn == 0) read_b(next, pb);
+                if (sn == 0) read_b(b_of(next, k + 1), pb);
                 read_a(next, sn, afn[sn]);
             }
 #pragma unroll
             for (int i = 0; i < A_CH; ++i)
                 if (i % 4 == s) store_a(later, i, SS.a[i], live);
-            if (s == 1) {
+            if constexpr (!BDMA) {
+                if (s == 1) {
 #pragma unroll
-                for (int j = 0; j < B_CH; ++j) *reinterpret_cast<v4u*>(later + b_off[j]) = SS.b[j];
+                    for (int j = 0; j < B_CH; ++j) *reinterpret_cast<v4u*>(later + b_off[j]) = SS.b[j];
+                }
             }
 #pragma unroll
             for (int u = 0; u < NT; ++u) {
@@ -295,21 +382,36 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
     // Stage j lives in register set j % NS from its load (step j - NS - 1)
     // until its LDS store (step j - 2), and in LDS buffer j % 3 from its store
     // until it is multiplied.
+    // With BDMA, stage j's B tiles are written into ring slot j % NB at step
+    // j - NS - 1, after that step's barrier: the slot's previous stage, j - NB,
+    // was last read during step j - NB - 1, which is why NB = NS + 1.
     constexpr int LEAD = NS + 1;
-    StageRegs<A_CH, B_CH> sets[NS];
+    Regs sets[NS];
 #pragma unroll
-    for (int i = 0; i < NS; ++i) load_stage(i, sets[i]);
+    for (int i = 0; i < NS; ++i) {
+        load_stage(i, sets[i]);
+        if constexpr (BDMA) __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) store_a(lds, i, sets[0].a[i], 1);
+    if constexpr (!BDMA) {
 #pragma unroll
-    for (int j = 0; j < B_CH; ++j) *reinterpret_cast<v4u*>(lds + b_off[j]) = sets[0].b[j];
+        for (int j = 0; j < B_CH; ++j) *reinterpret_cast<v4u*>(lds + b_off[j]) = sets[0].b[j];
+    }
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) store_a(lds + S::STAGE, i, sets[1].a[i], nk > 1 ? 1 : 0);
+    for (int i = 0; i < A_CH; ++i) store_a(lds + S::A_BUF, i, sets[1].a[i], nk > 1 ? 1 : 0);
+    if constexpr (!BDMA) {
 #pragma unroll
-    for (int j = 0; j < B_CH; ++j) *reinterpret_cast<v4u*>(lds + S::STAGE + b_off[j]) = sets[1].b[j];
+        for (int j = 0; j < B_CH; ++j) *reinterpret_cast<v4u*>(lds + S::STAGE + b_off[j]) = sets[1].b[j];
+    }
     load_stage(NS, sets[0]);
-    __syncthreads();
-    read_b(lds, pb);
+    if constexpr (BDMA) {
+        wait_vmcnt<B_WAIT>();  // B tiles of stages 0 and 1 have landed
+        lds_barrier();
+    } else {
+        __syncthreads();
+    }
+    read_b(b_of(lds, 0), pb);
 #pragma unroll
     for (int j = 0; j < A_AHEAD; ++j) read_a(lds, j, afn[j]);
     // stage k + i sits in LDS buffer (k + i) % 3; k advances by NS, so with
@@ -324,6 +426,9 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
     for (int i = 0; i < NS - 1; ++i)
         if (k + i < nk) step(NS % 3 == 0 ? i % 3 : (k + i) % 3, k + i, sets[(i + 2) % NS], sets[(i + LEAD) % NS]);
 
+    // The B tiles of the clamped stages past the end must land before the
+    // workgroup ends and its LDS is reused.
+    if constexpr (BDMA) wait_vmcnt<0>();
     // ---- row sums (the 8 threads of a row are aligned lanes) and row scales to LDS
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
@@ -580,13 +685,13 @@ __global__ __launch_bounds__(64) void gemm_plain(uint16_t* __restrict__ out, int
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int WAVES_PER_EU, int NS, bool OUT_I32>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int WAVES_PER_EU, int NS, bool BDMA, bool OUT_I32>
 hipError_t launch_mfma(uint16_t* out, int32_t* acc, const int8_t* x, const uint8_t* w, const uint16_t* sa,
                        const uint16_t* sw, int M, int N, int K, hipStream_t s) {
-    using S = GemmShape<BM, BN, WAVES_M, WAVES_N>;
+    using S = GemmShape<BM, BN, WAVES_M, WAVES_N, BDMA, NS>;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
-    auto kern = gemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, WAVES_PER_EU, NS, OUT_I32>;
+    auto kern = gemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, WAVES_PER_EU, NS, BDMA, OUT_I32>;
     if (S::LDS > 65536) {  // beyond the default dynamic LDS limit: raise it (idempotent)
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::LDS);
@@ -801,10 +906,10 @@ hipError_t launch_tiles(uint16_t* out, int32_t* acc, const int8_t* x, const uint
         // output columns, which costs more than leaving CUs idle in a block-tiled
         // kernel.  Take the largest block tile that still gives GM_MID_BLOCKS
         // blocks (measured on the LLaMA-7B shapes at M = 128 ... 1024).
-        if (tiles >= GM_MID_BLOCKS) return launch_mfma<128, 256, 2, 4, 2, 3, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+        if (tiles >= GM_MID_BLOCKS) return launch_mfma<128, 256, 2, 4, 2, 3, true, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
         if ((int64_t)((M + 127) / 128) * ((N + 127) / 128) >= GM_MID_BLOCKS)
-            return launch_mfma<128, 128, 2, 2, 2, 3, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
-        return launch_mfma<64, 128, 1, 2, 2, 3, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+            return launch_mfma<128, 128, 2, 2, 2, 3, true, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+        return launch_mfma<64, 128, 1, 2, 2, 3, false, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
     }
     if (tiles < 256 && K % GS_KS == 0 && K / GS_KS >= 4) {
         // LDS-staged skinny kernel (configurations measured on the LLaMA-7B
@@ -840,8 +945,8 @@ hipError_t launch_tiles(uint16_t* out, int32_t* acc, const int8_t* x, const uint
     }
     const int64_t wide_tiles = (int64_t)((M + 127) / 128) * ((N + 511) / 512);
     if (wide_tiles >= 2 * 256)
-        return launch_mfma<128, 512, 1, 8, 2, 3, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
-    return launch_mfma<128, 256, 2, 4, 2, 3, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+        return launch_mfma<128, 512, 1, 8, 2, 3, true, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+    return launch_mfma<128, 256, 2, 4, 2, 3, true, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
 }
 
 template <bool OUT_I32>

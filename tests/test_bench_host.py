@@ -94,6 +94,7 @@ def test_summarize_gemm_pmc(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "GEMM_PMC_FILE", str(out))
     bench.summarize_gemm_pmc(dirs)
     text = out.read_text()
+    assert "(`gemm_mfma_kernel<...>`, 256 workgroups" in text
     assert "| dispatch duration (profiled) | 35.00 µs |" in text
     frac = 1048576 * 32 / (35000e-9 * 2.4e9 * 1024)
     assert f"| MFMA busy / (duration × 2.4 GHz × 1024 SIMDs) | {frac:.3f} |" in text
