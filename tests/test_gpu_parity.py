@@ -122,6 +122,9 @@ GEMM_SHAPES = [
     (200, 9001, 2048), (250, 300, 1024), (5, 4096, 768), (77, 2000, 1280),
     # mid-sized M (M * N >= 2^21 with few 128 x 256 tiles): 128 x 256, 128 x 128 and 64 x 128 blocks
     (513, 10000, 256), (300, 13000, 384), (1000, 2200, 512),
+    # weights straight into the LDS ring, ragged M and N: 128 x 128 blocks over 10 stages (the ring
+    # wraps), 128 x 256 blocks over 5 stages, 128 x 512 blocks with a single stage
+    (700, 4000, 1280), (1100, 8200, 640), (1030, 32770, 128),
 ]
 
 
@@ -164,7 +167,8 @@ def test_gemm_i32_misaligned_plain_path():
 # ----------------------------------------------------------------------------- bf16 GEMM
 
 @pytest.mark.parametrize("M,N,K", [(4, 128, 256), (16, 4096, 4096), (200, 300, 1024), (33, 65, 68),
-                                   (513, 10000, 256), (300, 13000, 384), (1000, 2200, 512)])
+                                   (513, 10000, 256), (300, 13000, 384), (1000, 2200, 512), (700, 4000, 1280),
+                                   (1100, 8200, 640)])
 def test_gemm_bf16_parity(M, N, K):
     x, W, P, _ = problem(M, N, K, seed=3000 + M)
     sw = synth.row_scales_bf16(N, seed=3100 + M)
