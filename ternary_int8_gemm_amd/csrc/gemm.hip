@@ -57,6 +57,8 @@
 #include "bitnet_device.h"
 #include "launch.h"
 
+#include <atomic>
+
 namespace bitnet {
 
 namespace {
@@ -685,6 +687,22 @@ __global__ __launch_bounds__(64) void gemm_plain(uint16_t* __restrict__ out, int
     }
 }
 
+// Raise a kernel's dynamic LDS limit above the 64 KB default, once per device
+// for each kernel instance (each instance has its own flag word; devices past
+// 63 set the attribute on every launch).
+template <typename Kern>
+hipError_t raise_lds_limit(Kern kern, size_t lds) {
+    static std::atomic<unsigned long long> done{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const unsigned long long bit = (dev >= 0 && dev < 64) ? 1ull << dev : 0;
+    if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int WAVES_PER_EU, int NS, bool BDMA, bool OUT_I32>
 hipError_t launch_mfma(uint16_t* out, int32_t* acc, const int8_t* x, const uint8_t* w, const uint16_t* sa,
                        const uint16_t* sw, int M, int N, int K, hipStream_t s) {
@@ -692,9 +710,8 @@ hipError_t launch_mfma(uint16_t* out, int32_t* acc, const int8_t* x, const uint8
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     auto kern = gemm_mfma_kernel<BM, BN, WAVES_M, WAVES_N, WAVES_PER_EU, NS, BDMA, OUT_I32>;
-    if (S::LDS > 65536) {  // beyond the default dynamic LDS limit: raise it (idempotent)
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::LDS);
+    if (S::LDS > 65536) {
+        const hipError_t e = raise_lds_limit(kern, S::LDS);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n)), dim3(S::THREADS), S::LDS, s, out, acc, x, w, sa,
