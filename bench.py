@@ -26,6 +26,8 @@ Profiling helpers (not part of the timed benchmark):
   python bench.py --pmc-target-gemm       eager launches for the counter passes over the M=2048 GEMM
   python bench.py --summarize-gemm-pmc A B F W
                                           turn those four passes into profiles/gemm_m2048_qkvo_counters.md
+  python bench.py --gemv-scaling          M=1 bitnet_linear (quantise + GEMV) time against N at K=2560,
+                                          and a line fit: fixed cost per launch and marginal stream rate
 """
 import argparse
 import csv
@@ -464,6 +466,45 @@ def lm_head_inputs(device, copies):
     return N, K, Ps, sw, x
 
 
+GEMV_SCALING_N = (4008, 8016, 16032, 32064, 64128, 128256, 256512, 513024)
+
+
+def run_gemv_scaling(device, stream):
+    """bitnet_linear at M=1, K=2560 for the N in GEMV_SCALING_N: the lm_head weight
+    rows repeated to N rows, enough copies to cycle through about 1 GiB (none stays
+    in the caches), one graph of back-to-back launches per N, the best of three
+    ramped timings.  A least-squares line over N >= 32064 splits the time into a
+    fixed cost per launch and the marginal streaming rate."""
+    N0, K, Ps0, sw0, x = lm_head_inputs(device, 1)
+    P0 = Ps0[0]
+    rows = []
+    for N in GEMV_SCALING_N:
+        P = torch.cat([P0] * (-(-N // N0)))[:N].contiguous()
+        Ps = [P] + [P.clone() for _ in range(max(2, (1 << 30) // P.numel()) - 1)]
+        sw = torch.cat([sw0] * (-(-N // N0)))[:N].contiguous()
+        out = torch.empty((1, N), dtype=torch.bfloat16, device=device)
+
+        def launches():
+            for Q in Ps:
+                tg.bitnet_linear(x, Q, sw, out=out)
+        g = capture(launches, stream)
+        best = float("inf")
+        for _ in range(3):
+            ramp(g, stream)
+            best = min(best, time_graph(g, 5, stream) / (5 * len(Ps)))
+        mb = N * K / 4 / 1e6
+        rows.append((N, mb, best))
+        print(f"N={N:7d}  weights {mb:8.2f} MB  {best * 1e6:8.2f} us  {mb / best / 1e6:5.2f} TB/s  "
+              f"({len(Ps)} copies)", flush=True)
+        del Ps, P, g
+        torch.cuda.empty_cache()
+    fit = [(mb, t * 1e6) for N, mb, t in rows if N >= 32064]
+    A = np.array([[1.0, mb] for mb, _ in fit])
+    c = np.linalg.lstsq(A, np.array([t for _, t in fit]), rcond=None)[0]
+    print(json.dumps({"gemv_scaling": [{"N": N, "MB": round(mb, 2), "us": round(t * 1e6, 2)} for N, mb, t in rows],
+                      "fit_fixed_us": round(float(c[0]), 2), "fit_marginal_TBs": round(float(1 / c[1]), 2)}))
+
+
 def run_pmc_target(device, reps=3):
     """Eager launches for hardware-counter passes (counter collection serialises
     dispatches, so no graph): a plain device-to-device copy of CALIB_COPY_BYTES,
@@ -717,6 +758,7 @@ def main():
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     ap.add_argument("--pmc-target-gemm", action="store_true")
     ap.add_argument("--summarize-gemm-pmc", nargs=4, metavar=("A_DIR", "B_DIR", "FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--gemv-scaling", action="store_true")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -747,6 +789,9 @@ def main():
         run_pmc_target_gemm(device)
         return
     stream = torch.cuda.Stream(device)
+    if args.gemv_scaling:
+        run_gemv_scaling(device, stream)
+        return
 
     shapes, host, dev_sets = build_decode(device, log)
     log("decode GEMV M=1 (BitNet-2B-4T shapes):")
