@@ -42,7 +42,7 @@
 //    (one barrier per stage).  Every step issues the same loads (stage indices
 //    past the end are clamped and never multiplied), so the waits the compiler
 //    derives are exact.
-//  * On the larger blocks (BDMA) the packed weights skip the registers: LDS
+//  * With BDMA (every block shape in use) the packed weights skip the registers: LDS
 //    DMA loads (16 bytes per lane) put each stage into a ring of NS + 1 weight
 //    stages, issued with that stage's activation loads, and each wave counts
 //    its own outstanding loads down (vmcnt) before the barrier that publishes
@@ -66,7 +66,10 @@ namespace {
 constexpr int GM_KS = 128;     // K elements per pipeline stage (4 MFMA k-steps of 32)
 constexpr int GROUP_M = 8;     // row panels swept per column tile (tile order)
 constexpr int GM_FRAG = 1024;  // bytes of one 32 x 32 int8 A operand fragment (64 lanes x 16 B)
-constexpr int64_t GM_MID_MN = (int64_t)1 << 21;  // M * N from which few tiles still beat split-K
+// M * N from which few block tiles beat split-K: measured on the LLaMA-7B shapes,
+// split-K still wins at 256 x 4096 (1.05 M outputs), the block tiles at
+// 128 x 11008 (1.41 M) and 384 x 4096 (1.57 M).
+constexpr int64_t GM_MID_MN = (int64_t)5 << 18;
 constexpr int64_t GM_MID_BLOCKS = 160;           // blocks a mid-M block tile should give
 // Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format;
 // stride 0, so bounds are checked against the byte count in word 2).
@@ -922,11 +925,13 @@ hipError_t launch_tiles(uint16_t* out, int32_t* acc, const int8_t* x, const uint
         // Mid-sized M: the split-K kernels re-read the activations once per 64
         // output columns, which costs more than leaving CUs idle in a block-tiled
         // kernel.  Take the largest block tile that still gives GM_MID_BLOCKS
-        // blocks (measured on the LLaMA-7B shapes at M = 128 ... 1024).
+        // blocks (measured on the LLaMA-7B shapes at M = 128 ... 1024); the
+        // smallest, 64 x 128, has four 32 x 64 wave tiles, so that even a few
+        // blocks put one wave on every SIMD they occupy.
         if (tiles >= GM_MID_BLOCKS) return launch_mfma<128, 256, 2, 4, 2, 3, true, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
         if ((int64_t)((M + 127) / 128) * ((N + 127) / 128) >= GM_MID_BLOCKS)
             return launch_mfma<128, 128, 2, 2, 2, 3, true, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
-        return launch_mfma<64, 128, 1, 2, 2, 3, false, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+        return launch_mfma<64, 128, 2, 2, 2, 3, true, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
     }
     if (tiles < 256 && K % GS_KS == 0 && K / GS_KS >= 4) {
         // LDS-staged skinny kernel (configurations measured on the LLaMA-7B

@@ -120,8 +120,10 @@ GEMM_SHAPES = [
     # LDS-staged split-K kernel (K % 256 == 0): every configuration, wide and ragged N, ragged M
     (32, 8200, 2048), (33, 300, 2048), (64, 9000, 1024), (100, 8192, 2048), (128, 500, 2048),
     (200, 9001, 2048), (250, 300, 1024), (5, 4096, 768), (77, 2000, 1280),
-    # mid-sized M (M * N >= 2^21 with few 128 x 256 tiles): 128 x 256, 128 x 128 and 64 x 128 blocks
-    (513, 10000, 256), (300, 13000, 384), (1000, 2200, 512),
+    # mid-sized M (M * N >= 5 * 2^18 with few 128 x 256 tiles): 128 x 256, 128 x 128 and 64 x 128
+    # blocks (the LDS-staged shape (200, 9001, 2048) above takes 64 x 128 blocks too); (200, 4000, 2048)
+    # keeps the split-K kernel for M > 128 and K >= 2048 covered
+    (513, 10000, 256), (300, 13000, 384), (1000, 2200, 512), (200, 4000, 2048),
     # weights straight into the LDS ring, ragged M and N: 128 x 128 blocks over 10 stages (the ring
     # wraps), 128 x 256 blocks over 5 stages, 128 x 512 blocks with a single stage
     (700, 4000, 1280), (1100, 8200, 640), (1030, 32770, 128),
