@@ -228,6 +228,36 @@ def test_linear_dispatch_neutral(M):
         assert np.array_equal(host_bf16(out2), host_bf16(out))
 
 
+# bitnet_linear where the GEMM is the LDS-staged split-K kernel: every configuration of that kernel
+# (rows 32 / 64 / 128 / more, one or two column tiles, 4 or >= 8 chunks of 256), ragged M and N, an
+# all-zero row (eps floor) and outliers; the result must equal the oracle, and the separately called
+# quantise and GEMM entry points, bit for bit.
+LINEAR_XQ_SHAPES = [(5, 300, 1024), (16, 2560, 2560), (16, 3840, 2560), (16, 13824, 2560), (16, 2560, 6912),
+                    (40, 1000, 2048), (64, 9000, 1024), (100, 3000, 2048), (100, 8192, 2048), (100, 500, 1024),
+                    (200, 4000, 2048), (250, 300, 1024), (33, 70, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", LINEAR_XQ_SHAPES)
+def test_linear_split_k_shapes(M, N, K):
+    x, W, P, sw = problem(M, N, K, seed=7000 + M + N, outliers=0.01)
+    x[M // 2, :] = 0
+    ref = oracle.linear(x, P, sw)
+    xd, Pd, swd = dev_bf16(x), dev(P), dev_bf16(sw)
+    out = tg.bitnet_linear(xd, Pd, swd)
+    assert_bf16_parity(host_bf16(out), ref["out"], f"linear {M}x{N}x{K}")
+    q, sa = tg.quantize_activation(xd)
+    out2 = tg.bitnet_gemm(q, Pd, sa, swd)
+    assert np.array_equal(host_bf16(out2), host_bf16(out))
+
+
+def test_linear_split_k_misaligned_activations():
+    M, N, K = 8, 300, 1024   # a split-K shape, with activations 2 bytes off a 16-byte boundary
+    x, W, P, sw = problem(M, N, K, seed=71)
+    ref = oracle.linear(x, P, sw)
+    out = tg.bitnet_linear(misaligned(dev_bf16(x)), dev(P), dev_bf16(sw))
+    assert_bf16_parity(host_bf16(out), ref["out"], "linear misaligned")
+
+
 def test_linear_leading_dims():
     x, W, P, sw = problem(6, 64, 256, seed=61)
     ref = oracle.linear(x, P, sw)
