@@ -127,6 +127,8 @@ GEMM_SHAPES = [
     # weights straight into the LDS ring, ragged M and N: 128 x 128 blocks over 10 stages (the ring
     # wraps), 128 x 256 blocks over 5 stages, 128 x 512 blocks with a single stage
     (700, 4000, 1280), (1100, 8200, 640), (1030, 32770, 128),
+    # few rows, very many columns: 32- and 64-row blocks
+    (5, 66000, 1024), (32, 65600, 512), (40, 70000, 512), (64, 65537, 256),
 ]
 
 
@@ -170,7 +172,7 @@ def test_gemm_i32_misaligned_plain_path():
 
 @pytest.mark.parametrize("M,N,K", [(4, 128, 256), (16, 4096, 4096), (200, 300, 1024), (33, 65, 68),
                                    (513, 10000, 256), (300, 13000, 384), (1000, 2200, 512), (700, 4000, 1280),
-                                   (1100, 8200, 640)])
+                                   (1100, 8200, 640), (16, 128256, 512), (40, 70000, 512)])
 def test_gemm_bf16_parity(M, N, K):
     x, W, P, _ = problem(M, N, K, seed=3000 + M)
     sw = synth.row_scales_bf16(N, seed=3100 + M)
