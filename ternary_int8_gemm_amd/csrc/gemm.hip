@@ -914,8 +914,9 @@ hipError_t launch_tiles(uint16_t* out, int32_t* acc, const int8_t* x, const uint
     // spend the least VALU per MFMA; they are used when there are enough of them
     // to give every CU at least two.  Otherwise 128 x 256 blocks (eight 64 x 64
     // wave tiles), which keep two waves per SIMD busy on N = 4096-sized shapes.
-    // Too few 128 x 256 tiles to give every CU one: a split-K skinny kernel
-    // (each wave needs at least one chunk of K): the LDS-staged one when
+    // Too few 128 x 256 tiles to give every CU one, and fewer than GM_MID_MN
+    // outputs (else the mid-M blocks below): a split-K skinny kernel (each
+    // wave needs at least one chunk of K): the LDS-staged one when
     // K % 256 == 0, else the direct one.  Configurations measured on the
     // LLaMA-7B layer shapes: short rings and more resident waves beat deep
     // per-wave prefetch here.
