@@ -584,7 +584,6 @@ hipError_t launch_w8a16(float* y, const uint16_t* x, const int8_t* q, const floa
         return launch_w8a16_stream<2>(y, x, q, scale, (int)M, (int)N, (int)K, s);
     }
     constexpr int KW = 4;
-    // 32-bit buffer offsets: weights and activations below 2 GiB
     // 32-bit buffer offsets: weight rows up to the last 64-column block's padding, activation rows up to 64
     const bool fits = aligned16(x) && aligned16(q) && (N + 63) * K < ((int64_t)1 << 31) && 64 * K * 2 < ((int64_t)1 << 31);
     const dim3 grid((unsigned)((N + 31) / 32)), block(64 * KW);
