@@ -467,14 +467,25 @@ def lm_head_inputs(device, copies):
 
 
 GEMV_SCALING_N = (4008, 8016, 16032, 32064, 64128, 128256, 256512, 513024)
+GEMV_SCALING_FIT_MIN_N = 32064
+
+
+def scaling_fit(rows):
+    """Least-squares line time_us = fixed + MB / rate over the (N, MB, seconds)
+    rows with N >= GEMV_SCALING_FIT_MIN_N; returns (fixed_us, rate_TBs)."""
+    fit = [(mb, t * 1e6) for N, mb, t in rows if N >= GEMV_SCALING_FIT_MIN_N]
+    A = np.array([[1.0, mb] for mb, _ in fit])
+    c = np.linalg.lstsq(A, np.array([t for _, t in fit]), rcond=None)[0]
+    return float(c[0]), float(1.0 / c[1])
 
 
 def run_gemv_scaling(device, stream):
     """bitnet_linear at M=1, K=2560 for the N in GEMV_SCALING_N: the lm_head weight
     rows repeated to N rows, enough copies to cycle through about 1 GiB (none stays
     in the caches), one graph of back-to-back launches per N, the best of three
-    ramped timings.  A least-squares line over N >= 32064 splits the time into a
-    fixed cost per launch and the marginal streaming rate."""
+    ramped timings.  A least-squares line over N >= GEMV_SCALING_FIT_MIN_N
+    (scaling_fit) splits the time into a fixed cost per launch and the marginal
+    streaming rate."""
     N0, K, Ps0, sw0, x = lm_head_inputs(device, 1)
     P0 = Ps0[0]
     rows = []
@@ -498,11 +509,9 @@ def run_gemv_scaling(device, stream):
               f"({len(Ps)} copies)", flush=True)
         del Ps, P, g
         torch.cuda.empty_cache()
-    fit = [(mb, t * 1e6) for N, mb, t in rows if N >= 32064]
-    A = np.array([[1.0, mb] for mb, _ in fit])
-    c = np.linalg.lstsq(A, np.array([t for _, t in fit]), rcond=None)[0]
+    fixed_us, rate = scaling_fit(rows)
     print(json.dumps({"gemv_scaling": [{"N": N, "MB": round(mb, 2), "us": round(t * 1e6, 2)} for N, mb, t in rows],
-                      "fit_fixed_us": round(float(c[0]), 2), "fit_marginal_TBs": round(float(1 / c[1]), 2)}))
+                      "fit_fixed_us": round(fixed_us, 2), "fit_marginal_TBs": round(rate, 2)}))
 
 
 def run_pmc_target(device, reps=3):

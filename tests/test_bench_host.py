@@ -116,3 +116,15 @@ def test_summarize_gemm_pmc_needs_enough_dispatches(tmp_path):
         dirs.append(str(d))
     with pytest.raises(SystemExit):
         bench.summarize_gemm_pmc(dirs)
+
+
+def test_gemv_scaling_fit():
+    """The line fit recovers a known fixed cost and rate, and ignores the small-N rows."""
+    K = 2560
+    rows = []
+    for N in bench.GEMV_SCALING_N:
+        mb = N * K / 4 / 1e6
+        t_us = 3.5 + mb / 6.7 if N >= bench.GEMV_SCALING_FIT_MIN_N else 100.0  # small N: off the line
+        rows.append((N, mb, t_us * 1e-6))
+    fixed, rate = bench.scaling_fit(rows)
+    assert abs(fixed - 3.5) < 1e-9 and abs(rate - 6.7) < 1e-9
