@@ -486,6 +486,20 @@ def run_gemv_scaling(device, stream):
     ramped timings.  A least-squares line over N >= GEMV_SCALING_FIT_MIN_N
     (scaling_fit) splits the time into a fixed cost per launch and the marginal
     streaming rate."""
+    # the floor of a dependent launch in a graph: one-element kernels back to back
+    one = torch.zeros(1, device=device)
+
+    def tiny():
+        for _ in range(200):
+            one.add_(1.0)
+    g = capture(tiny, stream)
+    floor = float("inf")
+    for _ in range(3):
+        ramp(g, stream)
+        floor = min(floor, time_graph(g, 5, stream) / (5 * 200))
+    print(f"launch floor: {floor * 1e6:.2f} us per one-element kernel in a graph", flush=True)
+    del g
+
     N0, K, Ps0, sw0, x = lm_head_inputs(device, 1)
     P0 = Ps0[0]
     rows = []
@@ -511,7 +525,8 @@ def run_gemv_scaling(device, stream):
         torch.cuda.empty_cache()
     fixed_us, rate = scaling_fit(rows)
     print(json.dumps({"gemv_scaling": [{"N": N, "MB": round(mb, 2), "us": round(t * 1e6, 2)} for N, mb, t in rows],
-                      "fit_fixed_us": round(fixed_us, 2), "fit_marginal_TBs": round(rate, 2)}))
+                      "fit_fixed_us": round(fixed_us, 2), "fit_marginal_TBs": round(rate, 2),
+                      "launch_floor_us": round(floor * 1e6, 2)}))
 
 
 def run_pmc_target(device, reps=3):
