@@ -579,16 +579,20 @@ def _grid(row):
         return -1
 
 
-def summarize_trace(folder):
-    """Markdown summary of a rocprofv3 --kernel-trace --stats run of this script:
-    the --stats table as rocprofv3 wrote it, then the trace split by launch grid
-    (one template instance serves several projection shapes)."""
-    out = ["# rocprofv3 kernel trace of the benchmark", "",
+TRACE_ARGS = "--steps 22 --warmup 5 --no-cpu-baseline"
+
+
+def summarize_trace(folder, bench_args=TRACE_ARGS):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of this script
+    (with bench_args): the --stats table as rocprofv3 wrote it, then the trace
+    split by launch grid (one template instance serves several shapes)."""
+    extra = "" if bench_args == TRACE_ARGS else f' --trace-args "{bench_args}"'
+    out = [f"# rocprofv3 kernel trace of `bench.py {bench_args}`", "",
            "Command (from the repository root, after `cd /tmp && export TMPDIR=/tmp`):", "",
-           "    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_bench -o bench -- "
-           "python3 bench.py --steps 22 --warmup 5 --no-cpu-baseline",
-           "    gzip gpurun_out/trace_bench/*kernel_trace.csv   # the per-dispatch trace, compressed for transfer",
-           f"    python bench.py --summarize-trace gpurun_out/trace_bench", "",
+           f"    rocprofv3 --kernel-trace --stats --output-format csv -d {folder} -o bench -- "
+           f"python3 bench.py {bench_args}",
+           f"    gzip {folder}/*kernel_trace.csv   # the per-dispatch trace, compressed for transfer",
+           f"    python bench.py --summarize-trace {folder}{extra}", "",
            "## --stats (kernel_stats.csv)", "",
            "| kernel | calls | total ms | avg us | min us | max us | % |", "|---|---:|---:|---:|---:|---:|---:|"]
     for r in _csv_rows(folder, "kernel_stats.csv"):
@@ -780,6 +784,7 @@ def main():
     ap.add_argument("--pmc-target", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
+    ap.add_argument("--trace-args", default=TRACE_ARGS, help="the bench.py arguments of the traced run")
     ap.add_argument("--pmc-target-gemm", action="store_true")
     ap.add_argument("--summarize-gemm-pmc", nargs=4, metavar=("A_DIR", "B_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--gemv-scaling", action="store_true")
@@ -789,7 +794,7 @@ def main():
         summarize_pmc(*args.summarize_pmc)
         return
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace)
+        summarize_trace(args.summarize_trace, args.trace_args)
         return
     if args.summarize_gemm_pmc:
         summarize_gemm_pmc(args.summarize_gemm_pmc)
