@@ -586,7 +586,7 @@ def summarize_trace(folder, bench_args=TRACE_ARGS):
     """Markdown summary of a rocprofv3 --kernel-trace --stats run of this script
     (with bench_args): the --stats table as rocprofv3 wrote it, then the trace
     split by launch grid (one template instance serves several shapes)."""
-    extra = "" if bench_args == TRACE_ARGS else f' --trace-args "{bench_args}"'
+    extra = "" if bench_args == TRACE_ARGS else f' --trace-args="{bench_args}"'
     out = [f"# rocprofv3 kernel trace of `bench.py {bench_args}`", "",
            "Command (from the repository root, after `cd /tmp && export TMPDIR=/tmp`):", "",
            f"    rocprofv3 --kernel-trace --stats --output-format csv -d {folder} -o bench -- "
