@@ -15,8 +15,11 @@
  *   - Shapes: x / x_int8 are [M][K]; packed weights are [N][K/4]; outputs are
  *     [M][N]; scale_act is [M]; scale_wt is [N].
  *   - Buffers are owned by the caller.  The library never allocates, frees or
- *     synchronises device memory, and keeps no state besides a cached
- *     per-device architecture check.
+ *     synchronises device memory.  Its only state is per device and set once:
+ *     a cached architecture check, a flag per GEMM kernel instance recording
+ *     that its dynamic LDS limit has been raised (hipFuncSetAttribute), and
+ *     the device's static arrays (a small always-cached pad that the decode
+ *     GEMV's surplus loads read).
  *   - Except bitnet_pack_weights (host memory), every pointer is device memory
  *     and every call is enqueued on `stream` (a hipStream_t; NULL = the null
  *     stream) and returns without waiting.  Faults during execution surface at

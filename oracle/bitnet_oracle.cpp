@@ -229,11 +229,6 @@ void oracle_epilogue(const int32_t* acc, const uint16_t* sa, const uint16_t* sw,
 }
 
 // ---------------------------------------------------------------------------
-// The whole layer (bitnet-cpu, bitnet_linear and bitnet_gemv_fused; reading
-// R6): quantise each row, contract, scale.  Fills q/scale_act/acc when the
-// caller passes buffers for them (NULL to skip).
-// ---------------------------------------------------------------------------
-// ---------------------------------------------------------------------------
 // INT8 weight-only decode matmul (W8A16), as in "CoolDip00/tiny-llm,
 // src/tinyllm/kernels/int8_gemv.py" (docstring of the module and of
 // int8_matmul): y[m][n] = scale[n] * sum_k x[m][k] * q[n][k], with bf16 x,
@@ -352,6 +347,11 @@ int oracle_rmsnorm_quantize(const uint16_t* x, const uint16_t* gain, float eps, 
     return ORC_OK;
 }
 
+// ---------------------------------------------------------------------------
+// The whole layer (bitnet-cpu, bitnet_linear and bitnet_gemv_fused; reading
+// R6): quantise each row, contract, scale.  Fills q/scale_act/acc when the
+// caller passes buffers for them (NULL to skip).
+// ---------------------------------------------------------------------------
 int oracle_linear(const uint16_t* x, const uint8_t* P, const uint16_t* sw, int64_t M, int64_t N, int64_t K,
                   uint16_t* out, int8_t* q_out, uint16_t* sa_out, int32_t* acc_out) {
     if (M < 0 || N < 0 || K <= 0 || K % 4 != 0) return ORC_ERR_SHAPE;
@@ -367,8 +367,6 @@ int oracle_linear(const uint16_t* x, const uint8_t* P, const uint16_t* sw, int64
     return rc;
 }
 
-// One output element of the layer from an already quantised row: used to
-// check sampled outputs of full-size problems one by one.
 // The whole layer on f32 activations: quantise (f32), contract, scale.
 int oracle_linear_f32(const float* x, const uint8_t* P, const uint16_t* sw, int64_t M, int64_t N, int64_t K,
                       uint16_t* out, int8_t* q_out, uint16_t* sa_out, int32_t* acc_out) {
@@ -385,6 +383,8 @@ int oracle_linear_f32(const float* x, const uint8_t* P, const uint16_t* sw, int6
     return rc;
 }
 
+// One output element of the layer from an already quantised row: used to
+// check sampled outputs of full-size problems one by one.
 uint16_t oracle_linear_one(const int8_t* q_row, uint16_t sa, const uint8_t* P, const uint16_t* sw, int64_t K,
                            int64_t n, int32_t* acc_out) {
     const int64_t s = oracle_dot_i64(q_row, P, K, n);

@@ -123,6 +123,48 @@ def _need(t, dtype, name, device=True):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _need_out(t, dtype, shape, name, like):
+    """A caller-supplied output: `dtype`, dense, on the device of `like`, and
+    holding exactly prod(shape) elements (its own shape may be any view of
+    them); the kernels write that many elements from its first one."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != like.device:
+        raise ValueError(f"{name} must be on {like.device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    n = 1
+    for d in shape:
+        n *= int(d)
+    if t.numel() != n:
+        raise ValueError(f"{name} must hold {tuple(shape)} = {n} elements, got {tuple(t.shape)}")
+    return t
+
+
+def _out_or_new(out, dtype, shape, name, like):
+    if out is None:
+        return torch.empty(tuple(shape), dtype=dtype, device=like.device)
+    return _need_out(out, dtype, shape, name, like)
+
+
+def _workspace(ws, need, like):
+    """A caller-supplied workspace: dense uint8 bytes on the device of `like`,
+    at least `need` of them.  Returns (tensor or None, its byte count)."""
+    if ws is None:
+        if need == 0:
+            return None, 0
+        ws = torch.empty((need,), dtype=torch.uint8, device=like.device)
+    if ws.dtype != torch.uint8:
+        raise TypeError(f"workspace must be torch.uint8, got {ws.dtype}")
+    if ws.device != like.device:
+        raise ValueError(f"workspace must be on {like.device}, got {ws.device}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {need} needed")
+    return ws, ws.numel()
+
+
 # ----------------------------------------------------------------------------- host packing
 
 def pack_weights(W):
@@ -146,8 +188,8 @@ def quantize_activation(x, out=None, scale=None):
     K = x.shape[-1]
     M = x.numel() // K if K else 0
     x2 = x.reshape(M, K)
-    q = out if out is not None else torch.empty((M, K), dtype=torch.int8, device=x.device)
-    s = scale if scale is not None else torch.empty((M,), dtype=torch.bfloat16, device=x.device)
+    q = _out_or_new(out, torch.int8, (M, K), "out", x)
+    s = _out_or_new(scale, torch.bfloat16, (M,), "scale", x)
     if x.dtype == torch.float32:
         _check(load_library().bitnet_quantize_act_f32(_ptr(q), _ptr(s), _ptr(x2), M, K, _stream(x)),
                "bitnet_quantize_act_f32")
@@ -166,7 +208,7 @@ def bitnet_gemm(x_int8, w_packed, scale_act, scale_wt, out=None):
     N = w_packed.shape[0]
     if w_packed.shape[1] * 4 != K or scale_act.numel() != M or scale_wt.numel() != N:
         raise ValueError("bitnet_gemm: inconsistent shapes")
-    o = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x_int8.device)
+    o = _out_or_new(out, torch.bfloat16, (M, N), "out", x_int8)
     _check(load_library().bitnet_gemm(_ptr(o), _ptr(x_int8), _ptr(w_packed), _ptr(scale_act), _ptr(scale_wt),
                                       M, N, K, _stream(x_int8)), "bitnet_gemm")
     return o
@@ -181,7 +223,7 @@ def bitnet_gemv_fused(x, w_packed, scale_wt, out=None):
     N = w_packed.shape[0]
     if w_packed.shape[1] * 4 != K or scale_wt.numel() != N:
         raise ValueError("bitnet_gemv_fused: inconsistent shapes")
-    o = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    o = _out_or_new(out, torch.bfloat16, (M, N), "out", x)
     _check(load_library().bitnet_gemv_fused(_ptr(o), _ptr(x), _ptr(w_packed), _ptr(scale_wt), M, N, K, _stream(x)),
            "bitnet_gemv_fused")
     return o
@@ -219,12 +261,9 @@ def bitnet_linear(x, w_packed, scale_wt, out=None, workspace=None, bias=None):
         raise ValueError("bitnet_linear: inconsistent shapes")
     plain = x.dtype == torch.bfloat16 and bias is None
     ws_bytes = linear_workspace_bytes(M, K) if plain else linear_ex_workspace_bytes(M, K, x.dtype)
-    ws = workspace
-    if ws is None and ws_bytes > 0:
-        ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=x.device)
-    o = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    ws, ws_n = _workspace(workspace, ws_bytes, x)
+    o = _out_or_new(out, torch.bfloat16, (M, N), "out", x)
     lib = load_library()
-    ws_n = ws.numel() if ws is not None else 0
     if plain:
         _check(lib.bitnet_linear(_ptr(o), _ptr(x), _ptr(w_packed), _ptr(scale_wt), M, N, K, _ptr(ws), ws_n,
                                  _stream(x)), "bitnet_linear")
@@ -243,7 +282,7 @@ def bitnet_gemm_i32(x_int8, w_packed, out=None):
     N = w_packed.shape[0]
     if w_packed.shape[1] * 4 != K:
         raise ValueError("bitnet_gemm_i32: inconsistent shapes")
-    o = out if out is not None else torch.empty((M, N), dtype=torch.int32, device=x_int8.device)
+    o = _out_or_new(out, torch.int32, (M, N), "out", x_int8)
     _check(load_library().bitnet_gemm_i32(_ptr(o), _ptr(x_int8), _ptr(w_packed), M, N, K, _stream(x_int8)),
            "bitnet_gemm_i32")
     return o
@@ -270,7 +309,9 @@ def bitnet_scale_epilogue(acc, scale_act, scale_wt, out=None):
     _need(scale_act, torch.bfloat16, "scale_act")
     _need(scale_wt, torch.bfloat16, "scale_wt")
     M, N = acc.shape
-    o = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=acc.device)
+    if scale_act.numel() != M or scale_wt.numel() != N:
+        raise ValueError("bitnet_scale_epilogue: inconsistent shapes")
+    o = _out_or_new(out, torch.bfloat16, (M, N), "out", acc)
     _check(load_library().bitnet_scale_epilogue(_ptr(o), _ptr(acc), _ptr(scale_act), _ptr(scale_wt), M, N,
                                                 _stream(acc)), "bitnet_scale_epilogue")
     return o
@@ -288,7 +329,7 @@ def w8a16_gemv(x, q, scale, out=None):
     N = q.shape[0]
     if q.shape[1] != K or scale.numel() != N:
         raise ValueError("w8a16_gemv: inconsistent shapes")
-    o = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=x.device)
+    o = _out_or_new(out, torch.float32, (M, N), "out", x)
     _check(load_library().bitnet_w8a16_gemv(_ptr(o), _ptr(x), _ptr(q), _ptr(scale), M, N, K, _stream(x)),
            "bitnet_w8a16_gemv")
     return o
@@ -308,14 +349,14 @@ def rmsnorm_quantize(x, gain=None, eps=RMS_EPS_DEFAULT, out=None, scale=None, x_
     _need(x, torch.bfloat16, "x")
     if gain is not None:
         _need(gain, torch.bfloat16, "gain")
-    if x_norm is not None:
-        _need(x_norm, torch.bfloat16, "x_norm")
     K = x.shape[-1]
     M = x.numel() // K if K else 0
     if gain is not None and gain.numel() != K:
         raise ValueError("rmsnorm_quantize: gain must have K elements")
-    q = out if out is not None else torch.empty((M, K), dtype=torch.int8, device=x.device)
-    sa = scale if scale is not None else torch.empty((M,), dtype=torch.bfloat16, device=x.device)
+    if x_norm is not None:
+        _need_out(x_norm, torch.bfloat16, (M, K), "x_norm", x)
+    q = _out_or_new(out, torch.int8, (M, K), "out", x)
+    sa = _out_or_new(scale, torch.bfloat16, (M,), "scale", x)
     _check(load_library().bitnet_rmsnorm_quantize(_ptr(q), _ptr(sa), _ptr(x_norm), _ptr(x), _ptr(gain), eps, M, K,
                                                   _stream(x)), "bitnet_rmsnorm_quantize")
     return q, sa
@@ -333,10 +374,8 @@ def bitnet_linear_rms(x, w_packed, scale_wt, gain=None, eps=RMS_EPS_DEFAULT, out
     N = w_packed.shape[0]
     if w_packed.shape[1] * 4 != K or scale_wt.numel() != N or (gain is not None and gain.numel() != K):
         raise ValueError("bitnet_linear_rms: inconsistent shapes")
-    ws = workspace
-    if ws is None:
-        ws = torch.empty((max(linear_rms_workspace_bytes(M, K), 1),), dtype=torch.uint8, device=x.device)
-    o = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    ws, ws_n = _workspace(workspace, linear_rms_workspace_bytes(M, K), x)
+    o = _out_or_new(out, torch.bfloat16, (M, N), "out", x)
     _check(load_library().bitnet_linear_rms(_ptr(o), _ptr(x), _ptr(gain), eps, _ptr(w_packed), _ptr(scale_wt), M, N,
-                                            K, _ptr(ws), ws.numel(), _stream(x)), "bitnet_linear_rms")
+                                            K, _ptr(ws), ws_n, _stream(x)), "bitnet_linear_rms")
     return o.view(*x.shape[:-1], N)

@@ -276,15 +276,15 @@ __device__ __forceinline__ uint32_t quantize_bf16x2(uint32_t w, const QuantScale
 
 // ----------------------------------------------------------------- epilogue
 
-// out = bf16_rne( fp32( (float)acc * fp32(sa * sw) ) ).  sa * sw is exact (two
-// bf16 significands fit in fp32), (float)acc is exact for |acc| < 2^24, so the
-// result has a single fp32 rounding followed by the bf16 rounding.  There is
-// no addition, so no contraction can change it.
 // The bias on a bf16 layer output: bf16_rne(fp32(y) + fp32(bias)).
 __device__ __forceinline__ uint16_t add_bias_bf16(uint32_t y, uint32_t b) {
     return f32_to_bf16(bf16_to_f32(y) + bf16_to_f32(b));
 }
 
+// out = bf16_rne( fp32( (float)acc * fp32(sa * sw) ) ).  sa * sw is exact (two
+// bf16 significands fit in fp32), (float)acc is exact for |acc| < 2^24, so the
+// result has a single fp32 rounding followed by the bf16 rounding.  There is
+// no addition, so no contraction can change it.
 __device__ __forceinline__ uint16_t epilogue_bf16(int acc, float sa, float sw) {
     const float scale = sa * sw;
     const float y = (float)acc * scale;

@@ -16,7 +16,9 @@
 //    rows; they stay in L2) into LDS as int8, each 16-element group stored as
 //    the 4x4 byte transpose the unpack needs, in 64-element segments padded to
 //    80 bytes so that the eight sub-lanes of a step hit distinct LDS banks.
-//    The first weight loads are issued before this prologue.
+//    Each thread first issues its loads of x, then the weight ring's first D
+//    loads, and only then waits for x to compute the absmax and quantise, so
+//    the weights are in flight during the prologue.
 //  * Weights.  Work is split into units of 8 output rows; a workgroup owns up
 //    to 32 consecutive units and its 4 waves take them round-robin.  Eight
 //    consecutive lanes share a row and read 8 x 16 B = 128 contiguous bytes of

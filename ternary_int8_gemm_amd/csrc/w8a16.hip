@@ -8,15 +8,18 @@
 // products accumulate in fp32, and the per-row scale is applied at the end.
 //
 // At decode the call is bound by reading q (one byte per weight), so it is laid
-// out like the split-K path of the ternary GEMM: a block owns 32 output columns
-// and 32 * MT rows (MT = 1 for M <= 32, else 2; rows past M read as zeros), and
-// its KW waves split K into 64-element chunks.  Operands go from global memory
-// straight into v_mfma_f32_32x32x16_bf16 registers: lane (r, h) loads, per chunk,
-// the 32 int8 weights 32h .. 32h + 31 of column r (two 16-byte loads) and for
-// each of the four MFMA k-steps s the 8 activations 32h + 8s .. 32h + 8s + 7 of
-// row r (one 16-byte load), so both operands see the same k order.  A ring of D
-// chunks keeps loads in flight.  The waves' partial fp32 tiles are summed in
-// LDS in a fixed order (deterministic results), scaled and stored.
+// out like the split-K path of the ternary GEMM: a block owns 32 (or 64) output
+// columns and 32 * MT rows (MT = 1 for M <= 32, else 2; rows past M read as
+// zeros), and its KW waves split K into chunks on v_mfma_f32_32x32x16_bf16.
+// The main kernel for M >= 3, w8a16_lds_kernel (K % 128 == 0), stages each
+// wave's 128-element chunk of both operands through a private LDS region and
+// reads the MFMA fragments from there (see its own comment).  w8a16_kernel,
+// for other K % 64 == 0 shapes, loads 64- or 128-element chunks straight into
+// MFMA registers instead: lane (r, h) loads the int8 weights of its half of
+// the chunk of column r and, per MFMA k-step, the matching 8 activations of
+// row r, so both operands see the same k order; a ring of D chunks keeps loads
+// in flight.  Either way the waves' partial fp32 tiles are summed in LDS in a
+// fixed order (deterministic results), scaled and stored.
 //
 // w8a16_stream_kernel (M <= 2, the decode case).  Padding M to an MFMA tile
 // forces the lanes of one load onto 32 different weight rows; for a handful of

@@ -152,3 +152,42 @@ def test_status_strings():
     for code in range(7):
         assert lib.bitnet_status_string(code).decode() not in ("", "unknown status")
     assert lib.bitnet_version() >= 100
+
+
+# ----------------------------------------------------------------------------- binding argument checks
+
+def test_binding_rejects_bad_outputs():
+    """Caller-supplied outputs are checked before any call: dtype, device,
+    density and element count (the kernels write prod(shape) elements)."""
+    like = torch.empty((2, 8), dtype=torch.bfloat16)
+    ok = torch.empty((4, 6), dtype=torch.bfloat16)
+    assert tg._need_out(ok, torch.bfloat16, (4, 6), "out", like) is ok
+    assert tg._need_out(ok.view(24), torch.bfloat16, (4, 6), "out", like).numel() == 24   # any view of them
+    with pytest.raises(TypeError):
+        tg._need_out(torch.empty((4, 6), dtype=torch.float32), torch.bfloat16, (4, 6), "out", like)
+    with pytest.raises(ValueError):
+        tg._need_out(torch.empty((4, 5), dtype=torch.bfloat16), torch.bfloat16, (4, 6), "out", like)   # too small
+    with pytest.raises(ValueError):
+        tg._need_out(torch.empty((4, 7), dtype=torch.bfloat16), torch.bfloat16, (4, 6), "out", like)   # too large
+    with pytest.raises(ValueError):
+        tg._need_out(torch.empty((6, 4), dtype=torch.bfloat16).t(), torch.bfloat16, (4, 6), "out", like)  # strided
+    with pytest.raises(ValueError):
+        tg._need_out(torch.empty((4, 6), dtype=torch.bfloat16, device="meta"), torch.bfloat16, (4, 6), "out", like)
+    assert tg._out_or_new(None, torch.int8, (3, 5), "out", like).shape == (3, 5)
+
+
+def test_binding_rejects_bad_workspace():
+    like = torch.empty((2, 8), dtype=torch.bfloat16)
+    assert tg._workspace(None, 0, like) == (None, 0)
+    ws, n = tg._workspace(None, 100, like)
+    assert n == 100 and ws.dtype == torch.uint8
+    ws = torch.empty((300,), dtype=torch.uint8)
+    assert tg._workspace(ws, 256, like)[1] == 300
+    with pytest.raises(ValueError):
+        tg._workspace(ws, 301, like)                                       # too small
+    with pytest.raises(TypeError):
+        tg._workspace(torch.empty((300,), dtype=torch.int32), 256, like)   # bytes are uint8
+    with pytest.raises(ValueError):
+        tg._workspace(torch.empty((300, 2), dtype=torch.uint8)[:, 0], 256, like)   # strided
+    with pytest.raises(ValueError):
+        tg._workspace(torch.empty((300,), dtype=torch.uint8, device="meta"), 256, like)

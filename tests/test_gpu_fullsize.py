@@ -12,11 +12,16 @@
 * Small-batch GEMM, M in {8..256}, LLaMA-7B shapes, pre-quantised activations:
   the int32 accumulators over the whole output against an exact float64 product
   (every partial sum is an integer below 2^53, so any summation order is exact),
-  and sampled rows and columns of the bf16 output and accumulators against the oracle.
+  the whole bf16 output against the oracle's epilogue of that exact product, and
+  sampled rows and columns of both against the oracle's own contraction.
 * Prefill, M in {2048, 4096}, LLaMA-7B shapes, activations with 1% outlier
   channels: the quantised activations and scales over the whole input against
-  the oracle, the accumulators against the exact float64 product, and sampled
-  rows and columns of bitnet_linear's output against the oracle.
+  the oracle, the accumulators against the exact float64 product of the
+  oracle's quantised activations, the whole output of bitnet_linear against the
+  oracle's epilogue of that product, and sampled rows and columns against the
+  oracle's own contraction.
+* Every weight matrix is packed by the library's host packer, whose bytes must
+  equal the oracle's.
 """
 import functools
 
@@ -50,6 +55,13 @@ def assert_bf16_equal(got, want, what):
     assert bad.size == 0, f"{what}: {len(bad)} outputs differ, first at {tuple(bad[0])}: {got[tuple(bad[0])]:#06x} vs {want[tuple(bad[0])]:#06x}"
 
 
+def lib_pack(W):
+    """The library's host packer, required to give the oracle's bytes."""
+    P = tg.pack_weights(torch.from_numpy(np.ascontiguousarray(W))).numpy()
+    assert np.array_equal(P, oracle.pack(W)), "bitnet_pack_weights differs from the oracle's pack"
+    return P
+
+
 def exact_product(q_dev, W_host):
     """acc = q @ W^T in float64 on the GPU: exact for |acc| < 2^53."""
     Wt = torch.from_numpy(W_host).to(DEV).to(torch.float64).t().contiguous()
@@ -61,6 +73,17 @@ def sample_rows_cols(M, N, seed, n_cols=48):
     rows = sorted({0, M - 1, M // 2, int(g.integers(0, M))})
     cols = sorted({0, N - 1} | set(int(c) for c in g.choice(N, size=min(n_cols, N), replace=False)))
     return np.array(rows), np.array(cols)
+
+
+def check_whole(out_dev, exact, sa, sw, what):
+    """Every bf16 output against the oracle's epilogue applied to the exact
+    accumulators (a float64 product whose partial sums are integers below 2^53,
+    so it is the exact integer result; it is computed by torch, not by this
+    library) with the oracle's activation scales."""
+    acc_exact = exact.cpu().numpy()
+    assert np.abs(acc_exact).max(initial=0) < 2 ** 31
+    want = oracle.epilogue(acc_exact.astype(np.int32), sa, sw)
+    assert_bf16_equal(host_bf16(out_dev), want, f"{what} (whole output)")
 
 
 def check_samples(out_dev, acc_dev, q, sa, P, sw, seed, what):
@@ -85,7 +108,7 @@ def decode_problem(i):
     """Projection i of the decode step with the benchmark's seeds (workload 1)."""
     name, N, K = synth.BITNET_2B_DECODE[i]
     W = synth.ternary_weights(N, K, synth.seed_for(1, 16 * i + synth.T_WEIGHT))
-    P = oracle.pack(W)
+    P = lib_pack(W)
     del W
     sw = synth.weight_scale_bf16(N, K, synth.seed_for(1, 16 * i + synth.T_SCALE))
     x = synth.activations_bf16(1, K, synth.seed_for(1, 16 * i + synth.T_ACT))
@@ -182,7 +205,7 @@ def test_decode_f32_bias_full(i):
 def llama_weights(j):
     name, N, K = synth.LLAMA7B_SHAPES[j]
     W = synth.ternary_weights(N, K, synth.seed_for(3, 16 * j + synth.T_WEIGHT))
-    P = oracle.pack(W)
+    P = lib_pack(W)
     sw = synth.weight_scale_bf16(N, K, synth.seed_for(3, 16 * j + synth.T_SCALE))
     return name, N, K, W, P, sw
 
@@ -201,8 +224,9 @@ def test_small_batch_gemm(j):
         qd, sad = dev(q), dev_bf16(sa)
         out = tg.bitnet_gemm(qd, Pd, sad, swd)
         acc = tg.bitnet_gemm_i32(qd, Pd)
-        exact = exact_product(qd, W)
+        exact = exact_product(dev(q), W)
         assert torch.equal(acc.to(torch.float64), exact), f"{name} M={M}: accumulators"
+        check_whole(out, exact, sa, sw, f"{name} M={M}")
         check_samples(out, acc, q, sa, P, sw, seed=M * 31 + j, what=f"{name} M={M}")
 
 
@@ -216,11 +240,14 @@ def test_prefill_linear(j, M):
     q, sa = tg.quantize_activation(xd)
     assert np.array_equal(q.cpu().numpy(), q_ref), f"{name} M={M}: quantised activations"
     assert np.array_equal(host_bf16(sa), sa_ref), f"{name} M={M}: activation scales"
+    exact = exact_product(dev(q_ref), W)                     # from the oracle's quantised activations
     acc = tg.bitnet_gemm_i32(q, Pd)
-    assert torch.equal(acc.to(torch.float64), exact_product(q, W)), f"{name} M={M}: accumulators"
+    assert torch.equal(acc.to(torch.float64), exact), f"{name} M={M}: accumulators"
     del acc
     ws = torch.empty((tg.linear_workspace_bytes(M, K),), dtype=torch.uint8, device=DEV)
     out = tg.bitnet_linear(xd, Pd, swd, workspace=ws)       # the benchmark's quantise + GEMM launch
+    check_whole(out, exact, sa_ref, sw, f"{name} M={M}")
+    del exact
     check_samples(out, None, q_ref, sa_ref, P, sw, seed=M + j, what=f"{name} M={M}")
     out2 = tg.bitnet_gemm(q, Pd, sa, swd)                    # pre-quantised launch: same bits
     assert torch.equal(out2.view(torch.int16), out.view(torch.int16)), f"{name} M={M}: gemm vs linear"

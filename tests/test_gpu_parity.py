@@ -57,10 +57,18 @@ def misaligned(t):
     return view.view(t.shape)
 
 
+def lib_pack(W):
+    """Pack with the library's host packer (the chain the kernels see in use) and
+    require the oracle's bytes: the kernels then run on library-packed weights."""
+    P = tg.pack_weights(torch.from_numpy(np.ascontiguousarray(W))).numpy()
+    assert np.array_equal(P, oracle.pack(W)), "bitnet_pack_weights differs from the oracle's pack"
+    return P
+
+
 def problem(M, N, K, seed, outliers=0.0, row_scales=False):
     x = synth.activations_bf16(M, K, seed, outlier_frac=outliers)
     W = synth.ternary_weights(N, K, seed + 1)
-    P = oracle.pack(W)
+    P = lib_pack(W)
     sw = synth.row_scales_bf16(N, seed + 2) if row_scales else synth.weight_scale_bf16(N, K, seed + 2)
     return x, W, P, sw
 
@@ -136,7 +144,7 @@ GEMM_SHAPES = [
 def test_gemm_i32_parity(M, N, K):
     q = synth.random_int8((M, K), seed=2000 + M + N + K)
     W = synth.ternary_weights(N, K, seed=2100 + M + N + K)
-    P = oracle.pack(W)
+    P = lib_pack(W)
     acc_ref = oracle.gemm_i32(q, P)
     acc = tg.bitnet_gemm_i32(dev(q), dev(P))
     assert np.array_equal(acc.cpu().numpy(), acc_ref)
@@ -155,7 +163,7 @@ def test_gemm_i32_extremes():
     q[1::2] = -127
     W = np.ones((N, K), dtype=np.int8)
     W[::3] = -1
-    P = oracle.pack(W)
+    P = lib_pack(W)
     assert np.array_equal(tg.bitnet_gemm_i32(dev(q), dev(P)).cpu().numpy(), oracle.gemm_i32(q, P))
 
 
@@ -163,7 +171,7 @@ def test_gemm_i32_misaligned_plain_path():
     M, N, K = 9, 20, 128
     q = synth.random_int8((M, K), seed=41)
     W = synth.ternary_weights(N, K, seed=42)
-    P = oracle.pack(W)
+    P = lib_pack(W)
     acc = tg.bitnet_gemm_i32(misaligned(dev(q)), dev(P))
     assert np.array_equal(acc.cpu().numpy(), oracle.gemm_i32(q, P))
 
@@ -172,7 +180,10 @@ def test_gemm_i32_misaligned_plain_path():
 
 @pytest.mark.parametrize("M,N,K", [(4, 128, 256), (16, 4096, 4096), (200, 300, 1024), (33, 65, 68),
                                    (513, 10000, 256), (300, 13000, 384), (1000, 2200, 512), (700, 4000, 1280),
-                                   (1100, 8200, 640), (16, 128256, 512), (40, 70000, 512)])
+                                   (1100, 8200, 640), (16, 128256, 512), (40, 70000, 512),
+                                   # the bf16-output 128 x 512 block tile (>= 2 such blocks per CU), ragged M
+                                   # and N: one stage, and two stages
+                                   (1030, 32770, 128), (600, 70000, 256)])
 def test_gemm_bf16_parity(M, N, K):
     x, W, P, _ = problem(M, N, K, seed=3000 + M)
     sw = synth.row_scales_bf16(N, seed=3100 + M)
@@ -312,7 +323,7 @@ def test_zero_activation_row_and_constant_weights():
     W = np.ones((N, K), dtype=np.int8)
     W[N // 2:] = -1
     W[N - 1] = 0
-    P = oracle.pack(W)
+    P = lib_pack(W)
     sw = np.full((N,), 0x3F80, dtype=np.uint16)
     ref = oracle.linear(x, P, sw)
     for fn in (lambda: tg.bitnet_gemv_fused(dev_bf16(x), dev(P), dev_bf16(sw)),):
@@ -338,8 +349,10 @@ def test_device_errors_raise():
     sw = torch.ones((8,), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(tg.BitnetError):
         tg.bitnet_gemv_fused(x, P, sw)                   # M = 16 > 15
-    with pytest.raises(tg.BitnetError):
+    with pytest.raises(ValueError):                       # the binding checks the workspace first
         tg.bitnet_linear(x, P, sw, workspace=torch.empty((8,), dtype=torch.uint8, device=DEV))
+    with pytest.raises(ValueError):                       # and the size of a given output
+        tg.bitnet_linear(x, P, sw, out=torch.empty((16, 7), dtype=torch.bfloat16, device=DEV))
 
 
 # ----------------------------------------------------------------------------- f32 activations and bias
@@ -399,7 +412,7 @@ def test_linear_f32_parity(M, N, K):
     g = synth.rng(6100 + M + N + K)
     x = g.standard_normal((M, K)).astype(np.float32)
     W = synth.ternary_weights(N, K, seed=6200 + M)
-    P = oracle.pack(W)
+    P = lib_pack(W)
     sw = synth.row_scales_bf16(N, seed=6300 + M)
     ref = oracle.linear_f32(x, P, sw)
     out = tg.bitnet_linear(dev_f32(x), dev(P), dev_bf16(sw))
@@ -412,7 +425,7 @@ def test_linear_f32_parity(M, N, K):
 def test_linear_bias_parity(dtype, M, N, K):
     g = synth.rng(6400 + M + N + K)
     W = synth.ternary_weights(N, K, seed=6500 + M)
-    P = oracle.pack(W)
+    P = lib_pack(W)
     sw = synth.row_scales_bf16(N, seed=6600 + M)
     bias = synth.row_scales_bf16(N, seed=6700 + M, lo=-4.0, hi=4.0)
     if dtype == "bf16":
@@ -438,7 +451,7 @@ def test_linear_f32_fused_special_rows():
     x[2, :] = np.float32(2.0 ** -31)
     x[3, 17] = np.float32(3.0e4)
     W = synth.ternary_weights(N, K, seed=6901)
-    P = oracle.pack(W)
+    P = lib_pack(W)
     sw = synth.row_scales_bf16(N, seed=6902)
     ref = oracle.linear_f32(x, P, sw)
     out = tg.bitnet_linear(dev_f32(x), dev(P), dev_bf16(sw))
@@ -452,7 +465,7 @@ def test_linear_ex_fused_equals_split(dtype, M, N, K):
     and the quantise + GEMM + bias path give the same bits: a misaligned x
     sends the same call down the second."""
     W = synth.ternary_weights(N, K, seed=7000 + M)
-    P = dev(oracle.pack(W))
+    P = dev(lib_pack(W))
     sw = dev_bf16(synth.row_scales_bf16(N, seed=7001 + M))
     bias = dev_bf16(synth.row_scales_bf16(N, seed=7002 + M, lo=-4.0, hi=4.0))
     if dtype == "bf16":
@@ -616,7 +629,7 @@ def test_rmsnorm_quantize_misaligned_plain_path():
 def test_linear_rms_parity(M, N, K, with_gain):
     x = synth.activations_bf16(M, K, seed=8200 + M + N + K)
     W = synth.ternary_weights(N, K, seed=8300 + M)
-    P = oracle.pack(W)
+    P = lib_pack(W)
     sw = synth.row_scales_bf16(N, seed=8400 + M)
     gain = synth.row_scales_bf16(K, seed=8500 + K, lo=0.5, hi=1.5) if with_gain else None
     eps = oracle.FP32_EPS
@@ -631,7 +644,7 @@ def test_linear_rms_fused_equals_split_on_unambiguous_rows():
     M, N, K = 4, 4096, 2560
     x = synth.activations_bf16(M, K, seed=8600)
     W = synth.ternary_weights(N, K, seed=8601)
-    Pd, swd = dev(oracle.pack(W)), dev_bf16(synth.row_scales_bf16(N, seed=8602))
+    Pd, swd = dev(lib_pack(W)), dev_bf16(synth.row_scales_bf16(N, seed=8602))
     xd = dev_bf16(x)
     fused = tg.bitnet_linear_rms(xd, Pd, swd)                 # fused decode GEMV with the prologue
     q, sa = tg.rmsnorm_quantize(xd)
