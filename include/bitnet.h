@@ -19,7 +19,8 @@
  *     a cached architecture check, a flag per GEMM kernel instance recording
  *     that its dynamic LDS limit has been raised (hipFuncSetAttribute), and
  *     the device's static arrays (a small always-cached pad that the decode
- *     GEMV's surplus loads read).
+ *     GEMV's surplus loads read, and the scratch of bitnet_linear_noalloc with
+ *     its device address, looked up on that call's first use of the device).
  *   - Except bitnet_pack_weights (host memory), every pointer is device memory
  *     and every call is enqueued on `stream` (a hipStream_t; NULL = the null
  *     stream) and returns without waiting.  Faults during execution surface at
@@ -57,7 +58,9 @@ typedef enum bitnet_status {
     BITNET_ERR_VALUE = 3,     /* a weight outside {-1, 0, +1} given to the packer   */
     BITNET_ERR_WORKSPACE = 4, /* workspace smaller than bitnet_linear_workspace_bytes */
     BITNET_ERR_DEVICE = 5,    /* current device is not gfx950, or no device         */
-    BITNET_ERR_LAUNCH = 6     /* the HIP runtime rejected a kernel launch           */
+    BITNET_ERR_LAUNCH = 6,    /* the HIP runtime rejected a kernel launch           */
+    BITNET_ERR_TOO_LARGE = 7  /* bitnet_linear_noalloc: the workspace this call needs
+                                 exceeds BITNET_NOALLOC_SCRATCH_BYTES               */
 } bitnet_status;
 
 /* A hipStream_t, kept opaque so that this header needs no HIP headers. */
@@ -133,6 +136,31 @@ size_t bitnet_linear_workspace_bytes(int64_t M, int64_t K);
 bitnet_status bitnet_linear(uint16_t* out, const uint16_t* x, const uint8_t* w_packed, const uint16_t* scale_wt,
                             int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
                             bitnet_stream_t stream);
+
+/* Size of the per-device static scratch of bitnet_linear_noalloc (32 MiB). */
+#define BITNET_NOALLOC_SCRATCH_BYTES (32 << 20)
+
+/*
+ * bitnet_linear for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, dispatch and bits as bitnet_linear, with the
+ * workspace (x_int8 [M][K] and scale_act [M]) held in a static array of
+ * BITNET_NOALLOC_SCRATCH_BYTES bytes that the library keeps on each device
+ * until the process ends, instead of a caller buffer.  No call allocates or
+ * frees memory (no hipMalloc, hipFree or allocating library routine); the
+ * device address of the array is looked up on the first call on each device.
+ * out: bf16 [M][N] (written); x: bf16 [M][K]; w_packed: uint8 [N][K/4];
+ * scale_wt: bf16 [N].  Device pointers, enqueued on stream.
+ * Every call on one device shares that device's array and leaves its contents
+ * behind; the quantiser writes every byte the GEMM reads before it reads it, so
+ * no clearing is needed, but calls that overlap on one device (other streams,
+ * other threads) race and must be serialised by the caller.
+ * Errors: bitnet_linear_workspace_bytes(M, K) > BITNET_NOALLOC_SCRATCH_BYTES
+ * -> TOO_LARGE (e.g. M * K above about 33.5 million); others as bitnet_linear.
+ */
+bitnet_status bitnet_linear_noalloc(uint16_t* out, const uint16_t* x, const uint8_t* w_packed,
+                                    const uint16_t* scale_wt, int64_t M, int64_t N, int64_t K,
+                                    bitnet_stream_t stream);
 
 /* Activation element types accepted by bitnet_linear_ex. */
 #define BITNET_DTYPE_BF16 0

@@ -29,8 +29,9 @@ MAX_K = 131072
 
 STATUS = {
     0: "BITNET_OK", 1: "BITNET_ERR_NULL", 2: "BITNET_ERR_SHAPE", 3: "BITNET_ERR_VALUE",
-    4: "BITNET_ERR_WORKSPACE", 5: "BITNET_ERR_DEVICE", 6: "BITNET_ERR_LAUNCH",
+    4: "BITNET_ERR_WORKSPACE", 5: "BITNET_ERR_DEVICE", 6: "BITNET_ERR_LAUNCH", 7: "BITNET_ERR_TOO_LARGE",
 }
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libbitnet_hip.so")
@@ -67,6 +68,7 @@ def load_library():
         "bitnet_gemm": [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p],
         "bitnet_gemv_fused": [_p, _p, _p, _p, _i64, _i64, _i64, _p],
         "bitnet_linear": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _sz, _p],
+        "bitnet_linear_noalloc": [_p, _p, _p, _p, _i64, _i64, _i64, _p],
         "bitnet_gemm_i32": [_p, _p, _p, _i64, _i64, _i64, _p],
         "bitnet_gemv_fused_i32": [_p, _p, _p, _p, _i64, _i64, _i64, _p],
         "bitnet_scale_epilogue": [_p, _p, _p, _p, _i64, _i64, _p],
@@ -272,6 +274,25 @@ def bitnet_linear(x, w_packed, scale_wt, out=None, workspace=None, bias=None):
         _check(lib.bitnet_linear_ex(_ptr(o), _ptr(x), code, _ptr(w_packed), _ptr(scale_wt), _ptr(bias), M, N, K,
                                     _ptr(ws), ws_n, _stream(x)), "bitnet_linear_ex")
     return o.view(*x.shape[:-1], N)
+
+
+def bitnet_linear_noalloc(x, w_packed, scale_wt, out):
+    """bitnet_linear for callers that cannot allocate: bf16 x[..., K] -> the
+    given bf16 out [..., N].  The workspace is the library's static per-device
+    scratch (NOALLOC_SCRATCH_BYTES); nothing is allocated, so `out` is required.
+    Calls that overlap on one device race on that scratch."""
+    _need(x, torch.bfloat16, "x")
+    _need(w_packed, torch.uint8, "w_packed")
+    _need(scale_wt, torch.bfloat16, "scale_wt")
+    K = x.shape[-1]
+    M = x.numel() // K if K else 0
+    N = w_packed.shape[0]
+    if w_packed.shape[1] * 4 != K or scale_wt.numel() != N:
+        raise ValueError("bitnet_linear_noalloc: inconsistent shapes")
+    _need_out(out, torch.bfloat16, (M, N), "out", x)
+    _check(load_library().bitnet_linear_noalloc(_ptr(out), _ptr(x), _ptr(w_packed), _ptr(scale_wt), M, N, K,
+                                                _stream(x)), "bitnet_linear_noalloc")
+    return out
 
 
 def bitnet_gemm_i32(x_int8, w_packed, out=None):

@@ -68,6 +68,7 @@ BITNET_API const char* bitnet_status_string(bitnet_status status) {
         case BITNET_ERR_WORKSPACE: return "workspace too small";
         case BITNET_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
         case BITNET_ERR_LAUNCH: return "kernel launch failed";
+        case BITNET_ERR_TOO_LARGE: return "problem exceeds the static scratch of bitnet_linear_noalloc";
     }
     return "unknown status";
 }
@@ -182,6 +183,52 @@ BITNET_API bitnet_status bitnet_linear(uint16_t* out, const uint16_t* x, const u
     hipStream_t s = (hipStream_t)stream;
     if (hipError_t e = launch_quantize(x_int8, scale_act, x, M, K, s)) return launched(e);
     return launched(launch_gemm(out, nullptr, x_int8, w_packed, scale_act, scale_wt, M, N, K, s));
+}
+
+// ---------------------------------------------------------------- bitnet_linear without allocation
+//
+// bitnet_linear_noalloc keeps its workspace (the quantised activations and
+// their scales) in this array instead of a caller buffer.  The array exists
+// once per device, for as long as the library stays loaded; every call on a
+// device shares it (overlapping calls on one device race).  Its host-side name
+// is only a handle: the device address is looked up once per device with
+// hipGetSymbolAddress and kept in g_scratch.
+static __device__ __align__(256) uint8_t scratch[BITNET_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::atomic<uint8_t*> g_scratch[kMaxDevices];
+
+// This device's copy of `scratch` (the current device; check_device has run).
+bitnet_status scratch_ptr(uint8_t** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BITNET_ERR_DEVICE;
+    uint8_t* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        if (hipGetSymbolAddress((void**)&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return BITNET_ERR_DEVICE;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return BITNET_OK;
+}
+}  // namespace
+
+BITNET_API bitnet_status bitnet_linear_noalloc(uint16_t* out, const uint16_t* x, const uint8_t* w_packed,
+                                               const uint16_t* scale_wt, int64_t M, int64_t N, int64_t K,
+                                               bitnet_stream_t stream) {
+    if (!sizes_ok(M, N)) return BITNET_ERR_SHAPE;
+    if (bitnet_status st = check_k(K)) return st;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!out || !x || !w_packed || !scale_wt) return BITNET_ERR_NULL;
+    const size_t need = bitnet_linear_workspace_bytes(M, K);
+    if (need > (size_t)BITNET_NOALLOC_SCRATCH_BYTES) return BITNET_ERR_TOO_LARGE;
+    if (need == 0) return bitnet_gemv_fused(out, x, w_packed, scale_wt, M, N, K, stream);
+    if (bitnet_status st = check_device()) return st;
+    uint8_t* ws = nullptr;
+    if (bitnet_status st = scratch_ptr(&ws)) return st;
+    // Every byte the GEMM reads is written by the quantiser first, so nothing
+    // of the previous call's contents needs clearing.
+    return bitnet_linear(out, x, w_packed, scale_wt, M, N, K, ws, need, stream);
 }
 
 BITNET_API bitnet_status bitnet_quantize_act_f32(int8_t* x_int8, uint16_t* scale_act, const float* x, int64_t M,

@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
                      "bitnet_linear_workspace_bytes", "bitnet_status_string", "bitnet_version",
                      "bitnet_quantize_act_f32", "bitnet_linear_ex", "bitnet_linear_ex_workspace_bytes",
                      "bitnet_w8a16_gemv", "bitnet_rmsnorm_quantize", "bitnet_linear_rms",
-                     "bitnet_linear_rms_workspace_bytes"]:
+                     "bitnet_linear_rms_workspace_bytes", "bitnet_linear_noalloc"]:
         assert required in names
 
 
@@ -120,6 +120,10 @@ def test_shape_errors_precede_device_use():
     assert lib.bitnet_linear_rms(d, d, None, -1.0, d, d, 1, 8, 64, d, 1 << 20, None) == 3
     assert lib.bitnet_linear_rms(None, d, None, 1e-5, d, d, 1, 8, 64, d, 1 << 20, None) == 1
     assert lib.bitnet_linear_rms(d, d, None, 1e-5, d, d, 1, 0, 64, None, 0, None) == 0   # N == 0: no-op
+    assert lib.bitnet_linear_noalloc(d, d, d, d, 4, 8, 62, None) == 2                   # K % 4
+    assert lib.bitnet_linear_noalloc(None, d, d, d, 4, 8, 64, None) == 1
+    assert lib.bitnet_linear_noalloc(d, d, d, d, 8193, 8, 4096, None) == 7             # beyond the scratch
+    assert lib.bitnet_linear_noalloc(d, d, d, d, 0, 8, 64, None) == 0                  # M == 0: no-op
 
 
 def test_workspace_size():
@@ -149,7 +153,7 @@ def test_rms_workspace_size():
 
 def test_status_strings():
     lib = tg.load_library()
-    for code in range(7):
+    for code in range(8):
         assert lib.bitnet_status_string(code).decode() not in ("", "unknown status")
     assert lib.bitnet_version() >= 100
 
