@@ -35,7 +35,10 @@ import gzip
 import glob
 import hashlib
 import json
+import math
 import os
+import platform
+import subprocess
 import re
 import sys
 import time
@@ -80,32 +83,73 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def time_graph(graph, replays, stream):
-    """Replay `graph` on `stream` and time the replays with events on that stream."""
+SPIN_CYCLES = 200_000   # a short spin kernel ahead of each timed region (tens of microseconds)
+
+
+def time_launches(launch, stream):
+    """GPU seconds of the work that `launch()` enqueues on `stream`, from events
+    recorded on `stream` around it, after a device-wide synchronisation and
+    followed by one.  A short spin kernel goes first, so that the GPU is still
+    busy while the host enqueues the work: the start event then marks when the
+    work can begin, not the host's launch latency."""
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
+        torch.cuda._sleep(SPIN_CYCLES)
         start.record(stream)
-        for _ in range(replays):
-            graph.replay()   # launches on the current stream, i.e. `stream`
+        launch()
         end.record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) * 1e-3  # seconds
+    return start.elapsed_time(end) * 1e-3
+
+
+def time_graph(graph, replays, stream):
+    """Replay `graph` `replays` times on `stream` and time the replays (time_launches)."""
+    def launch():
+        for _ in range(replays):
+            graph.replay()   # launches on the current stream, i.e. `stream`
+    return time_launches(launch, stream)
+
+
+MIN_REPEATS = 50        # timed repeats of a measurement ...
+MIN_TIMED_S = 0.1       # ... and at least this much timed GPU time
+MAX_REPEATS = 400
+
+
+def repeat_timing(launch, stream, units, min_repeats=MIN_REPEATS, min_seconds=MIN_TIMED_S, max_repeats=MAX_REPEATS):
+    """Time `launch()` (which does `units` units of work) over repeats: at least
+    min_repeats of them, or as many as give min_seconds of timed work, whichever
+    is more (at most max_repeats).  Returns the seconds per unit of each repeat."""
+    out, total = [], 0.0
+    while len(out) < max_repeats and (len(out) < min_repeats or total < min_seconds):
+        t = time_launches(launch, stream)
+        total += t
+        out.append(t / units)
+    return out
+
+
+def pstats(per_unit_s, scale=1e6):
+    """Median, 10th and 90th percentile (linear interpolation) of per-unit seconds, times `scale`."""
+    a = np.asarray(per_unit_s, dtype=np.float64) * scale
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90)),
+            "n": int(a.size)}
 
 
 RAMP_SECONDS = 0.03
 
 
 def ramp(graph, stream, seconds=RAMP_SECONDS):
-    """Untimed replays of `graph` until `seconds` of GPU time have passed.  The
-    GPU's clocks take several milliseconds of sustained work to settle (about
-    10 ms measured on MI355X after an idle gap), so a warm-up of one or two short
-    replays would leave the timed replays inside that ramp."""
+    """Untimed replays of `graph` until `seconds` of GPU time have passed (returns
+    the time spent).  The GPU's clocks take several milliseconds of sustained
+    work to settle (about 10 ms measured on MI355X after an idle gap), so a
+    warm-up of one or two short replays would leave the timed replays inside
+    that ramp."""
     spent, n = 0.0, 1
     while spent < seconds:
         spent += time_graph(graph, n, stream)
         n = min(2 * n, 1024)
+    return spent
 
 
 def capture(fn, stream):
@@ -148,24 +192,89 @@ def build_decode(device, log):
     return shapes, host, dev_sets
 
 
+WINDOW_GRAPH_MAX_NODES = 60000   # kernel nodes over all the window graphs of the headline
+
+
+def step_plan(start, n, copies):
+    """Graph replays that run exactly n decode steps from step index `start`:
+    step i uses weight copy i % copies; None stands for the graph of a whole
+    rotation (copies 0 .. copies-1), an integer c for the one-step graph of copy
+    c.  Returns (replays, the next step index)."""
+    plan, i, left = [], start, n
+    while left > 0:
+        if i % copies == 0 and left >= copies:
+            plan.append(None)
+            i, left = i + copies, left - copies
+        else:
+            plan.append(i % copies)
+            i, left = i + 1, left - 1
+    return plan, i
+
+
 def run_decode(shapes, dev_sets, steps, warmup, stream, log):
+    """The headline.  One step is the five projections of one token on one copy
+    of the weights; consecutive steps use consecutive copies, so no step finds
+    its weights in a cache.  After a clock ramp (untimed replays, reported),
+    exactly `warmup` steps run untimed, then exactly `steps` steps are timed,
+    and that timed window is repeated (each repeat on the next copies, timed on
+    its own) to give the median, 10th and 90th percentile; the reported step
+    time is the median window's."""
     copies = len(dev_sets)
 
-    def one_rotation():
-        for d in dev_sets:
-            for name, N, K in shapes:
-                Pd, swd, xd, od = d[name]
-                tg.bitnet_linear(xd, Pd, swd, out=od)
+    def one_step(d):
+        for name, N, K in shapes:
+            Pd, swd, xd, od = d[name]
+            tg.bitnet_linear(xd, Pd, swd, out=od)
 
-    g = capture(one_rotation, stream)
-    reps = max(1, -(-steps // copies))
-    wreps = max(1, -(-warmup // copies))
-    time_graph(g, wreps, stream)
-    secs = time_graph(g, reps, stream)
-    n_steps = reps * copies
+    step_graphs = [capture(lambda d=d: one_step(d), stream) for d in dev_sets]
+    rotation = capture(lambda: [one_step(d) for d in dev_sets], stream)
+    cursor = [0]  # index of the next step's weight copy
+
+    def run_steps(n):
+        plan, cursor[0] = step_plan(cursor[0], n, copies)
+        for c in plan:
+            (rotation if c is None else step_graphs[c]).replay()
+
+    # The timed window is one graph of exactly `steps` steps (one per starting
+    # copy it is used at), so that no boundary between graph launches falls
+    # inside it; very long windows replay the rotation graphs instead, where
+    # such boundaries are one in `copies` steps.
+    starts = copies // math.gcd(steps, copies)
+    windows = {}
+    whole_graph = 5 * steps * starts <= WINDOW_GRAPH_MAX_NODES
+
+    if whole_graph:  # captured before the ramp: the timed windows start at steps warmup + r * steps
+        for r in range(starts):
+            o = (warmup + r * steps) % copies
+            if o not in windows:
+                windows[o] = capture(lambda o=o: [one_step(dev_sets[(o + j) % copies]) for j in range(steps)], stream)
+
+    def run_window():
+        if whole_graph:
+            windows[cursor[0] % copies].replay()
+            cursor[0] += steps
+        else:
+            run_steps(steps)
+
+    t_ramp = ramp(rotation, stream)
+    with torch.cuda.stream(stream):
+        run_steps(warmup)
+    torch.cuda.synchronize()
+    window = time_launches(run_window, stream)
+    reps = max(11, min(MAX_REPEATS, math.ceil(MIN_TIMED_S / window)))
+    per_step = [window / steps] + repeat_timing(run_window, stream, steps, min_repeats=reps - 1, min_seconds=0.0)
+    st = pstats(per_step, 1e3)
     step_bytes = sum(gemv_bytes(1, N, K) for _, N, K in shapes)
-    result = {"steps": n_steps, "warmup": wreps * copies, "seconds": secs, "ms_per_step": secs / n_steps * 1e3,
-              "gbs": step_bytes * n_steps / secs / 1e9, "step_bytes": step_bytes}
+    ms = st["median"]
+    result = {"steps": steps, "warmup": warmup, "ms_per_step": ms, "gbs": step_bytes / (ms * 1e-3) / 1e9,
+              "step_bytes": step_bytes,
+              "timing": {"repeats_of_steps": st["n"],
+                         "window": ("one captured graph of the timed steps" if whole_graph else
+                                    "replays of whole-rotation graphs and one-step graphs"),
+                         "ms_per_step_median": round(st["median"], 6),
+                         "ms_per_step_p10": round(st["p10"], 6), "ms_per_step_p90": round(st["p90"], 6),
+                         "ms_per_step_first_repeat": round(per_step[0] * 1e3, 6),
+                         "clock_ramp_ms": round(t_ramp * 1e3, 2), "weight_copies": copies}}
 
     # Per-projection launch durations: a graph of back-to-back launches of one
     # shape over the rotating copies, timed with events around its replays.
@@ -177,11 +286,13 @@ def run_decode(shapes, dev_sets, steps, warmup, stream, log):
                 tg.bitnet_linear(xd, Pd, swd, out=od)
         gs = capture(launches, stream)
         ramp(gs, stream)
-        r = 30
-        t = time_graph(gs, r, stream) / (r * copies)
-        per_shape[name] = {"N": N, "K": K, "us": t * 1e6, "gbs": gemv_bytes(1, N, K) / t / 1e9,
-                           "bytes": gemv_bytes(1, N, K)}
-        log(f"  {name:8s} N={N:6d} K={K:5d}: {t * 1e6:8.2f} us  {per_shape[name]['gbs']:8.1f} GB/s")
+        r = 5
+        st = pstats(repeat_timing(lambda gs=gs: [gs.replay() for _ in range(r)], stream, r * copies))
+        us = st["median"]
+        per_shape[name] = {"N": N, "K": K, "us": us, "us_p10": st["p10"], "us_p90": st["p90"], "repeats": st["n"],
+                           "gbs": gemv_bytes(1, N, K) / (us * 1e-6) / 1e9, "bytes": gemv_bytes(1, N, K)}
+        log(f"  {name:8s} N={N:6d} K={K:5d}: {us:8.2f} us (p10 {st['p10']:.2f}, p90 {st['p90']:.2f})  "
+            f"{per_shape[name]['gbs']:8.1f} GB/s")
     result["per_shape"] = per_shape
     return result
 
@@ -219,17 +330,17 @@ def run_gemm(device, stream, M, log, rotate=4):
         for tag, fn in (("gemm", gemm_only), ("linear", linear_full), ("quant", quant_only)):
             g = capture(fn, stream)
             ramp(g, stream)
-            reps = 10
-            t = time_graph(g, reps, stream) / (reps * rotate)
-            res[tag + "_us"] = t * 1e6
+            st = pstats(repeat_timing(g.replay, stream, rotate, min_repeats=30))
+            res[tag + "_us"] = st["median"]
+            res[tag + "_us_p10"], res[tag + "_us_p90"], res[tag + "_repeats"] = st["p10"], st["p90"], st["n"]
         ops = 2.0 * M * N * K
         res["tops"] = ops / (res["gemm_us"] * 1e-6) / 1e12
         res["linear_tops"] = ops / (res["linear_us"] * 1e-6) / 1e12
         res["frac_int8_peak"] = res["tops"] / INT8_PEAK_TOPS
         out[name] = res
-        log(f"  M={M} {name:8s} N={N:6d} K={K:5d}: gemm {res['gemm_us']:8.1f} us {res['tops']:7.1f} TOPS "
-            f"({100 * res['frac_int8_peak']:.1f}% of peak); quant {res['quant_us']:.1f} us; "
-            f"linear {res['linear_us']:.1f} us")
+        log(f"  M={M} {name:8s} N={N:6d} K={K:5d}: gemm {res['gemm_us']:8.1f} us (p10 {res['gemm_us_p10']:.1f}, "
+            f"p90 {res['gemm_us_p90']:.1f}) {res['tops']:7.1f} TOPS ({100 * res['frac_int8_peak']:.1f}% of peak); "
+            f"quant {res['quant_us']:.1f} us; linear {res['linear_us']:.1f} us")
         del Ps, q, sa, o, ws, x
         torch.cuda.empty_cache()
     return out
@@ -268,9 +379,11 @@ def run_small_batch(device, stream, log):
 
             g = capture(run, stream)
             ramp(g, stream)
-            t = time_graph(g, 3, stream) / (3 * copies)
+            st = pstats(repeat_timing(g.replay, stream, copies, min_repeats=15))
+            t = st["median"] * 1e-6
             ops, nbytes = 2.0 * M * N * K, gemm_bytes(M, N, K)
-            r = {"us": round(t * 1e6, 2), "gbs": round(nbytes / t / 1e9, 1), "tops": round(ops / t / 1e12, 1),
+            r = {"us": round(t * 1e6, 2), "us_p10": round(st["p10"], 2), "us_p90": round(st["p90"], 2),
+                 "gbs": round(nbytes / t / 1e9, 1), "tops": round(ops / t / 1e12, 1),
                  "frac_roofline": round(roofline_frac(ops, nbytes, t), 4)}
             out[f"{name}_M{M}"] = r
             log(f"  {name:8s} M={M:4d}: {r['us']:8.2f} us {r['gbs']:8.1f} GB/s {r['tops']:8.1f} TOPS "
@@ -324,14 +437,15 @@ def run_decode_full(device, stream, log, layers=30):
 
         g = capture(step, stream)
         ramp(g, stream)
-        reps = 20
-        t = time_graph(g, reps, stream) / reps
+        st = pstats(repeat_timing(g.replay, stream, 1, min_repeats=50))
+        t = st["median"] * 1e-6
         if M == 1:
             nbytes = sum(gemv_bytes(M, N, K) for _, N, K, _, _ in calls)
         else:  # quantise (2MK in, MK + 2M out) + GEMM
             nbytes = sum(gemm_bytes(M, N, K) + 3 * M * K + 2 * M for _, N, K, _, _ in calls)
         key = f"M{M}_rmsnorm" if rms else f"M{M}"
-        res[key] = {"us_per_step": round(t * 1e6, 2), "tokens_per_s": round(M / t, 1),
+        res[key] = {"us_per_step": round(t * 1e6, 2), "us_p10": round(st["p10"], 2), "us_p90": round(st["p90"], 2),
+                    "tokens_per_s": round(M / t, 1),
                     "gbs": round(nbytes / t / 1e9, 1), "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
                     "step_bytes": nbytes}
         log(f"  full decode step M={M:2d}{' +RMSNorm' if rms else '         '}: {t * 1e6:8.1f} us/step, {M / t:9.1f} tok/s, "
@@ -369,8 +483,7 @@ def run_options(device, stream, log):
                     tg.bitnet_linear(x, Pd, sw, out=o, workspace=ws, bias=b)
             g = capture(run, stream)
             ramp(g, stream)
-            t = time_graph(g, 3, stream) / (3 * copies)
-            r[tag + "_us"] = round(t * 1e6, 2)
+            r[tag + "_us"] = round(pstats(repeat_timing(g.replay, stream, copies, min_repeats=15))["median"], 2)
         out[f"{name}_M{M}"] = r
         log(f"  {name:10s} M={M:5d} N={N:6d} K={K:5d}: bf16 {r['bf16_us']:8.2f} us, +bias {r['bf16_bias_us']:8.2f} us, "
             f"f32 input {r['f32_us']:8.2f} us")
@@ -405,7 +518,7 @@ def run_w8a16(device, stream, log):
                     tg.w8a16_gemv(x, qd, sc, out=y)
             g = capture(run, stream)
             ramp(g, stream)
-            t = time_graph(g, 3, stream) / (3 * copies)
+            t = pstats(repeat_timing(g.replay, stream, copies, min_repeats=15))["median"] * 1e-6
             r[f"M{M}_us"] = round(t * 1e6, 2)
             r[f"M{M}_gbs"] = round(w8a16_bytes(M, N, K) / t / 1e9, 1)
         out[name] = r
@@ -418,25 +531,169 @@ def run_w8a16(device, stream, log):
 
 # ----------------------------------------------------------------------------- CPU oracle
 
+def host_facts():
+    """What the CPU baseline ran on: logical CPUs (nproc), the CPUs this process
+    may use, and the CPU model."""
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model,
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
+
+
 def run_cpu_baseline(host, shapes, budget_s, log):
+    """The oracle on the host cores over a bounded sample of the headline
+    workload (whole M=1 decode steps of the five projections): first on one
+    thread (about a third of the budget, at least one step), then on every
+    thread OpenMP gives it (the rest).  The value is the multi-threaded rate."""
     import oracle  # the oracle is only ever used here, for the CPU baseline leg
     packed = {name: oracle.pack(host[name][0]) for name, _, _ in shapes}
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        for name, N, K in shapes:
-            _, _, sw, x = host[name]
-            oracle.linear(x, packed[name], sw)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 1000:
-            break
     step_bytes = sum(gemv_bytes(1, N, K) for _, N, K in shapes)
-    gbs = step_bytes * n / el / 1e9
-    log(f"cpu oracle: {n} steps in {el:.1f} s -> {gbs:.3f} GB/s on {oracle.num_threads()} threads")
-    return {"value": gbs, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{n} full M=1 decode steps (all five BitNet-2B-4T projections), {el:.1f} s",
-            "ms_per_step": el / n * 1e3}
+    threads_all = oracle.num_threads()
+
+    def timed_steps(threads, seconds):
+        oracle.set_num_threads(threads)
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            for name, N, K in shapes:
+                _, _, sw, x = host[name]
+                oracle.linear(x, packed[name], sw)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or n >= 1000:
+                return n, el
+
+    n1, el1 = timed_steps(1, budget_s / 3)
+    nm, elm = timed_steps(threads_all, budget_s - el1)
+    oracle.set_num_threads(threads_all)
+    gbs1, gbsm = step_bytes * n1 / el1 / 1e9, step_bytes * nm / elm / 1e9
+    facts = host_facts()
+    log(f"cpu oracle: 1 thread {n1} steps in {el1:.1f} s -> {gbs1:.3f} GB/s; {threads_all} threads {nm} steps in "
+        f"{elm:.1f} s -> {gbsm:.3f} GB/s ({facts['cpu_model']}, nproc {facts['nproc']})")
+    return {"value": gbsm, "unit": "GB/s", "cores": threads_all, "kind": "oracle",
+            "sample": f"{nm} full M=1 decode steps (all five BitNet-2B-4T projections) on {threads_all} threads, "
+                      f"{elm:.1f} s; before that {n1} steps on one thread, {el1:.1f} s",
+            "ms_per_step": elm / nm * 1e3,
+            "single_thread": {"value": gbs1, "unit": "GB/s", "ms_per_step": el1 / n1 * 1e3, "steps": n1},
+            **facts}
+
+
+def gpu_clock_info():
+    """Clocks as the SMI tool reports them right now (a child process; null when
+    neither amd-smi nor rocm-smi answers)."""
+    for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+        except (OSError, subprocess.SubprocessError):
+            continue
+        if r.returncode != 0 or not r.stdout.strip():
+            continue
+        try:
+            return {"tool": cmd[0], "report": json.loads(r.stdout)}
+        except ValueError:
+            return {"tool": cmd[0], "text": r.stdout.strip()[:2000]}
+    return None
+
+
+# ----------------------------------------------------------------------------- machine ceilings
+
+PROBE_LIB = os.path.join(ROOT, "ternary_int8_gemm_amd", "libbitnet_probe.so")
+
+
+def load_probe():
+    """libbitnet_probe.so (built beside the layer's library): read, copy and
+    int8-MFMA loops that measure this box's practical ceilings."""
+    import ctypes
+    lib = ctypes.CDLL(PROBE_LIB)
+    p, i64, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.probe_read.argtypes = [p, i64, p, i, p]
+    lib.probe_copy.argtypes = [p, p, i64, i, p]
+    lib.probe_mfma_i8.argtypes = [p, i, p, i, p]
+    for fn in (lib.probe_read, lib.probe_copy, lib.probe_mfma_i8):
+        fn.restype = i
+    return lib
+
+
+def run_machine(device, stream, log):
+    """Practical ceilings of this GPU, measured with the probe kernels:
+    the int8 MFMA rate of back-to-back v_mfma_i32_32x32x32_i8 (2 waves per SIMD),
+    with the shader clock it ran at; the HBM read rate over 1 GiB and over
+    82 MB pieces of a 1 GiB pool (the LM head's weight size); the copy rate
+    over 512 MiB.  Each is the median of repeated, ramped timings."""
+    import ctypes
+    lib = load_probe()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    res = {}
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with status {rc}")
+
+    blocks, iters = 512, 20000
+    out = torch.empty((blocks * 256,), dtype=torch.int32, device=device)
+    clk = torch.zeros((2,), dtype=torch.int64, device=device)
+
+    def mfma():
+        check(lib.probe_mfma_i8(ctypes.c_void_p(out.data_ptr()), iters, ctypes.c_void_p(clk.data_ptr()), blocks, sp),
+              "probe_mfma_i8")
+    g = capture(mfma, stream)
+    ramp(g, stream)
+    st = pstats(repeat_timing(g.replay, stream, 1, min_repeats=20), 1.0)
+    ops = blocks * 4 * 4 * iters * 65536.0
+    ticks, real = (int(v) for v in clk.cpu())
+    res["mfma_i8"] = {"tops": round(ops / st["median"] / 1e12, 1), "tops_p10_time": round(ops / st["p90"] / 1e12, 1),
+                      "tops_p90_time": round(ops / st["p10"] / 1e12, 1),
+                      "frac_of_published": round(ops / st["median"] / 1e12 / INT8_PEAK_TOPS, 4),
+                      "sclk_mhz": round(ticks / real * 100.0, 1) if real > 0 else None,
+                      "kernel_ms": round(st["median"] * 1e3, 3), "waves_per_simd": 2}
+    log(f"  int8 MFMA loop: {res['mfma_i8']['tops']:.1f} TOPS ({100 * res['mfma_i8']['frac_of_published']:.1f}% of "
+        f"5.0 POPS), shader clock {res['mfma_i8']['sclk_mhz']} MHz")
+    del g, out
+
+    pool = torch.empty((1 << 30,), dtype=torch.uint8, device=device)
+    pool.fill_(3)
+    sink = torch.empty((2048 * 256,), dtype=torch.int32, device=device)
+
+    def read(lo, n):
+        check(lib.probe_read(ctypes.c_void_p(pool.data_ptr() + lo), n, ctypes.c_void_p(sink.data_ptr()), 2048, sp),
+              "probe_read")
+    g = capture(lambda: read(0, 1 << 30), stream)
+    ramp(g, stream)
+    st = pstats(repeat_timing(g.replay, stream, 1, min_repeats=20), 1.0)
+    res["read_1GiB"] = {"tbs": round((1 << 30) / st["median"] / 1e12, 3), "us": round(st["median"] * 1e6, 1)}
+    piece = 82_080_768  # the LM head's packed weights, 128256 x 640 bytes
+    npieces = (1 << 30) // piece
+    g = capture(lambda: [read(i * piece, piece) for i in range(npieces)], stream)
+    ramp(g, stream)
+    st = pstats(repeat_timing(g.replay, stream, npieces, min_repeats=20), 1.0)
+    res["read_82MB"] = {"tbs": round(piece / st["median"] / 1e12, 3), "us": round(st["median"] * 1e6, 2),
+                        "us_p10": round(st["p10"] * 1e6, 2), "us_p90": round(st["p90"] * 1e6, 2)}
+    half = 1 << 29
+
+    def copy():
+        check(lib.probe_copy(ctypes.c_void_p(pool.data_ptr() + half), ctypes.c_void_p(pool.data_ptr()), half, 2048, sp),
+              "probe_copy")
+    g = capture(copy, stream)
+    ramp(g, stream)
+    st = pstats(repeat_timing(g.replay, stream, 1, min_repeats=20), 1.0)
+    res["copy_512MiB"] = {"tbs_read_plus_write": round(2 * half / st["median"] / 1e12, 3),
+                          "us": round(st["median"] * 1e6, 1)}
+    log(f"  HBM read 1 GiB {res['read_1GiB']['tbs']:.2f} TB/s; 82 MB pieces {res['read_82MB']['tbs']:.2f} TB/s "
+        f"({res['read_82MB']['us']:.2f} us); copy 512 MiB {res['copy_512MiB']['tbs_read_plus_write']:.2f} TB/s")
+    del g, pool, sink
+    torch.cuda.empty_cache()
+    return res
 
 
 def load_traffic(lm_head_launch_bytes):
@@ -774,13 +1031,15 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2200)
-    ap.add_argument("--warmup", type=int, default=660)
-    ap.add_argument("--gemm-m", type=int, default=2048)
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--warmup", type=int, default=220)
+    ap.add_argument("--gemm-m", type=int, nargs="+", default=[2048, 4096])
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the small-batch GEMM and full decode-step lines")
+    ap.add_argument("--no-machine", action="store_true", help="skip the machine-ceiling probes")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--machine", action="store_true", help="only the machine-ceiling probes (MFMA loop, read, copy)")
     ap.add_argument("--pmc-target", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
@@ -803,6 +1062,9 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: there is no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
 
     def log(msg):
         if not args.quiet:
@@ -821,21 +1083,29 @@ def main():
     if args.gemv_scaling:
         run_gemv_scaling(device, stream)
         return
+    if args.machine:
+        print(json.dumps({"machine_ceilings": run_machine(device, stream, log)}), flush=True)
+        return
 
+    clock_before = gpu_clock_info()
     shapes, host, dev_sets = build_decode(device, log)
-    log("decode GEMV M=1 (BitNet-2B-4T shapes):")
+    log(f"decode GEMV M=1 (BitNet-2B-4T shapes), {args.steps} timed steps after {args.warmup} warm-up steps:")
     dec = run_decode(shapes, dev_sets, args.steps, args.warmup, stream, log)
-    log(f"decode step: {dec['ms_per_step'] * 1e3:.2f} us/step, {dec['gbs']:.1f} GB/s "
-        f"({100 * dec['gbs'] / HBM_PEAK_GBS:.1f}% of HBM peak)")
+    tm = dec["timing"]
+    log(f"decode step: {dec['ms_per_step'] * 1e3:.2f} us/step (median of {tm['repeats_of_steps']} windows of "
+        f"{args.steps} steps; p10 {tm['ms_per_step_p10'] * 1e3:.2f}, p90 {tm['ms_per_step_p90'] * 1e3:.2f}), "
+        f"{dec['gbs']:.1f} GB/s ({100 * dec['gbs'] / HBM_PEAK_GBS:.1f}% of HBM peak)")
     del dev_sets
     torch.cuda.empty_cache()
+    clock_after = gpu_clock_info()
 
-    gemm = None
+    gemms = {}
     if not args.no_gemm:
-        log(f"prefill GEMM M={args.gemm_m} (LLaMA-7B shapes):")
-        gemm = run_gemm(device, stream, args.gemm_m, log)
+        for M in args.gemm_m:
+            log(f"prefill GEMM M={M} (LLaMA-7B shapes):")
+            gemms[M] = run_gemm(device, stream, M, log)
 
-    small = full = options = w8 = None
+    small = full = options = w8 = machine = None
     if not args.no_extra:
         log("small-batch GEMM M=8..256 (LLaMA-7B layer shapes, pre-quantised):")
         small = run_small_batch(device, stream, log)
@@ -845,13 +1115,19 @@ def main():
         options = run_options(device, stream, log)
         log("INT8 weight-only matmul (W8A16), decode shapes:")
         w8 = run_w8a16(device, stream, log)
+    if not args.no_machine:
+        log("machine ceilings (probe kernels):")
+        machine = run_machine(device, stream, log)
 
     lm = dec["per_shape"]["lm_head"]
     traffic = load_traffic(lm["bytes"])
     roofline = {"bound": "hbm", "achieved": round(lm["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(lm["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "gemv_stream_kernel (lm_head 128256x2560, M=1)",
-                "bytes_per_launch": lm["bytes"], "avg_launch_us": round(lm["us"], 3)}
+                "bytes_per_launch": lm["bytes"], "avg_launch_us": round(lm["us"], 3),
+                "launch_us_p10": round(lm["us_p10"], 3), "launch_us_p90": round(lm["us_p90"], 3),
+                "launch_time": f"median over {lm['repeats']} repeats of back-to-back graph launches, HIP events on the "
+                               "launch stream"}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -864,7 +1140,7 @@ def main():
         "n_gpus": 1,
         "steps": dec["steps"],
         "warmup": dec["warmup"],
-        "ms_per_step": round(dec["ms_per_step"], 5),
+        "ms_per_step": round(dec["ms_per_step"], 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -876,19 +1152,25 @@ def main():
             "M": 1, "step_bytes": dec["step_bytes"],
             "per_shape_gbs": {k: round(v["gbs"], 1) for k, v in dec["per_shape"].items()},
             "per_shape_us": {k: round(v["us"], 3) for k, v in dec["per_shape"].items()},
+            "per_shape_us_p10_p90": {k: [round(v["us_p10"], 3), round(v["us_p90"], 3)]
+                                     for k, v in dec["per_shape"].items()},
             "frac_hbm_peak": round(dec["gbs"] / HBM_PEAK_GBS, 4),
+            "timing": dec["timing"],
+            "gpu_clocks_smi": {"before": clock_before, "after_headline": clock_after},
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
-    if gemm is not None:
-        tot_ops = sum(2.0 * args.gemm_m * v["N"] * v["K"] for v in gemm.values())
+    for M, gemm in gemms.items():
+        tot_ops = sum(2.0 * M * v["N"] * v["K"] for v in gemm.values())
         tot_t = sum(v["gemm_us"] for v in gemm.values()) * 1e-6
-        line["gemm"] = {
-            "metric": f"GEMM INT8 TOPS (M={args.gemm_m}), LLaMA-7B shapes, pre-quantised activations",
+        line["gemm" if M == 2048 else f"gemm_m{M}"] = {
+            "metric": f"GEMM INT8 TOPS (M={M}), LLaMA-7B shapes, pre-quantised activations",
             "value": round(tot_ops / tot_t / 1e12, 1), "unit": "TOPS",
             "frac_int8_peak": round(tot_ops / tot_t / 1e12 / INT8_PEAK_TOPS, 4),
             "per_shape": {k: {"tops": round(v["tops"], 1), "gemm_us": round(v["gemm_us"], 2),
+                              "gemm_us_p10": round(v["gemm_us_p10"], 2), "gemm_us_p90": round(v["gemm_us_p90"], 2),
+                              "frac_int8_peak": round(v["frac_int8_peak"], 4),
                               "quant_us": round(v["quant_us"], 2), "linear_us": round(v["linear_us"], 2)}
                           for k, v in gemm.items()},
         }
@@ -897,6 +1179,8 @@ def main():
         line["decode_full_step"] = full
         line["linear_options"] = options
         line["w8a16_gemv"] = w8
+    if machine is not None:
+        line["machine_ceilings"] = machine
     print(json.dumps(line), flush=True)
 
 

@@ -1,8 +1,10 @@
 """Build libbitnet_hip.so (the C ABI of include/bitnet.h) for gfx950 with hipcc.
 
-Every source under csrc/ is compiled for gfx950 only and linked into one shared
-library next to this file.  No fast-math, no floating-point contraction, and
-no packed fp32 instructions.
+The layer's sources under csrc/ are compiled for gfx950 only and linked into
+one shared library next to this file.  No fast-math, no floating-point
+contraction, and no packed fp32 instructions.  csrc/probe.hip (machine-ceiling
+microbenchmarks for the benchmark script, not part of the C ABI) becomes a
+second library, libbitnet_probe.so.
 """
 import os
 import subprocess
@@ -13,6 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbitnet_hip.so")
 SOURCES = ["api.hip", "quant.hip", "gemv.hip", "gemm.hip", "epilogue.hip", "w8a16.hip"]
+PROBE_SOURCE = "probe.hip"
+PROBE_LIB = os.path.join(HERE, "libbitnet_probe.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -29,8 +33,9 @@ SOURCE_FLAGS = {
 }
 
 
-def build(out=LIB, extra_flags=(), verbose=False):
-    """Compile every source to an object (in parallel), then link the library."""
+def build(out=LIB, extra_flags=(), verbose=False, probe_out=PROBE_LIB):
+    """Compile every source to an object (in parallel), then link the library
+    (and the probe library, unless probe_out is None)."""
     from concurrent.futures import ThreadPoolExecutor
 
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -46,14 +51,21 @@ def build(out=LIB, extra_flags=(), verbose=False):
         subprocess.run(cmd, check=True)
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 4)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = out + ".tmp"
-    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), file=sys.stderr)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, out)
+    srcs = SOURCES + ([PROBE_SOURCE] if probe_out else [])
+    with ThreadPoolExecutor(max_workers=min(len(srcs), 4)) as ex:
+        objs = dict(zip(srcs, ex.map(compile_one, srcs)))
+
+    def link(obj_list, dst):
+        tmp = dst + ".tmp"
+        cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *obj_list, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), file=sys.stderr)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, dst)
+
+    link([objs[s] for s in SOURCES], out)
+    if probe_out:
+        link([objs[PROBE_SOURCE]], probe_out)
     return out
 
 

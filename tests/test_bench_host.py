@@ -128,3 +128,39 @@ def test_gemv_scaling_fit():
         rows.append((N, mb, t_us * 1e-6))
     fixed, rate = bench.scaling_fit(rows)
     assert abs(fixed - 3.5) < 1e-9 and abs(rate - 6.7) < 1e-9
+
+
+def test_step_plan_runs_exactly_the_asked_steps():
+    """The headline's replay plan covers exactly n steps, on consecutive weight
+    copies, whatever the starting step and the number of copies."""
+    for copies in (1, 2, 11):
+        for start in (0, 3, 11, 25):
+            for n in (0, 1, 5, 20, 22, 2200):
+                plan, nxt = bench.step_plan(start, n, copies)
+                steps = []
+                i = start
+                for c in plan:
+                    if c is None:
+                        assert i % copies == 0
+                        steps += list(range(copies))
+                        i += copies
+                    else:
+                        assert c == i % copies
+                        steps.append(c)
+                        i += 1
+                assert len(steps) == n and nxt == start + n
+                assert steps == [(start + j) % copies for j in range(n)]
+    # whole rotations are one replay each
+    assert bench.step_plan(0, 22, 11) == ([None, None], 22)
+    assert bench.step_plan(5, 20, 11)[0] == [5, 6, 7, 8, 9, 10, None, 0, 1, 2]
+
+
+def test_percentiles():
+    st = bench.pstats([1e-6 * v for v in range(1, 12)])      # 1 .. 11 us
+    assert st["n"] == 11 and abs(st["median"] - 6.0) < 1e-9
+    assert abs(st["p10"] - 2.0) < 1e-9 and abs(st["p90"] - 10.0) < 1e-9
+
+
+def test_host_facts():
+    f = bench.host_facts()
+    assert f["nproc"] == os.cpu_count() and f["usable_cpus"] >= 1 and f["cpu_model"]
