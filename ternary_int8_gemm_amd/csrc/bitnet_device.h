@@ -172,12 +172,13 @@ __device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t w) { return max(w & 0
 
 struct QuantScale {
     float s;  // fp32(absmax / 127): the divisor
-    float r;  // fp32(1 / s): used only for a pre-rounding estimate
+    float r;  // fp32(1 / s), correctly rounded: drives the quotient below
 };
 
 // From the row absmax (quant_scale_f32: an fp32 value; quant_scale: bf16
 // magnitude bits): clamp below at fp32(1e-5), then the IEEE fp32 quotient by
-// 127 (the compiler's division is correctly rounded).
+// 127 and the IEEE reciprocal of that (the compiler's division is correctly
+// rounded).  Both are computed once per row.
 __device__ __forceinline__ QuantScale quant_scale_f32(float a) {
     a = a < 1e-5f ? 1e-5f : a;
     QuantScale q;
@@ -195,18 +196,28 @@ __device__ __forceinline__ QuantScale quant_scale(uint32_t absmax_bits) {
     return q;
 }
 
+// fp32(x / s), correctly rounded, from r = fp32(1 / s) with three FMAs and a
+// multiply instead of a division (Markstein's FMA division):
+//  * q0 = fp32(x r) has a relative error below 2^-23 + 2^-48, i.e. it is
+//    within 2 ulp of x / s;
+//  * q0 + fp32(x - s q0) r (one FMA, one rounding) differs from x / s by at
+//    most about 2^-22 ulp, so its rounding q1 is faithful (one of the two fp32
+//    neighbours of x / s);
+//  * for a faithful q1 the residual x - s q1 is exact in fp32 (one FMA), and
+//    with r within half an ulp of 1 / s, fp32(q1 + (x - s q1) r) is the
+//    correctly rounded x / s (Markstein's theorem).
+// Valid while no step underflows: whenever |x / s| >= 1/4 every intermediate is
+// a normal number (s >= 1e-5 / 127), and below 1/4 the value rounds to 0 to
+// an integer whatever the last bits are.  |x| <= absmax keeps |x / s| <= 127.5.
+__device__ __forceinline__ float quotient_rn(float x, const QuantScale& q) {
+    const float q0 = x * q.r;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, q.s, x), q.r, q0);
+    return __builtin_fmaf(__builtin_fmaf(-q1, q.s, x), q.r, q1);
+}
+
 // q = clamp(round_half_even(fp32(x / s)), -127, 127), exactly.
-//
-// y = x * r is within 2^-23 + 2^-48 (relative) of x / s and |x / s| <= 127 * (1 + 2^-23),
-// so |y - fp32(x / s)| < 2.5e-5.  Rounding to an integer only depends on which
-// side of a half-integer the value falls, so unless y lies within 2^-12 of a
-// half-integer, round(y) == round(fp32(x / s)); in that rare case the correctly
-// rounded quotient is computed and used instead.
 __device__ __forceinline__ int quantize_one(float x, const QuantScale& q) {
-    const float y = x * q.r;
-    float t = __builtin_rintf(y);
-    // y within 2^-12 of a half-integer <=> |y - rint(y)| > 1/2 - 2^-12
-    if (__builtin_expect(__builtin_fabsf(y - t) > 0.5f - 0x1p-12f, 0)) t = __builtin_rintf(x / q.s);
+    float t = __builtin_rintf(quotient_rn(x, q));
     t = __builtin_fminf(__builtin_fmaxf(t, -127.0f), 127.0f);
     return (int)t;
 }
@@ -231,33 +242,20 @@ __device__ __forceinline__ uint32_t absmax_f32x4(const uint4& v) {
 //  * Rounding by addition: for |y| <= 2^22, y + 1.5 * 2^23 lands in [2^23,
 //    2^24), where the spacing is 1, so the sum is 1.5 * 2^23 + rint(y) with
 //    ties to even, and its low byte is rint(y) as a two's-complement int8.
-//  * No clamp is needed: |x| <= absmax and r = fp32(1 / fp32(absmax / 127)),
-//    so |y| <= 127 * (1 + 3 * 2^-24) < 127.5 (also when absmax is clamped to
-//    1e-5, since then |x| < 1e-5).
-//  * The near-half-integer test is taken once for the group: one branch per
-//    eight elements; the rare elements it finds get the correctly rounded x / s.
-// Needs FP contraction off (y must be the rounded product before the add).
+//  * No clamp is needed: |x| <= absmax and s = fp32(absmax / 127), so
+//    |fp32(x / s)| <= 127 * (1 + 2^-23) < 127.5 (also when absmax is clamped
+//    to 1e-5, since then |x| < 1e-5).
+//  * Branch-free: every element takes the same few FMAs (quotient_rn).
+// Needs FP contraction off (the sum with 1.5 * 2^23 must see the rounded quotient).
 __device__ __forceinline__ uint2 quantize_bf16x8(const uint4& v, const QuantScale& q) {
     constexpr float RND = 12582912.0f;  // 1.5 * 2^23
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float x[8], m[8], dev = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        x[e] = bf16_to_f32((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu));
-        const float y = x[e] * q.r;
-        m[e] = y + RND;
-        dev = __builtin_fmaxf(dev, __builtin_fabsf(y - (m[e] - RND)));
-    }
-    if (__builtin_expect(dev > 0.5f - 0x1p-12f, 0)) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float y = x[e] * q.r;
-            if (__builtin_fabsf(y - (m[e] - RND)) > 0.5f - 0x1p-12f) m[e] = x[e] / q.s + RND;
-        }
-    }
     uint32_t u[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) u[e] = __builtin_bit_cast(uint32_t, m[e]);
+    for (int e = 0; e < 8; ++e) {
+        const float x = bf16_to_f32((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu));
+        u[e] = __builtin_bit_cast(uint32_t, quotient_rn(x, q) + RND);
+    }
     // byte 0 of each value: perm selects bytes 0 (second operand) and 4 (first)
     const uint32_t p01 = __builtin_amdgcn_perm(u[1], u[0], 0x0C0C0400u);
     const uint32_t p23 = __builtin_amdgcn_perm(u[3], u[2], 0x0C0C0400u);

@@ -107,6 +107,80 @@ def test_quantize_golden_vectors_on_gpu():
         assert int(host_bf16(s)[0]) == int(r["scale_bf16"][0], 16)
 
 
+def exhaustive_bf16_rows(seed=1234, rows=45):
+    """Rows whose absmax is A and which hold every bf16 value v with A/512 <= |v| <= A (both
+    signs): every bf16 input the quantiser can see at that scale outside the band that
+    rounds to 0.  A runs over powers of two, 127, values near the 1e-5 floor and random
+    bf16 values from 2^-20 to 2^100; rows are zero-padded to one length (K % 64 == 0)."""
+    g = synth.rng(seed)
+    special = [0x3F80, 0x42FE, 0x3727, 0x3728, 0x3729, 0x3000, 0x7F7F, 0x0080]    # 1, 127, ~1e-5, 2^-31, max, min normal
+    randoms = [int(b) for b in g.integers(0x3580, 0x71FF, size=rows - len(special))]
+    out = []
+    allv = np.arange(0x0080, 0x7F80, dtype=np.uint32)                 # positive normal bf16 bit patterns
+    vals = (allv << 16).view(np.float32)
+    for A_bits in special + randoms:
+        A = float(np.array([A_bits << 16], dtype=np.uint32).view(np.float32)[0])
+        keep = allv[(vals <= A) & (vals >= A / 512)]
+        row = np.concatenate([np.array([A_bits], dtype=np.uint32), keep, keep | 0x8000]).astype(np.uint16)
+        g.shuffle(row)
+        out.append(row)
+    K = max(len(r) for r in out)
+    K = (K + 63) // 64 * 64
+    x = np.zeros((len(out), K), dtype=np.uint16)
+    for i, r in enumerate(out):
+        x[i, :len(r)] = r
+    return x
+
+
+def test_quantize_exhaustive_bf16():
+    """Every bf16 value at many scales through the standalone quantiser (the
+    workgroup-per-row kernel), bit-exact against the oracle."""
+    x = exhaustive_bf16_rows()
+    q_ref, s_ref = oracle.quantize(x)
+    q, s = tg.quantize_activation(dev_bf16(x))
+    assert np.array_equal(host_bf16(s), s_ref)
+    bad = np.argwhere(q.cpu().numpy() != q_ref)
+    assert bad.size == 0, f"{len(bad)} int8 values differ, first at {tuple(bad[0])}"
+
+
+def test_gemv_prologue_exhaustive_bf16():
+    """The same rows quantised in the fused decode GEMV's prologue: with one-hot
+    weights (w[n][k] = 1 iff k == n) the int32 outputs are the int8 activations."""
+    x = exhaustive_bf16_rows(seed=4321, rows=30)
+    M, K = x.shape
+    q_ref, s_ref = oracle.quantize(x)
+    W = np.zeros((K, K), dtype=np.int8)
+    np.fill_diagonal(W, 1)
+    Pd = dev(lib_pack(W))
+    # 1, 2, 4 and 8 rows take the streaming kernel; 15 rows of this length its K-chunked variant
+    for m0, m1 in ((0, 1), (1, 3), (3, 7), (7, 15), (15, 30)):
+        xs = x[m0:m1]
+        acc, sa = tg.bitnet_gemv_fused_i32(dev_bf16(xs), Pd)
+        assert np.array_equal(host_bf16(sa), s_ref[m0:m1])
+        assert np.array_equal(acc.cpu().numpy(), q_ref[m0:m1].astype(np.int32)), f"rows {m0}..{m1}"
+
+
+def test_quantize_f32_near_ties():
+    """f32 activations placed on and next to the values whose quotient by s is a
+    half-integer (where a wrong last bit of x / s flips the rounded int8)."""
+    g = synth.rng(99)
+    M, K = 40, 1024
+    x = np.zeros((M, K), dtype=np.float32)
+    for m in range(M):
+        A = np.float32(10.0 ** g.uniform(-4, 4))
+        s = np.float32(A / np.float32(127.0))
+        k = g.integers(0, 127, size=K - 1)
+        base = ((k + 0.5) * np.float64(s)).astype(np.float32) * np.where(g.random(K - 1) < 0.5, 1, -1).astype(np.float32)
+        d = g.integers(-2, 3, size=K - 1).astype(np.int32)
+        x[m, 1:] = (base.view(np.int32) + d).view(np.float32)
+        x[m, 0] = A
+        x[m] = np.clip(x[m], -A, A)
+    q_ref, s_ref = oracle.quantize_f32(x)
+    q, s = tg.quantize_activation(dev_f32(x))
+    assert np.array_equal(host_bf16(s), s_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
 def test_quantize_misaligned_plain_path():
     x = synth.activations_bf16(6, 96, seed=7)
     q_ref, s_ref = oracle.quantize(x)
