@@ -152,6 +152,19 @@ def ramp(graph, stream, seconds=RAMP_SECONDS):
     return spent
 
 
+MIN_GRAPH_LAUNCHES = 64  # launches per timed graph: a replay of a short graph adds microseconds of its own
+
+
+def launches_graph(launch, n, stream, min_launches=MIN_GRAPH_LAUNCHES):
+    """A captured graph of L launches, launch(i % n) for i < L, with L the
+    smallest multiple of n that is >= min_launches; returns (graph, L).  Each
+    replay of a captured graph costs some microseconds of its own on the GPU
+    (measured: about 11 us per replay of a graph of four 2 us kernels), so a
+    timed graph holds enough launches for that cost to vanish in the average."""
+    L = n * max(1, math.ceil(min_launches / n))
+    return capture(lambda: [launch(i % n) for i in range(L)], stream), L
+
+
 def capture(fn, stream):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
@@ -280,14 +293,13 @@ def run_decode(shapes, dev_sets, steps, warmup, stream, log):
     # shape over the rotating copies, timed with events around its replays.
     per_shape = {}
     for name, N, K in shapes:
-        def launches(name=name):
-            for d in dev_sets:
-                Pd, swd, xd, od = d[name]
-                tg.bitnet_linear(xd, Pd, swd, out=od)
-        gs = capture(launches, stream)
+        def launch(i, name=name):
+            Pd, swd, xd, od = dev_sets[i][name]
+            tg.bitnet_linear(xd, Pd, swd, out=od)
+        gs, L = launches_graph(launch, copies, stream)
         ramp(gs, stream)
-        r = 5
-        st = pstats(repeat_timing(lambda gs=gs: [gs.replay() for _ in range(r)], stream, r * copies))
+        r = 2
+        st = pstats(repeat_timing(lambda gs=gs: [gs.replay() for _ in range(r)], stream, r * L))
         us = st["median"]
         per_shape[name] = {"N": N, "K": K, "us": us, "us_p10": st["p10"], "us_p90": st["p90"], "repeats": st["n"],
                            "gbs": gemv_bytes(1, N, K) / (us * 1e-6) / 1e9, "bytes": gemv_bytes(1, N, K)}
@@ -314,23 +326,20 @@ def run_gemm(device, stream, M, log, rotate=4):
         o = torch.empty((M, N), dtype=torch.bfloat16, device=device)
         ws = torch.empty((tg.linear_workspace_bytes(M, K),), dtype=torch.uint8, device=device)
 
-        def gemm_only():
-            for Pd in Ps:
-                tg.bitnet_gemm(q, Pd, sa, sw, out=o)
+        def gemm_only(i):
+            tg.bitnet_gemm(q, Ps[i], sa, sw, out=o)
 
-        def linear_full():
-            for Pd in Ps:
-                tg.bitnet_linear(x, Pd, sw, out=o, workspace=ws)
+        def linear_full(i):
+            tg.bitnet_linear(x, Ps[i], sw, out=o, workspace=ws)
 
-        def quant_only():
-            for _ in Ps:
-                tg.quantize_activation(x, out=q, scale=sa)
+        def quant_only(i):
+            tg.quantize_activation(x, out=q, scale=sa)
 
         res = {"N": N, "K": K}
-        for tag, fn in (("gemm", gemm_only), ("linear", linear_full), ("quant", quant_only)):
-            g = capture(fn, stream)
+        for tag, fn, least in (("gemm", gemm_only, 16), ("linear", linear_full, 16), ("quant", quant_only, 64)):
+            g, L = launches_graph(fn, rotate, stream, least)
             ramp(g, stream)
-            st = pstats(repeat_timing(g.replay, stream, rotate, min_repeats=30))
+            st = pstats(repeat_timing(g.replay, stream, L, min_repeats=30))
             res[tag + "_us"] = st["median"]
             res[tag + "_us_p10"], res[tag + "_us_p90"], res[tag + "_repeats"] = st["p10"], st["p90"], st["n"]
         ops = 2.0 * M * N * K
@@ -373,13 +382,9 @@ def run_small_batch(device, stream, log):
             q, sa = tg.quantize_activation(x)
             o = torch.empty((M, N), dtype=torch.bfloat16, device=device)
 
-            def run():
-                for Pd in Ps:
-                    tg.bitnet_gemm(q, Pd, sa, sw, out=o)
-
-            g = capture(run, stream)
+            g, L = launches_graph(lambda i: tg.bitnet_gemm(q, Ps[i], sa, sw, out=o), copies, stream)
             ramp(g, stream)
-            st = pstats(repeat_timing(g.replay, stream, copies, min_repeats=15))
+            st = pstats(repeat_timing(g.replay, stream, L, min_repeats=15))
             t = st["median"] * 1e-6
             ops, nbytes = 2.0 * M * N * K, gemm_bytes(M, N, K)
             r = {"us": round(t * 1e6, 2), "us_p10": round(st["p10"], 2), "us_p90": round(st["p90"], 2),
@@ -478,12 +483,10 @@ def run_options(device, stream, log):
         ws = torch.empty((tg.linear_ex_workspace_bytes(M, K, torch.float32) + 256,), dtype=torch.uint8, device=device)
         r = {"M": M, "N": N, "K": K}
         for tag, x, b in (("bf16", xb, None), ("bf16_bias", xb, bias), ("f32", xf, None)):
-            def run(x=x, b=b):
-                for Pd in Ps:
-                    tg.bitnet_linear(x, Pd, sw, out=o, workspace=ws, bias=b)
-            g = capture(run, stream)
+            g, L = launches_graph(lambda i, x=x, b=b: tg.bitnet_linear(x, Ps[i], sw, out=o, workspace=ws, bias=b),
+                                  copies, stream)
             ramp(g, stream)
-            r[tag + "_us"] = round(pstats(repeat_timing(g.replay, stream, copies, min_repeats=15))["median"], 2)
+            r[tag + "_us"] = round(pstats(repeat_timing(g.replay, stream, L, min_repeats=15))["median"], 2)
         out[f"{name}_M{M}"] = r
         log(f"  {name:10s} M={M:5d} N={N:6d} K={K:5d}: bf16 {r['bf16_us']:8.2f} us, +bias {r['bf16_bias_us']:8.2f} us, "
             f"f32 input {r['f32_us']:8.2f} us")
@@ -513,12 +516,9 @@ def run_w8a16(device, stream, log):
             x = dev_bf16(synth.activations_bf16(M, K, synth.seed_for(7, 16 * i + synth.T_ACT) + M), device)
             y = torch.empty((M, N), dtype=torch.float32, device=device)
 
-            def run(x=x, y=y):
-                for qd in qs:
-                    tg.w8a16_gemv(x, qd, sc, out=y)
-            g = capture(run, stream)
+            g, L = launches_graph(lambda i, x=x, y=y: tg.w8a16_gemv(x, qs[i], sc, out=y), copies, stream, 16)
             ramp(g, stream)
-            t = pstats(repeat_timing(g.replay, stream, copies, min_repeats=15))["median"] * 1e-6
+            t = pstats(repeat_timing(g.replay, stream, L, min_repeats=15))["median"] * 1e-6
             r[f"M{M}_us"] = round(t * 1e6, 2)
             r[f"M{M}_gbs"] = round(w8a16_bytes(M, N, K) / t / 1e9, 1)
         out[name] = r
@@ -668,29 +668,40 @@ def run_machine(device, stream, log):
     def read(lo, n):
         check(lib.probe_read(ctypes.c_void_p(pool.data_ptr() + lo), n, ctypes.c_void_p(sink.data_ptr()), 2048, sp),
               "probe_read")
-    g = capture(lambda: read(0, 1 << 30), stream)
+    g = capture(lambda: [read(0, 1 << 30) for _ in range(8)], stream)
     ramp(g, stream)
-    st = pstats(repeat_timing(g.replay, stream, 1, min_repeats=20), 1.0)
+    st = pstats(repeat_timing(g.replay, stream, 8, min_repeats=20), 1.0)
     res["read_1GiB"] = {"tbs": round((1 << 30) / st["median"] / 1e12, 3), "us": round(st["median"] * 1e6, 1)}
     piece = 82_080_768  # the LM head's packed weights, 128256 x 640 bytes
     npieces = (1 << 30) // piece
-    g = capture(lambda: [read(i * piece, piece) for i in range(npieces)], stream)
+    g = capture(lambda: [read(i * piece, piece) for _ in range(4) for i in range(npieces)], stream)
     ramp(g, stream)
-    st = pstats(repeat_timing(g.replay, stream, npieces, min_repeats=20), 1.0)
+    st = pstats(repeat_timing(g.replay, stream, 4 * npieces, min_repeats=20), 1.0)
     res["read_82MB"] = {"tbs": round(piece / st["median"] / 1e12, 3), "us": round(st["median"] * 1e6, 2),
-                        "us_p10": round(st["p10"] * 1e6, 2), "us_p90": round(st["p90"] * 1e6, 2)}
+                        "us_p10": round(st["p10"] * 1e6, 2), "us_p90": round(st["p90"] * 1e6, 2),
+                        "workgroups": 2048}
+
+    def read256(lo, n):
+        check(lib.probe_read(ctypes.c_void_p(pool.data_ptr() + lo), n, ctypes.c_void_p(sink.data_ptr()), 256, sp),
+              "probe_read")
+    g = capture(lambda: [read256(i * piece, piece) for _ in range(4) for i in range(npieces)], stream)
+    ramp(g, stream)
+    st = pstats(repeat_timing(g.replay, stream, 4 * npieces, min_repeats=20), 1.0)
+    res["read_82MB_256wg"] = {"tbs": round(piece / st["median"] / 1e12, 3), "us": round(st["median"] * 1e6, 2),
+                              "workgroups": 256}
     half = 1 << 29
 
     def copy():
         check(lib.probe_copy(ctypes.c_void_p(pool.data_ptr() + half), ctypes.c_void_p(pool.data_ptr()), half, 2048, sp),
               "probe_copy")
-    g = capture(copy, stream)
+    g = capture(lambda: [copy() for _ in range(8)], stream)
     ramp(g, stream)
-    st = pstats(repeat_timing(g.replay, stream, 1, min_repeats=20), 1.0)
+    st = pstats(repeat_timing(g.replay, stream, 8, min_repeats=20), 1.0)
     res["copy_512MiB"] = {"tbs_read_plus_write": round(2 * half / st["median"] / 1e12, 3),
                           "us": round(st["median"] * 1e6, 1)}
     log(f"  HBM read 1 GiB {res['read_1GiB']['tbs']:.2f} TB/s; 82 MB pieces {res['read_82MB']['tbs']:.2f} TB/s "
-        f"({res['read_82MB']['us']:.2f} us); copy 512 MiB {res['copy_512MiB']['tbs_read_plus_write']:.2f} TB/s")
+        f"({res['read_82MB']['us']:.2f} us; {res['read_82MB_256wg']['us']:.2f} us with 256 workgroups); "
+        f"copy 512 MiB {res['copy_512MiB']['tbs_read_plus_write']:.2f} TB/s")
     del g, pool, sink
     torch.cuda.empty_cache()
     return res

@@ -886,11 +886,18 @@ hipError_t launch_stream(uint16_t* out, int32_t* acc, uint16_t* sa_out, const vo
     const size_t lds = (size_t)MT * steps * 8 * GV_SEG;
     const int xw = (MT * steps * (GV_STEP / 16) + 255) / 256;  // x words per thread (<= 8 by the budget)
     // Ring depth: 16 loads per lane for long rows, 8 normally, 4 when the MT
-    // accumulators already take most of the register file.
+    // accumulators already take most of the register file.  With one
+    // activation row and a single unit per wave (the smaller decode
+    // projections), 4: a deeper ring would only add loads past the wave's few
+    // steps, which stall the issue of the prologue behind them (measured on the
+    // BitNet-2B-4T gate_up projection: 5.17 -> 4.83 us).
     constexpr int D_SHORT = MT >= 8 ? 4 : 8;
     constexpr int D_LONG = MT == 1 ? 16 : D_SHORT;
     const dim3 grid(blocks);
     if constexpr (MT == 1) {
+        if (ks == 1 && upb <= groups && steps <= 8)
+            return launch_stream_xw<MT, 4, OUT_I32, RMS, 1, XF32, BIAS>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N,
+                                                                  K, steps, units, upb, gain, eps, bias);
         if (ks == 4) {
             if (steps / 4 >= 12)
                 return launch_stream_xw<MT, D_LONG, OUT_I32, RMS, 4, XF32, BIAS>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N,
