@@ -28,6 +28,11 @@ Profiling helpers (not part of the timed benchmark):
                                           turn those four passes into profiles/gemm_m2048_qkvo_counters.md
   python bench.py --gemv-scaling          M=1 bitnet_linear (quantise + GEMV) time against N at K=2560,
                                           and a line fit: fixed cost per launch and marginal stream rate
+  python bench.py --pmc-target-small      eager launches for counter passes over the small kernels (M=1 decode
+                                          GEMV on qkv / o_proj, small-batch GEMM at M=16 / 64)
+  python bench.py --summarize-small-pmc W F R
+                                          turn those three passes into profiles/small_kernels_counters.md
+  python bench.py --machine               machine ceilings only (int8 MFMA loop, HBM read and copy)
 """
 import argparse
 import csv
@@ -847,7 +852,7 @@ def _grid(row):
         return -1
 
 
-TRACE_ARGS = "--steps 22 --warmup 5 --no-cpu-baseline"
+TRACE_ARGS = "--steps 22 --warmup 5 --no-cpu-baseline --no-extra --no-machine"
 
 
 def summarize_trace(folder, bench_args=TRACE_ARGS):
@@ -1038,6 +1043,127 @@ def summarize_gemm_pmc(dirs):
     print("\n".join(md))
 
 
+SMALL_PMC_FILE = os.path.join(ROOT, "profiles", "small_kernels_counters.md")
+SMALL_PMC_PASSES = {  # pass name -> counters (each pass a run of its own)
+    "waits": "SQ_WAIT_INST_ANY SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAVES GRBM_GUI_ACTIVE",
+    "fetch": "FETCH_SIZE",
+    "write": "WRITE_SIZE",
+}
+SMALL_PMC_WARM, SMALL_PMC_REPS = 100, 20
+
+
+def small_pmc_cases():
+    """(tag, kind, M, N, K, seed index) of the small-kernel counter passes: the M=1
+    decode GEMV on the BitNet-2B-4T qkv and o_proj projections, and the
+    small-batch GEMM (pre-quantised activations) at M=16 and 64 on the LLaMA-7B
+    qkvo and gate_up shapes."""
+    cases = [("gemv qkv M=1", "gemv", 1, 3840, 2560, 0), ("gemv o_proj M=1", "gemv", 1, 2560, 2560, 1)]
+    for j, (name, N, K) in enumerate(synth.LLAMA7B_SHAPES[:2]):
+        for M in (16, 64):
+            cases.append((f"gemm {name} M={M}", "gemm", M, N, K, j))
+    return cases
+
+
+def run_pmc_target_small(device):
+    """Eager launches for counter passes over the small kernels: the calibration
+    copy, then for each case of small_pmc_cases SMALL_PMC_WARM + SMALL_PMC_REPS
+    launches over 16 weight copies (the summary keeps the last SMALL_PMC_REPS)."""
+    a = torch.full((CALIB_COPY_BYTES,), 7, dtype=torch.uint8, device=device)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    for tag, kind, M, N, K, j in small_pmc_cases():
+        W = synth.ternary_weights(N, K, synth.seed_for(8, 16 * j + synth.T_WEIGHT))
+        P = tg.pack_weights(torch.from_numpy(W)).to(device)
+        del W
+        Ps = [P] + [P.clone() for _ in range(15)]
+        sw = dev_bf16(synth.weight_scale_bf16(N, K, synth.seed_for(8, 16 * j + synth.T_SCALE)), device)
+        x = dev_bf16(synth.activations_bf16(M, K, synth.seed_for(8, 16 * j + synth.T_ACT)), device)
+        o = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+        q, sa = tg.quantize_activation(x)
+        torch.cuda.synchronize()
+        for i in range(SMALL_PMC_WARM + SMALL_PMC_REPS):
+            if kind == "gemv":
+                tg.bitnet_linear(x, Ps[i % 16], sw, out=o)
+            else:
+                tg.bitnet_gemm(q, Ps[i % 16], sa, sw, out=o)
+        torch.cuda.synchronize()
+        del Ps, P
+    print(json.dumps({"pmc_target_small": "done", "cases": [c[0] for c in small_pmc_cases()]}), flush=True)
+
+
+def summarize_small_pmc(dirs):
+    """Markdown summary of the counter passes of run_pmc_target_small (directories
+    in SMALL_PMC_PASSES order): per case, per-dispatch averages over its last
+    SMALL_PMC_REPS dispatches; byte counters scaled by the calibration copy."""
+    per = {}   # case index -> counter -> values
+    dur = {}
+    calib = {}
+    for (pname, counters), folder in zip(SMALL_PMC_PASSES.items(), dirs):
+        rows = _csv_rows(folder, "counter_collection.csv")
+        disp = {}
+        for r in rows:
+            name = _col(r, "Kernel_Name")
+            did = int(_col(r, "Dispatch_Id"))
+            cname = _col(r, "Counter_Name")
+            v = float(_col(r, "Counter_Value"))
+            if "copyBuffer" in name:
+                if cname in ("FETCH_SIZE", "WRITE_SIZE"):
+                    calib.setdefault(cname, []).append(v)
+                continue
+            if "gemv_stream_kernel" in name or "gemm_" in name:
+                d = disp.setdefault(did, {"name": name, "vals": {}, "dur": float(_col(r, "End_Timestamp")) -
+                                          float(_col(r, "Start_Timestamp"))})
+                d["vals"][cname] = d["vals"].get(cname, 0.0) + v
+        ids = sorted(disp)
+        n_case = len(small_pmc_cases())
+        per_case = SMALL_PMC_WARM + SMALL_PMC_REPS
+        if len(ids) < n_case * per_case:
+            raise SystemExit(f"pass {pname}: {len(ids)} layer dispatches in {folder}, expected {n_case * per_case}")
+        ids = ids[-n_case * per_case:]
+        for c in range(n_case):
+            keep = ids[c * per_case + SMALL_PMC_WARM:(c + 1) * per_case]
+            for did in keep:
+                for cname, v in disp[did]["vals"].items():
+                    per.setdefault(c, {}).setdefault(cname, []).append(v)
+                if pname == "waits":
+                    dur.setdefault(c, []).append(disp[did]["dur"])
+                per[c].setdefault("_name", []).append(disp[did]["name"])
+    factor = {cn: CALIB_COPY_BYTES / (1024.0 * max(v)) for cn, v in calib.items()}
+    cmds = [f"timeout -s KILL 90 rocprofv3 --pmc {cs} --output-format csv -d gpurun_out/pmc_small_{p} -o run -- "
+            "python3 bench.py --pmc-target-small" for p, cs in SMALL_PMC_PASSES.items()]
+    cmds.append("python bench.py --summarize-small-pmc " + " ".join(f"gpurun_out/pmc_small_{p}" for p in SMALL_PMC_PASSES))
+    md = ["# Counters of the small kernels (decode GEMV at M=1, small-batch GEMM at M=16 and 64)", "",
+          "Commands (each pass a run of its own, from the repository root after `cd /tmp && export TMPDIR=/tmp`):", ""]
+    md += ["    " + c for c in cmds]
+    md += ["", f"Per-dispatch averages over the last {SMALL_PMC_REPS} of {SMALL_PMC_WARM + SMALL_PMC_REPS} eager launches "
+           "of each case (16 weight copies in rotation). HBM bytes are FETCH_SIZE and WRITE_SIZE scaled by what they "
+           f"read for a plain copy of {CALIB_COPY_BYTES >> 20} MiB in the same run "
+           f"(factors {factor.get('FETCH_SIZE', float('nan')):.3f} and {factor.get('WRITE_SIZE', float('nan')):.3f}). "
+           "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES is the fraction of the waves' lifetime spent waiting to issue "
+           "(on memory, LDS or barriers).", "",
+           "| case | kernel | dispatch µs (profiled) | HBM bytes | algorithmic bytes | ratio | HBM GB/s | wait / wave cycles | waves |",
+           "|---|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for c, (tag, kind, M, N, K, j) in enumerate(small_pmc_cases()):
+        a = {k: sum(v) / len(v) for k, v in per[c].items() if k != "_name"}
+        name = per[c]["_name"][-1]
+        m = re.search(r"(gemv_stream_kernel|gemm_\w+?kernel)<[^>]*>", name)
+        kname = m.group(0) if m else name[:60]
+        hbm = a.get("FETCH_SIZE", 0.0) * 1024 * factor.get("FETCH_SIZE", 1.0) + \
+            a.get("WRITE_SIZE", 0.0) * 1024 * factor.get("WRITE_SIZE", 1.0)
+        algo = gemv_bytes(M, N, K) if kind == "gemv" else gemm_bytes(M, N, K)
+        d_us = sum(dur[c]) / len(dur[c]) / 1e3
+        md.append(f"| {tag} | `{kname}` | {d_us:.2f} | {hbm:.4g} | {algo} | {hbm / algo:.3f} | "
+                  f"{hbm / (d_us * 1e-6) / 1e9:.0f} | {a['SQ_WAIT_INST_ANY'] / a['SQ_WAVE_CYCLES']:.3f} | "
+                  f"{a.get('SQ_WAVES', 0):.0f} |")
+    with open(SMALL_PMC_FILE, "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -1058,6 +1184,8 @@ def main():
     ap.add_argument("--pmc-target-gemm", action="store_true")
     ap.add_argument("--summarize-gemm-pmc", nargs=4, metavar=("A_DIR", "B_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--gemv-scaling", action="store_true")
+    ap.add_argument("--pmc-target-small", action="store_true")
+    ap.add_argument("--summarize-small-pmc", nargs=3, metavar=("WAITS_DIR", "FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -1068,6 +1196,9 @@ def main():
         return
     if args.summarize_gemm_pmc:
         summarize_gemm_pmc(args.summarize_gemm_pmc)
+        return
+    if args.summarize_small_pmc:
+        summarize_small_pmc(args.summarize_small_pmc)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -1089,6 +1220,9 @@ def main():
         return
     if args.pmc_target_gemm:
         run_pmc_target_gemm(device)
+        return
+    if args.pmc_target_small:
+        run_pmc_target_small(device)
         return
     stream = torch.cuda.Stream(device)
     if args.gemv_scaling:

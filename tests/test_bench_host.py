@@ -164,3 +164,42 @@ def test_percentiles():
 def test_host_facts():
     f = bench.host_facts()
     assert f["nproc"] == os.cpu_count() and f["usable_cpus"] >= 1 and f["cpu_model"]
+
+
+def test_summarize_small_pmc(tmp_path, monkeypatch):
+    """Per case, the last SMALL_PMC_REPS of its dispatches are averaged; byte
+    counters are scaled by the calibration copy; the ratio to the algorithmic
+    bytes and the wait fraction follow."""
+    monkeypatch.setattr(bench, "SMALL_PMC_WARM", 2)
+    monkeypatch.setattr(bench, "SMALL_PMC_REPS", 3)
+    monkeypatch.setattr(bench, "SMALL_PMC_FILE", str(tmp_path / "small.md"))
+    cases = bench.small_pmc_cases()
+    header = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    dirs = []
+    for p, counters in bench.SMALL_PMC_PASSES.items():
+        d = tmp_path / p
+        d.mkdir()
+        rows = []
+        if p in ("fetch", "write"):
+            cn = "FETCH_SIZE" if p == "fetch" else "WRITE_SIZE"
+            rows.append([1, "__amd_rocclr_copyBuffer", cn, bench.CALIB_COPY_BYTES / 1024 / (2 if p == "fetch" else 1), 0, 1])
+        did = 10
+        for c, (tag, kind, M, N, K, j) in enumerate(cases):
+            name = "void gemv_stream_kernel<1, 4>" if kind == "gemv" else "void gemm_skinny_lds_kernel<1, 1, 8, false>"
+            algo = bench.gemv_bytes(M, N, K) if kind == "gemv" else bench.gemm_bytes(M, N, K)
+            for i in range(5):
+                kept = i >= 2
+                vals = {"SQ_WAIT_INST_ANY": 300 if kept else 0, "SQ_WAVE_CYCLES": 1000, "SQ_BUSY_CYCLES": 1,
+                        "SQ_WAVES": 480, "GRBM_GUI_ACTIVE": 1,
+                        "FETCH_SIZE": (algo / 2 / 1024) if kept else 0.0, "WRITE_SIZE": 0.0}
+                for cn in counters.split():
+                    rows.append([did, name, cn, vals[cn], 0, 4000])
+                did += 1
+        _write_csv(d / "run_counter_collection.csv", header, rows)
+        dirs.append(str(d))
+    bench.summarize_small_pmc(dirs)
+    text = (tmp_path / "small.md").read_text()
+    # FETCH_SIZE x 2 = algorithmic bytes: ratio 1.000; 4 us dispatches; wait fraction 0.3
+    tag, kind, M, N, K, j = cases[0]
+    assert f"| {tag} | `gemv_stream_kernel<1, 4>` | 4.00 | " in text
+    assert "| 1.000 | " in text and "| 0.300 | 480 |" in text
