@@ -74,6 +74,9 @@ constexpr int64_t GM_MID_BLOCKS = 160;           // blocks a mid-M block tile sh
 // Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format;
 // stride 0, so bounds are checked against the byte count in word 2).
 constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
+// Cache policy of the output tile stores: sc0 | sc1 (system coherence), i.e.
+// written through the L2.
+constexpr int STORE_WT = 17;
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool BDMA, int NS>
 struct GemmShape {
@@ -158,6 +161,90 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Epilogue of one wave's (32 MT) x (32 NT) accumulator tile, straight from
+// the accumulators: register r of lane l of a 32 x 32 tile holds row
+// 8(r/4) + 4(l/32) + r%4, column l%32.  (gm0, gn0) is the tile's first output
+// element, (lr0, lc0) the same position within the block, whose row sums,
+// row scales and column scales are in LDS.  whole: the block tile lies inside
+// the output, so no bounds checks are needed.
+template <int MT, int NT, bool OUT_I32>
+__device__ __forceinline__ void store_tile(const v16i (&acc)[MT][NT], uint16_t* __restrict__ out,
+                                           int32_t* __restrict__ acc_out, int M, int N, int gm0, int gn0, bool whole,
+                                           int lr0, int lc0, int lane, const int* rowsum, const float* rowscale,
+                                           const float* colscale) {
+    if (whole) {
+        // Branch-free buffer stores whose per-register row offset is a scalar,
+        // two rows per bf16 conversion.  The stores write through the L2
+        // (system-coherence bits): the tile is not read again by this kernel,
+        // and lines left dirty in the L2s would be written back when the
+        // kernel ends, after the last tile (measured: 1-3 % faster).
+        constexpr int ES = OUT_I32 ? 4 : 2;
+        void* dst = OUT_I32 ? static_cast<void*>(acc_out) : static_cast<void*>(out);
+        const __amdgpu_buffer_rsrc_t o_rsrc =
+            __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, M * N * ES, BUFFER_RSRC_WORD3);
+        const int lrow0 = lr0 + (lane >> 5) * 4;  // block row of (t = 0, r = 0)
+        const int lcol0 = lc0 + (lane & 31);
+        float swf[NT];
+#pragma unroll
+        for (int u = 0; u < NT; ++u) swf[u] = colscale[lcol0 + u * 32];
+        const int voff = ((gm0 + (lane >> 5) * 4) * N + gn0 + (lane & 31)) * ES;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const int dr = t * 32 + (r >> 2) * 8 + (r & 3);  // row offset, lane-independent
+                const int lr = lrow0 + dr;
+                const int c0 = 2 * rowsum[lr], c1 = 2 * rowsum[lr + 1];
+                const float a0 = rowscale[lr], a1 = rowscale[lr + 1];
+#pragma unroll
+                for (int u = 0; u < NT; ++u) {
+                    const int soff = (dr * N + u * 32) * ES;
+                    const int v0 = acc[t][u][r] - c0;
+                    const int v1 = acc[t][u][r + 1] - c1;
+                    if (OUT_I32) {
+                        __builtin_amdgcn_raw_buffer_store_b32(v0, o_rsrc, voff, soff, STORE_WT);
+                        __builtin_amdgcn_raw_buffer_store_b32(v1, o_rsrc, voff, soff + N * ES, STORE_WT);
+                    } else {
+                        const uint32_t pk = epilogue_bf16x2(v0, a0, v1, a1, swf[u]);
+                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, o_rsrc, voff, soff, STORE_WT);
+                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), o_rsrc, voff, soff + N * ES, STORE_WT);
+                    }
+                }
+            }
+        }
+        return;
+    }
+    float swf[NT];
+    int gcol[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+        const int lc = lc0 + u * 32 + (lane & 31);
+        gcol[u] = gn0 + u * 32 + (lane & 31);
+        swf[u] = colscale[lc];
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int dr = t * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            const int lr = lr0 + dr;
+            const int gm = gm0 + dr;
+            if (gm >= M) continue;
+            const int corr = 2 * rowsum[lr];
+            const float fa = rowscale[lr];
+#pragma unroll
+            for (int u = 0; u < NT; ++u) {
+                if (gcol[u] >= N) continue;
+                const int v = acc[t][u][r] - corr;
+                if (OUT_I32)
+                    acc_out[(int64_t)gm * N + gcol[u]] = v;
+                else
+                    out[(int64_t)gm * N + gcol[u]] = epilogue_bf16(v, fa, swf[u]);
+            }
+        }
+    }
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int WAVES_PER_EU, int NS, bool BDMA, bool OUT_I32>
@@ -444,75 +531,9 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
     if (tid < BN) colscale[tid] = sw_mine;
     __syncthreads();
 
-    // ---- epilogue straight from the accumulators: register r of lane l of a
-    //      32 x 32 tile holds row 8(r/4) + 4(l/32) + r%4, column l%32
-    if (m0 + BM <= M && n0 + BN <= N) {
-        // Whole tile in range: branch-free buffer stores whose per-register row
-        // offset is a scalar, two rows per bf16 conversion.
-        constexpr int ES = OUT_I32 ? 4 : 2;
-        void* dst = OUT_I32 ? static_cast<void*>(acc_out) : static_cast<void*>(out);
-        const __amdgpu_buffer_rsrc_t o_rsrc =
-            __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, M * N * ES, BUFFER_RSRC_WORD3);
-        const int lrow0 = wm * MT * 32 + (lane >> 5) * 4;  // block row of (t = 0, r = 0)
-        const int lcol0 = wn * NT * 32 + (lane & 31);
-        const int voff = ((m0 + lrow0) * N + n0 + lcol0) * ES;
-        float swf[NT];
-#pragma unroll
-        for (int u = 0; u < NT; ++u) swf[u] = colscale[lcol0 + u * 32];
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const int dr = t * 32 + (r >> 2) * 8 + (r & 3);  // row offset, lane-independent
-                const int lr = lrow0 + dr;
-                const int c0 = 2 * rowsum[lr], c1 = 2 * rowsum[lr + 1];
-                const float a0 = rowscale[lr], a1 = rowscale[lr + 1];
-#pragma unroll
-                for (int u = 0; u < NT; ++u) {
-                    const int soff = (dr * N + u * 32) * ES;
-                    const int v0 = acc[t][u][r] - c0;
-                    const int v1 = acc[t][u][r + 1] - c1;
-                    if (OUT_I32) {
-                        __builtin_amdgcn_raw_buffer_store_b32(v0, o_rsrc, voff, soff, 0);
-                        __builtin_amdgcn_raw_buffer_store_b32(v1, o_rsrc, voff, soff + N * ES, 0);
-                    } else {
-                        const uint32_t pk = epilogue_bf16x2(v0, a0, v1, a1, swf[u]);
-                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pk, o_rsrc, voff, soff, 0);
-                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pk >> 16), o_rsrc, voff, soff + N * ES, 0);
-                    }
-                }
-            }
-        }
-        return;
-    }
-    float swf[NT];
-    int gcol[NT];
-#pragma unroll
-    for (int u = 0; u < NT; ++u) {
-        const int lc = (wn * NT + u) * 32 + (lane & 31);
-        gcol[u] = n0 + lc;
-        swf[u] = colscale[lc];
-    }
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int lr = (wm * MT + t) * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            const int gm = m0 + lr;
-            if (gm >= M) continue;
-            const int corr = 2 * rowsum[lr];
-            const float fa = rowscale[lr];
-#pragma unroll
-            for (int u = 0; u < NT; ++u) {
-                if (gcol[u] >= N) continue;
-                const int v = acc[t][u][r] - corr;
-                if (OUT_I32)
-                    acc_out[(int64_t)gm * N + gcol[u]] = v;
-                else
-                    out[(int64_t)gm * N + gcol[u]] = epilogue_bf16(v, fa, swf[u]);
-            }
-        }
-    }
+    store_tile<MT, NT, OUT_I32>(acc, out, acc_out, M, N, m0 + wm * MT * 32, n0 + wn * NT * 32,
+                                m0 + BM <= M && n0 + BN <= N, wm * MT * 32, wn * NT * 32, lane, rowsum, rowscale,
+                                colscale);
 }
 
 // Skinny path: few rows (M up to a few hundred), where the block tiles above
@@ -909,16 +930,12 @@ hipError_t launch_skinny(uint16_t* out, int32_t* acc, const int8_t* x, const uin
 template <bool OUT_I32>
 hipError_t launch_tiles(uint16_t* out, int32_t* acc, const int8_t* x, const uint8_t* w, const uint16_t* sa,
                         const uint16_t* sw, int M, int N, int K, hipStream_t s) {
-    // Tile choice.  128 x 512 blocks (eight 128 x 64 wave tiles) decode each B
-    // fragment for four MFMAs and stage each A byte for 512 columns, so they
-    // spend the least VALU per MFMA; they are used when there are enough of them
-    // to give every CU at least two.  Otherwise 128 x 256 blocks (eight 64 x 64
-    // wave tiles), which keep two waves per SIMD busy on N = 4096-sized shapes.
-    // Too few 128 x 256 tiles to give every CU one, and fewer than GM_MID_MN
-    // outputs (else the mid-M blocks below): a split-K skinny kernel (each
-    // wave needs at least one chunk of K): the LDS-staged one when
-    // K % 256 == 0, else the direct one.  Configurations measured on the
-    // LLaMA-7B layer shapes: short rings and more resident waves beat deep
+    // Tile choice, by the number of 128 x 256 block tiles.  At least one per
+    // CU: the block-tiled kernel (the large-M choice at the end).  Fewer, and
+    // fewer than GM_MID_MN outputs (else the mid-M blocks below): a split-K
+    // skinny kernel (each wave needs at least one chunk of K): the LDS-staged
+    // one when K % 256 == 0, else the direct one.  Configurations measured on
+    // the LLaMA-7B layer shapes: short rings and more resident waves beat deep
     // per-wave prefetch here.
     const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 255) / 256);
     const int nc = K / GM_KS;
@@ -974,9 +991,20 @@ hipError_t launch_tiles(uint16_t* out, int32_t* acc, const int8_t* x, const uint
         if (M <= 128) return launch_skinny<1, 2, 4, 1, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
         return launch_skinny<2, 2, 4, 1, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
     }
+    // Large M.  128 x 512 blocks (eight 128 x 64 wave tiles, two waves per
+    // SIMD) spend the least VALU per MFMA; they are taken when their rounds of
+    // 256 blocks come out at least 85 % full.  Otherwise, with more than 256
+    // blocks of 128 x 256, four-wave 128 x 256 blocks (128 x 64 wave tiles),
+    // two resident per CU, so that a last partial round still keeps two waves
+    // on the SIMDs it occupies; with at most 256, one eight-wave block per CU
+    // (64 x 64 wave tiles).  Measured on the LLaMA-7B shapes at M = 2048 and
+    // 4096 (e.g. gate_up, M = 2048: 688 blocks, four-wave blocks 6 % faster;
+    // qkvo, M = 4096: 256 wide blocks, 15 % faster than 128 x 256).
     const int64_t wide_tiles = (int64_t)((M + 127) / 128) * ((N + 511) / 512);
-    if (wide_tiles >= 2 * 256)
+    const int64_t wide_rounds = (wide_tiles + 255) / 256;
+    if (wide_tiles >= 256 && wide_tiles * 100 >= wide_rounds * 256 * 85)
         return launch_mfma<128, 512, 1, 8, 2, 3, true, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
+    if (tiles > 256) return launch_mfma<128, 256, 1, 4, 2, 2, true, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
     return launch_mfma<128, 256, 2, 4, 2, 3, true, OUT_I32>(out, acc, x, w, sa, sw, M, N, K, s);
 }
 

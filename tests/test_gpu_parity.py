@@ -207,8 +207,9 @@ GEMM_SHAPES = [
     # keeps the split-K kernel for M > 128 and K >= 2048 covered
     (513, 10000, 256), (300, 13000, 384), (1000, 2200, 512), (200, 4000, 2048),
     # weights straight into the LDS ring, ragged M and N: 128 x 128 blocks over 10 stages (the ring
-    # wraps), 128 x 256 blocks over 5 stages, 128 x 512 blocks with a single stage
-    (700, 4000, 1280), (1100, 8200, 640), (1030, 32770, 128),
+    # wraps); four-wave 128 x 256 blocks (more than 256 of them, too few 128 x 512 blocks to fill their
+    # rounds) over 5 stages and over a single stage; 128 x 512 blocks with a single stage
+    (700, 4000, 1280), (1100, 8200, 640), (1030, 32770, 128), (1030, 65000, 128),
     # few rows, very many columns: 32- and 64-row blocks
     (5, 66000, 1024), (32, 65600, 512), (40, 70000, 512), (64, 65537, 256),
 ]
@@ -255,8 +256,8 @@ def test_gemm_i32_misaligned_plain_path():
 @pytest.mark.parametrize("M,N,K", [(4, 128, 256), (16, 4096, 4096), (200, 300, 1024), (33, 65, 68),
                                    (513, 10000, 256), (300, 13000, 384), (1000, 2200, 512), (700, 4000, 1280),
                                    (1100, 8200, 640), (16, 128256, 512), (40, 70000, 512),
-                                   # the bf16-output 128 x 512 block tile (>= 2 such blocks per CU), ragged M
-                                   # and N: one stage, and two stages
+                                   # ragged M and N: four-wave 128 x 256 blocks over one stage, the 128 x 512
+                                   # block tile (its rounds of 256 blocks at least 85 % full) over two stages
                                    (1030, 32770, 128), (600, 70000, 256)])
 def test_gemm_bf16_parity(M, N, K):
     x, W, P, _ = problem(M, N, K, seed=3000 + M)
