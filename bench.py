@@ -625,17 +625,55 @@ def load_probe():
     lib.probe_read.argtypes = [p, i64, p, i, p]
     lib.probe_copy.argtypes = [p, p, i64, i, p]
     lib.probe_mfma_i8.argtypes = [p, i, p, i, p]
-    for fn in (lib.probe_read, lib.probe_copy, lib.probe_mfma_i8):
+    lib.probe_gemm_loop.argtypes = [p, i, p, i, p]
+    for fn in (lib.probe_read, lib.probe_copy, lib.probe_mfma_i8, lib.probe_gemm_loop):
         fn.restype = i
     return lib
+
+
+def run_vendor_int8_gemm(device, stream, log, M=2048, N=4096, K=4096):
+    """torch._int_mm (hipBLASLt's int8 x int8 -> int32 GEMM) at the qkvo prefill
+    shape, on the workload's quantised activations and the ternary weights
+    unpacked to int8 [K][N] (column-major, as a weight matrix is stored):
+    a reference point for what a dense int8 library GEMM reaches on this GPU
+    and data.  Launched eagerly (library calls stay out of captured graphs)."""
+    try:
+        x = dev_bf16(synth.activations_bf16(M, K, synth.seed_for(3, synth.T_ACT), outlier_frac=0.01), device)
+        q, _ = tg.quantize_activation(x)
+        W = torch.from_numpy(synth.ternary_weights(N, K, synth.seed_for(3, synth.T_WEIGHT))).to(device)
+        Wt = W.t()  # [K][N] view of the row-major [N][K] weights
+        with torch.cuda.stream(stream):
+            torch._int_mm(q, Wt)
+        torch.cuda.synchronize()
+
+        def launch():
+            for _ in range(16):
+                torch._int_mm(q, Wt)
+        for _ in range(3):
+            time_launches(launch, stream)
+        st = pstats(repeat_timing(launch, stream, 16, min_repeats=10))
+        tops = 2.0 * M * N * K / (st["median"] * 1e-6) / 1e12
+        res = {"shape": [M, N, K], "us": round(st["median"], 2), "tops": round(tops, 1),
+               "frac_of_published": round(tops / INT8_PEAK_TOPS, 4)}
+        log(f"  vendor int8 GEMM (torch._int_mm) {M}x{N}x{K}: {res['us']:.2f} us, {res['tops']:.1f} TOPS "
+            f"({100 * res['frac_of_published']:.1f}% of 5.0 POPS)")
+        return res
+    except (RuntimeError, NotImplementedError) as e:
+        log(f"  vendor int8 GEMM unavailable: {e}")
+        return {"shape": [M, N, K], "error": str(e)[:200]}
 
 
 def run_machine(device, stream, log):
     """Practical ceilings of this GPU, measured with the probe kernels:
     the int8 MFMA rate of back-to-back v_mfma_i32_32x32x32_i8 (2 waves per SIMD),
-    with the shader clock it ran at; the HBM read rate over 1 GiB and over
-    82 MB pieces of a 1 GiB pool (the LM head's weight size); the copy rate
-    over 512 MiB.  Each is the median of repeated, ramped timings."""
+    with the shader clock it ran at; the same for the GEMM's inner loop alone
+    (LDS fragments, weight expansion, MFMAs; 128 x 64 wave tiles, 2 waves per
+    SIMD) on operand data distributed like the prefill workload's, which
+    changes every MFMA and draws more power; the vendor int8 GEMM
+    (torch._int_mm, hipBLASLt) at the M = 2048 qkvo shape with unpacked int8
+    weights; the HBM read rate over 1 GiB and over 82 MB pieces of a 1 GiB pool
+    (the LM head's weight size); the copy rate over 512 MiB.  Each is the median
+    of repeated, ramped timings."""
     import ctypes
     lib = load_probe()
     sp = ctypes.c_void_p(stream.cuda_stream)
@@ -664,7 +702,29 @@ def run_machine(device, stream, log):
                       "kernel_ms": round(st["median"] * 1e3, 3), "waves_per_simd": 2}
     log(f"  int8 MFMA loop: {res['mfma_i8']['tops']:.1f} TOPS ({100 * res['mfma_i8']['frac_of_published']:.1f}% of "
         f"5.0 POPS), shader clock {res['mfma_i8']['sclk_mhz']} MHz")
+    del g
+
+    gl_iters = 2000
+
+    def gemm_loop():
+        check(lib.probe_gemm_loop(ctypes.c_void_p(out.data_ptr()), gl_iters, ctypes.c_void_p(clk.data_ptr()), blocks,
+                                  sp), "probe_gemm_loop")
+    g = capture(gemm_loop, stream)
+    ramp(g, stream)
+    st = pstats(repeat_timing(g.replay, stream, 1, min_repeats=20), 1.0)
+    ops = blocks * 4 * gl_iters * 32 * 65536.0
+    ticks, real = (int(v) for v in clk.cpu())
+    res["gemm_loop_i8"] = {"tops": round(ops / st["median"] / 1e12, 1),
+                           "frac_of_published": round(ops / st["median"] / 1e12 / INT8_PEAK_TOPS, 4),
+                           "sclk_mhz": round(ticks / real * 100.0, 1) if real > 0 else None,
+                           "kernel_ms": round(st["median"] * 1e3, 3), "waves_per_simd": 2,
+                           "operands": "activation codes bell-shaped in -22..23 (sd about 8), ternary weight codes "
+                                       "P(0)=0.4, changing every MFMA"}
+    log(f"  GEMM inner loop on workload-like data: {res['gemm_loop_i8']['tops']:.1f} TOPS "
+        f"({100 * res['gemm_loop_i8']['frac_of_published']:.1f}% of 5.0 POPS), shader clock "
+        f"{res['gemm_loop_i8']['sclk_mhz']} MHz")
     del g, out
+    res["vendor_int8_gemm"] = run_vendor_int8_gemm(device, stream, log)
 
     pool = torch.empty((1 << 30,), dtype=torch.uint8, device=device)
     pool.fill_(3)

@@ -8,9 +8,15 @@
 //   probe_read      streams a buffer with 16-byte loads and reduces it (HBM read)
 //   probe_copy      copies a buffer with 16-byte loads and stores (HBM read + write)
 //   probe_mfma_i8   back-to-back v_mfma_i32_32x32x32_i8 on register operands
-// probe_mfma_i8 also reads the shader-clock counter (s_memtime) and the
-// constant 100 MHz counter (s_memrealtime) around its loop in one wave, which
-// gives the shader clock while the matrix units are loaded.
+//   probe_gemm_loop the ternary GEMM's inner loop alone (LDS fragment reads,
+//                   weight-code expansion, MFMAs) on operand data distributed
+//                   like the prefill workload's
+// The two MFMA probes also read the shader-clock counter (s_memtime) and the
+// constant 100 MHz counter (s_memrealtime) around their loops in one wave,
+// which gives the shader clock while the matrix units are loaded.  The
+// matrix units' power depends on the operand bits: probe_mfma_i8 repeats a
+// few small register operands, probe_gemm_loop changes them every MFMA as the
+// GEMM does, and the clock the chip sustains differs accordingly.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -101,6 +107,111 @@ __global__ __launch_bounds__(256) void probe_mfma_i8_kernel(int32_t* __restrict_
     out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// A 32-bit integer mixer (murmur3's finaliser), for synthetic operand data.
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+    x ^= x >> 16;
+    x *= 0x85ebca6bu;
+    x ^= x >> 13;
+    x *= 0xc2b2ae35u;
+    x ^= x >> 16;
+    return x;
+}
+
+// Four signed activation bytes, bell-shaped in -22 .. 23 with standard
+// deviation about 8: like the per-token absmax int8 codes of N(0, 1)
+// activations whose rows hold outlier channels eight times larger (the
+// prefill workload: the absmax is set by an outlier, the mean |code| is about
+// 6 and 96 % of the codes lie within +-15).
+__device__ __forceinline__ uint32_t activation_bytes(uint32_t h) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t a = mix32(h * 4u + j);
+        const int code = (int)(a & 15) + (int)((a >> 4) & 15) + (int)((a >> 8) & 15) - 22;
+        v |= (uint32_t)(code & 0xff) << (8 * j);
+    }
+    return v;
+}
+
+// Sixteen packed 2-bit weight codes (w + 2 for w in {-1, 0, +1}), P(w = 0) = 0.4.
+__device__ __forceinline__ uint32_t weight_codes(uint32_t h) {
+    uint32_t p = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const uint32_t r = mix32(h * 16u + j) % 10u;
+        p |= (r < 3 ? 1u : (r < 7 ? 2u : 3u)) << (2 * j);
+    }
+    return p;
+}
+
+// The inner loop of the tiled GEMM for one 128 x 64 wave tile (4 x 2 MFMA
+// tiles): per 128-element stage the packed weight dwords of the two column
+// tiles and, per 32-element k-step, the four activation fragments are read
+// from LDS, each weight dword is expanded into four code dwords, and eight
+// MFMAs are issued.  LDS holds one stage; the lanes rotate over it every
+// iteration, so operand data changes every MFMA.  No global loads, no
+// barriers: the rate this loop reaches bounds the GEMM's.
+constexpr int GL_MT = 4, GL_NT = 2;
+__global__ __launch_bounds__(256) void probe_gemm_loop_kernel(int32_t* __restrict__ out, int iters,
+                                                              uint64_t* __restrict__ clk) {
+    constexpr int A_BYTES = GL_MT * 4 * 1024;
+    __shared__ __align__(16) uint8_t lds[A_BYTES + GL_NT * 1024];
+    const int tid = threadIdx.x, lane = tid & 63;
+    for (int i = tid * 4; i < (int)sizeof(lds); i += 256 * 4) {
+        const uint32_t h = mix32((uint32_t)i * 2654435761u + blockIdx.x);
+        *reinterpret_cast<uint32_t*>(lds + i) = i < A_BYTES ? activation_bytes(h) : weight_codes(h);
+    }
+    __syncthreads();
+    v16i acc[GL_MT][GL_NT];
+#pragma unroll
+    for (int t = 0; t < GL_MT; ++t)
+#pragma unroll
+        for (int u = 0; u < GL_NT; ++u) acc[t][u] = v16i{};
+    const bool timer = blockIdx.x == 0 && threadIdx.x < 64;
+    uint64_t t0 = 0, r0 = 0;
+    if (timer) {
+        t0 = __builtin_amdgcn_s_memtime();
+        r0 = __builtin_amdgcn_s_memrealtime();
+    }
+    for (int it = 0; it < iters; ++it) {
+        const int slot = ((lane ^ it) & 63) * 16;
+        v4u pb[GL_NT];
+#pragma unroll
+        for (int u = 0; u < GL_NT; ++u) pb[u] = *reinterpret_cast<const v4u*>(lds + A_BYTES + u * 1024 + slot);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            v4i af[GL_MT];
+#pragma unroll
+            for (int t = 0; t < GL_MT; ++t) af[t] = *reinterpret_cast<const v4i*>(lds + (t * 4 + s) * 1024 + slot);
+#pragma unroll
+            for (int u = 0; u < GL_NT; ++u) {
+                const uint32_t p = pb[u][s];
+                const v4i bf = {(int)(p & 0x03030303u), (int)((p >> 2) & 0x03030303u), (int)((p >> 4) & 0x03030303u),
+                                (int)((p >> 6) & 0x03030303u)};
+#pragma unroll
+                for (int t = 0; t < GL_MT; ++t)
+                    acc[t][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[t], bf, acc[t][u], 0, 0, 0);
+            }
+        }
+    }
+    if (timer) {
+        const uint64_t t1 = __builtin_amdgcn_s_memtime();
+        const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+        if (lane == 0) {
+            clk[0] = t1 - t0;
+            clk[1] = r1 - r0;
+        }
+    }
+    int sum = 0;
+#pragma unroll
+    for (int t = 0; t < GL_MT; ++t)
+#pragma unroll
+        for (int u = 0; u < GL_NT; ++u)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) sum += acc[t][u][j];
+    out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
 }  // namespace
 
 // Reads n_bytes (a multiple of 16, 16-byte aligned src) with `blocks`
@@ -126,5 +237,13 @@ PROBE_API int probe_copy(void* dst, const void* src, int64_t n_bytes, int blocks
 PROBE_API int probe_mfma_i8(int32_t* out, int iters, uint64_t* clk, int blocks, void* stream) {
     if (iters <= 0 || blocks <= 0) return 2;
     hipLaunchKernelGGL(probe_mfma_i8_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters, clk);
+    return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+// blocks workgroups of 4 waves, each wave iters x 32 MFMAs (32 x 32 x 32 int8);
+// out holds blocks * 256 int32, clk two uint64 (written), as for probe_mfma_i8.
+PROBE_API int probe_gemm_loop(int32_t* out, int iters, uint64_t* clk, int blocks, void* stream) {
+    if (iters <= 0 || blocks <= 0) return 2;
+    hipLaunchKernelGGL(probe_gemm_loop_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters, clk);
     return hipGetLastError() == hipSuccess ? 0 : 6;
 }
