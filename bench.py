@@ -500,6 +500,50 @@ def run_options(device, stream, log):
     return out
 
 
+FUSED_M = (1, 2, 4, 5, 8, 12, 15)
+
+
+def run_fused_small_m(device, stream, log):
+    """bitnet_gemv_fused (quantise + product in one launch, without a workspace)
+    against the split path (bitnet_quantize_act, then bitnet_gemm) at
+    M = 1 ... 15 on the BitNet-2B-4T decode shapes, and bitnet_linear, which
+    takes whichever of the two its dispatch rule picks; weights rotate through
+    a 1 GiB pool.  Times are medians of graph-timed launches in microseconds."""
+    out = {}
+    for i, (name, N, K) in enumerate(synth.BITNET_2B_DECODE):
+        W = synth.ternary_weights(N, K, synth.seed_for(8, 16 * i + synth.T_WEIGHT))
+        P = tg.pack_weights(torch.from_numpy(W)).to(device)
+        del W
+        copies = max(2, -(-POOL_BYTES // P.numel()))
+        Ps = [P] + [P.clone() for _ in range(copies - 1)]
+        sw = dev_bf16(synth.weight_scale_bf16(N, K, synth.seed_for(8, 16 * i + synth.T_SCALE)), device)
+        rows = {}
+        for M in FUSED_M:
+            x = dev_bf16(synth.activations_bf16(M, K, synth.seed_for(8, 16 * i + synth.T_ACT) + M), device)
+            o = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+            q = torch.empty((M, K), dtype=torch.int8, device=device)
+            sa = torch.empty((M,), dtype=torch.bfloat16, device=device)
+            ws = torch.empty((max(tg.linear_workspace_bytes(M, K), 256),), dtype=torch.uint8, device=device)
+            r = {}
+            for tag, fn in (("fused_us", lambda j: tg.bitnet_gemv_fused(x, Ps[j], sw, out=o)),
+                            ("split_us", lambda j: (tg.quantize_activation(x, out=q, scale=sa),
+                                                    tg.bitnet_gemm(q, Ps[j], sa, sw, out=o))),
+                            ("linear_us", lambda j: tg.bitnet_linear(x, Ps[j], sw, out=o, workspace=ws))):
+                g, L = launches_graph(fn, copies, stream)
+                ramp(g, stream)
+                r[tag] = round(pstats(repeat_timing(g.replay, stream, L, min_repeats=10))["median"], 2)
+                del g
+            r["fused_over_split"] = round(r["fused_us"] / r["split_us"], 3)
+            rows[M] = r
+            del x, o, q, sa, ws
+        out[name] = {"N": N, "K": K, "by_M": rows}
+        log(f"  {name:8s} N={N:6d} K={K:5d}: " + " | ".join(
+            f"M={M} {r['fused_us']:.2f}/{r['split_us']:.2f}/{r['linear_us']:.2f}" for M, r in rows.items()))
+        del Ps, P
+        torch.cuda.empty_cache()
+    return out
+
+
 def w8a16_bytes(M, N, K):
     """Algorithmic bytes of the INT8 weight-only matmul: int8 W + fp32 scale + bf16 x + fp32 y."""
     return N * K + 4 * N + 2 * M * K + 4 * M * N
@@ -1310,7 +1354,7 @@ def main():
             log(f"prefill GEMM M={M} (LLaMA-7B shapes):")
             gemms[M] = run_gemm(device, stream, M, log)
 
-    small = full = options = w8 = machine = None
+    small = full = options = w8 = machine = fused_m = None
     if not args.no_extra:
         log("small-batch GEMM M=8..256 (LLaMA-7B layer shapes, pre-quantised):")
         small = run_small_batch(device, stream, log)
@@ -1318,6 +1362,8 @@ def main():
         full = run_decode_full(device, stream, log)
         log("bitnet_linear options (f32 activations, bias):")
         options = run_options(device, stream, log)
+        log("fused quantise + product (bitnet_gemv_fused) / quantise then GEMM / bitnet_linear, us, M = 1..15:")
+        fused_m = run_fused_small_m(device, stream, log)
         log("INT8 weight-only matmul (W8A16), decode shapes:")
         w8 = run_w8a16(device, stream, log)
     if not args.no_machine:
@@ -1383,6 +1429,7 @@ def main():
         line["small_batch_gemm"] = small
         line["decode_full_step"] = full
         line["linear_options"] = options
+        line["fused_small_m"] = fused_m
         line["w8a16_gemv"] = w8
     if machine is not None:
         line["machine_ceilings"] = machine

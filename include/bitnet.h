@@ -106,7 +106,9 @@ bitnet_status bitnet_gemm(uint16_t* out, const int8_t* x_int8, const uint8_t* w_
  * bitnet-cpu; the fused decode path of the bitnet-tc request).  Computes, for
  * 0 <= M <= BITNET_FUSED_MAX_M, exactly the composition
  *   bitnet_quantize_act(x) followed by bitnet_gemm,
- * bit for bit, without writing the int8 activations anywhere.
+ * bit for bit, without writing the int8 activations anywhere (every workgroup
+ * quantises the rows it needs: a streaming dot4 kernel for M <= 4, int8 MFMA
+ * from M = 5 when K % 128 == 0 and x, w are 16-byte aligned).
  * out: bf16 [M][N] (written); x: bf16 [M][K]; w_packed: uint8 [N][K/4];
  * scale_wt: bf16 [N].  Device pointers, enqueued on stream.
  * Errors: M > BITNET_FUSED_MAX_M -> SHAPE.
@@ -126,9 +128,12 @@ size_t bitnet_linear_workspace_bytes(int64_t M, int64_t K);
  * One-shot BitLinear forward (bitnet_linear of bitnet-cpu): dispatches on M.
  * bitnet-cpu sends M < 16 to its fused GEMV; here both paths give identical
  * bits, so the choice is made for speed: bitnet_gemv_fused for M <= 2 (and for
- * M <= 4 when K <= 8192), otherwise bitnet_quantize_act into the workspace,
- * then bitnet_gemm (one quantisation pass is cheaper than the fused kernel's
- * per-workgroup quantisation once there are more rows).  out: bf16 [M][N]; x: bf16 [M][K]; w_packed: uint8 [N][K/4];
+ * M <= 4 when K <= 8192), its matrix-unit kernel for 5 <= M <= 8 when
+ * M * K <= 20480 and N <= 65536 (16-byte aligned x and w, K % 128 == 0; the
+ * workspace is then required but unused), otherwise bitnet_quantize_act into
+ * the workspace, then bitnet_gemm (one quantisation pass is cheaper than the
+ * fused kernels' per-workgroup quantisation once there are more rows).
+ * out: bf16 [M][N]; x: bf16 [M][K]; w_packed: uint8 [N][K/4];
  * scale_wt: bf16 [N]; workspace: device memory of workspace_bytes bytes, 256-byte
  * aligned, used as scratch (may be NULL when bitnet_linear_workspace_bytes is 0).
  * Errors: workspace_bytes too small -> WORKSPACE.

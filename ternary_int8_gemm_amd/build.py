@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbitnet_hip.so")
-SOURCES = ["api.hip", "quant.hip", "gemv.hip", "gemm.hip", "epilogue.hip", "w8a16.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemv.hip", "gemv_mfma.hip", "gemm.hip", "epilogue.hip", "w8a16.hip"]
 PROBE_SOURCE = "probe.hip"
 PROBE_LIB = os.path.join(HERE, "libbitnet_probe.so")
 

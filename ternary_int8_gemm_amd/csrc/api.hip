@@ -147,18 +147,29 @@ BITNET_API bitnet_status bitnet_gemv_fused_i32(int32_t* acc, uint16_t* scale_act
     return launched(launch_gemv_fused(nullptr, acc, scale_act, x, w_packed, nullptr, M, N, K, (hipStream_t)stream));
 }
 
-// Which path bitnet_linear takes.  Both give the same bits; the fused GEMV
-// quantises the activations in every workgroup, which is cheapest for one or
-// two rows (or up to four that fit its LDS budget), while from there on one
-// quantisation pass plus the GEMM is faster (measured on the BitNet-2B-4T and
-// LLaMA-7B projection shapes).
+// Which path bitnet_linear takes.  Both give the same bits; the fused kernels
+// quantise the activations in every workgroup, which is cheapest for one or
+// two rows (or up to four that fit the streaming GEMV's LDS budget), and, on
+// the matrix units, for five to eight rows of short K over moderate N, while
+// otherwise one quantisation pass plus the GEMM is faster (measured on the
+// BitNet-2B-4T and LLaMA-7B projection shapes).
 // Longest K for which three or four rows stay on the fused GEMV (its streaming
 // kernel holds 4 x K int8 activations in 32 KB of LDS).
 constexpr int64_t LINEAR_FUSED_K_MAX_M4 = 8192;
+// Five to eight rows take the fused matrix-unit kernel while every workgroup's
+// share of quantising (M * K elements) stays this small and the columns do not
+// ask for more workgroups than the GPU holds at once (an LM head does).
+constexpr int64_t LINEAR_MFMA_MK_MAX = 8 * 2560;
+constexpr int64_t LINEAR_MFMA_N_MAX = 65536;
 
 static bool linear_takes_fused(int64_t M, int64_t K) {
     if (M <= 2) return true;
     return M <= 4 && K <= LINEAR_FUSED_K_MAX_M4;
+}
+
+static bool linear_takes_mfma(int64_t M, int64_t N, int64_t K, const void* x, const void* w) {
+    return M >= 5 && M <= 8 && M * K <= LINEAR_MFMA_MK_MAX && N <= LINEAR_MFMA_N_MAX &&
+           bitnet::gemv_mfma_fits(M, N, K, x, w);
 }
 
 BITNET_API size_t bitnet_linear_workspace_bytes(int64_t M, int64_t K) {
@@ -178,6 +189,9 @@ BITNET_API bitnet_status bitnet_linear(uint16_t* out, const uint16_t* x, const u
     const size_t need = bitnet_linear_workspace_bytes(M, K);
     if (workspace == nullptr || workspace_bytes < need) return BITNET_ERR_WORKSPACE;
     if (bitnet_status st = check_device()) return st;
+    if (linear_takes_mfma(M, N, K, x, w_packed))  // the workspace goes unused
+        return launched(bitnet::launch_gemv_mfma(out, nullptr, nullptr, x, w_packed, scale_wt, M, N, K,
+                                                 (hipStream_t)stream));
     int8_t* x_int8 = static_cast<int8_t*>(workspace);
     uint16_t* scale_act = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + round256((size_t)M * K));
     hipStream_t s = (hipStream_t)stream;

@@ -57,8 +57,6 @@
 #include "bitnet_device.h"
 #include "launch.h"
 
-#include <atomic>
-
 namespace bitnet {
 
 namespace {
@@ -709,22 +707,6 @@ __global__ __launch_bounds__(64) void gemm_plain(uint16_t* __restrict__ out, int
                 out[(int64_t)m * N + n] = epilogue_bf16(acc, bf16_to_f32(sa[m]), bf16_to_f32(sw[n]));
         }
     }
-}
-
-// Raise a kernel's dynamic LDS limit above the 64 KB default, once per device
-// for each kernel instance (each instance has its own flag word; devices past
-// 63 set the attribute on every launch).
-template <typename Kern>
-hipError_t raise_lds_limit(Kern kern, size_t lds) {
-    static std::atomic<unsigned long long> done{0};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    const unsigned long long bit = (dev >= 0 && dev < 64) ? 1ull << dev : 0;
-    if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
-    return e;
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int WAVES_PER_EU, int NS, bool BDMA, bool OUT_I32>

@@ -71,6 +71,7 @@ constexpr int GV_STEP = 512;            // weights per row per wave step (8 lane
 constexpr int GV_MAX_KS = 4;            // waves that can share one unit's K range
 constexpr int GV_SPLIT_UNITS = 4096;    // split K while units x parts stays below this
 constexpr int GV_LDS_BUDGET = 32768;    // bytes of quantised activations held per chunk
+constexpr int GV_MFMA_MIN_M = 5;        // rows from which the fused product runs on the matrix units
 
 __device__ __forceinline__ int lds_word_offset(int word) {
     // word = 16-element group within a chunk; seg = 64-element segment
@@ -916,6 +917,14 @@ hipError_t launch_stream(uint16_t* out, int32_t* acc, uint16_t* sa_out, const vo
     if (steps >= 12)
         return launch_stream_xw<MT, D_LONG, OUT_I32, RMS, 1, XF32, BIAS>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N, K,
                                                              steps, units, upb, gain, eps, bias);
+    // One activation row, several units per wave, short rows (the LM head): a
+    // ring of 6.  Fewer loads in flight per CU let every workgroup's activation
+    // loads through sooner, so the workgroups start streaming together and end
+    // closer together (BitNet-2B-4T LM head, 128256 x 2560: 15.2 -> 14.4 us
+    // against a ring of 8; 4 and 5 gave 14.4-14.9 us, 3 gave 16.2 us).
+    if constexpr (MT == 1)
+        return launch_stream_xw<MT, 6, OUT_I32, RMS, 1, XF32, BIAS>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N, K,
+                                                                steps, units, upb, gain, eps, bias);
     return launch_stream_xw<MT, D_SHORT, OUT_I32, RMS, 1, XF32, BIAS>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N, K,
                                                                 steps, units, upb, gain, eps, bias);
 }
@@ -947,6 +956,10 @@ hipError_t dispatch_mt(uint16_t* out, int32_t* acc, uint16_t* sa_out, const uint
 template <bool OUT_I32>
 hipError_t dispatch(uint16_t* out, int32_t* acc, uint16_t* sa_out, const uint16_t* x, const uint8_t* w,
                     const uint16_t* sw, int M, int N, int K, hipStream_t s) {
+    // From five rows the dot4 stream is bound by LDS reads of the activations
+    // (one per row and weight word): the matrix-unit kernel takes over.
+    if (M >= GV_MFMA_MIN_M && gemv_mfma_fits(M, N, K, x, w))
+        return launch_gemv_mfma(out, acc, sa_out, x, w, sw, M, N, K, s);
     const bool fast = (K % 64 == 0) && aligned16(x) && aligned16(w);
     if (!fast) {
         hipLaunchKernelGGL((gemv_fused_plain<OUT_I32>), dim3((unsigned)N), dim3(64), 0, s, out, acc, sa_out, x, w, sw,

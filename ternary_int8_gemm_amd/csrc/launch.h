@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace bitnet {
 
 // Per-token absmax INT8 quantisation of x [M][K] (bf16) into q [M][K] and the
@@ -20,6 +22,14 @@ hipError_t launch_gemm(uint16_t* out, int32_t* acc, const int8_t* x, const uint8
 hipError_t launch_gemv_fused(uint16_t* out, int32_t* acc, uint16_t* scale_act_out, const uint16_t* x,
                              const uint8_t* w, const uint16_t* scale_wt, int64_t M, int64_t N, int64_t K,
                              hipStream_t s);
+
+// The fused quantise + product on int8 MFMA for 1 <= M <= 16 rows (used from
+// five rows up), for shapes gemv_mfma_fits accepts; same outputs as
+// launch_gemv_fused.
+bool gemv_mfma_fits(int64_t M, int64_t N, int64_t K, const void* x, const void* w);
+hipError_t launch_gemv_mfma(uint16_t* out, int32_t* acc, uint16_t* scale_act_out, const uint16_t* x,
+                            const uint8_t* w, const uint16_t* scale_wt, int64_t M, int64_t N, int64_t K,
+                            hipStream_t s);
 
 // out[m][n] = epilogue(acc[m][n], scale_act[m], scale_wt[n]).
 hipError_t launch_epilogue(uint16_t* out, const int32_t* acc, const uint16_t* scale_act, const uint16_t* scale_wt,
@@ -55,5 +65,22 @@ hipError_t launch_w8a16(float* y, const uint16_t* x, const int8_t* q, const floa
                         int64_t K, hipStream_t s);
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Raise a kernel's dynamic LDS limit above the 64 KB default, once per device
+// for each kernel instance (each instance has its own flag word; devices past
+// 63 set the attribute on every launch).
+template <typename Kern>
+hipError_t raise_lds_limit(Kern kern, size_t lds) {
+    static std::atomic<unsigned long long> done{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const unsigned long long bit = (dev >= 0 && dev < 64) ? 1ull << dev : 0;
+    if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
+
 
 }  // namespace bitnet

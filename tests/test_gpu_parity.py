@@ -152,12 +152,26 @@ def test_gemv_prologue_exhaustive_bf16():
     W = np.zeros((K, K), dtype=np.int8)
     np.fill_diagonal(W, 1)
     Pd = dev(lib_pack(W))
-    # 1, 2, 4 and 8 rows take the streaming kernel; 15 rows of this length its K-chunked variant
+    # 1, 2 and 4 rows take the streaming kernel; 8 and 15 rows of this length (K % 128 != 0) its
+    # K-chunked variant
+    assert K % 128 != 0
     for m0, m1 in ((0, 1), (1, 3), (3, 7), (7, 15), (15, 30)):
         xs = x[m0:m1]
         acc, sa = tg.bitnet_gemv_fused_i32(dev_bf16(xs), Pd)
         assert np.array_equal(host_bf16(sa), s_ref[m0:m1])
         assert np.array_equal(acc.cpu().numpy(), q_ref[m0:m1].astype(np.int32)), f"rows {m0}..{m1}"
+    # zero-padded to K % 128 == 0, 5 to 15 rows take the matrix-unit kernel
+    K2 = (K + 127) // 128 * 128
+    x2 = np.zeros((M, K2), dtype=np.uint16)
+    x2[:, :K] = x
+    W2 = np.zeros((K2, K2), dtype=np.int8)
+    np.fill_diagonal(W2, 1)
+    Pd2 = dev(lib_pack(W2))
+    for m0, m1 in ((0, 5), (5, 13), (13, 28), (28, 30)):
+        acc, sa = tg.bitnet_gemv_fused_i32(dev_bf16(x2[m0:m1]), Pd2)
+        assert np.array_equal(host_bf16(sa), s_ref[m0:m1])
+        assert np.array_equal(acc.cpu().numpy()[:, :K], q_ref[m0:m1].astype(np.int32)), f"rows {m0}..{m1}"
+        assert not acc.cpu().numpy()[:, K:].any()
 
 
 def test_quantize_f32_near_ties():
@@ -257,8 +271,10 @@ def test_gemm_i32_misaligned_plain_path():
                                    (513, 10000, 256), (300, 13000, 384), (1000, 2200, 512), (700, 4000, 1280),
                                    (1100, 8200, 640), (16, 128256, 512), (40, 70000, 512),
                                    # ragged M and N: four-wave 128 x 256 blocks over one stage, the 128 x 512
-                                   # block tile (its rounds of 256 blocks at least 85 % full) over two stages
-                                   (1030, 32770, 128), (600, 70000, 256)])
+                                   # block tile (its rounds of 256 blocks at least 85 % full) over two stages;
+                                   # the same two block shapes over four and six stages, more blocks than
+                                   # are resident at once, edge tiles in M and N
+                                   (1030, 32770, 128), (600, 70000, 256), (1500, 11000, 512), (390, 55700, 768)])
 def test_gemm_bf16_parity(M, N, K):
     x, W, P, _ = problem(M, N, K, seed=3000 + M)
     sw = synth.row_scales_bf16(N, seed=3100 + M)
@@ -289,6 +305,37 @@ def test_gemv_fused_parity(M, N, K):
     assert np.array_equal(host_bf16(sa), ref["scale_act"])
     assert np.array_equal(acc.cpu().numpy(), ref["acc"])
     assert_bf16_parity(host_bf16(out), ref["out"], f"gemv {M}x{N}x{K}")
+
+
+# The matrix-unit fused kernel (five rows and more, K % 128 == 0): every number of K parts
+# per column tile (1, 2, 4, 8, 16 by the launch rule), K in one chunk, two chunks, ten chunks
+# and a last chunk of a single stage (K parts with no stage in it), ragged N, and M = 5 ... 15.
+GEMV_MFMA_SHAPES = [
+    (13, 66001, 256),    # 1 part (2063 tiles)
+    (6, 40001, 512),     # 2 parts
+    (6, 20001, 512),     # 4 parts
+    (14, 13824, 2560),   # 8 parts
+    (16 - 1, 3000, 2048),  # 16 parts, one chunk
+    (9, 100, 11008),     # 16 parts, two chunks
+    (7, 200, 8320),      # 16 parts, a last chunk of one stage
+    (12, 40, 40960),     # five chunks
+    (8, 3840, 2560), (5, 2560, 6912), (11, 10000, 1024),
+]
+
+
+@pytest.mark.parametrize("M,N,K", GEMV_MFMA_SHAPES)
+def test_gemv_fused_mfma_parity(M, N, K):
+    x, W, P, sw = problem(M, N, K, seed=4400 + M * 3 + N + K, outliers=0.01, row_scales=True)
+    x[M // 2] = 0  # an all-zero row: the 1e-5 absmax floor
+    ref = oracle.linear(x, P, sw)
+    xd, Pd = dev_bf16(x), dev(P)
+    out = tg.bitnet_gemv_fused(xd, Pd, dev_bf16(sw))
+    acc, sa = tg.bitnet_gemv_fused_i32(xd, Pd)
+    assert np.array_equal(host_bf16(sa), ref["scale_act"])
+    assert np.array_equal(acc.cpu().numpy(), ref["acc"])
+    assert_bf16_parity(host_bf16(out), ref["out"], f"gemv mfma {M}x{N}x{K}")
+    q, sa2 = tg.quantize_activation(xd)   # same bits as the split path
+    assert np.array_equal(host_bf16(tg.bitnet_gemm(q, Pd, sa2, dev_bf16(sw))), host_bf16(out))
 
 
 def test_gemv_fused_misaligned_plain_path():
