@@ -226,6 +226,9 @@ GEMM_SHAPES = [
     (700, 4000, 1280), (1100, 8200, 640), (1030, 32770, 128), (1030, 65000, 128),
     # few rows, very many columns: 32- and 64-row blocks
     (5, 66000, 1024), (32, 65600, 512), (40, 70000, 512), (64, 65537, 256),
+    # the eight-wave 128 x 256 block (one round of at most 256 blocks): 2, 3, 5 and 9 stages on
+    # ragged M and N
+    (300, 500, 256), (250, 300, 384), (2000, 3900, 640), (1930, 3850, 1152),
 ]
 
 
@@ -274,7 +277,9 @@ def test_gemm_i32_misaligned_plain_path():
                                    # block tile (its rounds of 256 blocks at least 85 % full) over two stages;
                                    # the same two block shapes over four and six stages, more blocks than
                                    # are resident at once, edge tiles in M and N
-                                   (1030, 32770, 128), (600, 70000, 256), (1500, 11000, 512), (390, 55700, 768)])
+                                   (1030, 32770, 128), (600, 70000, 256), (1500, 11000, 512), (390, 55700, 768),
+                                   # the eight-wave 128 x 256 block: 2 and 9 stages, ragged M and N
+                                   (300, 500, 256), (1930, 3850, 1152)])
 def test_gemm_bf16_parity(M, N, K):
     x, W, P, _ = problem(M, N, K, seed=3000 + M)
     sw = synth.row_scales_bf16(N, seed=3100 + M)
