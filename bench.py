@@ -25,7 +25,7 @@ Profiling helpers (not part of the timed benchmark):
                                           into a per-kernel, per-grid table on stdout
   python bench.py --pmc-target-gemm       eager launches for the counter passes over the M=2048 GEMM
   python bench.py --summarize-gemm-pmc A B F W
-                                          turn those four passes into profiles/gemm_m2048_qkvo_counters.md
+                                          turn those four passes into profiles/gemm_m2048_counters.md
   python bench.py --gemv-scaling          M=1 bitnet_linear (quantise + GEMV) time against N at K=2560,
                                           and a line fit: fixed cost per launch and marginal stream rate
   python bench.py --pmc-target-small      eager launches for counter passes over the small kernels (M=1 decode
@@ -1046,99 +1046,142 @@ def summarize_pmc(fetch_dir, write_dir):
     print(json.dumps(out))
 
 
-GEMM_PMC_FILE = os.path.join(ROOT, "profiles", "gemm_m2048_qkvo_counters.md")
+GEMM_PMC_FILE = os.path.join(ROOT, "profiles", "gemm_m2048_counters.md")
 GEMM_PMC_PASSES = {  # pass name -> counters (each pass a run of its own)
     "a": "SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_VALU_MFMA_COEXEC_CYCLES",
     "b": "SQ_WAIT_INST_ANY SQ_WAVE_CYCLES SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS SQ_BUSY_CYCLES",
     "fetch": "FETCH_SIZE",
     "write": "WRITE_SIZE",
 }
+# LLaMA-7B shapes the counter passes cover, in launch order: qkvo takes one round
+# of eight-wave 128 x 256 blocks, gate_up 1.34 rounds of two four-wave blocks per CU
+GEMM_PMC_SHAPES = ("qkvo", "gate_up")
+GEMM_PMC_M = 2048
 GEMM_PMC_WARM, GEMM_PMC_REPS = 300, 20
 
 
 def run_pmc_target_gemm(device):
     """Eager launches for counter passes over the prefill GEMM: a plain copy of
-    CALIB_COPY_BYTES (byte-counter calibration), then GEMM_PMC_WARM +
-    GEMM_PMC_REPS launches of bitnet_gemm on the LLaMA-7B qkvo shape at M=2048
-    (pre-quantised activations); the summary keeps the last GEMM_PMC_REPS, when
-    the clocks have settled."""
+    CALIB_COPY_BYTES (byte-counter calibration), then, for each shape of
+    GEMM_PMC_SHAPES in turn, GEMM_PMC_WARM + GEMM_PMC_REPS launches of
+    bitnet_gemm at M = GEMM_PMC_M (pre-quantised activations); the summary keeps
+    the last GEMM_PMC_REPS of each shape, when the clocks have settled."""
     a = torch.full((CALIB_COPY_BYTES,), 7, dtype=torch.uint8, device=device)
     b = torch.empty_like(a)
-    i, (name, N, K) = next((i, sh) for i, sh in enumerate(synth.LLAMA7B_SHAPES) if sh[0] == "qkvo")
-    M = 2048
-    P = tg.pack_weights(torch.from_numpy(synth.ternary_weights(N, K, synth.seed_for(3, 16 * i + synth.T_WEIGHT)))).to(device)
-    sw = dev_bf16(synth.weight_scale_bf16(N, K, synth.seed_for(3, 16 * i + synth.T_SCALE)), device)
-    x = dev_bf16(synth.activations_bf16(M, K, synth.seed_for(3, 16 * i + synth.T_ACT), outlier_frac=0.01), device)
-    q, sa = tg.quantize_activation(x)
-    o = torch.empty((M, N), dtype=torch.bfloat16, device=device)
     torch.cuda.synchronize()
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
-    for _ in range(GEMM_PMC_WARM + GEMM_PMC_REPS):
-        tg.bitnet_gemm(q, P, sa, sw, out=o)
-    torch.cuda.synchronize()
-    print(json.dumps({"pmc_target_gemm": "done", "M": M, "N": N, "K": K,
-                      "launches": GEMM_PMC_WARM + GEMM_PMC_REPS}), flush=True)
+    M = GEMM_PMC_M
+    for shape in GEMM_PMC_SHAPES:
+        i, (name, N, K) = next((i, sh) for i, sh in enumerate(synth.LLAMA7B_SHAPES) if sh[0] == shape)
+        P = tg.pack_weights(torch.from_numpy(synth.ternary_weights(N, K, synth.seed_for(3, 16 * i + synth.T_WEIGHT))))
+        P = P.to(device)
+        sw = dev_bf16(synth.weight_scale_bf16(N, K, synth.seed_for(3, 16 * i + synth.T_SCALE)), device)
+        x = dev_bf16(synth.activations_bf16(M, K, synth.seed_for(3, 16 * i + synth.T_ACT), outlier_frac=0.01), device)
+        q, sa = tg.quantize_activation(x)
+        o = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+        torch.cuda.synchronize()
+        for _ in range(GEMM_PMC_WARM + GEMM_PMC_REPS):
+            tg.bitnet_gemm(q, P, sa, sw, out=o)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_target_gemm": name, "M": M, "N": N, "K": K,
+                          "launches": GEMM_PMC_WARM + GEMM_PMC_REPS}), flush=True)
+        del P, sw, x, q, sa, o
+
+
+def _gemm_block(kernel_name):
+    """(block rows, block columns, waves) from a gemm_mfma_kernel<BM, BN, WM, WN, ...> name."""
+    m = re.search(r"gemm_mfma_kernel<\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+)", kernel_name)
+    if not m:
+        return None
+    bm, bn, wm, wn = (int(g) for g in m.groups())
+    return bm, bn, wm * wn
 
 
 def summarize_gemm_pmc(dirs):
     """Markdown summary of the four counter passes of run_pmc_target_gemm (the
-    directories in GEMM_PMC_PASSES order): per-launch averages over the last
-    GEMM_PMC_REPS GEMM dispatches of each pass."""
-    vals, durs, calib, kname = {}, [], {}, set()
+    directories in GEMM_PMC_PASSES order): per shape, per-launch averages over the
+    last GEMM_PMC_REPS of its GEMM dispatches (the dispatches of a pass, in
+    order, fall into len(GEMM_PMC_SHAPES) equal runs)."""
+    ns = len(GEMM_PMC_SHAPES)
+    vals = [{} for _ in range(ns)]
+    durs = [[] for _ in range(ns)]
+    knames = [set() for _ in range(ns)]
+    calib = {}
     for (pname, counters), folder in zip(GEMM_PMC_PASSES.items(), dirs):
         rows = _csv_rows(folder, "counter_collection.csv")
         gemm_ids = sorted({int(_col(r, "Dispatch_Id")) for r in rows if "gemm_mfma_kernel" in _col(r, "Kernel_Name")})
-        keep = set(gemm_ids[-GEMM_PMC_REPS:])
-        if len(keep) < GEMM_PMC_REPS:
-            raise SystemExit(f"pass {pname}: only {len(keep)} GEMM dispatches in {folder}")
+        if len(gemm_ids) % ns != 0 or len(gemm_ids) // ns < GEMM_PMC_REPS:
+            raise SystemExit(f"pass {pname}: {len(gemm_ids)} GEMM dispatches in {folder}, "
+                             f"expected {ns} runs of at least {GEMM_PMC_REPS}")
+        per = len(gemm_ids) // ns
+        which = {}
+        for s in range(ns):
+            for did in gemm_ids[(s + 1) * per - GEMM_PMC_REPS:(s + 1) * per]:
+                which[did] = s
         seen_dur = set()
         for r in rows:
             did = int(_col(r, "Dispatch_Id"))
             cname = _col(r, "Counter_Name")
             v = float(_col(r, "Counter_Value"))
-            if did in keep:
-                vals.setdefault(cname, []).append(v)
+            if did in which:
+                s = which[did]
+                vals[s].setdefault(cname, []).append(v)
                 m = re.search(r"gemm_mfma_kernel<[^>]*>", _col(r, "Kernel_Name"))
-                kname.add(m.group(0) if m else _col(r, "Kernel_Name"))
+                knames[s].add(m.group(0) if m else _col(r, "Kernel_Name"))
                 if pname == "a" and did not in seen_dur:
                     seen_dur.add(did)
-                    durs.append(float(_col(r, "End_Timestamp")) - float(_col(r, "Start_Timestamp")))
+                    durs[s].append(float(_col(r, "End_Timestamp")) - float(_col(r, "Start_Timestamp")))
             elif "copyBuffer" in _col(r, "Kernel_Name") and cname in ("FETCH_SIZE", "WRITE_SIZE"):
                 calib.setdefault(cname, []).append(v)
-    avg = {k: sum(v) / len(v) for k, v in vals.items()}
-    dur_ns = sum(durs) / len(durs)
-    i, (name, N, K) = next((i, sh) for i, sh in enumerate(synth.LLAMA7B_SHAPES) if sh[0] == "qkvo")
-    M = 2048
-    simds, clk = 256 * 4, 2.4e9
-    mfma_cycles = 32.0  # v_mfma_i32_32x32x32_i8 per SIMD
-    busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"]
     factor = {c: CALIB_COPY_BYTES / (1024.0 * max(v)) for c, v in calib.items()}
-    fetch_b = avg["FETCH_SIZE"] * 1024.0 * factor["FETCH_SIZE"]
-    write_b = avg["WRITE_SIZE"] * 1024.0 * factor["WRITE_SIZE"]
-    algo = gemm_bytes(M, N, K)
-    cmds = [f"timeout -s KILL 90 rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_gemm_{p} -o run -- "
+    M = GEMM_PMC_M
+    simds, clk = 256 * 4, 2.4e9
+    cmds = [f"timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_gemm_{p} -o run -- "
             "python3 bench.py --pmc-target-gemm" for p, c in GEMM_PMC_PASSES.items()]
     cmds.append("python bench.py --summarize-gemm-pmc " + " ".join(f"gpurun_out/pmc_gemm_{p}" for p in GEMM_PMC_PASSES))
-    md = [f"# Counters of the prefill GEMM (bitnet_gemm, LLaMA-7B qkvo, M={M}, N={N}, K={K})", "",
+    shapes = [next(sh for sh in synth.LLAMA7B_SHAPES if sh[0] == s) for s in GEMM_PMC_SHAPES]
+    md = [f"# Counters of the prefill GEMM (bitnet_gemm, LLaMA-7B shapes, M={M})", "",
           "Commands (each pass a run of its own, from the repository root after `cd /tmp && export TMPDIR=/tmp`):", ""]
     md += ["    " + c for c in cmds]
     md += ["", f"Per-launch averages over the last {GEMM_PMC_REPS} of {GEMM_PMC_WARM + GEMM_PMC_REPS} eager launches "
-           f"(`{', '.join(sorted(kname))}`, 256 workgroups of 8 waves).", "",
-           "| quantity | value |", "|---|---:|",
-           f"| dispatch duration (profiled) | {dur_ns / 1e3:.2f} µs |",
-           f"| SQ_INSTS_MFMA | {avg['SQ_INSTS_MFMA']:.0f} (2MNK / 65536 = {2 * M * N * K // 65536}) |",
-           f"| SQ_VALU_MFMA_BUSY_CYCLES | {busy:.4g} ({busy / avg['SQ_INSTS_MFMA']:.1f} per MFMA) |",
-           f"| MFMA busy / (duration × 2.4 GHz × {simds} SIMDs) | {busy / (dur_ns * 1e-9 * clk * simds):.3f} |",
-           f"| VALU instructions per MFMA | {avg['SQ_INSTS_VALU'] / avg['SQ_INSTS_MFMA']:.2f} |",
-           f"| MFMA cycles with VALU co-issued (COEXEC / MFMA busy) | {avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / busy:.3f} |",
-           f"| LDS instructions per MFMA | {avg['SQ_INSTS_LDS'] / avg['SQ_INSTS_MFMA']:.2f} |",
-           f"| LDS bank-conflict cycles per LDS instruction | {avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_INSTS_LDS']:.2f} |",
-           f"| SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES | {avg['SQ_WAIT_INST_ANY'] / avg['SQ_WAVE_CYCLES']:.3f} |",
-           f"| SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES | {avg['SQ_WAIT_INST_LDS'] / avg['SQ_WAVE_CYCLES']:.3f} |",
-           f"| HBM bytes (FETCH_SIZE × {factor['FETCH_SIZE']:.3f} + WRITE_SIZE × {factor['WRITE_SIZE']:.3f}) | "
-           f"{fetch_b + write_b:.4g} ({(fetch_b + write_b) / algo:.2f} × the {algo} algorithmic bytes) |"]
+           "of each shape.", "",
+           "| quantity | " + " | ".join(f"{n} ({N}×{K})" for n, N, K in shapes) + " |",
+           "|---|" + "---:|" * ns]
+    cols = {k: [] for k in ("kernel", "grid", "dur", "mfma", "busy", "frac", "valu", "coexec", "lds", "conf", "wait",
+                            "waitlds", "hbm")}
+    for s, (name, N, K) in enumerate(shapes):
+        avg = {k: sum(v) / len(v) for k, v in vals[s].items()}
+        dur_ns = sum(durs[s]) / len(durs[s])
+        busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"]
+        kn = ", ".join(f"`{k}`" for k in sorted(knames[s]))
+        blk = _gemm_block(next(iter(sorted(knames[s]))))
+        fetch_b = avg["FETCH_SIZE"] * 1024.0 * factor["FETCH_SIZE"]
+        write_b = avg["WRITE_SIZE"] * 1024.0 * factor["WRITE_SIZE"]
+        algo = gemm_bytes(M, N, K)
+        cols["kernel"].append(kn)
+        cols["grid"].append(f"{-(-M // blk[0]) * -(-N // blk[1])} of {blk[2]} waves" if blk else "?")
+        cols["dur"].append(f"{dur_ns / 1e3:.2f} µs")
+        cols["mfma"].append(f"{avg['SQ_INSTS_MFMA']:.0f} (2MNK / 65536 = {2 * M * N * K // 65536})")
+        cols["busy"].append(f"{busy:.4g} ({busy / avg['SQ_INSTS_MFMA']:.1f} per MFMA)")
+        cols["frac"].append(f"{busy / (dur_ns * 1e-9 * clk * simds):.3f}")
+        cols["valu"].append(f"{avg['SQ_INSTS_VALU'] / avg['SQ_INSTS_MFMA']:.2f}")
+        cols["coexec"].append(f"{avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / busy:.3f}")
+        cols["lds"].append(f"{avg['SQ_INSTS_LDS'] / avg['SQ_INSTS_MFMA']:.2f}")
+        cols["conf"].append(f"{avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_INSTS_LDS']:.2f}")
+        cols["wait"].append(f"{avg['SQ_WAIT_INST_ANY'] / avg['SQ_WAVE_CYCLES']:.3f}")
+        cols["waitlds"].append(f"{avg['SQ_WAIT_INST_LDS'] / avg['SQ_WAVE_CYCLES']:.3f}")
+        cols["hbm"].append(f"{fetch_b + write_b:.4g} ({(fetch_b + write_b) / algo:.2f} × the {algo} algorithmic bytes)")
+    labels = [("kernel", "kernel"), ("grid", "workgroups"), ("dur", "dispatch duration (profiled)"),
+              ("mfma", "SQ_INSTS_MFMA"), ("busy", "SQ_VALU_MFMA_BUSY_CYCLES"),
+              ("frac", f"MFMA busy / (duration × 2.4 GHz × {simds} SIMDs)"), ("valu", "VALU instructions per MFMA"),
+              ("coexec", "MFMA cycles with VALU co-issued (COEXEC / MFMA busy)"),
+              ("lds", "LDS instructions per MFMA"), ("conf", "LDS bank-conflict cycles per LDS instruction"),
+              ("wait", "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES"), ("waitlds", "SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES"),
+              ("hbm", f"HBM bytes (FETCH_SIZE × {factor['FETCH_SIZE']:.3f} + WRITE_SIZE × "
+                      f"{factor['WRITE_SIZE']:.3f})")]
+    md += [f"| {label} | " + " | ".join(cols[k]) + " |" for k, label in labels]
     md += ["", "The byte counters are scaled by what they read for a plain device copy of 256 MiB in the same run.",
            "The MFMA peak used for the fraction is the dense int8 rate at 2.4 GHz: 1024 SIMDs × 32768 MACs per",
            "32 cycles = 5.0 POPS."]

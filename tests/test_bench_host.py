@@ -62,47 +62,64 @@ def _counter_rows(kernel, dispatch, counters, start=0, end=35000):
 
 
 def test_summarize_gemm_pmc(tmp_path, monkeypatch):
-    """The last GEMM_PMC_REPS GEMM dispatches of each pass are averaged; the byte
-    counters are scaled by the calibration copy; the figures follow."""
+    """Per shape, the last GEMM_PMC_REPS of its run of GEMM dispatches are
+    averaged; the byte counters are scaled by the calibration copy; the figures
+    follow, one column per shape."""
     header = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
     reps = bench.GEMM_PMC_REPS
-    passes = {
-        "a": {"SQ_INSTS_MFMA": 1048576, "SQ_VALU_MFMA_BUSY_CYCLES": 1048576 * 32, "SQ_INSTS_VALU": 1048576 * 7.5,
-              "SQ_VALU_MFMA_COEXEC_CYCLES": 1048576 * 16},
-        "b": {"SQ_WAIT_INST_ANY": 400, "SQ_WAVE_CYCLES": 1000, "SQ_INSTS_LDS": 900000, "SQ_LDS_BANK_CONFLICT": 0,
-              "SQ_WAIT_INST_LDS": 50, "SQ_BUSY_CYCLES": 1},
-        "fetch": {"FETCH_SIZE": 14336.0},   # KiB; x2 by the calibration below
-        "write": {"WRITE_SIZE": 16384.0},   # KiB; x1
+    assert bench.GEMM_PMC_SHAPES == ("qkvo", "gate_up")
+    kernels = ["void bitnet::gemm_mfma_kernel<128, 256, 2, 4, 2, 3, true, false>(...)",
+               "void bitnet::gemm_mfma_kernel<128, 256, 1, 4, 2, 2, true, false>(...)"]
+    passes = {  # per shape: the kept dispatches' counters
+        "a": [{"SQ_INSTS_MFMA": 1048576, "SQ_VALU_MFMA_BUSY_CYCLES": 1048576 * 32, "SQ_INSTS_VALU": 1048576 * 7.5,
+               "SQ_VALU_MFMA_COEXEC_CYCLES": 1048576 * 16},
+              {"SQ_INSTS_MFMA": 2818048, "SQ_VALU_MFMA_BUSY_CYCLES": 2818048 * 32, "SQ_INSTS_VALU": 2818048 * 4,
+               "SQ_VALU_MFMA_COEXEC_CYCLES": 2818048 * 8}],
+        "b": [{"SQ_WAIT_INST_ANY": 400, "SQ_WAVE_CYCLES": 1000, "SQ_INSTS_LDS": 900000, "SQ_LDS_BANK_CONFLICT": 0,
+               "SQ_WAIT_INST_LDS": 50, "SQ_BUSY_CYCLES": 1},
+              {"SQ_WAIT_INST_ANY": 300, "SQ_WAVE_CYCLES": 1000, "SQ_INSTS_LDS": 900000, "SQ_LDS_BANK_CONFLICT": 9000,
+               "SQ_WAIT_INST_LDS": 20, "SQ_BUSY_CYCLES": 1}],
+        "fetch": [{"FETCH_SIZE": 14336.0}, {"FETCH_SIZE": 30000.0}],   # KiB; x2 by the calibration below
+        "write": [{"WRITE_SIZE": 16384.0}, {"WRITE_SIZE": 44032.0}],   # KiB; x1
     }
+    ends = [35000, 90000]
     calib = {"fetch": ("FETCH_SIZE", bench.CALIB_COPY_BYTES / 2 / 1024), "write": ("WRITE_SIZE",
                                                                                   bench.CALIB_COPY_BYTES / 1024)}
     dirs = []
-    for p, counters in passes.items():
+    for p, per_shape in passes.items():
         d = tmp_path / p
         d.mkdir()
         rows = []
         if p in calib:
             rows += [[1, "__amd_rocclr_copyBuffer", calib[p][0], calib[p][1], 0, 1]]
-        # warm-up dispatches with different values, then the kept ones
-        for i in range(5):
-            rows += _counter_rows("void gemm_mfma_kernel<...>", 10 + i, {k: 0 for k in counters}, end=99000)
-        for i in range(reps):
-            rows += _counter_rows("void gemm_mfma_kernel<...>", 100 + i, counters)
+        did = 10
+        for s, counters in enumerate(per_shape):
+            # warm-up dispatches with different values, then the kept ones
+            for i in range(5):
+                rows += _counter_rows(kernels[s], did, {k: 0 for k in counters}, end=99000)
+                did += 1
+            for i in range(reps):
+                rows += _counter_rows(kernels[s], did, counters, end=ends[s])
+                did += 1
         _write_csv(d / "run_counter_collection.csv", header, rows)
         dirs.append(str(d))
     out = tmp_path / "gemm.md"
     monkeypatch.setattr(bench, "GEMM_PMC_FILE", str(out))
     bench.summarize_gemm_pmc(dirs)
     text = out.read_text()
-    assert "(`gemm_mfma_kernel<...>`, 256 workgroups" in text
-    assert "| dispatch duration (profiled) | 35.00 µs |" in text
-    frac = 1048576 * 32 / (35000e-9 * 2.4e9 * 1024)
-    assert f"| MFMA busy / (duration × 2.4 GHz × 1024 SIMDs) | {frac:.3f} |" in text
-    assert "| VALU instructions per MFMA | 7.50 |" in text
-    assert "| MFMA cycles with VALU co-issued (COEXEC / MFMA busy) | 0.500 |" in text
-    assert "| SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES | 0.400 |" in text
-    hbm = 14336 * 1024 * 2 + 16384 * 1024
-    assert f"| HBM bytes (FETCH_SIZE × 2.000 + WRITE_SIZE × 1.000) | {hbm:.4g} " in text
+    assert "| workgroups | 256 of 8 waves | 688 of 4 waves |" in text
+    assert "| dispatch duration (profiled) | 35.00 µs | 90.00 µs |" in text
+    f0 = 1048576 * 32 / (35000e-9 * 2.4e9 * 1024)
+    f1 = 2818048 * 32 / (90000e-9 * 2.4e9 * 1024)
+    assert f"| MFMA busy / (duration × 2.4 GHz × 1024 SIMDs) | {f0:.3f} | {f1:.3f} |" in text
+    assert "| VALU instructions per MFMA | 7.50 | 4.00 |" in text
+    assert "| MFMA cycles with VALU co-issued (COEXEC / MFMA busy) | 0.500 | 0.250 |" in text
+    assert "| LDS bank-conflict cycles per LDS instruction | 0.00 | 0.01 |" in text
+    assert "| SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES | 0.400 | 0.300 |" in text
+    hbm0 = 14336 * 1024 * 2 + 16384 * 1024
+    hbm1 = 30000 * 1024 * 2 + 44032 * 1024
+    assert f"| HBM bytes (FETCH_SIZE × 2.000 + WRITE_SIZE × 1.000) | {hbm0:.4g} " in text
+    assert f"| {hbm1:.4g} (" in text
 
 
 def test_summarize_gemm_pmc_needs_enough_dispatches(tmp_path):
