@@ -12,7 +12,7 @@
 //    of the row up front (consecutive threads, consecutive groups), the absmax
 //    is reduced on the bf16 magnitude bits (an integer max; DPP inside each
 //    wave, LDS across the four), and the row is quantised from registers: one
-//    read of x, 8-byte int8 stores.
+//    read of x, 8-byte int8 stores written through the L2.
 //  * quantize_rows_vec (longer rows, K % 16 == 0): one wave per row, two
 //    passes over the row, the second re-reading it from L2.
 //  * quantize_rows_plain: any K and alignment, one element per lane.
@@ -31,6 +31,12 @@ namespace bitnet {
 namespace {
 
 constexpr int QUANT_ROWS_PER_BLOCK = 4;
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format,
+// stride 0: offsets are checked against the byte count in word 2).
+constexpr int QUANT_BUFFER_RSRC_WORD3 = 0x00020000;
+// Cache policy of the int8 row stores: sc0 | sc1, written through the L2.
+constexpr int QUANT_STORE_WT = 17;
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 // Vector path: K % 16 == 0, x and q 16-byte aligned.
 __global__ __launch_bounds__(256) void quantize_rows_vec(int8_t* __restrict__ q, uint16_t* __restrict__ scale,
@@ -154,11 +160,16 @@ __global__ __launch_bounds__(256) void quantize_rows_block(int8_t* __restrict__ 
     }
     const QuantScale qs = quant_scale(amax);
     if (tid == 0) scale[m] = f32_to_bf16(qs.s);
-    uint2* qv = reinterpret_cast<uint2*>(q + m * K);
+    // 8-byte stores written through the L2 (sc0 sc1) instead of left dirty
+    // there until the kernel ends: measured 5.45 -> 4.62 us for 2048 x 4096
+    // (12.6 -> 11.8 us for 2048 x 11008), the same bits.
+    const __amdgpu_buffer_rsrc_t q_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(q + m * K, (short)0, (int)K, QUANT_BUFFER_RSRC_WORD3);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int g = c * 256 + tid;
-        if (g < groups) qv[g] = quantize_bf16x8(v[c], qs);
+        const uint2 t = quantize_bf16x8(v[c], qs);
+        if (g < groups) __builtin_amdgcn_raw_buffer_store_b64(v2u{t.x, t.y}, q_rsrc, g * 8, 0, QUANT_STORE_WT);
     }
 }
 
