@@ -18,7 +18,10 @@
 //    80 bytes so that the eight sub-lanes of a step hit distinct LDS banks.
 //    Each thread first issues its loads of x, then the weight ring's first D
 //    loads, and only then waits for x to compute the absmax and quantise, so
-//    the weights are in flight during the prologue.
+//    the weights are in flight during the prologue.  Where every wave has a
+//    single short unit (the smaller decode projections), the ring goes out
+//    after the absmax barrier instead, so that no workgroup's weight loads
+//    hold up another's activations.
 //  * Weights.  Work is split into units of 8 output rows; a workgroup owns up
 //    to 32 consecutive units and its 4 waves take them round-robin.  Eight
 //    consecutive lanes share a row and read 8 x 16 B = 128 contiguous bytes of
@@ -272,7 +275,7 @@ __device__ __forceinline__ void dot_piece_padded(const uint4& wv, const uint8_t*
 
 // XF32: x holds f32 activations (quantised as they are, with the f32 absmax),
 // else bf16.  BIAS: bias [N] is added to the bf16 outputs.
-template <int MT, int D, int XW, bool OUT_I32, bool RMS, int KS, bool XF32, bool BIAS>
+template <int MT, int D, int XW, bool OUT_I32, bool RMS, int KS, bool XF32, bool BIAS, bool LATE>
 __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
                                                           uint16_t* __restrict__ sa_out,
                                                           const void* __restrict__ x,
@@ -283,6 +286,7 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
                                                           const uint16_t* __restrict__ bias) {
     static_assert(!(RMS && XF32), "the RMSNorm prologue takes bf16 activations");
     static_assert(!(BIAS && OUT_I32), "the bias applies to the bf16 outputs");
+    static_assert(!(LATE && RMS), "the weight ring goes out after the absmax barrier of the plain prologue");
     constexpr int WAVES = 4;
     constexpr int NT = WAVES * 64;
     extern __shared__ __align__(16) uint8_t lds_x[];  // [MT][steps * 8 segments of GV_SEG bytes]
@@ -369,9 +373,14 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
             set_unit();
         }
     };
+    // The ring goes out now, behind the activation loads, or with LATE once
+    // the workgroup holds its activations (after the absmax barrier).
     uint4 buf[D];
+    auto issue_ring = [&]() {
 #pragma unroll
-    for (int i = 0; i < D; ++i) issue(buf[i]);
+        for (int i = 0; i < D; ++i) issue(buf[i]);
+    };
+    if constexpr (!LATE) issue_ring();
 
     // ---- absmax of every activation row, per wave (of x itself)
     uint32_t am[MT];
@@ -456,6 +465,11 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(uint16_t* __restrict__
         sw_lds[tid] = sw_mine;
         if constexpr (BIAS) bias_lds[tid] = bias_mine;
         __syncthreads();
+    }
+    if constexpr (LATE) {
+        __builtin_amdgcn_sched_barrier(0);  // keep the ring's loads after the barrier
+        issue_ring();
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- scales (every thread), quantise own words into LDS, sum_k q
@@ -846,21 +860,21 @@ __global__ __launch_bounds__(64) void gemv_fused_plain(uint16_t* __restrict__ ou
 // over, never more than there are 4-wave groups of units.
 constexpr int GV_STREAM_MAX_BLOCKS = 512;
 
-template <int MT, int D, bool OUT_I32, bool RMS, int KS, bool XF32, bool BIAS>
+template <int MT, int D, bool OUT_I32, bool RMS, int KS, bool XF32, bool BIAS, bool LATE = false>
 hipError_t launch_stream_xw(int xw, dim3 grid, size_t lds, hipStream_t s, uint16_t* out, int32_t* acc, uint16_t* sa_out,
                             const void* x, const uint8_t* w, const uint16_t* sw, int M, int N, int K, int steps,
                             int units, int upb, const uint16_t* gain, float eps, const uint16_t* bias) {
     if (xw <= 1)
-        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 1, OUT_I32, RMS, KS, XF32, BIAS>), grid, dim3(256), lds, s, out, acc,
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 1, OUT_I32, RMS, KS, XF32, BIAS, LATE>), grid, dim3(256), lds, s, out, acc,
                            sa_out, x, w, sw, M, N, K, steps, units, upb, gain, eps, bias);
     else if (xw <= 2)
-        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 2, OUT_I32, RMS, KS, XF32, BIAS>), grid, dim3(256), lds, s, out, acc,
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 2, OUT_I32, RMS, KS, XF32, BIAS, LATE>), grid, dim3(256), lds, s, out, acc,
                            sa_out, x, w, sw, M, N, K, steps, units, upb, gain, eps, bias);
     else if (xw <= 4)
-        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 4, OUT_I32, RMS, KS, XF32, BIAS>), grid, dim3(256), lds, s, out, acc,
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 4, OUT_I32, RMS, KS, XF32, BIAS, LATE>), grid, dim3(256), lds, s, out, acc,
                            sa_out, x, w, sw, M, N, K, steps, units, upb, gain, eps, bias);
     else
-        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 8, OUT_I32, RMS, KS, XF32, BIAS>), grid, dim3(256), lds, s, out, acc,
+        hipLaunchKernelGGL((gemv_stream_kernel<MT, D, 8, OUT_I32, RMS, KS, XF32, BIAS, LATE>), grid, dim3(256), lds, s, out, acc,
                            sa_out, x, w, sw, M, N, K, steps, units, upb, gain, eps, bias);
     return hipGetLastError();
 }
@@ -891,14 +905,21 @@ hipError_t launch_stream(uint16_t* out, int32_t* acc, uint16_t* sa_out, const vo
     // activation row and a single unit per wave (the smaller decode
     // projections), 4: a deeper ring would only add loads past the wave's few
     // steps, which stall the issue of the prologue behind them (measured on the
-    // BitNet-2B-4T gate_up projection: 5.17 -> 4.83 us).
+    // BitNet-2B-4T gate_up projection: 5.17 -> 4.83 us).  Wherever a wave has
+    // a single unit of at most 8 steps, the ring goes out only after the
+    // absmax barrier, once the workgroup holds its activations: issued ahead
+    // of them, the loads of all workgroups delayed the activations and the
+    // prologue (BitNet-2B-4T projections at M = 2..4: 3-10% faster, e.g.
+    // gate_up M = 2 6.5 -> 5.9 us; M = 1: between even and 10% faster by box;
+    // the LM head, whose ring runs over many units, was 1% slower that way and
+    // keeps the early issue).
     constexpr int D_SHORT = MT >= 8 ? 4 : 8;
     constexpr int D_LONG = MT == 1 ? 16 : D_SHORT;
     const dim3 grid(blocks);
     if constexpr (MT == 1) {
         if (ks == 1 && upb <= groups && steps <= 8)
-            return launch_stream_xw<MT, 4, OUT_I32, RMS, 1, XF32, BIAS>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N,
-                                                                  K, steps, units, upb, gain, eps, bias);
+            return launch_stream_xw<MT, 4, OUT_I32, RMS, 1, XF32, BIAS, !RMS>(xw, grid, lds, s, out, acc, sa_out, x, w, sw,
+                                                                        M, N, K, steps, units, upb, gain, eps, bias);
         if (ks == 4) {
             if (steps / 4 >= 12)
                 return launch_stream_xw<MT, D_LONG, OUT_I32, RMS, 4, XF32, BIAS>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N,
@@ -924,6 +945,9 @@ hipError_t launch_stream(uint16_t* out, int32_t* acc, uint16_t* sa_out, const vo
     // against a ring of 8; 4 and 5 gave 14.4-14.9 us, 3 gave 16.2 us).
     if constexpr (MT == 1)
         return launch_stream_xw<MT, 6, OUT_I32, RMS, 1, XF32, BIAS>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N, K,
+                                                                steps, units, upb, gain, eps, bias);
+    if (upb <= groups && steps <= 8)
+        return launch_stream_xw<MT, D_SHORT, OUT_I32, RMS, 1, XF32, BIAS, !RMS>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N, K,
                                                                 steps, units, upb, gain, eps, bias);
     return launch_stream_xw<MT, D_SHORT, OUT_I32, RMS, 1, XF32, BIAS>(xw, grid, lds, s, out, acc, sa_out, x, w, sw, M, N, K,
                                                                 steps, units, upb, gain, eps, bias);
