@@ -229,6 +229,8 @@ GEMM_SHAPES = [
     # the eight-wave 128 x 256 block (one round of at most 256 blocks): 2, 3, 5 and 9 stages on
     # ragged M and N
     (300, 500, 256), (250, 300, 384), (2000, 3900, 640), (1930, 3850, 1152),
+    # the same block on exactly 256 tiles with ragged edges: 6, 8 and 10 stages
+    (1000, 8000, 768), (2000, 3900, 1024), (1930, 3850, 1280),
 ]
 
 
@@ -279,7 +281,9 @@ def test_gemm_i32_misaligned_plain_path():
                                    # are resident at once, edge tiles in M and N
                                    (1030, 32770, 128), (600, 70000, 256), (1500, 11000, 512), (390, 55700, 768),
                                    # the eight-wave 128 x 256 block: 2 and 9 stages, ragged M and N
-                                   (300, 500, 256), (1930, 3850, 1152)])
+                                   (300, 500, 256), (1930, 3850, 1152),
+                                   # exactly 256 tiles with ragged edges: 6 and 10 stages
+                                   (1000, 8000, 768), (1930, 3850, 1280)])
 def test_gemm_bf16_parity(M, N, K):
     x, W, P, _ = problem(M, N, K, seed=3000 + M)
     sw = synth.row_scales_bf16(N, seed=3100 + M)
