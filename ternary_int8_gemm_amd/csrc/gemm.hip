@@ -324,9 +324,15 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
         bd_voff[d] = (n0 + n) * KB + ((lane & 1) ^ ((lane >> 4) & 1)) * 16;
     }
     // Scales for the epilogue, fetched now so that their latency hides under
-    // the K loop, and parked in LDS until then.
-    const float sa_mine = (!OUT_I32 && tid < BM && m0 + tid < M) ? bf16_to_f32(sa[m0 + tid]) : 0.0f;
-    const float sw_mine = (!OUT_I32 && tid < BN && n0 + tid < N) ? bf16_to_f32(sw[n0 + tid]) : 0.0f;
+    // the K loop, and parked in LDS after it.  The loads are unconditional
+    // (clamped indices) and the values are converted only after the loop: a
+    // load inside a branch, or a use of its value, would make the compiler
+    // wait for it before the operand loads go out.
+    uint16_t sa_bits = 0, sw_bits = 0;
+    if constexpr (!OUT_I32) {
+        sa_bits = sa[min(m0 + tid, M - 1)];
+        sw_bits = sw[min(n0 + tid, N - 1)];
+    }
 
     int rs[A_CH];  // this thread's share of sum_k x over its A rows
 #pragma unroll
@@ -525,8 +531,8 @@ void gemm_mfma_kernel(uint16_t* __restrict__ out, int32_t* __restrict__ acc_out,
         const int v = group8_sum(rs[i]);
         if (ac == 0) rowsum[(tid >> 3) + (S::THREADS / 8) * i] = v;
     }
-    if (tid < BM) rowscale[tid] = sa_mine;
-    if (tid < BN) colscale[tid] = sw_mine;
+    if (tid < BM) rowscale[tid] = (!OUT_I32 && m0 + tid < M) ? bf16_to_f32(sa_bits) : 0.0f;
+    if (tid < BN) colscale[tid] = (!OUT_I32 && n0 + tid < N) ? bf16_to_f32(sw_bits) : 0.0f;
     __syncthreads();
 
     store_tile<MT, NT, OUT_I32>(acc, out, acc_out, M, N, m0 + wm * MT * 32, n0 + wn * NT * 32,
@@ -573,11 +579,16 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(uint16_t* __restri
     const int r = lane & 31, h = lane >> 5;
 
     for (int i = tid; i < BM * LDN; i += THREADS) red[i] = 0;
-    for (int i = tid; i < BM; i += THREADS) {
-        rsum[i] = 0;
-        rscale[i] = (!OUT_I32 && m0 + i < M) ? bf16_to_f32(sa[m0 + i]) : 0.0f;
+    for (int i = tid; i < BM; i += THREADS) rsum[i] = 0;
+    // This thread's row and column scale (THREADS >= BM, BN): loaded now,
+    // unconditionally from clamped indices, and converted and parked in LDS
+    // only after the K loop, so that no wait for them precedes the operand loads.
+    static_assert(THREADS >= BM && THREADS >= BN, "one thread per block row / column fetches its scale");
+    uint16_t sa_bits = 0, sw_bits = 0;
+    if constexpr (!OUT_I32) {
+        sa_bits = sa[min(m0 + tid, M - 1)];
+        sw_bits = sw[min(n0 + tid, N - 1)];
     }
-    for (int i = tid; i < BN; i += THREADS) cscale[i] = (!OUT_I32 && n0 + i < N) ? bf16_to_f32(sw[n0 + i]) : 0.0f;
 
     const __amdgpu_buffer_rsrc_t x_rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(x), (short)0, M * K, BUFFER_RSRC_WORD3);
@@ -658,6 +669,8 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(uint16_t* __restri
         if (j + i < nj) compute(ring[i]);
 
     // ---- split-K reduction in LDS, then the epilogue
+    if (tid < BM) rscale[tid] = (!OUT_I32 && m0 + tid < M) ? bf16_to_f32(sa_bits) : 0.0f;
+    if (tid < BN) cscale[tid] = (!OUT_I32 && n0 + tid < N) ? bf16_to_f32(sw_bits) : 0.0f;
     __syncthreads();  // the tile is zeroed
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -742,7 +755,7 @@ constexpr int GS_KS = 256;            // K elements per chunk
 constexpr int GS_XROW = GS_KS + 16;   // bytes per staged activation row (padded)
 constexpr int GS_WROW = GS_KS / 4 + 16;  // bytes per staged weight row (padded)
 
-template <int MT, int NT, int KW, bool OUT_I32>
+template <int MT, int NT, int KW, int D, bool OUT_I32>
 __global__ __launch_bounds__(64 * KW) void gemm_skinny_lds_kernel(uint16_t* __restrict__ out,
                                                                   int32_t* __restrict__ acc_out,
                                                                   const int8_t* __restrict__ x,
@@ -772,11 +785,16 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_lds_kernel(uint16_t* __re
     const int r = lane & 31, h = lane >> 5;
 
     for (int i = tid; i < BM * LDN; i += THREADS) red[i] = 0;
-    for (int i = tid; i < BM; i += THREADS) {
-        rsum[i] = 0;
-        rscale[i] = (!OUT_I32 && m0 + i < M) ? bf16_to_f32(sa[m0 + i]) : 0.0f;
+    for (int i = tid; i < BM; i += THREADS) rsum[i] = 0;
+    // This thread's row and column scale (THREADS >= BM, BN): loaded now,
+    // unconditionally from clamped indices, and converted and parked in LDS
+    // only after the K loop, so that no wait for them precedes the operand loads.
+    static_assert(THREADS >= BM && THREADS >= BN, "one thread per block row / column fetches its scale");
+    uint16_t sa_bits = 0, sw_bits = 0;
+    if constexpr (!OUT_I32) {
+        sa_bits = sa[min(m0 + tid, M - 1)];
+        sw_bits = sw[min(n0 + tid, N - 1)];
     }
-    for (int i = tid; i < BN; i += THREADS) cscale[i] = (!OUT_I32 && n0 + i < N) ? bf16_to_f32(sw[n0 + i]) : 0.0f;
 
     const __amdgpu_buffer_rsrc_t x_rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(x), (short)0, M * K, BUFFER_RSRC_WORD3);
@@ -792,23 +810,26 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_lds_kernel(uint16_t* __re
 
     constexpr int XI = BM / 4;   // activation load instructions per chunk
     constexpr int WI = BN / 16;  // weight load instructions per chunk
-    v4u xg[XI], wg[WI];
-    auto load = [&](int c) {
-#pragma unroll
-        for (int i = 0; i < XI; ++i)
-            xg[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, (m0 + 4 * i + xr_l) * K + 16 * xp_l, c * GS_KS, 0);
-#pragma unroll
-        for (int i = 0; i < WI; ++i)
-            wg[i] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, (n0 + 16 * i + wr_l) * KB + 16 * wp_l,
-                                                          c * (GS_KS / 4), 0);
+    struct ChunkRegs {
+        v4u xg[XI], wg[WI];
     };
-    auto store = [&]() {
+    ChunkRegs sets[D];  // the loads of D chunks in flight
+    auto load = [&](int c, ChunkRegs& G) {
 #pragma unroll
         for (int i = 0; i < XI; ++i)
-            *reinterpret_cast<v4u*>(xs + (4 * i + xr_l) * GS_XROW + 16 * xp_l) = xg[i];
+            G.xg[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, (m0 + 4 * i + xr_l) * K + 16 * xp_l, c * GS_KS, 0);
 #pragma unroll
         for (int i = 0; i < WI; ++i)
-            *reinterpret_cast<v4u*>(ws + (16 * i + wr_l) * GS_WROW + 16 * wp_l) = wg[i];
+            G.wg[i] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, (n0 + 16 * i + wr_l) * KB + 16 * wp_l,
+                                                            c * (GS_KS / 4), 0);
+    };
+    auto store = [&](const ChunkRegs& G) {
+#pragma unroll
+        for (int i = 0; i < XI; ++i)
+            *reinterpret_cast<v4u*>(xs + (4 * i + xr_l) * GS_XROW + 16 * xp_l) = G.xg[i];
+#pragma unroll
+        for (int i = 0; i < WI; ++i)
+            *reinterpret_cast<v4u*>(ws + (16 * i + wr_l) * GS_WROW + 16 * wp_l) = G.wg[i];
     };
 
     v16i acc[MT][NT];
@@ -852,17 +873,34 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_lds_kernel(uint16_t* __re
         }
     };
 
-    // chunks wave, wave + KW, ...: the next chunk's loads are issued (clamped,
-    // so always in bounds) before the current chunk is multiplied
+    // chunks wave, wave + KW, ...: the loads of the D chunks after the current
+    // one are in flight while it is multiplied; every load is issued (chunk
+    // indices clamped, so always in bounds), which keeps the compiler's waits
+    // exact: storing chunk j waits for its own loads only
     const int nj = (nc - 1 - wave) / KW + 1;  // the host guarantees nc >= KW
-    load(wave);
-    for (int j = 0; j < nj; ++j) {
-        store();  // after the previous chunk's fragment reads (same wave: in order)
-        load(min(wave + KW * (j + 1), nc - 1));
-        compute();
+    auto chunk = [&](int j) { return min(wave + KW * j, nc - 1); };
+#pragma unroll
+    for (int d = 0; d < D; ++d) load(chunk(d), sets[d]);
+    int j = 0;
+    for (; j + D <= nj; j += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            store(sets[d]);  // after the previous chunk's fragment reads (same wave: in order)
+            load(chunk(j + d + D), sets[d]);
+            compute();
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        if (j + d < nj) {
+            store(sets[d]);
+            compute();
+        }
     }
 
     // ---- split-K reduction in LDS, then the epilogue
+    if (tid < BM) rscale[tid] = (!OUT_I32 && m0 + tid < M) ? bf16_to_f32(sa_bits) : 0.0f;
+    if (tid < BN) cscale[tid] = (!OUT_I32 && n0 + tid < N) ? bf16_to_f32(sw_bits) : 0.0f;
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -894,7 +932,8 @@ hipError_t launch_skinny_lds(uint16_t* out, int32_t* acc, const int8_t* x, const
                              const uint16_t* sw, int M, int N, int K, hipStream_t s) {
     const int tiles_m = (M + 32 * MT - 1) / (32 * MT);
     const int tiles_n = (N + 32 * NT - 1) / (32 * NT);
-    hipLaunchKernelGGL((gemm_skinny_lds_kernel<MT, NT, KW, OUT_I32>), dim3((unsigned)(tiles_m * tiles_n)),
+    constexpr int D = 1;  // chunks in flight per wave besides the one being multiplied
+    hipLaunchKernelGGL((gemm_skinny_lds_kernel<MT, NT, KW, D, OUT_I32>), dim3((unsigned)(tiles_m * tiles_n)),
                        dim3(64 * KW), 0, s, out, acc, x, w, sa, sw, M, N, K, tiles_n);
     return hipGetLastError();
 }
