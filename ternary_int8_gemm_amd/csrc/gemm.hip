@@ -605,7 +605,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(uint16_t* __restri
         v4u b[NT];
     };
     auto load = [&](int j, Chunk& C) {
-        const int c = min(wave + KW * j, nc - 1);  // clamped repeats past the end are never multiplied
+        const int c = wave + KW * j;  // only chunks of this wave (j < nj)
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -650,18 +650,20 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_kernel(uint16_t* __restri
         }
     };
 
-    // The ring: every iteration issues the load D chunks ahead unconditionally,
-    // so the compiler's waits stay exact; the last < D chunks are already in.
+    // The ring: each iteration issues the load D chunks ahead, except past the
+    // wave's last chunk (such loads would only delay the split-K barrier); the
+    // last < D chunks are already in.
     const int nj = (nc - 1 - wave) / KW + 1;  // chunks of this wave (the host guarantees nc >= KW)
     Chunk ring[D];
 #pragma unroll
-    for (int i = 0; i < D; ++i) load(i, ring[i]);
+    for (int i = 0; i < D; ++i)
+        if (i < nj) load(i, ring[i]);
     int j = 0;
     for (; j + D <= nj; j += D) {
 #pragma unroll
         for (int i = 0; i < D; ++i) {
             compute(ring[i]);
-            load(j + D + i, ring[i]);
+            if (j + D + i < nj) load(j + D + i, ring[i]);
         }
     }
 #pragma unroll
@@ -874,19 +876,21 @@ __global__ __launch_bounds__(64 * KW) void gemm_skinny_lds_kernel(uint16_t* __re
     };
 
     // chunks wave, wave + KW, ...: the loads of the D chunks after the current
-    // one are in flight while it is multiplied; every load is issued (chunk
-    // indices clamped, so always in bounds), which keeps the compiler's waits
-    // exact: storing chunk j waits for its own loads only
+    // one are in flight while it is multiplied.  Nothing is loaded past the
+    // wave's last chunk: a load issued there would only delay the split-K
+    // barrier below, which waits for every load in flight (measured 3-9%
+    // faster at M = 32..128 than issuing clamped repeats of the last chunk).
     const int nj = (nc - 1 - wave) / KW + 1;  // the host guarantees nc >= KW
-    auto chunk = [&](int j) { return min(wave + KW * j, nc - 1); };
+    auto chunk = [&](int j) { return wave + KW * j; };
 #pragma unroll
-    for (int d = 0; d < D; ++d) load(chunk(d), sets[d]);
+    for (int d = 0; d < D; ++d)
+        if (d < nj) load(chunk(d), sets[d]);
     int j = 0;
     for (; j + D <= nj; j += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             store(sets[d]);  // after the previous chunk's fragment reads (same wave: in order)
-            load(chunk(j + d + D), sets[d]);
+            if (j + d + D < nj) load(chunk(j + d + D), sets[d]);
             compute();
         }
     }
