@@ -280,11 +280,14 @@ __global__ __launch_bounds__(64 * KW) void w8a16_lds_kernel(float* __restrict__ 
         }
     };
 
+    // Nothing is loaded past the wave's last chunk: such a load would only
+    // delay the barrier of the partial-tile sum below, which waits for every
+    // load in flight.
     const int nj = (nc - 1 - wave) / KW + 1;  // the host guarantees nc >= KW
     load(wave);
     for (int j = 0; j < nj; ++j) {
         store();  // after the previous chunk's fragment reads (same wave: in order)
-        load(min(wave + KW * (j + 1), nc - 1));
+        if (j + 1 < nj) load(wave + KW * (j + 1));
         compute();
     }
 
