@@ -18,9 +18,10 @@
  *     synchronises device memory.  Its only state is per device and set once:
  *     a cached architecture check, a flag per GEMM kernel instance recording
  *     that its dynamic LDS limit has been raised (hipFuncSetAttribute), and
- *     the device's static arrays (a small always-cached pad that the decode
- *     GEMV's surplus loads read, and the scratch of bitnet_linear_noalloc with
- *     its device address, looked up on that call's first use of the device).
+ *     the device's static arrays (two small always-cached pads that the
+ *     surplus ring loads of the decode GEMV kernels read, and the scratch of
+ *     bitnet_linear_noalloc with its device address, looked up on that call's
+ *     first use of the device).
  *   - Except bitnet_pack_weights (host memory), every pointer is device memory
  *     and every call is enqueued on `stream` (a hipStream_t; NULL = the null
  *     stream) and returns without waiting.  Faults during execution surface at

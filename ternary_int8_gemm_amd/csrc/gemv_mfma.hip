@@ -52,6 +52,11 @@ constexpr int GQ_PAD = 16;                   // bytes of padding per LDS row (ba
 constexpr int GQ_XG = GQ_ROWS * GQ_KC_MAX / 16 / GQ_THREADS;  // 16-element groups per thread (4)
 constexpr int GQ_RSRC_WORD3 = 0x00020000;    // raw buffer resource, 32-bit data, bounds-checked
 
+// Target of the ring's loads past a wave's last stage (never consumed): one
+// 16-byte piece per lane of a small array that stays in the CU's cache, so the
+// barrier after the last stage does not wait on weight lines for them.
+__device__ __align__(256) uint8_t gq_pad[64 * 16];
+
 // LDS byte offset of 16-element group g of activation row m (row stride kc + GQ_PAD).
 __device__ __forceinline__ int gq_slot(int m, int g, int kc) { return m * (kc + GQ_PAD) + g * 16; }
 
@@ -105,20 +110,22 @@ __global__ __launch_bounds__(GQ_THREADS) void gemv_mfma_kernel(uint16_t* __restr
     const uint16_t sw_lane = (!OUT_I32 && n0 + r < N) ? sw[n0 + r] : (uint16_t)0;
 
     // ---- weight ring: item j of chunk c is stage c * (KC / 128) + kp + KS * j
-    const __amdgpu_buffer_rsrc_t w_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w), (short)0, N * KB, GQ_RSRC_WORD3);
     const int w_voff = (n0 + r) * KB + 16 * h;  // rows past N lie past the buffer's end: zeros
     const int spc = KC / GQ_STAGE;               // stages per chunk
     auto items_of = [&](int c) {
         const int s0 = c * spc, s1 = min(s0 + spc, nst);
         return s1 - s0 > kp ? (s1 - s0 - kp + KS - 1) / KS : 0;
     };
-    // item i of chunk c, clamped to the chunk's last item (clamped loads are
-    // never consumed; they keep every ring load unconditional)
+    // item i of chunk c; items past the wave's last one of the chunk read
+    // gq_pad instead (never consumed: they keep every ring load unconditional,
+    // so the compiler's waits stay exact).  Uniform selects, no branch.
     auto issue = [&](int c, int i, int items) -> v4u {
-        const int ic = min(i, max(items - 1, 0));
-        const int st = min(c * spc + kp + KS * ic, nst - 1);
-        return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_voff, st * (GQ_STAGE / 4), 0));
+        const bool live = i < items;  // wave-uniform
+        const int st = c * spc + kp + KS * (live ? i : 0);
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            live ? const_cast<uint8_t*>(w) : gq_pad, (short)0, live ? N * KB : (int)sizeof(gq_pad), GQ_RSRC_WORD3);
+        return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsrc, live ? w_voff : lane * 16,
+                                                                             live ? st * (GQ_STAGE / 4) : 0, 0));
     };
     v4u buf[D];
     int items = items_of(0);
