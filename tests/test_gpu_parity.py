@@ -410,6 +410,40 @@ def test_linear_leading_dims():
     assert np.array_equal(host_bf16(out).reshape(6, 64), ref["out"])
 
 
+# bitnet_linear captured in a graph (the benchmark's launch mode) on each dispatch path, replayed three
+# times with eager work and a synchronisation in between: every replay must rewrite every output with the
+# oracle's bits.
+GRAPH_LINEAR_SHAPES = [(3, 1000, 1024),     # one-launch fused GEMV (M <= 4)
+                       (8, 3840, 2560),     # fused quantise + matrix-unit product
+                       (16, 2560, 2560),    # quantise + LDS-staged split-K GEMM
+                       (1024, 1536, 1024)]  # quantise + mid-M block tiles
+
+
+@pytest.mark.parametrize("M,N,K", GRAPH_LINEAR_SHAPES)
+def test_linear_graph_replays(M, N, K):
+    x, W, P, sw = problem(M, N, K, seed=7700 + M, outliers=0.01)
+    ref = oracle.linear(x, P, sw)["out"]
+    xd, Pd, swd = dev_bf16(x), dev(P), dev_bf16(sw)
+    od = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty((max(1, tg.linear_workspace_bytes(M, K)),), dtype=torch.uint8, device=DEV)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        tg.bitnet_linear(xd, Pd, swd, out=od, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16(od), ref), f"eager linear {M}x{N}x{K}"
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        tg.bitnet_linear(xd, Pd, swd, out=od, workspace=ws)
+    for rep in range(3):
+        od.fill_(1.0)                                   # a replay must rewrite every output
+        ws.fill_(0xA5)                                  # and must not depend on the workspace's old contents
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bf16(od), ref), f"replay {rep} of linear {M}x{N}x{K}"
+
+
 # ----------------------------------------------------------------------------- epilogue
 
 @pytest.mark.parametrize("M,N", [(3, 8), (5, 7), (64, 1000)])
