@@ -216,6 +216,8 @@ GEMM_SHAPES = [
     # LDS-staged split-K kernel (K % 256 == 0): every configuration, wide and ragged N, ragged M
     (32, 8200, 2048), (33, 300, 2048), (64, 9000, 1024), (100, 8192, 2048), (128, 500, 2048),
     (200, 9001, 2048), (250, 300, 1024), (5, 4096, 768), (77, 2000, 1280),
+    # the same kernel staging only 4, 8 or 16 activation rows (few rows), one and two column tiles
+    (3, 9000, 2048), (7, 9001, 2048), (2, 300, 1024), (6, 333, 2048), (13, 300, 2048), (16, 1000, 1024),
     # mid-sized M (M * N >= 5 * 2^18 with few 128 x 256 tiles): 128 x 256, 128 x 128 and 64 x 128
     # blocks (the LDS-staged shape (200, 9001, 2048) above takes 64 x 128 blocks too); (200, 4000, 2048)
     # keeps the split-K kernel for M > 128 and K >= 2048 covered
