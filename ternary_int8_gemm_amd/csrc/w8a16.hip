@@ -191,7 +191,10 @@ constexpr int WL_KS = 128;                 // K elements per chunk
 constexpr int WL_XROW = WL_KS * 2 + 16;    // bytes per staged activation row (bf16, padded)
 constexpr int WL_WROW = WL_KS + 16;        // bytes per staged weight row (int8, padded)
 
-template <int MT, int NT, int KW>
+// XR: activation rows staged per chunk (a multiple of 4, at most 32 * MT);
+// with XR < 32 * MT (M <= XR, one row tile) the wave zeroes the other rows of
+// its stage once and never loads them.
+template <int MT, int NT, int KW, int XR>
 __global__ __launch_bounds__(64 * KW) void w8a16_lds_kernel(float* __restrict__ y, const uint16_t* __restrict__ x,
                                                             const int8_t* __restrict__ q,
                                                             const float* __restrict__ scale, int M, int N, int K) {
@@ -229,7 +232,13 @@ __global__ __launch_bounds__(64 * KW) void w8a16_lds_kernel(float* __restrict__ 
     uint8_t* const xs = stage[wave];
     uint8_t* const ws = stage[wave] + XB;
 
-    constexpr int XI = BM / 4;
+    static_assert(XR % 4 == 0 && XR <= BM && (XR == BM || MT == 1), "staged rows: whole load instructions of one tile");
+    constexpr int XI = XR / 4;
+    if constexpr (XR < BM) {  // rows XR .. BM-1 of this wave's activation stage stay zero
+        constexpr int ZW = (BM - XR) * WL_XROW / 16;
+        for (int i = lane; i < ZW; i += 64)
+            *reinterpret_cast<v4u*>(xs + XR * WL_XROW + 16 * i) = v4u{0u, 0u, 0u, 0u};
+    }
     constexpr int WI = BN / 8;
     v4u xg[XI], wg[WI];
     auto load = [&](int c) {
@@ -581,6 +590,33 @@ __global__ __launch_bounds__(64) void w8a16_plain(float* __restrict__ y, const u
 
 }  // namespace
 
+// The LDS-staged kernel.  With one row tile and one column tile the activation
+// rows staged are rounded up to 4, 8 or 16 only: measured on the BitNet-2B-4T
+// and LLaMA-7B shapes 8-18% faster at M = 3-4, 2-8% at M = 8, 1-3% at M = 16;
+// with two column tiles (LM heads, wide layers at M >= 16) it was 0.5-4%
+// slower, so those stage all 32 rows.
+template <int MT, int NT, int KW>
+hipError_t launch_w8_lds(dim3 grid, hipStream_t s, float* y, const uint16_t* x, const int8_t* q, const float* scale,
+                         int64_t M, int64_t N, int64_t K) {
+    const dim3 block(64 * KW);
+    if constexpr (MT == 1 && NT == 1) {
+        if (M <= 4) {
+            hipLaunchKernelGGL((w8a16_lds_kernel<1, NT, KW, 4>), grid, block, 0, s, y, x, q, scale, (int)M, (int)N, (int)K);
+            return hipGetLastError();
+        }
+        if (M <= 8) {
+            hipLaunchKernelGGL((w8a16_lds_kernel<1, NT, KW, 8>), grid, block, 0, s, y, x, q, scale, (int)M, (int)N, (int)K);
+            return hipGetLastError();
+        }
+        if (M <= 16) {
+            hipLaunchKernelGGL((w8a16_lds_kernel<1, NT, KW, 16>), grid, block, 0, s, y, x, q, scale, (int)M, (int)N, (int)K);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((w8a16_lds_kernel<MT, NT, KW, 32 * MT>), grid, block, 0, s, y, x, q, scale, (int)M, (int)N, (int)K);
+    return hipGetLastError();
+}
+
 hipError_t launch_w8a16(float* y, const uint16_t* x, const int8_t* q, const float* scale, int64_t M, int64_t N,
                         int64_t K, hipStream_t s) {
     if (M <= 0 || N <= 0) return hipSuccess;
@@ -597,23 +633,12 @@ hipError_t launch_w8a16(float* y, const uint16_t* x, const int8_t* q, const floa
         constexpr int KW8 = 8;
         const dim3 grid2((unsigned)((N + 63) / 64));
         if (N >= W8_LDS_NT2_MIN_N || (M >= 16 && N >= W8_LDS_NT2_MIN_N_M16)) {
-            if (M <= 32)
-                hipLaunchKernelGGL((w8a16_lds_kernel<1, 2, KW>), grid2, block, 0, s, y, x, q, scale, (int)M, (int)N,
-                                   (int)K);
-            else
-                hipLaunchKernelGGL((w8a16_lds_kernel<2, 2, KW>), grid2, block, 0, s, y, x, q, scale, (int)M, (int)N,
-                                   (int)K);
-        } else if (M <= 32 && N <= W8_LDS_KW8_MAX_N && K / WL_KS >= KW8) {
-            hipLaunchKernelGGL((w8a16_lds_kernel<1, 1, KW8>), grid, dim3(64 * KW8), 0, s, y, x, q, scale, (int)M,
-                               (int)N, (int)K);
-        } else if (M <= 32) {
-            hipLaunchKernelGGL((w8a16_lds_kernel<1, 1, KW>), grid, block, 0, s, y, x, q, scale, (int)M, (int)N,
-                               (int)K);
-        } else {
-            hipLaunchKernelGGL((w8a16_lds_kernel<2, 1, KW>), grid, block, 0, s, y, x, q, scale, (int)M, (int)N,
-                               (int)K);
+            if (M <= 32) return launch_w8_lds<1, 2, KW>(grid2, s, y, x, q, scale, M, N, K);
+            return launch_w8_lds<2, 2, KW>(grid2, s, y, x, q, scale, M, N, K);
         }
-        return hipGetLastError();
+        if (M <= 32 && N <= W8_LDS_KW8_MAX_N && K / WL_KS >= KW8) return launch_w8_lds<1, 1, KW8>(grid, s, y, x, q, scale, M, N, K);
+        if (M <= 32) return launch_w8_lds<1, 1, KW>(grid, s, y, x, q, scale, M, N, K);
+        return launch_w8_lds<2, 1, KW>(grid, s, y, x, q, scale, M, N, K);
     }
     if (fits && K % (32 * W8_MFMA_NB) == 0 && K / (32 * W8_MFMA_NB) >= KW) {
         // whole 128-byte weight lines per wave and chunk

@@ -684,7 +684,9 @@ W8A16_EXACT_SHAPES = [(1, 64, 256), (5, 100, 4096), (32, 33, 1024), (33, 4096, 4
                       (1, 13, 2576), (2, 130, 1040), (3, 257, 4096), (4, 9, 4096), (1, 8, 16), (1, 5, 16384),
                       (2, 3, 8192), (4, 1000, 2560),
                       # two column tiles per workgroup on wide layers: ragged N, one and two row tiles
-                      (8, 16400, 512), (40, 16385, 1024), (17, 20000, 384), (3, 16392, 256), (20, 11000, 640)]
+                      (8, 16400, 512), (40, 16385, 1024), (17, 20000, 384), (3, 16392, 256), (20, 11000, 640),
+                      # one column tile staging only 4, 8 or 16 activation rows: ragged N
+                      (3, 1001, 1024), (7, 5000, 1280), (12, 300, 1024), (16, 4097, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", W8A16_EXACT_SHAPES)
