@@ -28,7 +28,9 @@
 //    128-element K stages.  Per stage a lane loads the 16 packed bytes of its
 //    column (lane (n, h): bytes 32 st + 16 h of row n0 + n), which hold its B
 //    operand dwords for the stage's four k-steps; a ring of D stages is kept in
-//    flight from the kernel's start, so the weights stream during the prologue.
+//    flight from the kernel's start, so the weights stream during the prologue
+//    (slots past a wave's last stage read gq_pad, a small array that stays
+//    cached, so that every ring load is still issued).
 //  * v_mfma_i32_32x32x32_i8 with rows 0..M-1 from LDS (lanes of the other rows
 //    feed zeros and read nothing), the codes (1, 2, 3) as B; the accumulator
 //    rows 0..M-1 are the output rows.
